@@ -1,0 +1,218 @@
+"""Python binding of libep.so, the fused GEMM + epilogue library for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels; PyTorch provides device memory and streams.  The API mirrors the stateful
+plan / execute / free sequence of the pages (nvmath-python's Matmul as described in
+"Fusing Matmul Epilogs with nvmath-python" and in the hotdry.top cuBLASLt post):
+
+    p = Plan(x, w, epilog="RELU_AUX_BIAS", epilog_inputs={"bias": b}, b_layout="KN")
+    y, aux = p.execute()          # aux["relu_aux"]: int32 view of the uint32 mask words
+    dp = Plan(dy, w, epilog="DRELU_BGRAD", epilog_inputs={"relu_aux": aux["relu_aux"]},
+              b_layout="NK")
+    dx, aux = dp.execute()        # aux["drelu_bgrad"]: float32 bias gradient
+    p.free(); dp.free()
+
+The library is loaded from this package directory; if it has not been built the import
+of the library fails loudly (there is no fallback).
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["Plan", "EPError", "EPILOGS", "lib", "library_path", "abi_version", "num_tile_cfgs"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libep.so")
+
+EPILOGS = {
+    "DEFAULT": 0, "BIAS": 1, "RELU_BIAS": 2, "RELU_AUX_BIAS": 3,
+    "DRELU_BGRAD": 4, "SWIGLU": 5, "DSWIGLU": 6,
+}
+_LAYOUTS = {"KN": 0, "NK": 1}
+_DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+_PATHS = {"fused": 0, "unfused": 1}
+_BGRAD = {"two_pass": 0, "atomic": 1}
+STATUS = {0: "EP_OK", 1: "EP_ERR_INVALID_ARG", 2: "EP_ERR_UNSUPPORTED", 3: "EP_ERR_OUT_OF_MEMORY",
+          4: "EP_ERR_HIP", 5: "EP_ERR_INTERNAL"}
+
+
+class ep_shape(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("b_layout", ctypes.c_int), ("a", ctypes.c_void_p), ("lda", ctypes.c_int64),
+                ("b", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("d", ctypes.c_void_p),
+                ("ldd", ctypes.c_int64)]
+
+
+class ep_epilog_io(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("relu_aux", ctypes.c_void_p),
+                ("relu_aux_in", ctypes.c_void_p), ("ld_aux", ctypes.c_int64),
+                ("bgrad", ctypes.c_void_p), ("b2", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("up", ctypes.c_void_p), ("ld_gu", ctypes.c_int64), ("d2", ctypes.c_void_p),
+                ("ldd2", ctypes.c_int64)]
+
+
+class ep_options(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("bgrad_mode", ctypes.c_int), ("tile_cfg", ctypes.c_int)]
+
+
+class EPError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libep.so (raises if it is missing: build it first)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is not built; run `python -m dense_gemm_epilogues_amd.build`")
+        L = ctypes.CDLL(library_path)
+        L.ep_plan_ex.argtypes = [ctypes.POINTER(ep_shape), ctypes.c_int, ctypes.c_int,
+                                 ctypes.POINTER(ep_epilog_io), ctypes.POINTER(ep_options),
+                                 ctypes.POINTER(ctypes.c_void_p)]
+        L.ep_plan_ex.restype = ctypes.c_int
+        L.ep_plan.argtypes = [ctypes.POINTER(ep_shape), ctypes.c_int, ctypes.c_int,
+                              ctypes.POINTER(ep_epilog_io), ctypes.POINTER(ctypes.c_void_p)]
+        L.ep_plan.restype = ctypes.c_int
+        L.ep_execute.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.ep_execute.restype = ctypes.c_int
+        L.ep_free.argtypes = [ctypes.c_void_p]
+        L.ep_free.restype = ctypes.c_int
+        L.ep_status_string.argtypes = [ctypes.c_int]
+        L.ep_status_string.restype = ctypes.c_char_p
+        L.ep_last_error.argtypes = []
+        L.ep_last_error.restype = ctypes.c_char_p
+        L.ep_plan_info.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_size_t]
+        L.ep_plan_info.restype = ctypes.c_int
+        L.ep_abi_version.argtypes = []
+        L.ep_abi_version.restype = ctypes.c_int
+        L.ep_num_tile_cfgs.argtypes = []
+        L.ep_num_tile_cfgs.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def abi_version():
+    return lib().ep_abi_version()
+
+
+def num_tile_cfgs():
+    return lib().ep_num_tile_cfgs()
+
+
+def _check(status):
+    if status != 0:
+        raise EPError(status, lib().ep_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("operands must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """A planned fused GEMM + epilog (the C library's ep_handle).
+
+    a: M x K.  b: K x N (b_layout "KN") or N x K ("NK").  epilog_inputs:
+      BIAS / RELU_BIAS / RELU_AUX_BIAS: {"bias": (N,)}
+      DRELU_BGRAD: {"relu_aux": (M, >= ceil(N/32)) int32 mask words}
+      SWIGLU: {"b2": up weight, same layout as b}
+      DSWIGLU: {"gate": (M, N), "up": (M, N)}
+    Outputs are allocated here with torch.empty unless `out` / `aux_out` are given and are
+    reused by every execute().  Tensors are kept alive for the plan's lifetime.
+    """
+
+    def __init__(self, a, b, epilog="DEFAULT", epilog_inputs=None, b_layout="KN", out=None,
+                 aux_out=None, path="fused", bgrad_mode="two_pass", tile_cfg=-1):
+        L = lib()
+        epilog_inputs = dict(epilog_inputs or {})
+        aux_out = dict(aux_out or {})
+        if epilog not in EPILOGS:
+            raise ValueError(f"unknown epilog {epilog!r}")
+        if a.dtype not in _DTYPES or b.dtype != a.dtype:
+            raise ValueError("a and b must both be float16 or both bfloat16")
+        m, k = a.shape
+        n = b.shape[1] if b_layout == "KN" else b.shape[0]
+        if out is None:
+            out = torch.empty((m, n), dtype=a.dtype, device=a.device)
+        self.epilog = epilog
+        self.out = out
+        self.aux = {}
+        io = ep_epilog_io()
+        if epilog in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS"):
+            io.bias = _ptr(epilog_inputs["bias"])
+        if epilog == "RELU_AUX_BIAS":
+            ra = aux_out.get("relu_aux")
+            if ra is None:
+                ra = torch.empty((m, (n + 31) // 32), dtype=torch.int32, device=a.device)
+            io.relu_aux = _ptr(ra)
+            io.ld_aux = ra.stride(0)
+            self.aux["relu_aux"] = ra
+        if epilog == "DRELU_BGRAD":
+            ri = epilog_inputs["relu_aux"]
+            io.relu_aux_in = _ptr(ri)
+            io.ld_aux = ri.stride(0)
+            bg = aux_out.get("drelu_bgrad")
+            if bg is None:
+                bg = torch.empty((n,), dtype=torch.float32, device=a.device)
+            io.bgrad = _ptr(bg)
+            self.aux["drelu_bgrad"] = bg
+        if epilog == "SWIGLU":
+            io.b2 = _ptr(epilog_inputs["b2"])
+        if epilog == "DSWIGLU":
+            g, u = epilog_inputs["gate"], epilog_inputs["up"]
+            if g.stride(0) != u.stride(0):
+                raise ValueError("gate and up must share a row stride")
+            io.gate, io.up, io.ld_gu = _ptr(g), _ptr(u), g.stride(0)
+            d2 = aux_out.get("d_up")
+            if d2 is None:
+                d2 = torch.empty_like(out)
+            io.d2, io.ldd2 = _ptr(d2), d2.stride(0)
+            self.aux["d_up"] = d2
+        shape = ep_shape(m=m, n=n, k=k, b_layout=_LAYOUTS[b_layout], a=_ptr(a), lda=_ld(a),
+                         b=_ptr(b), ldb=_ld(b), d=_ptr(out), ldd=_ld(out))
+        opt = ep_options(path=_PATHS[path], bgrad_mode=_BGRAD[bgrad_mode], tile_cfg=tile_cfg)
+        handle = ctypes.c_void_p()
+        self._keep = (a, b, out, epilog_inputs, dict(self.aux))
+        _check(L.ep_plan_ex(ctypes.byref(shape), _DTYPES[a.dtype], EPILOGS[epilog], ctypes.byref(io),
+                            ctypes.byref(opt), ctypes.byref(handle)))
+        self._h = handle
+
+    def execute(self, stream=None):
+        """Enqueue on `stream` (default: torch's current stream); returns (out, aux)."""
+        if self._h is None:
+            raise RuntimeError("plan has been freed")
+        _check(lib().ep_execute(self._h, _stream_handle(stream)))
+        return self.out, self.aux
+
+    def info(self):
+        buf = ctypes.create_string_buffer(1024)
+        _check(lib().ep_plan_info(self._h, buf, len(buf)))
+        return buf.value.decode()
+
+    def free(self):
+        if getattr(self, "_h", None) is not None:
+            _check(lib().ep_free(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

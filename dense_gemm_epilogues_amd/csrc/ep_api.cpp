@@ -1,0 +1,484 @@
+// C ABI of the fused GEMM + epilogue library: validation, planning, workspace ownership,
+// dispatch.  The plan/execute/free split follows the stateful Matmul object described in
+// "Fusing Matmul Epilogs with nvmath-python" ("The problem addressed by fused epilogs")
+// and the hotdry.top cuBLASLt post (paragraphs 3-6): planning validates, chooses a
+// configuration and allocates once; execution only enqueues kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "ep.h"
+#include "ep_internal.hpp"
+
+namespace ep {
+
+const TileCfg kTileCfgs[kNumTileCfgs] = {
+    {256, 256, 131072, 1, "256x256x64"},
+    {128, 128, 65536, 2, "128x128x64"},
+    {256, 128, 98304, 1, "256x128x64"},
+    {128, 256, 98304, 1, "128x256x64"},
+};
+
+#define EP_DECL_TABLE(dt, lay, epi) extern const GemmLauncher kLaunch_##dt##_##lay##_##epi[kNumTileCfgs];
+#define EP_DECL_EPIS(dt, lay)                                                                    \
+  EP_DECL_TABLE(dt, lay, 0) EP_DECL_TABLE(dt, lay, 1) EP_DECL_TABLE(dt, lay, 2)                  \
+  EP_DECL_TABLE(dt, lay, 3) EP_DECL_TABLE(dt, lay, 4) EP_DECL_TABLE(dt, lay, 5) EP_DECL_TABLE(dt, lay, 6)
+EP_DECL_EPIS(0, 0)
+EP_DECL_EPIS(0, 1)
+EP_DECL_EPIS(1, 0)
+EP_DECL_EPIS(1, 1)
+
+#define EP_ROW(dt, lay)                                                                          \
+  {                                                                                              \
+    kLaunch_##dt##_##lay##_0, kLaunch_##dt##_##lay##_1, kLaunch_##dt##_##lay##_2,                \
+        kLaunch_##dt##_##lay##_3, kLaunch_##dt##_##lay##_4, kLaunch_##dt##_##lay##_5,            \
+        kLaunch_##dt##_##lay##_6                                                                 \
+  }
+static const GemmLauncher* const kTables[2][2][E_NUM] = {{EP_ROW(0, 0), EP_ROW(0, 1)},
+                                                         {EP_ROW(1, 0), EP_ROW(1, 1)}};
+
+GemmLauncher gemm_launcher(int dtype, int layout, int epi, int cfg) {
+  if (dtype < 0 || dtype > 1 || layout < 0 || layout > 1 || epi < 0 || epi >= E_NUM || cfg < 0 ||
+      cfg >= kNumTileCfgs)
+    return nullptr;
+  return kTables[dtype][layout][epi][cfg];
+}
+
+static const char* kEpiNames[E_NUM] = {"DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS",
+                                       "DRELU_BGRAD", "SWIGLU", "DSWIGLU"};
+
+}  // namespace ep
+
+using namespace ep;
+
+namespace {
+
+constexpr uint64_t kMagic = 0x6570706c616e3031ULL;  // "epplan01"
+constexpr uint64_t kDead = 0xdeadbeefdeadbeefULL;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxLd = (int64_t)1 << 22;
+
+thread_local std::string t_last_error;
+
+ep_status fail(ep_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  t_last_error = buf;
+  return s;
+}
+
+struct UnfusedBufs {
+  void* z = nullptr;   // GEMM result (DEFAULT epilog) in the element type
+  void* z2 = nullptr;  // second GEMM result (SwiGLU up branch)
+  int64_t ldz = 0;
+};
+
+}  // namespace
+
+struct ep_plan_s {
+  uint64_t magic;
+  ep_shape shape;
+  ep_dtype dtype;
+  ep_epilog epilog;
+  ep_epilog_io io;
+  ep_options opt;
+  int device;
+  int cfg;
+  GemmArgs args;       // fused launch (or the DEFAULT GEMM of the unfused path)
+  GemmArgs args2;      // unfused SwiGLU: the up-branch GEMM
+  GemmLauncher launch;
+  void* workspace;     // single allocation owned by the plan
+  size_t workspace_bytes;
+  float* part;         // bgrad partials (two-pass)
+  int nparts;
+  UnfusedBufs uf;
+  int colsum_rows;     // unfused colsum rows per partial block
+};
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int choose_cfg(int64_t m, int64_t n, bool dual, int cus) {
+  // Estimated time ~ rounds of resident tiles x work per tile / relative efficiency.
+  static const double kEff[kNumTileCfgs] = {1.0, 0.80, 0.92, 0.92};
+  int best = 0;
+  double best_t = 1e300;
+  for (int c = 0; c < kNumTileCfgs; ++c) {
+    const int64_t bn = dual ? kTileCfgs[c].bnt / 2 : kTileCfgs[c].bnt;
+    const int64_t tiles = ((m + kTileCfgs[c].bm - 1) / kTileCfgs[c].bm) * ((n + bn - 1) / bn);
+    const int64_t slots = (int64_t)cus * kTileCfgs[c].wgs_per_cu;
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    const double t = (double)rounds * (double)(kTileCfgs[c].bm * bn) * kTileCfgs[c].wgs_per_cu / kEff[c];
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best = c;
+    }
+  }
+  return best;
+}
+
+ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io,
+                   const ep_options* opt) {
+  if (!s) return fail(EP_ERR_INVALID_ARG, "shape is NULL");
+  if (!io) return fail(EP_ERR_INVALID_ARG, "epilog_io is NULL");
+  if (dtype != EP_F16 && dtype != EP_BF16) return fail(EP_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if ((int)epi < 0 || (int)epi >= E_NUM) return fail(EP_ERR_UNSUPPORTED, "unknown epilog %d", (int)epi);
+  if (s->b_layout != EP_B_KN && s->b_layout != EP_B_NK)
+    return fail(EP_ERR_UNSUPPORTED, "unknown B layout %d", (int)s->b_layout);
+  if (s->m < 1 || s->n < 1 || s->k < 1) return fail(EP_ERR_INVALID_ARG, "m, n, k must be >= 1");
+  if (s->m >= kMaxDim || s->n >= kMaxDim || s->k >= kMaxDim)
+    return fail(EP_ERR_UNSUPPORTED, "m, n, k must be < 2^31");
+  if (s->n % 8 || s->k % 8) return fail(EP_ERR_UNSUPPORTED, "n and k must be multiples of 8");
+  if (opt) {
+    if (opt->path != EP_PATH_FUSED && opt->path != EP_PATH_UNFUSED)
+      return fail(EP_ERR_INVALID_ARG, "unknown path %d", (int)opt->path);
+    if (opt->bgrad_mode != EP_BGRAD_TWO_PASS && opt->bgrad_mode != EP_BGRAD_ATOMIC)
+      return fail(EP_ERR_INVALID_ARG, "unknown bgrad mode %d", (int)opt->bgrad_mode);
+    if (opt->tile_cfg < -1 || opt->tile_cfg >= kNumTileCfgs)
+      return fail(EP_ERR_INVALID_ARG, "tile_cfg %d out of range", opt->tile_cfg);
+  }
+  // operand pointers
+  if (!s->a || !s->b || !s->d) return fail(EP_ERR_INVALID_ARG, "a, b and d must be non-NULL");
+  if (!aligned(s->a, 16) || !aligned(s->b, 16) || !aligned(s->d, 16))
+    return fail(EP_ERR_INVALID_ARG, "a, b and d must be 16-byte aligned");
+  const int64_t brow = s->b_layout == EP_B_KN ? s->n : s->k;
+  if (s->lda < s->k || s->lda % 8 || s->lda >= kMaxLd)
+    return fail(EP_ERR_INVALID_ARG, "lda must be a multiple of 8 in [k, 2^22)");
+  if (s->ldb < brow || s->ldb % 8 || s->ldb >= kMaxLd)
+    return fail(EP_ERR_INVALID_ARG, "ldb must be a multiple of 8 in [row length, 2^22)");
+  if (s->ldd < s->n || s->ldd % 8 || s->ldd >= kMaxLd)
+    return fail(EP_ERR_INVALID_ARG, "ldd must be a multiple of 8 in [n, 2^22)");
+
+  const bool wants_bias = epi == EP_EPILOG_BIAS || epi == EP_EPILOG_RELU_BIAS || epi == EP_EPILOG_RELU_AUX_BIAS;
+  const bool wants_aux_out = epi == EP_EPILOG_RELU_AUX_BIAS;
+  const bool wants_aux_in = epi == EP_EPILOG_DRELU_BGRAD;
+  const bool wants_b2 = epi == EP_EPILOG_SWIGLU;
+  const bool wants_gu = epi == EP_EPILOG_DSWIGLU;
+  if (wants_bias != (io->bias != nullptr))
+    return fail(EP_ERR_INVALID_ARG, wants_bias ? "bias is required" : "bias must be NULL for this epilog");
+  if (wants_aux_out != (io->relu_aux != nullptr))
+    return fail(EP_ERR_INVALID_ARG, wants_aux_out ? "relu_aux output is required" : "relu_aux must be NULL");
+  if (wants_aux_in != (io->relu_aux_in != nullptr))
+    return fail(EP_ERR_INVALID_ARG, wants_aux_in ? "relu_aux_in is required" : "relu_aux_in must be NULL");
+  if (wants_aux_in != (io->bgrad != nullptr))
+    return fail(EP_ERR_INVALID_ARG, wants_aux_in ? "bgrad output is required" : "bgrad must be NULL");
+  if (wants_b2 != (io->b2 != nullptr))
+    return fail(EP_ERR_INVALID_ARG, wants_b2 ? "b2 (up weight) is required" : "b2 must be NULL");
+  if (wants_gu != (io->gate != nullptr) || wants_gu != (io->up != nullptr) || wants_gu != (io->d2 != nullptr))
+    return fail(EP_ERR_INVALID_ARG, wants_gu ? "gate, up and d2 are required" : "gate, up, d2 must be NULL");
+  if (wants_bias && !aligned(io->bias, 16)) return fail(EP_ERR_INVALID_ARG, "bias must be 16-byte aligned");
+  if (wants_b2 && !aligned(io->b2, 16)) return fail(EP_ERR_INVALID_ARG, "b2 must be 16-byte aligned");
+  if (wants_gu && (!aligned(io->gate, 16) || !aligned(io->up, 16) || !aligned(io->d2, 16)))
+    return fail(EP_ERR_INVALID_ARG, "gate, up and d2 must be 16-byte aligned");
+  if ((wants_aux_out && !aligned(io->relu_aux, 4)) || (wants_aux_in && !aligned(io->relu_aux_in, 4)) ||
+      (wants_aux_in && !aligned(io->bgrad, 16)))
+    return fail(EP_ERR_INVALID_ARG, "relu_aux must be 4-byte and bgrad 16-byte aligned");
+  if (wants_aux_out || wants_aux_in) {
+    const int64_t nw = (s->n + 31) / 32;
+    const int64_t ld = io->ld_aux == 0 ? nw : io->ld_aux;
+    if (ld < nw || ld >= kMaxLd) return fail(EP_ERR_INVALID_ARG, "ld_aux must be >= ceil(n/32)");
+  } else if (io->ld_aux != 0) {
+    return fail(EP_ERR_INVALID_ARG, "ld_aux must be 0 for this epilog");
+  }
+  if (wants_gu) {
+    const int64_t ldgu = io->ld_gu == 0 ? s->n : io->ld_gu;
+    const int64_t ldd2 = io->ldd2 == 0 ? s->ldd : io->ldd2;
+    if (ldgu < s->n || ldgu % 8 || ldgu >= kMaxLd) return fail(EP_ERR_INVALID_ARG, "ld_gu must be a multiple of 8 in [n, 2^22)");
+    if (ldd2 < s->n || ldd2 % 8 || ldd2 >= kMaxLd) return fail(EP_ERR_INVALID_ARG, "ldd2 must be a multiple of 8 in [n, 2^22)");
+  } else if (io->ld_gu != 0 || io->ldd2 != 0) {
+    return fail(EP_ERR_INVALID_ARG, "ld_gu and ldd2 must be 0 for this epilog");
+  }
+  if (opt && opt->bgrad_mode == EP_BGRAD_ATOMIC && opt->path == EP_PATH_UNFUSED)
+    return fail(EP_ERR_UNSUPPORTED, "the unfused path uses the two-pass bias-gradient reduction only");
+  return EP_OK;
+}
+
+GemmArgs base_args(const ep_shape* s, int cfg, bool dual) {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  a.a = s->a;
+  a.b = s->b;
+  a.d = s->d;
+  a.lda = s->lda;
+  a.ldb = s->ldb;
+  a.ldd = s->ldd;
+  a.M = (int)s->m;
+  a.N = (int)s->n;
+  a.K = (int)s->k;
+  const int bm = kTileCfgs[cfg].bm;
+  const int bn = dual ? kTileCfgs[cfg].bnt / 2 : kTileCfgs[cfg].bnt;
+  a.tiles_m = (int)((s->m + bm - 1) / bm);
+  a.tiles_n = (int)((s->n + bn - 1) / bn);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_abi_version(void) { return EP_ABI_VERSION; }
+
+int ep_num_tile_cfgs(void) { return kNumTileCfgs; }
+
+const char* ep_status_string(ep_status s) {
+  switch (s) {
+    case EP_OK: return "EP_OK";
+    case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
+    case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED";
+    case EP_ERR_OUT_OF_MEMORY: return "EP_ERR_OUT_OF_MEMORY";
+    case EP_ERR_HIP: return "EP_ERR_HIP";
+    case EP_ERR_INTERNAL: return "EP_ERR_INTERNAL";
+  }
+  return "EP_ERR_UNKNOWN";
+}
+
+const char* ep_last_error(void) { return t_last_error.c_str(); }
+
+ep_status ep_plan(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog, const ep_epilog_io* io, ep_handle* out) {
+  return ep_plan_ex(shape, dtype, epilog, io, nullptr, out);
+}
+
+ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io,
+                     const ep_options* opt_in, ep_handle* out) {
+  t_last_error.clear();
+  if (!out) return fail(EP_ERR_INVALID_ARG, "out handle pointer is NULL");
+  *out = nullptr;
+  ep_status st = validate(s, dtype, epi, io, opt_in);
+  if (st != EP_OK) return st;
+  ep_options opt = opt_in ? *opt_in : ep_options{EP_PATH_FUSED, EP_BGRAD_TWO_PASS, -1};
+
+  // ---- first HIP call: the device must exist and be usable
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return fail(EP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(he));
+  hipDeviceProp_t prop;
+  he = hipGetDeviceProperties(&prop, dev);
+  if (he != hipSuccess) return fail(EP_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(he));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(EP_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+
+  const bool dual = epi == EP_EPILOG_SWIGLU;
+  const bool unfused = opt.path == EP_PATH_UNFUSED;
+  // the unfused path runs plain DEFAULT GEMMs (single-B) into intermediates
+  const bool kernel_dual = dual && !unfused;
+  const int cfg = opt.tile_cfg >= 0 ? opt.tile_cfg : choose_cfg(s->m, s->n, kernel_dual, prop.multiProcessorCount);
+
+  ep_plan_s* h = new (std::nothrow) ep_plan_s;
+  if (!h) return fail(EP_ERR_OUT_OF_MEMORY, "host allocation failed");
+  memset(h, 0, sizeof *h);
+  h->magic = kMagic;
+  h->shape = *s;
+  h->dtype = dtype;
+  h->epilog = epi;
+  h->io = *io;
+  if (h->io.ld_aux == 0) h->io.ld_aux = (s->n + 31) / 32;
+  if (h->io.ld_gu == 0) h->io.ld_gu = s->n;
+  if (h->io.ldd2 == 0) h->io.ldd2 = s->ldd;
+  h->opt = opt;
+  h->device = dev;
+  h->cfg = cfg;
+
+  GemmArgs a = base_args(s, cfg, kernel_dual);
+  const int fused_epi = unfused ? (int)E_DEFAULT : (int)epi;
+  h->launch = gemm_launcher((int)dtype, (int)s->b_layout, fused_epi, cfg);
+  if (!h->launch) {
+    delete h;
+    return fail(EP_ERR_INTERNAL, "no kernel instantiated for this combination");
+  }
+
+  // ---- workspace sizing
+  const int64_t M = s->m, N = s->n;
+  size_t part_bytes = 0, z_bytes = 0, z2_bytes = 0;
+  if (epi == EP_EPILOG_DRELU_BGRAD) {
+    if (unfused) {
+      h->colsum_rows = 256;
+      h->nparts = (int)((M + h->colsum_rows - 1) / h->colsum_rows);
+      part_bytes = (size_t)h->nparts * N * sizeof(float);
+    } else if (opt.bgrad_mode == EP_BGRAD_TWO_PASS) {
+      h->nparts = a.tiles_m;
+      part_bytes = (size_t)h->nparts * N * sizeof(float);
+    }
+  }
+  if (unfused && dual) {
+    // the two branch GEMMs of the unfused SwiGLU need intermediates; every other unfused
+    // sequence runs its elementwise passes in place on the output
+    z_bytes = (size_t)M * N * 2;
+    z2_bytes = z_bytes;
+  }
+  auto round_up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  h->workspace_bytes = round_up(part_bytes) + round_up(z_bytes) + round_up(z2_bytes);
+  if (h->workspace_bytes) {
+    he = hipMalloc(&h->workspace, h->workspace_bytes);
+    if (he != hipSuccess) {
+      const size_t bytes = h->workspace_bytes;
+      delete h;
+      (void)hipGetLastError();
+      return fail(EP_ERR_OUT_OF_MEMORY, "hipMalloc(%zu): %s", bytes, hipGetErrorString(he));
+    }
+    char* w = (char*)h->workspace;
+    if (part_bytes) { h->part = (float*)w; w += round_up(part_bytes); }
+    if (z_bytes) { h->uf.z = w; w += round_up(z_bytes); }
+    if (z2_bytes) { h->uf.z2 = w; }
+    h->uf.ldz = N;
+  }
+
+  // ---- kernel arguments
+  if (!unfused) {
+    a.bias = io->bias;
+    a.aux_out = io->relu_aux;
+    a.aux_in = io->relu_aux_in;
+    a.ld_aux = h->io.ld_aux;
+    a.b2 = io->b2;
+    a.gate = io->gate;
+    a.up = io->up;
+    a.ld_gu = h->io.ld_gu;
+    a.d2 = io->d2;
+    a.ldd2 = h->io.ldd2;
+    if (epi == EP_EPILOG_DRELU_BGRAD) {
+      a.bgrad_atomic = opt.bgrad_mode == EP_BGRAD_ATOMIC;
+      a.bgrad_part = a.bgrad_atomic ? io->bgrad : h->part;
+    }
+    h->args = a;
+  } else {
+    // unfused: the GEMM writes its DEFAULT result straight to d (or, for SwiGLU, to the
+    // two branch intermediates)
+    if (dual) {
+      a.d = h->uf.z;
+      a.ldd = h->uf.ldz;
+    }
+    h->args = a;
+    if (dual) {
+      GemmArgs a2 = a;
+      a2.b = io->b2;
+      a2.d = h->uf.z2;
+      h->args2 = a2;
+    }
+  }
+  if (getenv("EP_LOG")) {
+    fprintf(stderr, "[ep] plan m=%lld n=%lld k=%lld %s %s %s cfg=%s tiles=%dx%d ws=%zu\n", (long long)M,
+            (long long)N, (long long)s->k, dtype == EP_F16 ? "f16" : "bf16", s->b_layout == EP_B_KN ? "KN" : "NK",
+            kEpiNames[epi], kTileCfgs[cfg].name, a.tiles_m, a.tiles_n, h->workspace_bytes);
+  }
+  *out = h;
+  return EP_OK;
+}
+
+static ep_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return EP_OK;
+}
+
+ep_status ep_execute(ep_handle h, void* stream) {
+  if (!h || h->magic != kMagic) return fail(EP_ERR_INVALID_ARG, "invalid or freed handle");
+  hipStream_t s = (hipStream_t)stream;
+  const ep_shape& sh = h->shape;
+  const int dt = (int)h->dtype;
+  const int M = (int)sh.m, N = (int)sh.n;
+  ep_status st;
+  if (h->opt.path == EP_PATH_FUSED) {
+    if (h->epilog == EP_EPILOG_DRELU_BGRAD && h->opt.bgrad_mode == EP_BGRAD_ATOMIC) {
+      if (launch_fill_zero_f32(h->io.bgrad, N, s) != hipSuccess) return check_launch("fill_zero");
+    }
+    h->launch(h->args, s);
+    if ((st = check_launch("fused gemm")) != EP_OK) return st;
+    if (h->epilog == EP_EPILOG_DRELU_BGRAD && h->opt.bgrad_mode == EP_BGRAD_TWO_PASS) {
+      launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s);
+      if ((st = check_launch("bgrad_reduce")) != EP_OK) return st;
+    }
+    return EP_OK;
+  }
+  // ---- unfused baseline: DEFAULT GEMM(s) then separate kernels through HBM, in place on d
+  h->launch(h->args, s);
+  if ((st = check_launch("gemm")) != EP_OK) return st;
+  switch (h->epilog) {
+    case EP_EPILOG_DEFAULT:
+      break;
+    case EP_EPILOG_BIAS:
+      launch_bias_add(dt, sh.d, sh.ldd, h->io.bias, M, N, s);
+      break;
+    case EP_EPILOG_RELU_BIAS:
+    case EP_EPILOG_RELU_AUX_BIAS:
+      launch_bias_add(dt, sh.d, sh.ldd, h->io.bias, M, N, s);
+      if ((st = check_launch("bias_add")) != EP_OK) return st;
+      launch_relu_pack(dt, sh.d, sh.ldd, sh.d, sh.ldd, h->io.relu_aux, h->io.ld_aux, M, N,
+                       h->epilog == EP_EPILOG_RELU_AUX_BIAS, s);
+      break;
+    case EP_EPILOG_DRELU_BGRAD:
+      launch_mask_apply(dt, sh.d, sh.ldd, h->io.relu_aux_in, h->io.ld_aux, sh.d, sh.ldd, M, N, s);
+      if ((st = check_launch("mask_apply")) != EP_OK) return st;
+      launch_colsum_partial(dt, sh.d, sh.ldd, h->part, M, N, h->colsum_rows, s);
+      if ((st = check_launch("colsum")) != EP_OK) return st;
+      launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s);
+      break;
+    case EP_EPILOG_SWIGLU:
+      h->launch(h->args2, s);
+      if ((st = check_launch("gemm up")) != EP_OK) return st;
+      launch_silu_mul(dt, h->uf.z, h->uf.z2, h->uf.ldz, sh.d, sh.ldd, M, N, s);
+      break;
+    case EP_EPILOG_DSWIGLU:
+      launch_dswiglu(dt, sh.d, sh.ldd, h->io.gate, h->io.up, h->io.ld_gu, sh.d, sh.ldd, h->io.d2, h->io.ldd2, M,
+                     N, s);
+      break;
+  }
+  return check_launch("unfused epilogue");
+}
+
+ep_status ep_free(ep_handle h) {
+  if (!h) return EP_OK;
+  if (h->magic != kMagic) return fail(EP_ERR_INVALID_ARG, "invalid or already freed handle");
+  h->magic = kDead;
+  if (h->workspace) {
+    hipError_t e = hipFree(h->workspace);
+    h->workspace = nullptr;
+    delete h;
+    if (e != hipSuccess) return fail(EP_ERR_HIP, "hipFree: %s", hipGetErrorString(e));
+    return EP_OK;
+  }
+  delete h;
+  return EP_OK;
+}
+
+ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
+  if (!h || h->magic != kMagic) return fail(EP_ERR_INVALID_ARG, "invalid or freed handle");
+  if (!buf || n == 0) return fail(EP_ERR_INVALID_ARG, "buffer is NULL or empty");
+  const ep_shape& s = h->shape;
+  const char* dt = h->dtype == EP_F16 ? "f16" : "bf16";
+  const char* lay = s.b_layout == EP_B_KN ? "KN" : "NK";
+  std::string kern = std::string("gemm_kernel<") + dt + "," + lay + "," +
+                     (h->opt.path == EP_PATH_FUSED ? kEpiNames[h->epilog] : "DEFAULT") + "," +
+                     kTileCfgs[h->cfg].name + ">";
+  std::string extra;
+  if (h->opt.path == EP_PATH_FUSED) {
+    if (h->epilog == EP_EPILOG_DRELU_BGRAD)
+      extra = h->opt.bgrad_mode == EP_BGRAD_TWO_PASS ? " + bgrad_reduce" : " (after fill_zero; atomic bgrad)";
+  } else {
+    switch (h->epilog) {
+      case EP_EPILOG_BIAS: extra = " + bias_add"; break;
+      case EP_EPILOG_RELU_BIAS: extra = " + bias_add + relu"; break;
+      case EP_EPILOG_RELU_AUX_BIAS: extra = " + bias_add + relu_pack"; break;
+      case EP_EPILOG_DRELU_BGRAD: extra = " + mask_apply + colsum + bgrad_reduce"; break;
+      case EP_EPILOG_SWIGLU: extra = " x2 + silu_mul"; break;
+      case EP_EPILOG_DSWIGLU: extra = " + dswiglu"; break;
+      default: break;
+    }
+  }
+  snprintf(buf, n,
+           "epilog=%s path=%s dtype=%s layout=%s m=%lld n=%lld k=%lld tile=%s tile_cfg=%d grid=%dx%d "
+           "workspace_bytes=%zu kernels=%s%s",
+           kEpiNames[h->epilog], h->opt.path == EP_PATH_FUSED ? "fused" : "unfused", dt, lay, (long long)s.m,
+           (long long)s.n, (long long)s.k, kTileCfgs[h->cfg].name, h->cfg, h->args.tiles_m, h->args.tiles_n,
+           h->workspace_bytes, kern.c_str(), extra.c_str());
+  return EP_OK;
+}
+
+}  // extern "C"

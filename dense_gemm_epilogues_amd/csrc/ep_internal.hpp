@@ -1,0 +1,77 @@
+// Internal interface between the C ABI layer (ep_api.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+enum Epi : int {
+  E_DEFAULT = 0,
+  E_BIAS = 1,
+  E_RELU_BIAS = 2,
+  E_RELU_AUX_BIAS = 3,
+  E_DRELU_BGRAD = 4,
+  E_SWIGLU = 5,
+  E_DSWIGLU = 6,
+  E_NUM = 7
+};
+
+enum Layout : int { L_KN = 0, L_NK = 1 };
+enum DType : int { T_F16 = 0, T_BF16 = 1 };
+
+// Everything a GEMM launch needs; passed by value as the kernel argument.
+struct GemmArgs {
+  const void* a;
+  const void* b;
+  const void* b2;       // SWIGLU up weight
+  void* d;
+  int64_t lda, ldb, ldd;
+  int M, N, K;          // N = output columns
+  int tiles_m, tiles_n;
+  const void* bias;
+  uint32_t* aux_out;
+  const uint32_t* aux_in;
+  int64_t ld_aux;
+  float* bgrad_part;    // two-pass: [tiles_m][N] partial column sums; atomic: bgrad itself
+  int bgrad_atomic;
+  const void* gate;
+  const void* up;
+  int64_t ld_gu;
+  void* d2;
+  int64_t ldd2;
+};
+
+// Tile configurations.  bm = workgroup rows, bnt = rows of the B tile held in LDS
+// (output columns per workgroup are bnt, or bnt/2 for the dual-B SwiGLU kernel).
+struct TileCfg {
+  int bm, bnt;
+  int lds_bytes;
+  int wgs_per_cu;  // expected resident workgroups per CU
+  const char* name;
+};
+constexpr int kNumTileCfgs = 4;
+extern const TileCfg kTileCfgs[kNumTileCfgs];
+
+typedef void (*GemmLauncher)(const GemmArgs&, hipStream_t);
+
+// [dtype][layout][epi][cfg]; null where not instantiated
+GemmLauncher gemm_launcher(int dtype, int layout, int epi, int cfg);
+const char* gemm_kernel_name(int dtype, int layout, int epi, int cfg);
+
+// ---- unfused baseline and reduction kernels (elementwise.hip)
+hipError_t launch_bias_add(int dtype, void* z, int64_t ldz, const void* bias, int M, int N, hipStream_t s);
+hipError_t launch_relu_pack(int dtype, const void* z, int64_t ldz, void* y, int64_t ldy, uint32_t* aux,
+                            int64_t ld_aux, int M, int N, int with_mask, hipStream_t s);
+hipError_t launch_mask_apply(int dtype, const void* g, int64_t ldg, const uint32_t* aux, int64_t ld_aux,
+                             void* dx, int64_t lddx, int M, int N, hipStream_t s);
+hipError_t launch_colsum_partial(int dtype, const void* x, int64_t ldx, float* part, int M, int N,
+                                 int rows_per_block, hipStream_t s);
+hipError_t launch_bgrad_reduce(const float* part, int nparts, float* bgrad, int N, hipStream_t s);
+hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t s);
+hipError_t launch_silu_mul(int dtype, const void* g, const void* u, int64_t ldgu, void* h, int64_t ldh,
+                           int M, int N, hipStream_t s);
+hipError_t launch_dswiglu(int dtype, const void* dh, int64_t lddh, const void* gate, const void* up,
+                          int64_t ld_gu, void* dg, int64_t lddg, void* du, int64_t lddu, int M, int N,
+                          hipStream_t s);
+
+}  // namespace ep

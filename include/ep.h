@@ -1,0 +1,187 @@
+/*
+ * ep.h -- C ABI of the fused GEMM + epilogue library for AMD Instinct MI355X (gfx950).
+ *
+ * The call sequence mirrors the stateful plan/execute/free split described on the pages:
+ *   - "Fusing Matmul Epilogs with nvmath-python", section "The problem addressed by fused
+ *     epilogs": a stateful Matmul separates setup and planning from repeated execution;
+ *   - the hotdry.top post "nvmath-python wraps cuBLASLt" (paragraphs 3-6): construct with
+ *     the operands, plan once with an epilog and its epilog_inputs, execute many times
+ *     asynchronously on a stream, free the internal resources at the end.
+ *
+ * Conventions used by every entry point:
+ *   - A is row-major M x K with leading dimension lda (elements).
+ *   - B is row-major K x N (EP_B_KN, N contiguous) or row-major N x K (EP_B_NK, K contiguous,
+ *     i.e. a torch Linear weight, used as B^T) with leading dimension ldb (elements).
+ *   - D is row-major M x N with leading dimension ldd (elements).
+ *   - Elements are IEEE binary16 (EP_F16) or bfloat16 (EP_BF16); products are formed
+ *     exactly and accumulated in float32; outputs are rounded to the input type with
+ *     round-to-nearest-even.
+ *   - All pointers are device pointers (hipMalloc / torch CUDA tensors) except the ones
+ *     to the ep_* structs and the char buffer of ep_plan_info, which are host pointers.
+ *   - Every call returns ep_status; nothing aborts, exits or throws across the ABI.
+ *     On any error no output buffer is written. ep_last_error() gives a thread-local
+ *     text for the last error of the calling thread.
+ *
+ * Ownership: the caller owns every tensor (inputs and outputs). The library owns the
+ * handle and the workspace it allocates in ep_plan (bias-gradient partial sums, and the
+ * intermediates of the unfused baseline path); ep_free releases both.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_ABI_VERSION 1
+
+typedef struct ep_plan_s* ep_handle;
+
+typedef enum {
+  EP_OK = 0,
+  EP_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or leading dimension */
+  EP_ERR_UNSUPPORTED = 2,   /* well-formed request this library does not implement */
+  EP_ERR_OUT_OF_MEMORY = 3, /* workspace allocation failed */
+  EP_ERR_HIP = 4,           /* a HIP runtime call failed (no device, launch failure) */
+  EP_ERR_INTERNAL = 5
+} ep_status;
+
+typedef enum { EP_F16 = 0, EP_BF16 = 1 } ep_dtype;
+
+typedef enum { EP_B_KN = 0, EP_B_NK = 1 } ep_b_layout;
+
+/*
+ * Epilogs.  Each is applied to the float32 accumulator tile inside the GEMM kernel before
+ * the single store to HBM.
+ *
+ * EP_EPILOG_DEFAULT        D = A.B.
+ * EP_EPILOG_BIAS           D = A.B + bias, one bias value per output column (feature);
+ *                          hotdry.top post, paragraph 7 (BIAS epilog).
+ * EP_EPILOG_RELU_BIAS      D = relu(A.B + bias); "Fusing Matmul Epilogs with nvmath-python",
+ *                          "Forward-pass capabilities in the source".  relu(v) = v if v > 0
+ *                          else +0, evaluated on the float32 value before rounding.
+ * EP_EPILOG_RELU_AUX_BIAS  as RELU_BIAS, and also writes relu_aux, the bit-encoded ReLU
+ *                          mask (same section): bit (j mod 32) of word (j / 32) in row i is
+ *                          1 iff the float32 pre-activation of element (i, j) is > 0; the
+ *                          least significant bit is the lowest column; bits past column
+ *                          N-1 are 0; words are uint32, row stride ld_aux words.
+ * EP_EPILOG_DRELU_BGRAD    D = mask .* (A.B) with mask read from relu_aux_in (same bit
+ *                          layout, N bits per row), and bgrad[j] = sum_i D[i][j] summed in
+ *                          float32 over the unrounded masked values;  "Backward-pass path
+ *                          shown in the example".  Typically A = dY (M x N_out) and B = the
+ *                          forward weight W (N_in x N_out row-major) as EP_B_NK, so that
+ *                          D = dY W^T has N = N_in columns.
+ * EP_EPILOG_SWIGLU         D = silu(A.B) .* (A.B2) with B2 (the up weight) in the same
+ *                          layout and leading dimension as B (the gate weight); both
+ *                          products are kept in float32 until the single store.
+ *                          gemm_swiglu_mlp_fusion.py, module docstring (forward).
+ * EP_EPILOG_DSWIGLU        with dh = A.B (float32), s = sigmoid(gate):
+ *                          D = d_gate = dh .* up .* s .* (1 + gate .* (1 - s)),
+ *                          D2 = d_up = dh .* gate .* s;  gate and up are M x N inputs in
+ *                          the element type (row stride ld_gu).  gemm_swiglu_mlp_fusion.py,
+ *                          module docstring (backward dSwiGLU as a matmul epilogue).
+ */
+typedef enum {
+  EP_EPILOG_DEFAULT = 0,
+  EP_EPILOG_BIAS = 1,
+  EP_EPILOG_RELU_BIAS = 2,
+  EP_EPILOG_RELU_AUX_BIAS = 3,
+  EP_EPILOG_DRELU_BGRAD = 4,
+  EP_EPILOG_SWIGLU = 5,
+  EP_EPILOG_DSWIGLU = 6
+} ep_epilog;
+
+/* The GEMM operands, bound at plan time. Sizes and leading dimensions are in elements. */
+typedef struct {
+  int64_t m, n, k;        /* 1 <= m, n, k < 2^31; n and k multiples of 8 */
+  ep_b_layout b_layout;
+  const void* a;          /* M x K, lda >= k */
+  int64_t lda;
+  const void* b;          /* K x N (ldb >= n) or N x K (ldb >= k) */
+  int64_t ldb;
+  void* d;                /* M x N output, ldd >= n */
+  int64_t ldd;
+} ep_shape;
+
+/* Epilog inputs and auxiliary outputs (the epilog_inputs dictionary and the aux dictionary
+ * of the pages).  Fields an epilog does not use must be NULL / 0. */
+typedef struct {
+  const void* bias;            /* BIAS, RELU_BIAS, RELU_AUX_BIAS: n elements, input dtype */
+  uint32_t* relu_aux;          /* RELU_AUX_BIAS output: m rows of ld_aux words */
+  const uint32_t* relu_aux_in; /* DRELU_BGRAD input: m rows of ld_aux words */
+  int64_t ld_aux;              /* words per mask row; 0 means ceil(n/32) */
+  float* bgrad;                /* DRELU_BGRAD output: n floats */
+  const void* b2;              /* SWIGLU: the up weight, same layout/ldb as b */
+  const void* gate;            /* DSWIGLU inputs: m x n, row stride ld_gu */
+  const void* up;
+  int64_t ld_gu;               /* 0 means n */
+  void* d2;                    /* DSWIGLU output d_up: m x n, row stride ldd2 (0 means ldd) */
+  int64_t ldd2;
+} ep_epilog_io;
+
+typedef enum { EP_PATH_FUSED = 0, EP_PATH_UNFUSED = 1 } ep_path;
+typedef enum { EP_BGRAD_TWO_PASS = 0, EP_BGRAD_ATOMIC = 1 } ep_bgrad_mode;
+
+typedef struct {
+  ep_path path;            /* EP_PATH_UNFUSED runs the same GEMM core with the DEFAULT
+                              epilog followed by separate elementwise / reduction kernels
+                              through HBM intermediates (the baseline fusion is measured
+                              against); results agree with the fused path to rounding */
+  ep_bgrad_mode bgrad_mode;/* DRELU_BGRAD: deterministic two-pass reduction (default) or
+                              float32 atomics into bgrad (order-dependent rounding) */
+  int tile_cfg;            /* -1 = choose by shape; otherwise an index < ep_num_tile_cfgs() */
+} ep_options;
+
+/*
+ * ep_plan: validate the request, pick a tile configuration, allocate the workspace and
+ * bind all pointers.  Checks, in order, before any HIP call: non-null handle out-pointer
+ * and shape; 1 <= m, n, k < 2^31; n % 8 == 0 and k % 8 == 0; the pointers the epilog needs
+ * are non-null and the ones it does not use are null; a, b, b2, d, d2, bias, gate, up are
+ * 16-byte aligned and relu_aux/relu_aux_in/bgrad 4-byte aligned; every leading dimension is
+ * a multiple of 8 elements, at least the row length and below 2^22; ld_aux >= ceil(n/32).
+ * Returns EP_ERR_INVALID_ARG or EP_ERR_UNSUPPORTED on a failed check and EP_ERR_HIP when no
+ * HIP device is usable.  On success *out is a new handle, otherwise *out is set to NULL.
+ */
+ep_status ep_plan(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog,
+                  const ep_epilog_io* io, ep_handle* out);
+
+/* ep_plan with options (opt may be NULL for the defaults {FUSED, TWO_PASS, -1}). */
+ep_status ep_plan_ex(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog,
+                     const ep_epilog_io* io, const ep_options* opt, ep_handle* out);
+
+/*
+ * ep_execute: enqueue the planned computation on `stream` (a hipStream_t; NULL = the null
+ * stream) and return without synchronizing.  Does no validation beyond the handle check
+ * and no allocation.  A handle may be executed any number of times, on any stream, but
+ * not concurrently on two streams (they would share its workspace).  Returns
+ * EP_ERR_INVALID_ARG for a NULL or freed handle and EP_ERR_HIP if a launch fails.
+ */
+ep_status ep_execute(ep_handle h, void* stream);
+
+/* ep_free: release the handle and its workspace.  ep_free(NULL) is EP_OK. The caller must
+ * make sure no execution of the handle is still running. */
+ep_status ep_free(ep_handle h);
+
+/* Human-readable name of a status code (static storage). */
+const char* ep_status_string(ep_status s);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* ep_last_error(void);
+
+/* Writes a NUL-terminated description (tile configuration, grid, workspace bytes, kernel
+ * names) into buf[0..n-1]; truncates to fit. */
+ep_status ep_plan_info(ep_handle h, char* buf, size_t n);
+
+/* Number of selectable tile configurations (valid ep_options.tile_cfg values). */
+int ep_num_tile_cfgs(void);
+
+/* EP_ABI_VERSION of the library. */
+int ep_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EP_H */

@@ -1,0 +1,167 @@
+"""GPU parity on small and ragged shapes: every epilog x dtype x B layout x tile config.
+
+Each case compares the HIP kernel's outputs element by element with the float64 oracle on
+the same seeded inputs, and checks that padding around every output (extra columns of
+the leading dimension, an extra row, extra mask words, extra bgrad entries) still holds
+its sentinel afterwards.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._gpu import assert_bgrad, assert_half, assert_mask, f64, require_gpu, say, words
+
+pytestmark = pytest.mark.gpu
+
+EPIS = ["DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "DRELU_BGRAD", "SWIGLU", "DSWIGLU"]
+SHAPES = [(300, 200, 136), (37, 8, 8), (130, 264, 520), (1, 64, 72)]
+DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
+SENT16 = -1  # 0xFFFF, a NaN pattern in both half types
+SENT32 = -1
+
+
+def padded(m, n, dtype, dev, pad_cols=8):
+    """An m x n view into an (m+1) x (n+pad) buffer filled with a sentinel."""
+    buf = torch.full((m + 1, n + pad_cols), SENT16, dtype=torch.int16, device=dev).view(dtype)
+    return buf, buf[:m, :n]
+
+
+def dec(t, dtype):
+    return f64(t) if dtype != "np" else t
+
+
+def make_inputs(epi, dt, layout, m, n, k, seed, dev):
+    g = torch.Generator().manual_seed(seed)
+    rn = lambda *s, scale=1.0: (torch.randn(*s, generator=g) * scale).to(dt)
+    x = rn(m, k)
+    b = rn(k, n, scale=k ** -0.5) if layout == "KN" else rn(n, k, scale=k ** -0.5)
+    ins = {"a": x, "b": b}
+    if epi in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS"):
+        ins["bias"] = rn(n, scale=0.5)
+    if epi == "DRELU_BGRAD":
+        p = torch.randn(m, n, generator=g).numpy()
+        ins["mask"] = torch.from_numpy(oracle.pack_relu_mask(p > 0).view(np.int32).copy())
+    if epi == "SWIGLU":
+        ins["b2"] = rn(*b.shape, scale=k ** -0.5)
+    if epi == "DSWIGLU":
+        ins["gate"] = rn(m, n, scale=1.5)
+        ins["up"] = rn(m, n, scale=1.5)
+    return {kk: v.to(dev) for kk, v in ins.items()}
+
+
+def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0):
+    import dense_gemm_epilogues_amd as ep
+    dev = torch.device("cuda")
+    dt = DTYPES[dtname]
+    ins = make_inputs(epi, dt, layout, m, n, k, seed, dev)
+    obuf, out = padded(m, n, dt, dev)
+    aux_out, epi_in = {}, {}
+    nw = (n + 31) // 32
+    if epi in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS"):
+        epi_in["bias"] = ins["bias"]
+    if epi == "RELU_AUX_BIAS":
+        abuf = torch.full((m + 1, nw + 1), SENT32, dtype=torch.int32, device=dev)
+        aux_out["relu_aux"] = abuf[:m, :nw]
+    if epi == "DRELU_BGRAD":
+        epi_in["relu_aux"] = ins["mask"]
+        gbuf = torch.full((n + 4,), float("nan"), dtype=torch.float32, device=dev)
+        aux_out["drelu_bgrad"] = gbuf[:n]
+    if epi == "SWIGLU":
+        epi_in["b2"] = ins["b2"]
+    if epi == "DSWIGLU":
+        epi_in["gate"], epi_in["up"] = ins["gate"], ins["up"]
+        ubuf, uview = padded(m, n, dt, dev)
+        aux_out["d_up"] = uview
+    say(f"case epi={epi} dt={dtname} layout={layout} m={m} n={n} k={k} cfg={cfg} path={path}")
+    p = ep.Plan(ins["a"], ins["b"], epilog=epi, epilog_inputs=epi_in, b_layout=layout, out=out,
+                aux_out=aux_out, path=path, tile_cfg=cfg)
+    p.execute()
+    torch.cuda.synchronize()
+
+    a64, b64 = f64(ins["a"]), f64(ins["b"])
+    what = f"{epi}/{dtname}/{layout}/{m}x{n}x{k}/cfg{cfg}/{path}"
+    if epi == "DEFAULT":
+        assert_half(f64(out), oracle.matmul(a64, b64, layout), what)
+    elif epi == "BIAS":
+        assert_half(f64(out), oracle.bias_epilog(a64, b64, f64(ins["bias"]), layout), what)
+    elif epi == "RELU_BIAS":
+        assert_half(f64(out), oracle.relu_bias(a64, b64, f64(ins["bias"]), layout), what)
+    elif epi == "RELU_AUX_BIAS":
+        y, _, pre = oracle.relu_aux_bias(a64, b64, f64(ins["bias"]), layout)
+        assert_half(f64(out), y, what)
+        assert_mask(words(aux_out["relu_aux"]), pre, what)
+        # invariants: bit 0 => Y == 0 exactly; Y >= 0
+        bits = oracle.unpack_relu_mask(words(aux_out["relu_aux"]), n)
+        yg = f64(out)
+        assert np.all(yg >= 0) and np.all(yg[~bits] == 0), what
+        ab = words(abuf)
+        assert np.all(ab[m, :] == 0xFFFFFFFF) and np.all(ab[:, nw] == 0xFFFFFFFF), f"{what}: mask padding written"
+    elif epi == "DRELU_BGRAD":
+        dx, bg = oracle.drelu_bgrad(a64, b64, layout, words(ins["mask"]))
+        assert_half(f64(out), dx, what)
+        assert_bgrad(aux_out["drelu_bgrad"].cpu().numpy(), bg, what)
+        assert torch.isnan(gbuf[n:]).all(), f"{what}: bgrad padding written"
+    elif epi == "SWIGLU":
+        h, _, _ = oracle.swiglu(a64, b64, f64(ins["b2"]), layout)
+        assert_half(f64(out), h, what)
+    elif epi == "DSWIGLU":
+        dg, du, _ = oracle.dswiglu(a64, b64, f64(ins["gate"]), f64(ins["up"]), layout)
+        assert_half(f64(out), dg, what)
+        assert_half(f64(aux_out["d_up"]), du, what)
+        ub = ubuf.view(torch.int16).cpu().numpy()
+        assert np.all(ub[m, :] == -1) and np.all(ub[:, n:] == -1), f"{what}: d_up padding written"
+    ob = obuf.view(torch.int16).cpu().numpy()
+    assert np.all(ob[m, :] == -1) and np.all(ob[:, n:] == -1), f"{what}: output padding written"
+    p.free()
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+@pytest.mark.parametrize("layout", ["KN", "NK"])
+@pytest.mark.parametrize("dtname", ["f16", "bf16"])
+@pytest.mark.parametrize("epi", EPIS)
+def test_small_shapes_fused(epi, dtname, layout, cfg):
+    require_gpu()
+    for (m, n, k) in SHAPES:
+        run_and_check(epi, dtname, layout, m, n, k, cfg)
+
+
+@pytest.mark.parametrize("layout", ["KN", "NK"])
+@pytest.mark.parametrize("epi", EPIS)
+def test_small_shapes_unfused(epi, layout):
+    require_gpu()
+    for (m, n, k) in SHAPES:
+        run_and_check(epi, "f16" if epi not in ("SWIGLU", "DSWIGLU") else "bf16", layout, m, n, k, -1,
+                      path="unfused")
+
+
+def test_tiny_linear_layer_config():
+    """The tiny fp16 linear layer: X 32x128, W 128x64, bias 64; backward dY 32x64 masked by a
+    separate 32x128 pre-activation's relu_aux."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    c = workloads.LINEAR[1]
+    inp = workloads.linear_inputs(c)
+    p_sep = workloads.randn((c.m, c.k), workloads.seed_of(1, 5), 1.0, torch.float32)
+    mask_in = torch.from_numpy(oracle.pack_relu_mask(p_sep.numpy() > 0).view(np.int32).copy())
+    dev = torch.device("cuda")
+    x, w, bias, dy = (inp[kk].to(dev) for kk in ("x", "w", "bias", "dy"))
+    x64, w64, b64, dy64 = f64(x), f64(w), f64(bias), f64(dy)
+    p1 = ep.Plan(x, w, "RELU_BIAS", {"bias": bias}, b_layout="KN")
+    y1, _ = p1.execute()
+    p2 = ep.Plan(x, w, "RELU_AUX_BIAS", {"bias": bias}, b_layout="KN")
+    y2, aux = p2.execute()
+    p3 = ep.Plan(dy, w, "DRELU_BGRAD", {"relu_aux": mask_in.to(dev)}, b_layout="NK")
+    dx, aux3 = p3.execute()
+    torch.cuda.synchronize()
+    yref, _, pre = oracle.relu_aux_bias(x64, w64, b64, "KN")
+    assert_half(f64(y1), yref, "cfg1 RELU_BIAS")
+    assert_half(f64(y2), yref, "cfg1 RELU_AUX_BIAS")
+    assert torch.equal(y1, y2), "RELU_BIAS and RELU_AUX_BIAS outputs differ"
+    assert_mask(words(aux["relu_aux"]), pre, "cfg1 relu_aux")
+    dxref, bgref = oracle.drelu_bgrad(dy64, w64, "NK", words(mask_in))
+    assert_half(f64(dx), dxref, "cfg1 DRELU_BGRAD dX")
+    assert_bgrad(aux3["drelu_bgrad"].cpu().numpy(), bgref, "cfg1 bgrad")
+    for p in (p1, p2, p3):
+        p.free()
