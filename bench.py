@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GEMM + epilogue library on one MI355X.
+
+Prints ONE JSON line.  The headline workload is the square fp16 ReLU linear layer
+(M = N = K = 4096): one step is the fused forward RELU_AUX_BIAS followed by the fused
+backward DRELU_BGRAD that consumes the forward's relu_aux.  `value` is that step's
+GEMM throughput in TFLOP/s (2*M*N*K per GEMM; epilog flops not counted).  The same line
+carries the unfused-path step time (same GEMM core, DEFAULT epilog, separate kernels
+through HBM) and, under "configs", the fused/unfused timings of the large workloads:
+the H200-shape fp16 layer (65536 x 16384 x 8192), the bf16 SwiGLU forward
+(M 2048, H 5120, I 17408) and the GEMM + dSwiGLU backward (M 16384).
+
+Timing: HIP events on the stream the kernels run on, around each step; a 512 MiB
+buffer is overwritten between steps (outside the events) so no step starts with its
+operands in L2 / Infinity Cache.  Inputs are seeded synthetic tensors generated on the
+device.  The CPU oracle (float64 numpy) is timed on this host as a baseline only.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+PEAK_F16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense fp16/bf16 FLOP/clk/CU
+METRIC = "fused GEMM+epilogue TFLOP/s, % MFMA peak, speedup vs unfused path"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-large", action="store_true", help="skip the large-workload summary")
+    ap.add_argument("--only", default=None,
+                    help="profile helper: run only one workload's fused path "
+                         "(sq4096, h200, swiglu, down, dswiglu) and print its line")
+    ap.add_argument("--no-flush", action="store_true")
+    return ap.parse_args()
+
+
+class Timer:
+    """Per-step HIP event pairs on torch's current stream (the stream ep_execute uses)."""
+
+    def __init__(self, n):
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.ev]
+
+
+def flush_cache(buf):
+    if buf is not None:
+        buf.zero_()
+
+
+def run_steps(fns, steps, warmup, flush):
+    """fns: list of callables forming one step.  Returns per-step ms and per-fn ms lists."""
+    for _ in range(warmup):
+        flush_cache(flush)
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    n = len(fns)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    for s in range(steps):
+        flush_cache(flush)
+        marks[s][0].record()
+        for i, f in enumerate(fns):
+            f()
+            marks[s][i + 1].record()
+    torch.cuda.synchronize()
+    step_ms = [m[0].elapsed_time(m[n]) for m in marks]
+    per_fn = [[m[i].elapsed_time(m[i + 1]) for m in marks] for i in range(n)]
+    return step_ms, per_fn
+
+
+def linear_layer(c, steps, warmup, flush, dev, with_unfused=True):
+    """Fused fwd RELU_AUX_BIAS + bwd DRELU_BGRAD (mask chained from the forward)."""
+    import dense_gemm_epilogues_amd as ep
+    import workloads as W
+    inp = W.linear_inputs(c, device=dev)
+    x, w, bias, dy = inp["x"], inp["w"], inp["bias"], inp["dy"]
+    m, n, k = c.m, c.n, c.k
+    if c.mask_from == "separate":
+        mask_bwd = inp["mask_in"]
+    else:
+        mask_bwd = None
+    res = {}
+    for path in (["fused", "unfused"] if with_unfused else ["fused"]):
+        pf = ep.Plan(x, w, "RELU_AUX_BIAS", {"bias": bias}, b_layout="KN", path=path)
+        y, aux = pf.execute()
+        mb = aux["relu_aux"] if mask_bwd is None else mask_bwd
+        pb = ep.Plan(dy, w, "DRELU_BGRAD", {"relu_aux": mb}, b_layout="NK", path=path)
+        step_ms, per = run_steps([pf.execute, pb.execute], steps, warmup, flush)
+        res[path] = {"step_ms": float(np.mean(step_ms)), "fwd_ms": float(np.mean(per[0])),
+                     "bwd_ms": float(np.mean(per[1])), "fwd_info": pf.info(), "bwd_info": pb.info()}
+        pf.free()
+        pb.free()
+    flop = 2.0 * m * n * k
+    out = {"flop_per_gemm": flop, "fused": res["fused"]}
+    f = res["fused"]
+    f["tflops_step"] = 2 * flop / (f["step_ms"] * 1e-3) / 1e12
+    f["tflops_fwd"] = flop / (f["fwd_ms"] * 1e-3) / 1e12
+    f["tflops_bwd"] = flop / (f["bwd_ms"] * 1e-3) / 1e12
+    if with_unfused:
+        u = res["unfused"]
+        out["unfused"] = u
+        out["speedup_step"] = u["step_ms"] / f["step_ms"]
+        out["speedup_fwd"] = u["fwd_ms"] / f["fwd_ms"]
+        out["speedup_bwd"] = u["bwd_ms"] / f["bwd_ms"]
+    out["inputs"] = {"x": x, "w": w, "bias": bias, "dy": dy}
+    return out
+
+
+def swiglu_fwd(c, steps, warmup, flush, dev):
+    import dense_gemm_epilogues_amd as ep
+    import workloads as W
+    inp = W.swiglu_inputs(c, device=dev)
+    x, wg, wu, wd = inp["x"], inp["wg"], inp["wu"], inp["wd"]
+    m, h, i = c.m, c.h, c.i
+    res = {}
+    for path in ("fused", "unfused"):
+        ps = ep.Plan(x, wg, "SWIGLU", {"b2": wu}, b_layout="NK", path=path)
+        hh, _ = ps.execute()
+        pd = ep.Plan(hh, wd, "DEFAULT", b_layout="NK")
+        step_ms, per = run_steps([ps.execute, pd.execute], steps, warmup, flush)
+        res[path] = {"step_ms": float(np.mean(step_ms)), "swiglu_ms": float(np.mean(per[0])),
+                     "down_ms": float(np.mean(per[1])), "swiglu_info": ps.info(), "down_info": pd.info()}
+        ps.free()
+        pd.free()
+    f, u = res["fused"], res["unfused"]
+    flop_s, flop_d = 2.0 * 2 * m * h * i, 2.0 * m * h * i
+    f["tflops_swiglu"] = flop_s / (f["swiglu_ms"] * 1e-3) / 1e12
+    f["tflops_down"] = flop_d / (f["down_ms"] * 1e-3) / 1e12
+    f["tflops_step"] = (flop_s + flop_d) / (f["step_ms"] * 1e-3) / 1e12
+    return {"fused": f, "unfused": u, "speedup_swiglu": u["swiglu_ms"] / f["swiglu_ms"],
+            "speedup_step": u["step_ms"] / f["step_ms"]}
+
+
+def dswiglu_bwd(c, steps, warmup, flush, dev):
+    import dense_gemm_epilogues_amd as ep
+    import workloads as W
+    inp = W.dswiglu_inputs(c, device=dev)
+    res = {}
+    for path in ("fused", "unfused"):
+        p = ep.Plan(inp["dout"], inp["wd"], "DSWIGLU", {"gate": inp["gate"], "up": inp["up"]},
+                    b_layout="KN", path=path)
+        step_ms, per = run_steps([p.execute], steps, warmup, flush)
+        res[path] = {"ms": float(np.mean(step_ms)), "info": p.info()}
+        p.free()
+    flop = 2.0 * c.m * c.h * c.i
+    f, u = res["fused"], res["unfused"]
+    f["tflops"] = flop / (f["ms"] * 1e-3) / 1e12
+    return {"fused": f, "unfused": u, "speedup": u["ms"] / f["ms"]}
+
+
+def cpu_baseline(inputs, c):
+    """The float64 oracle on the same inputs: one full forward + backward step of the square
+    layer, repeated until about 10 s of CPU work (at least once)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    x = oracle.decode_f16(inputs["x"].cpu().numpy())
+    w = oracle.decode_f16(inputs["w"].cpu().numpy())
+    b = oracle.decode_f16(inputs["bias"].cpu().numpy())
+    dy = oracle.decode_f16(inputs["dy"].cpu().numpy())
+    reps, t_total = 0, 0.0
+    while reps == 0 or (t_total < 10.0 and reps < 5):
+        t0 = time.perf_counter()
+        _, words, _ = oracle.relu_aux_bias(x, w, b, "KN")
+        oracle.drelu_bgrad(dy, w, "NK", words)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    flop = 2 * 2.0 * c.m * c.n * c.k
+    sec = t_total / reps
+    return {"value": flop / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"full fp64 forward RELU_AUX_BIAS + backward DRELU_BGRAD at M=N=K={c.m} on the "
+                      f"same inputs, {reps} rep(s), {sec:.2f} s each; host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of "
+                                   "this build (see the sharding notes in DESIGN.md)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU available"}))
+        sys.exit(1)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import workloads as W
+    import dense_gemm_epilogues_amd as ep
+    ep.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    if args.only:
+        st, wu = args.steps, args.warmup
+        if args.only == "sq4096":
+            r = linear_layer(W.LINEAR[2], st, wu, flush, dev, with_unfused=False)
+            r.pop("inputs")
+        elif args.only == "h200":
+            r = linear_layer(W.LINEAR[3], st, wu, flush, dev, with_unfused=False)
+            r.pop("inputs")
+        elif args.only == "swiglu":
+            r = swiglu_fwd(W.SWIGLU[4], st, wu, flush, dev)
+        elif args.only == "dswiglu":
+            r = dswiglu_bwd(W.SWIGLU[5], st, wu, flush, dev)
+        else:
+            raise SystemExit(f"unknown --only {args.only}")
+        print(json.dumps({"only": args.only, "result": r}))
+        return
+
+    c2 = W.LINEAR[2]
+    t_start = time.time()
+    r2 = linear_layer(c2, args.steps, args.warmup, flush, dev)
+    f2 = r2["fused"]
+    fwd_tflops = f2["tflops_fwd"]
+    line = {
+        "metric": METRIC,
+        "value": round(f2["tflops_step"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(f2["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "square ReLU linear layer, fp16 in / fp32 acc: fused RELU_AUX_BIAS forward "
+                               "(X 4096x4096 . W 4096x4096 + bias) then fused DRELU_BGRAD backward "
+                               "(dY . W^T masked by the forward relu_aux, + bgrad)",
+                   "m": c2.m, "n": c2.n, "k": c2.k, "cache": "flushed between steps" if flush is not None else "warm"},
+        "pct_peak": round(100.0 * f2["tflops_step"] / PEAK_F16_TFLOPS, 2),
+        "speedup_vs_unfused": round(r2["speedup_step"], 4),
+        "unfused_ms_per_step": round(r2["unfused"]["step_ms"], 5),
+        "fwd_ms": round(f2["fwd_ms"], 5), "bwd_ms": round(f2["bwd_ms"], 5),
+        "roofline": {"bound": "mfma", "kernel": f2["fwd_info"].split("kernels=")[1],
+                     "achieved": round(fwd_tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fwd_tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_per_launch": f"{r2['flop_per_gemm']:.6g} FLOP (2*4096^3)",
+                     "avg_launch_ms": round(f2["fwd_ms"], 5)},
+    }
+    if not args.no_large:
+        large = {}
+        s_l, w_l = max(3, args.steps // 4), max(1, args.warmup // 2)
+        r3 = linear_layer(W.LINEAR[3], s_l, w_l, flush, dev)
+        r3.pop("inputs")
+        large["h200_fp16_65536x16384x8192"] = {
+            "fused_fwd_tflops": round(r3["fused"]["tflops_fwd"], 1),
+            "fused_bwd_tflops": round(r3["fused"]["tflops_bwd"], 1),
+            "fwd_pct_peak": round(100 * r3["fused"]["tflops_fwd"] / PEAK_F16_TFLOPS, 2),
+            "bwd_pct_peak": round(100 * r3["fused"]["tflops_bwd"] / PEAK_F16_TFLOPS, 2),
+            "fused_fwd_ms": round(r3["fused"]["fwd_ms"], 4), "fused_bwd_ms": round(r3["fused"]["bwd_ms"], 4),
+            "unfused_fwd_ms": round(r3["unfused"]["fwd_ms"], 4), "unfused_bwd_ms": round(r3["unfused"]["bwd_ms"], 4),
+            "speedup_fwd": round(r3["speedup_fwd"], 4), "speedup_bwd": round(r3["speedup_bwd"], 4)}
+        torch.cuda.empty_cache()
+        r4 = swiglu_fwd(W.SWIGLU[4], args.steps, args.warmup, flush, dev)
+        large["swiglu_fwd_bf16_M2048_H5120_I17408"] = {
+            "fused_swiglu_tflops": round(r4["fused"]["tflops_swiglu"], 1),
+            "swiglu_pct_peak": round(100 * r4["fused"]["tflops_swiglu"] / PEAK_F16_TFLOPS, 2),
+            "down_gemm_tflops": round(r4["fused"]["tflops_down"], 1),
+            "fused_swiglu_ms": round(r4["fused"]["swiglu_ms"], 4),
+            "unfused_swiglu_ms": round(r4["unfused"]["swiglu_ms"], 4),
+            "speedup_swiglu": round(r4["speedup_swiglu"], 4), "speedup_fwd_step": round(r4["speedup_step"], 4)}
+        torch.cuda.empty_cache()
+        r5 = dswiglu_bwd(W.SWIGLU[5], args.steps, args.warmup, flush, dev)
+        large["dswiglu_bwd_bf16_M16384_H5120_I17408"] = {
+            "fused_tflops": round(r5["fused"]["tflops"], 1),
+            "pct_peak": round(100 * r5["fused"]["tflops"] / PEAK_F16_TFLOPS, 2),
+            "fused_ms": round(r5["fused"]["ms"], 4), "unfused_ms": round(r5["unfused"]["ms"], 4),
+            "speedup": round(r5["speedup"], 4)}
+        line["configs"] = large
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(r2["inputs"], c2)
+    line["wall_s"] = round(time.time() - t_start, 1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
