@@ -18,10 +18,10 @@
 namespace ep {
 
 const TileCfg kTileCfgs[kNumTileCfgs] = {
-    {256, 256, 131072, 1, "256x256x64"},
-    {128, 128, 65536, 2, "128x128x64"},
-    {256, 128, 98304, 1, "256x128x64"},
-    {128, 256, 98304, 1, "128x256x64"},
+    {256, 256, 131072, 1, "256x256x32x4st"},
+    {128, 128, 131072, 1, "128x128x64x4st"},
+    {256, 128, 98304, 1, "256x128x32x4st"},
+    {128, 256, 98304, 1, "128x256x32x4st"},
 };
 
 #define EP_DECL_TABLE(dt, lay, epi) extern const GemmLauncher kLaunch_##dt##_##lay##_##epi[kNumTileCfgs];
@@ -107,12 +107,19 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-int choose_cfg(int64_t m, int64_t n, bool dual, int cus) {
+// The dual-B kernel with a K x N B operand keeps the gate and up columns in separate
+// 128-column LDS sub-tiles, which needs a 256-row B tile.
+bool cfg_allowed(int cfg, bool dual, ep_b_layout lay) {
+  return !(dual && lay == EP_B_KN && kTileCfgs[cfg].bnt < 256);
+}
+
+int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   // Estimated time ~ rounds of resident tiles x work per tile / relative efficiency.
   static const double kEff[kNumTileCfgs] = {1.0, 0.80, 0.92, 0.92};
   int best = 0;
   double best_t = 1e300;
   for (int c = 0; c < kNumTileCfgs; ++c) {
+    if (!cfg_allowed(c, dual, lay)) continue;
     const int64_t bn = dual ? kTileCfgs[c].bnt / 2 : kTileCfgs[c].bnt;
     const int64_t tiles = ((m + kTileCfgs[c].bm - 1) / kTileCfgs[c].bm) * ((n + bn - 1) / bn);
     const int64_t slots = (int64_t)cus * kTileCfgs[c].wgs_per_cu;
@@ -270,7 +277,11 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   const bool unfused = opt.path == EP_PATH_UNFUSED;
   // the unfused path runs plain DEFAULT GEMMs (single-B) into intermediates
   const bool kernel_dual = dual && !unfused;
-  const int cfg = opt.tile_cfg >= 0 ? opt.tile_cfg : choose_cfg(s->m, s->n, kernel_dual, prop.multiProcessorCount);
+  if (opt.tile_cfg >= 0 && !cfg_allowed(opt.tile_cfg, kernel_dual, s->b_layout))
+    return fail(EP_ERR_UNSUPPORTED, "tile_cfg %d cannot run SWIGLU with a K x N weight (needs a 256-row B tile)",
+                opt.tile_cfg);
+  const int cfg = opt.tile_cfg >= 0 ? opt.tile_cfg
+                                    : choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount);
 
   ep_plan_s* h = new (std::nothrow) ep_plan_s;
   if (!h) return fail(EP_ERR_OUT_OF_MEMORY, "host allocation failed");

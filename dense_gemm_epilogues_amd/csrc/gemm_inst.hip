@@ -12,10 +12,10 @@
 
 namespace ep {
 // Explicit kernel instantiations (emitted in the device pass).
-template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, cfg_bm(0), cfg_bnt(0)>(GemmArgs);
-template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, cfg_bm(1), cfg_bnt(1)>(GemmArgs);
-template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, cfg_bm(2), cfg_bnt(2)>(GemmArgs);
-template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, cfg_bm(3), cfg_bnt(3)>(GemmArgs);
+template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 0>(GemmArgs);
+template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 1>(GemmArgs);
+template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 2>(GemmArgs);
+template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 3>(GemmArgs);
 
 #if !defined(__HIP_DEVICE_COMPILE__)
 // Host-side launcher table, indexed by tile configuration.

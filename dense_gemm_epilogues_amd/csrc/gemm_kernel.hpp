@@ -20,6 +20,8 @@
 // RELU_AUX_BIAS; backward: DRELU_BGRAD), the hotdry.top cuBLASLt post (BIAS, the
 // plan/execute split) and gemm_swiglu_mlp_fusion.py (SwiGLU forward, dSwiGLU epilogue).
 #pragma once
+#include <type_traits>
+
 #include "ep_internal.hpp"
 
 namespace ep {
@@ -31,13 +33,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 64;
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every num_records we build
 
+// Tile configurations: workgroup rows, B-tile rows, k-step, LDS stages.
 constexpr int cfg_bm(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 128 : cfg == 2 ? 256 : 128; }
 constexpr int cfg_bnt(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 128 : cfg == 2 ? 128 : 256; }
+constexpr int cfg_bk(int cfg) { return cfg == 1 ? 64 : 32; }
+constexpr int cfg_nst(int cfg) { return 4; }
 
 template <int DT>
 struct Elem;
@@ -101,8 +105,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
+// descriptor from an already clamped extent
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_raw(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// 32-bit LDS address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // byte offset of 16-byte chunk `c` of row `r` in a k-contiguous LDS tile
@@ -127,8 +141,19 @@ __device__ __forceinline__ void map_tile(int bid, int nblocks, int tiles_m, int 
   pn = w / gm;
 }
 
-template <int DT, int LAY, int EPI, int BM, int BNT>
+// XOR swizzle of the 16-byte chunks of an LDS tile row (CPR chunks per row): chunk c of row r
+// is stored at chunk c ^ swf(r).  For 8 chunks (128-byte rows) every 8 and every 16
+// consecutive rows read at one logical chunk land on distinct banks; for 4 chunks (64-byte
+// rows) the same holds for (row mod 2, chunk) and (row mod 4, chunk) pairs.
+template <int CPR>
+__device__ __forceinline__ int swf(int r) {
+  if constexpr (CPR == 8) return (r ^ (r >> 3)) & 7;
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+template <int DT, int LAY, int EPI, int CFG>
 struct GemmTraits {
+  static constexpr int BM = cfg_bm(CFG), BNT = cfg_bnt(CFG), BK = cfg_bk(CFG), NST = cfg_nst(CFG);
   static constexpr bool DUAL = EPI == E_SWIGLU;
   static constexpr int WTM = BM / 2;             // rows per wave
   static constexpr int WTB = BNT / 2;            // B-tile rows per wave
@@ -136,36 +161,47 @@ struct GemmTraits {
   static constexpr int NB = WTB / 32;            // ... along the B tile
   static constexpr int BN_OUT = DUAL ? BNT / 2 : BNT;
   static constexpr int WTN = DUAL ? WTB / 2 : WTB;  // output columns per wave
-  static constexpr int A_BYTES = BM * 128;
-  static constexpr int B_BYTES = BNT * 128;
+  static constexpr int KS = BK / 16;             // MFMA k-slices per k-step
+  static constexpr int ROWB = BK * 2;            // bytes per k-contiguous tile row
+  static constexpr int CPR = BK / 8;             // 16-byte chunks per row
+  static constexpr int A_BYTES = BM * ROWB;
+  static constexpr int B_BYTES = BNT * ROWB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_PER = BM / 32;          // 16-byte chunks per thread per k-step
-  static constexpr int B_PER = BNT / 32;
+  static constexpr int A_SLOTS = A_BYTES / 1024 / 4;   // 1 KiB DMA slots per wave per stage
+  static constexpr int B_SLOTS = B_BYTES / 1024 / 4;
+  static constexpr int RPS = 1024 / ROWB;        // rows per DMA slot (k-contiguous tiles)
+  static constexpr int KN_SUB = BK * 256;        // bytes of one [BK k][128 n] sub-tile
+  static constexpr int KN_SPS = BK / 4;          // DMA slots per sub-tile
   static constexpr int SPITCH = WTN + 8;         // staging pitch in floats
   static constexpr int NARR = DUAL ? 2 : 1;
   static constexpr int STG_FLOATS = NARR * 32 * SPITCH;  // per wave
   static constexpr int BG_OFF = 4 * STG_FLOATS * 4;      // bytes; cross-wave bgrad exchange
   static constexpr int EPI_BYTES = BG_OFF + 2 * WTN * 4;
-  static constexpr int LDS_BYTES = (2 * STAGE > EPI_BYTES) ? 2 * STAGE : EPI_BYTES;
+  static constexpr int LDS_BYTES = (NST * STAGE > EPI_BYTES) ? NST * STAGE : EPI_BYTES;
   static constexpr int LPR = WTN / 4;            // lanes per staged row
   static constexpr int RPI = 64 / LPR;           // staged rows per iteration
   static constexpr int ITERS = 32 / RPI;
   static_assert(LPR >= 8 && LPR <= 64, "a relu_aux word must span whole lanes");
+  static_assert(KS == 2 || KS == 4, "k-slices per step must be even");
+  static_assert(A_SLOTS >= 1 && B_SLOTS >= 1, "tile too small for 1 KiB DMA slots");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DT, int LAY, int EPI, int BM, int BNT>
+template <int DT, int LAY, int EPI, int CFG>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
   using E = Elem<DT>;
-  using TR = GemmTraits<DT, LAY, EPI, BM, BNT>;
+  using TR = GemmTraits<DT, LAY, EPI, CFG>;
   constexpr bool DUAL = TR::DUAL;
+  constexpr int BM = TR::BM, BNT = TR::BNT, BK = TR::BK, NST = TR::NST;
   constexpr int MB = TR::MB, NB = TR::NB, WTM = TR::WTM, WTB = TR::WTB, WTN = TR::WTN;
-  constexpr int A_PER = TR::A_PER, B_PER = TR::B_PER;
+  constexpr int KS = TR::KS, ROWB = TR::ROWB, CPR = TR::CPR, RPS = TR::RPS;
+  constexpr int A_SLOTS = TR::A_SLOTS, B_SLOTS = TR::B_SLOTS;
 
   __shared__ __attribute__((aligned(16))) char smem[TR::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int wm = wave >> 1, wn = wave & 1;
 
   int pm, pn;
@@ -173,122 +209,118 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
   const int m0 = pm * BM;
   const int n0 = pn * TR::BN_OUT;
   const int M = p.M, N = p.N, K = p.K;
-  const int KT = (K + kBK - 1) / kBK;
+  const int KT = (K + BK - 1) / BK;
 
   const char* Ag = (const char*)p.a;
   const char* Bg = (const char*)p.b;
   const char* B2g = DUAL ? (const char*)p.b2 : (const char*)p.b;
 
   // ---------------------------------------------------------------- loader setup
-  // A: chunk i of this thread is row i*32 + tid/8, 16-byte column chunk tid%8.
-  uint32_t a_off[A_PER], a_lds[A_PER];
-  const int ld_c = tid & 7;
+  // Tiles move HBM/L2 -> LDS with 16-byte buffer loads that write LDS directly (no VGPR
+  // staging), NST stages deep.  One load per wave fills a contiguous 1 KiB LDS slot: lane L
+  // writes bytes [16L, 16L+16) of the slot, so the swizzle is applied by choosing which
+  // global chunk each lane fetches.  Out-of-range offsets (rows/columns past the matrix, the
+  // k tail, k-steps past the end) read as zero and write zeros to LDS.
+  // Buffer descriptors are built once per tile: A (and an N x K B) start at the tile's first
+  // row, k = 0, and extend to the last row of the matrix, so rows past M (N) fall outside
+  // num_records; the k offset of a k-step is added to the per-lane offset.  A K x N B is
+  // re-based per k-step (its rows are k).
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(Ag + (int64_t)m0 * p.lda * 2, (int64_t)(M - m0) * p.lda * 2);
+  uint32_t a_voff[A_SLOTS];
+  int a_klim[A_SLOTS];  // the k-step offset k0 is valid for this lane iff k0 < klim
 #pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    const int row = i * 32 + (tid >> 3);
-    a_off[i] = (uint32_t)(row * p.lda * 2) + ld_c * 16;
-    a_lds[i] = swz(row, ld_c);
+  for (int q = 0; q < A_SLOTS; ++q) {
+    const int row = (wave * A_SLOTS + q) * RPS + lane / CPR;
+    const int c = (lane % CPR) ^ swf<CPR>(row);
+    a_voff[q] = (uint32_t)(row * p.lda * 2) + c * 16;
+    a_klim[q] = K - c * 8;
   }
-  // B, N x K layout: like A over the BNT rows of the B tile (DUAL: first half Wg, second Wu).
-  // B, K x N layout: thread owns KR consecutive k-rows of one 8-column chunk.
-  constexpr int NCH = BNT / 8;              // 8-column chunks across the B tile
-  constexpr int KR = (LAY == L_KN) ? BNT / 32 : 1;
-  uint32_t b_off[B_PER], b_lds[B_PER];
-  bool b_second[B_PER];
-  int kn_b = 0, kn_g = 0;
-  bool kn_colok = true;
-  if constexpr (LAY == L_NK) {
+  // Each wave's B slots come from a single source: for N x K the wave loads BNT/4 rows
+  // (DUAL: waves 0-1 the gate rows, waves 2-3 the up rows); for K x N the wave's slots lie in
+  // one 128-column sub-tile.
+  static_assert((B_SLOTS * 4) % 2 == 0, "B slots");
+  const bool w_second = DUAL && wave >= 2;
+  const int w_sub = (wave * B_SLOTS) / TR::KN_SPS;  // K x N sub-tile of this wave
+  const int w_cbase = DUAL ? 0 : w_sub * 128;
+  const char* w_bsrc = (DUAL && (LAY == L_NK ? w_second : w_sub == 1)) ? B2g : Bg;
+  const __amdgpu_buffer_rsrc_t rB_nk =
+      make_rsrc(w_bsrc + (int64_t)n0 * p.ldb * 2, (int64_t)(N - n0) * p.ldb * 2);
+  uint32_t b_voff[B_SLOTS];
+  int b_klim[B_SLOTS];
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int row = i * 32 + (tid >> 3);
-      const int srow = DUAL ? (row % (BNT / 2)) : row;
-      b_second[i] = DUAL && row >= BNT / 2;
-      b_off[i] = (uint32_t)(srow * p.ldb * 2) + ld_c * 16;
-      b_lds[i] = swz(row, ld_c);
-    }
-  } else {
-    kn_b = tid % NCH;
-    kn_g = tid / NCH;
-    const int sb = DUAL ? (kn_b % (NCH / 2)) : kn_b;
-    const bool second = DUAL && kn_b >= NCH / 2;
-    kn_colok = (n0 + sb * 8) < N;
-#pragma unroll
-    for (int r = 0; r < B_PER; ++r) {  // B_PER == KR for this layout
-      b_second[r] = second;
-      b_off[r] = (uint32_t)((kn_g * KR + r) * p.ldb * 2) + sb * 16;
-      b_lds[r] = 0;
-    }
-  }
-
-  u32x4 ra[A_PER], rb[B_PER];
-
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * kBK;
-    const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc(Ag + ((int64_t)m0 * p.lda + k0) * 2, ((int64_t)(M - m0) * p.lda - k0) * 2);
-    const bool kok = (k0 + ld_c * 8) < K;
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) ra[i] = bload16(rA, kok ? a_off[i] : kOOB);
+  for (int q = 0; q < B_SLOTS; ++q) {
+    const int s = wave * B_SLOTS + q;
     if constexpr (LAY == L_NK) {
-      const int64_t bbytes = ((int64_t)(N - n0) * p.ldb - k0) * 2;
-      const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bg + ((int64_t)n0 * p.ldb + k0) * 2, bbytes);
-      const __amdgpu_buffer_rsrc_t rB2 = make_rsrc(B2g + ((int64_t)n0 * p.ldb + k0) * 2, bbytes);
-#pragma unroll
-      for (int i = 0; i < B_PER; ++i)
-        rb[i] = bload16(b_second[i] ? rB2 : rB, kok ? b_off[i] : kOOB);
+      const int row = s * RPS + lane / CPR;
+      const int c = (lane % CPR) ^ swf<CPR>(row);
+      const int srow = DUAL ? (row % (BNT / 2)) : row;
+      b_voff[q] = (uint32_t)(srow * p.ldb * 2) + c * 16;
+      b_klim[q] = K - c * 8;
     } else {
-      const int64_t bbytes = ((int64_t)(K - k0) * p.ldb - n0) * 2;
-      const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bg + ((int64_t)k0 * p.ldb + n0) * 2, bbytes);
-      const __amdgpu_buffer_rsrc_t rB2 = make_rsrc(B2g + ((int64_t)k0 * p.ldb + n0) * 2, bbytes);
-#pragma unroll
-      for (int r = 0; r < B_PER; ++r)
-        rb[r] = bload16(b_second[r] ? rB2 : rB, kn_colok ? b_off[r] : kOOB);
+      // B tile = BNT/128 sub-tiles of [BK k][128 n] (256-byte rows); 64-byte segment g of
+      // k-row k is stored at segment g ^ (k & 3).  DUAL: sub-tile 0 = gate, 1 = up columns.
+      const int t = s % TR::KN_SPS;
+      const int k = 4 * t + (lane >> 4);
+      const int pch = lane & 15;
+      const int nl = (((pch >> 2) ^ (k & 3)) << 5) + ((pch & 3) << 3);
+      // relative to the sub-tile's column base; columns past N read as zero
+      b_voff[q] = (n0 + w_cbase + nl < N) ? (uint32_t)(k * p.ldb * 2) + nl * 2 : kOOB;
+      b_klim[q] = 0;
     }
+  }
+  // K x N: base and clamped extent of this wave's sub-tile for the k-step being loaded
+  // (descriptor values are not passed between functions: the host pass cannot take them)
+  struct KnSrc {
+    const char* base;
+    uint32_t num;
+  };
+  auto kn_rsrc = [&](int kt) {
+    const int k0 = kt * BK;
+    const int64_t bytes = ((int64_t)(K - k0) * p.ldb - (n0 + w_cbase)) * 2;
+    KnSrc s;
+    s.base = w_bsrc + ((int64_t)k0 * p.ldb + n0 + w_cbase) * 2;
+    s.num = bytes <= 0 ? 0u : (bytes >= 0x7fffffffLL ? 0x7fffffffu : (uint32_t)bytes);
+    return s;
   };
 
-  auto store_tile = [&](int st) {
-    char* As = smem + st * TR::STAGE;
-    char* Bs = As + TR::A_BYTES;
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) *(u32x4*)(As + a_lds[i]) = ra[i];
-    if constexpr (LAY == L_NK) {
-#pragma unroll
-      for (int i = 0; i < B_PER; ++i) *(u32x4*)(Bs + b_lds[i]) = rb[i];
+  // One DMA op = one 1 KiB slot of a stage (A slots first, then B slots).
+  constexpr int N_DMA = A_SLOTS + B_SLOTS;
+  auto dma_op = [&](int kt, char* As, int t, const KnSrc& kr) {
+    const int k0 = kt * BK;
+    if (t < A_SLOTS) {
+      const int q = t;
+      const uint32_t off = (k0 < a_klim[q]) ? a_voff[q] + k0 * 2 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rA, (__attribute__((address_space(3))) void*)(As + (wave * A_SLOTS + q) * 1024), 16, (int)off, 0, 0, 0);
     } else {
-      // transpose KR k-rows x 8 columns: column j gets the KR halves of its k-rows
-      const int kbase = kn_g * KR;
-      const int c = kbase >> 3;
-      const int sub = (kbase & 7) * 2;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int nr = kn_b * 8 + j;
-        char* dst = Bs + swz(nr, c) + sub;
-        uint32_t w[KR / 2];
-#pragma unroll
-        for (int q = 0; q < KR / 2; ++q) {
-          const uint32_t lo = rb[2 * q][j >> 1], hi = rb[2 * q + 1][j >> 1];
-          w[q] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        if constexpr (KR == 8) {
-          *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
-        } else if constexpr (KR == 4) {
-          *(u32x2*)dst = u32x2{w[0], w[1]};
-        } else {
-          *(uint32_t*)dst = w[0];
-        }
+      const int q = t - A_SLOTS;
+      char* Bs = As + TR::A_BYTES;
+      if constexpr (LAY == L_NK) {
+        const uint32_t off = (k0 < b_klim[q]) ? b_voff[q] + k0 * 2 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rB_nk, (__attribute__((address_space(3))) void*)(Bs + (wave * B_SLOTS + q) * 1024), 16, (int)off, 0, 0, 0);
+      } else {
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc_raw(kr.base, kr.num);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)(Bs + (wave * B_SLOTS + q) * 1024), 16, (int)b_voff[q], 0, 0, 0);
       }
     }
   };
+  auto issue_tile = [&](int kt, char* As) {
+    const KnSrc kr = kn_rsrc(kt);
+#pragma unroll
+    for (int t = 0; t < N_DMA; ++t) dma_op(kt, As, t, kr);
+  };
 
-  // fragment-read rows
+  // fragment-read addresses
   const int hlf = lane >> 5;
   uint32_t a_rd[MB], b_rd[NB];
   int a_f[MB], b_f[NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int row = wm * WTM + i * 32 + (lane & 31);
-    a_rd[i] = row * 128;
-    a_f[i] = (row ^ (row >> 3)) & 7;
+    a_rd[i] = row * ROWB;
+    a_f[i] = swf<CPR>(row);
   }
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
@@ -298,9 +330,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
     } else {
       brow = wn * WTB + j * 32;
     }
-    const int row = brow + (lane & 31);
-    b_rd[j] = row * 128;
-    b_f[j] = (row ^ (row >> 3)) & 7;
+    if constexpr (LAY == L_NK) {
+      const int row = brow + (lane & 31);
+      b_rd[j] = row * ROWB;
+      b_f[j] = swf<CPR>(row);
+    } else {
+      // transpose reads: within each 16-lane group g, lane i fetches 4 columns of k-row
+      // kbase + i/4; the hardware hands lane i the 4 k-values of column i.
+      const int g = lane >> 4, i = lane & 15;
+      const int u = brow >> 7, cb = brow & 127;
+      b_rd[j] = u * TR::KN_SUB + (8 * (g >> 1) + (i >> 2)) * 256 + ((((cb >> 5) ^ (i >> 2)) & 3) << 6) +
+                32 * (g & 1) + 8 * (i & 3);
+      b_f[j] = 0;
+    }
   }
 
   f32x16 acc[MB][NB];
@@ -312,31 +354,146 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // ---------------------------------------------------------------- main loop
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < KT) load_tile(kt + 1);
-    const char* As = smem + st * TR::STAGE;
-    const char* Bs = As + TR::A_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      u32x4 af[MB], bf[NB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-        af[i] = *(const u32x4*)(As + a_rd[i] + ((((ks * 2 + hlf) ^ a_f[i]) & 7) << 4));
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        bf[j] = *(const u32x4*)(Bs + b_rd[j] + ((((ks * 2 + hlf) ^ b_f[j]) & 7) << 4));
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = E::mfma(af[i], bf[j], acc[i][j]);
+  u32x4 fa[2][MB], fb[2][NB];
+  // One read op = one LDS fragment read: A blocks first, then B blocks (K x N: two
+  // transpose reads of 4 k-values each per block).
+  constexpr int B_OPS = (LAY == L_NK) ? NB : 2 * NB;
+  constexpr int N_RD = MB + B_OPS;
+  auto read_op = [&](const char* As, int ks, int r, u32x4* A, u32x4* B) {
+    if (r < MB) {
+      A[r] = *(const u32x4*)(As + a_rd[r] + ((((ks * 2 + hlf) ^ a_f[r]) & (CPR - 1)) << 4));
+      return;
     }
-    if (kt + 1 < KT) store_tile(st ^ 1);
-    __syncthreads();
-  }
+    const char* Bs = As + TR::A_BYTES;
+    if constexpr (LAY == L_NK) {
+      const int j = r - MB;
+      B[j] = *(const u32x4*)(Bs + b_rd[j] + ((((ks * 2 + hlf) ^ b_f[j]) & (CPR - 1)) << 4));
+    } else {
+      // Issued as inline asm: the compiler's LDS-DMA alias check would otherwise make every
+      // transpose read wait for all in-flight loads of later stages (which never alias the
+      // stage being read).  Completion is awaited explicitly (lgkm_fence) before use.
+      const int j = (r - MB) >> 1, half = (r - MB) & 1;
+      const uint32_t addr = lds_addr(Bs + b_rd[j]) + ks * 4096 + half * 1024;
+      u32x2 w;
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(w) : "v"(addr));
+      B[j][2 * half] = w[0];
+      B[j][2 * half + 1] = w[1];
+    }
+  };
+  auto read_frags = [&](const char* As, int ks, u32x4* A, u32x4* B) {
+#pragma unroll
+    for (int r = 0; r < N_RD; ++r) read_op(As, ks, r, A, B);
+  };
+  // Wait for every outstanding LDS read and tie the wait to the B fragments, so no MFMA that
+  // consumes them can be scheduled above it.
+  auto lgkm_fence = [&](u32x4* B) {
+    if constexpr (LAY == L_KN) {
+      if constexpr (NB == 4) {
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B[0]), "+v"(B[1]), "+v"(B[2]), "+v"(B[3]));
+      } else if constexpr (NB == 2) {
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B[0]), "+v"(B[1]));
+      } else {
+        static_assert(NB == 1 || NB == 2 || NB == 4, "unsupported NB");
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B[0]));
+      }
+    }
+  };
+  // The instruction order inside a k-step is fixed explicitly: every sched_barrier below
+  // stops the scheduler from moving instructions across it.  Each MFMA is followed by its
+  // share of the fragment reads of the next k-slice, and the DMA loads of the stage NST-1
+  // k-steps ahead are spread evenly over the whole k-step (one every DSTRIDE MFMAs): issued
+  // in bursts they fill the texture-address FIFO and stall the MFMA stream behind them.
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  constexpr int NMMA = MB * NB;
+  constexpr int TOT = KS * NMMA;                       // MFMAs per k-step
+  constexpr int DSTRIDE = TOT / N_DMA > 0 ? TOT / N_DMA : 1;
+  constexpr int DPER = (N_DMA + TOT - 1) / TOT;        // DMA ops per issue point
+  auto slice = [&](auto rd_c, auto g0_c, const u32x4* A, const u32x4* B, auto t0_c, auto t1_c, int kt,
+                   char* dst, const KnSrc& kr, const char* rstage, int rks, u32x4* RA, u32x4* RB) {
+    constexpr bool RD = decltype(rd_c)::value;
+    constexpr int G0 = decltype(g0_c)::value;        // k-step MFMA index of MFMA t = 0
+    constexpr int T0 = decltype(t0_c)::value, T1 = decltype(t1_c)::value;
+    // fragment reads per MFMA so that they finish (when the slice is long enough) 4 MFMAs
+    // before the end of the slice
+    constexpr int RSPAN = (T1 - T0) > 8 ? (T1 - T0) - 4 : (T1 - T0);
+    constexpr int RPM = (N_RD + RSPAN - 1) / RSPAN;
+#pragma unroll
+    for (int t = T0; t < T1; ++t) {
+      acc[t / NB][t % NB] = E::mfma(A[t / NB], B[t % NB], acc[t / NB][t % NB]);
+      const int g = G0 + t;
+      if (g % DSTRIDE == 0) {
+#pragma unroll
+        for (int d = (g / DSTRIDE) * DPER; d < (g / DSTRIDE + 1) * DPER; ++d)
+          if (d < N_DMA) dma_op(kt, dst, d, kr);
+      }
+      if constexpr (RD) {
+#pragma unroll
+        for (int r = (t - T0) * RPM; r < (t - T0 + 1) * RPM; ++r)
+          if (r < N_RD) read_op(rstage, rks, r, RA, RB);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using Z_ = std::integral_constant<int, 0>;
+  constexpr int HB = NMMA >= 8 ? NMMA / 4 : NMMA / 2;  // MFMAs of the last slice before the barrier
+  using H_ = std::integral_constant<int, HB>;
+  using W_ = std::integral_constant<int, NMMA>;
+  // DMA ops of the current k-step issued before its barrier
+  constexpr int GBAR = (KS - 1) * NMMA + HB;
+  constexpr int DPRE_RAW = ((GBAR + DSTRIDE - 1) / DSTRIDE) * DPER;
+  constexpr int DPRE = DPRE_RAW < N_DMA ? DPRE_RAW : N_DMA;
+  // Workgroup barrier that does not drain the DMA ring: wait until this wave's loads of the
+  // stage needed next (k-step kt+1) have landed -- everything younger may stay in flight --
+  // and for its LDS reads, then s_barrier.  The memory clobber keeps the compiler from
+  // moving LDS accesses across it (__syncthreads would also wait for every younger stage).
+  constexpr int VMC_LOOP = N_DMA * (NST - 3) + DPRE;   // younger loads allowed in flight
+  constexpr int VMC_PRO = N_DMA * (NST - 2);           // after the prologue
+  static_assert(NST >= 3, "the ring needs at least 3 stages");
+  static_assert(VMC_LOOP <= 63 && VMC_PRO <= 63, "vmcnt range");
+  auto ring_barrier = [&](auto vmc_c) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(decltype(vmc_c)::value) : "memory");
+  };
+  // Loads for k-step kt + NST - 1 are issued during k-step kt.
+  auto kstep = [&](int kt) {
+    const char* cur = smem + (kt % NST) * TR::STAGE;
+    const char* nxt = smem + ((kt + 1) % NST) * TR::STAGE;
+    char* dst = smem + ((kt + NST - 1) % NST) * TR::STAGE;
+    const int kl = kt + NST - 1;
+    const KnSrc kr = kn_rsrc(kl);
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      u32x4* A = fa[ks & 1];
+      u32x4* B = fb[ks & 1];
+      lgkm_fence(B);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks == 0)
+        slice(T_{}, std::integral_constant<int, 0>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, fa[1], fb[1]);
+      else if (ks == 1)
+        slice(T_{}, std::integral_constant<int, NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, fa[0], fb[0]);
+      else
+        slice(T_{}, std::integral_constant<int, 2 * NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, fa[1], fb[1]);
+    }
+    constexpr int L = (KS - 1) & 1;  // buffer of the last slice
+    using GL = std::integral_constant<int, (KS - 1) * NMMA>;
+    lgkm_fence(fb[L]);
+    __builtin_amdgcn_sched_barrier(0);
+    slice(F_{}, GL{}, fa[L], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[0], fb[0]);
+    ring_barrier(std::integral_constant<int, VMC_LOOP>{});
+    __builtin_amdgcn_sched_barrier(0);
+    slice(T_{}, GL{}, fa[L], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[0], fb[0]);
+  };
+
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue_tile(s, smem + s * TR::STAGE);
+  ring_barrier(std::integral_constant<int, VMC_PRO>{});
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(smem, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < KT; ++kt) kstep(kt);
+  // loads issued past the last k-step (they read as zeros) must land before LDS is reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lgkm_fence(fb[0]);
+  __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
   float* stg = (float*)smem + wave * TR::STG_FLOATS;
@@ -453,9 +610,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
 
 template <int DT, int LAY, int EPI, int CFG>
 void launch_gemm(const GemmArgs& a, hipStream_t s) {
-  constexpr int BM = cfg_bm(CFG), BNT = cfg_bnt(CFG);
   const int nblocks = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<DT, LAY, EPI, BM, BNT>), dim3(nblocks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<DT, LAY, EPI, CFG>), dim3(nblocks), dim3(kThreads), 0, s, a);
 }
 
 #define EP_LAUNCH_ROW(DT, LAY, EPI) \

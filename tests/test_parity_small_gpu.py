@@ -123,6 +123,13 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0):
 @pytest.mark.parametrize("epi", EPIS)
 def test_small_shapes_fused(epi, dtname, layout, cfg):
     require_gpu()
+    if epi == "SWIGLU" and layout == "KN" and cfg in (1, 2):
+        import dense_gemm_epilogues_amd as ep
+        dev = torch.device("cuda")
+        a = torch.zeros((64, 64), dtype=DTYPES[dtname], device=dev)
+        with pytest.raises(ep.EPError, match="EP_ERR_UNSUPPORTED"):
+            ep.Plan(a, a, "SWIGLU", {"b2": a}, b_layout="KN", tile_cfg=cfg)
+        return
     for (m, n, k) in SHAPES:
         run_and_check(epi, dtname, layout, m, n, k, cfg)
 
