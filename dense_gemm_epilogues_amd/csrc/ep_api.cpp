@@ -22,6 +22,7 @@ const TileCfg kTileCfgs[kNumTileCfgs] = {
     {128, 128, 131072, 1, "128x128x64x4st"},
     {256, 128, 98304, 1, "256x128x32x4st"},
     {128, 256, 98304, 1, "128x256x32x4st"},
+    {256, 256, 131072, 1, "256x256x64x2st"},
 };
 
 #define EP_DECL_TABLE(dt, lay, epi) extern const GemmLauncher kLaunch_##dt##_##lay##_##epi[kNumTileCfgs];
@@ -115,7 +116,7 @@ bool cfg_allowed(int cfg, bool dual, ep_b_layout lay) {
 
 int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   // Estimated time ~ rounds of resident tiles x work per tile / relative efficiency.
-  static const double kEff[kNumTileCfgs] = {1.0, 0.80, 0.92, 0.92};
+  static const double kEff[kNumTileCfgs] = {1.0, 0.80, 0.92, 0.92, 0.99};
   int best = 0;
   double best_t = 1e300;
   for (int c = 0; c < kNumTileCfgs; ++c) {

@@ -49,7 +49,7 @@ struct TileCfg {
   int wgs_per_cu;  // expected resident workgroups per CU
   const char* name;
 };
-constexpr int kNumTileCfgs = 4;
+constexpr int kNumTileCfgs = 5;
 extern const TileCfg kTileCfgs[kNumTileCfgs];
 
 typedef void (*GemmLauncher)(const GemmArgs&, hipStream_t);

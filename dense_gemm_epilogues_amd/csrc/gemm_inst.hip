@@ -16,12 +16,14 @@ template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 0>(GemmArgs);
 template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 1>(GemmArgs);
 template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 2>(GemmArgs);
 template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 3>(GemmArgs);
+template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 4>(GemmArgs);
 
 #if !defined(__HIP_DEVICE_COMPILE__)
 // Host-side launcher table, indexed by tile configuration.
 extern const GemmLauncher EP_TABLE_NAME(EP_DT, EP_LAY, EP_EPI)[kNumTileCfgs];
 const GemmLauncher EP_TABLE_NAME(EP_DT, EP_LAY, EP_EPI)[kNumTileCfgs] = {
     launch_gemm<EP_DT, EP_LAY, EP_EPI, 0>, launch_gemm<EP_DT, EP_LAY, EP_EPI, 1>,
-    launch_gemm<EP_DT, EP_LAY, EP_EPI, 2>, launch_gemm<EP_DT, EP_LAY, EP_EPI, 3>};
+    launch_gemm<EP_DT, EP_LAY, EP_EPI, 2>, launch_gemm<EP_DT, EP_LAY, EP_EPI, 3>,
+    launch_gemm<EP_DT, EP_LAY, EP_EPI, 4>};
 #endif
 }  // namespace ep

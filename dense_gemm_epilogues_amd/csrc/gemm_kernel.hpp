@@ -38,10 +38,10 @@ constexpr int kGroupM = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every num_records we build
 
 // Tile configurations: workgroup rows, B-tile rows, k-step, LDS stages.
-constexpr int cfg_bm(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 128 : cfg == 2 ? 256 : 128; }
-constexpr int cfg_bnt(int cfg) { return cfg == 0 ? 256 : cfg == 1 ? 128 : cfg == 2 ? 128 : 256; }
-constexpr int cfg_bk(int cfg) { return cfg == 1 ? 64 : 32; }
-constexpr int cfg_nst(int cfg) { return 4; }
+constexpr int cfg_bm(int cfg) { return (cfg == 1 || cfg == 3) ? 128 : 256; }
+constexpr int cfg_bnt(int cfg) { return (cfg == 1 || cfg == 2) ? 128 : 256; }
+constexpr int cfg_bk(int cfg) { return (cfg == 1 || cfg == 4) ? 64 : 32; }
+constexpr int cfg_nst(int cfg) { return cfg == 4 ? 2 : 4; }
 
 template <int DT>
 struct Elem;
@@ -407,8 +407,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
   using F_ = std::integral_constant<bool, false>;
   constexpr int NMMA = MB * NB;
   constexpr int TOT = KS * NMMA;                       // MFMAs per k-step
-  constexpr int DSTRIDE = TOT / N_DMA > 0 ? TOT / N_DMA : 1;
-  constexpr int DPER = (N_DMA + TOT - 1) / TOT;        // DMA ops per issue point
+  // With only 2 stages the loads of the next stage must land before this k-step's barrier,
+  // so they are issued in the first half of the k-step; with more stages, over all of it.
+  constexpr int DWIN = NST == 2 ? TOT / 2 : TOT;
+  constexpr int DSTRIDE = DWIN / N_DMA > 0 ? DWIN / N_DMA : 1;
+  constexpr int DPER = (N_DMA + DWIN - 1) / DWIN;      // DMA ops per issue point
   auto slice = [&](auto rd_c, auto g0_c, const u32x4* A, const u32x4* B, auto t0_c, auto t1_c, int kt,
                    char* dst, const KnSrc& kr, const char* rstage, int rks, u32x4* RA, u32x4* RB) {
     constexpr bool RD = decltype(rd_c)::value;
@@ -447,9 +450,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
   // stage needed next (k-step kt+1) have landed -- everything younger may stay in flight --
   // and for its LDS reads, then s_barrier.  The memory clobber keeps the compiler from
   // moving LDS accesses across it (__syncthreads would also wait for every younger stage).
-  constexpr int VMC_LOOP = N_DMA * (NST - 3) + DPRE;   // younger loads allowed in flight
+  constexpr int VMC_LOOP = NST >= 3 ? N_DMA * (NST - 3) + DPRE : 0;  // younger loads allowed in flight
   constexpr int VMC_PRO = N_DMA * (NST - 2);           // after the prologue
-  static_assert(NST >= 3, "the ring needs at least 3 stages");
+  static_assert(NST >= 2, "the ring needs at least 2 stages");
   static_assert(VMC_LOOP <= 63 && VMC_PRO <= 63, "vmcnt range");
   auto ring_barrier = [&](auto vmc_c) {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(decltype(vmc_c)::value) : "memory");
