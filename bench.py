@@ -25,6 +25,8 @@ import numpy as np
 import torch
 
 PEAK_F16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense fp16/bf16 FLOP/clk/CU
+# read X, W, bias once; write Y and the relu_aux words once (4096^3 fp16 forward)
+ALGO_BYTES_SQ4096_FWD = 3 * 4096 * 4096 * 2 + 4096 * 2 + 4096 * 128 * 4
 METRIC = "fused GEMM+epilogue TFLOP/s, % MFMA peak, speedup vs unfused path"
 
 
@@ -39,7 +41,27 @@ def parse():
                     help="profile helper: run only one workload's fused path "
                          "(sq4096, h200, swiglu, down, dswiglu) and print its line")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--calib-copy", type=int, default=0,
+                    help="profile helper: first run one device-to-device copy of this many bytes "
+                         "(the known-size reference for HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "traffic_gemm_relu_aux_bias_f16_KN_4096.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary, or None when it is missing or was measured on different kernel sources."""
+    try:
+        from dense_gemm_epilogues_amd.profiling import read_record, source_hash
+        rec = read_record(TRAFFIC_FILE)
+        if rec.get("source_hash") != source_hash():
+            return None
+        return rec
+    except Exception:
+        return None
 
 
 class Timer:
@@ -202,6 +224,12 @@ def main():
     dev = torch.device("cuda:0")
     flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
+    if args.calib_copy:
+        src = torch.empty(args.calib_copy, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.only:
         st, wu = args.steps, args.warmup
         if args.only == "sq4096":
@@ -249,8 +277,13 @@ def main():
                      "achieved": round(fwd_tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fwd_tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
                      "algorithmic_per_launch": f"{r2['flop_per_gemm']:.6g} FLOP (2*4096^3)",
+                     "algorithmic_bytes_per_launch": ALGO_BYTES_SQ4096_FWD,
                      "avg_launch_ms": round(f2["fwd_ms"], 5)},
     }
+    tr = measured_traffic()
+    if tr is not None:
+        line["roofline"]["traffic"] = round(tr["traffic_bytes_per_launch"])
+        line["roofline"]["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     if not args.no_large:
         large = {}
         s_l, w_l = max(3, args.steps // 4), max(1, args.warmup // 2)

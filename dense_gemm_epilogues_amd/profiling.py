@@ -1,0 +1,154 @@
+"""Summaries of rocprofv3 output for this library's kernels.
+
+  python -m dense_gemm_epilogues_amd.profiling stats DIR
+      per-kernel call count and average duration from a `--kernel-trace --stats
+      --output-format csv` run (reads *_kernel_stats.csv).
+  python -m dense_gemm_epilogues_amd.profiling trace DIR
+      per (kernel, grid size) call count and average duration from the kernel trace
+      (reads *_kernel_trace.csv), so launches of one kernel at different shapes separate.
+  python -m dense_gemm_epilogues_amd.profiling traffic FETCH_DIR WRITE_DIR KERNEL_SUBSTR \
+      --copy-bytes B [--grid G] [--out FILE]
+      HBM bytes per launch of the kernel whose name contains KERNEL_SUBSTR (and, with
+      --grid, whose grid size is G), from a `--pmc FETCH_SIZE` run and a `--pmc WRITE_SIZE`
+      run (KiB per dispatch).  Each counter is scaled by what it reads for a plain device
+      copy of B bytes recorded in the same run (the largest dispatch of a kernel whose name
+      contains "copy"), and the result is tagged with the hash of the kernel sources it was
+      measured on.
+
+A traffic file is '#' comment lines (how it was made) followed by one JSON object;
+read_record() parses it.  source_hash() is the hash of the HIP/C++ sources of libep.so; a stored traffic figure is
+only valid while it matches.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(_HERE, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_record(path):
+    with open(path) as f:
+        return json.loads("".join(l for l in f if not l.startswith("#")))
+
+
+def _find(d, pattern):
+    hits = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no {pattern} under {d}")
+    return hits[0]
+
+
+def kernel_stats(d):
+    """[(name, calls, avg_ns, total_ns)] sorted by total time."""
+    rows = list(csv.DictReader(open(_find(d, "*kernel_stats.csv"))))
+    out = []
+    for r in rows:
+        out.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["TotalDurationNs"])))
+    return sorted(out, key=lambda x: -x[3])
+
+
+def kernel_trace(d):
+    """[(name, grid, calls, avg_ns)] from the per-dispatch kernel trace."""
+    rows = list(csv.DictReader(open(_find(d, "*kernel_trace.csv"))))
+    acc = defaultdict(list)
+    for r in rows:
+        g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        acc[(r["Kernel_Name"], g)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = [(k[0], k[1], len(v), sum(v) / len(v)) for k, v in acc.items()]
+    return sorted(out, key=lambda x: -x[2] * x[3])
+
+
+def pmc_dispatches(d, counter):
+    """[(kernel name, grid size, value)] per dispatch for one counter."""
+    rows = list(csv.DictReader(open(_find(d, "*counter_collection.csv"))))
+    return [(r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]))
+            for r in rows if r["Counter_Name"] == counter]
+
+
+def _mean(rows, substr, grid=None):
+    vals = [v for (k, g, v) in rows if substr in k and (grid is None or g == grid)]
+    if not vals:
+        raise KeyError(f"no dispatch of a kernel containing {substr!r}")
+    return sum(vals) / len(vals), len(vals), next(k for (k, g, v) in rows if substr in k)
+
+
+def traffic(fetch_dir, write_dir, kernel, copy_bytes, grid=None):
+    f = pmc_dispatches(fetch_dir, "FETCH_SIZE")
+    w = pmc_dispatches(write_dir, "WRITE_SIZE")
+    fk, fn, kname = _mean(f, kernel, grid)
+    wk, wn, _ = _mean(w, kernel, grid)
+    cf = max(v for (k, g, v) in f if "copy" in k)
+    cw = max(v for (k, g, v) in w if "copy" in k)
+    fetch_scale = copy_bytes / (cf * 1024.0)
+    write_scale = copy_bytes / (cw * 1024.0)
+    return {
+        "kernel": kname,
+        "grid": grid,
+        "dispatches": [fn, wn],
+        "fetch_kib_per_launch_raw": fk,
+        "write_kib_per_launch_raw": wk,
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib_raw": cf,
+        "copy_write_kib_raw": cw,
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "fetch_bytes_per_launch": fk * 1024.0 * fetch_scale,
+        "write_bytes_per_launch": wk * 1024.0 * write_scale,
+        "traffic_bytes_per_launch": fk * 1024.0 * fetch_scale + wk * 1024.0 * write_scale,
+        "source_hash": source_hash(),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    tr = sub.add_parser("trace")
+    tr.add_argument("dir")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("kernel")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--grid", type=int, default=None)
+    t.add_argument("--out")
+    t.add_argument("--how", action="append", default=[],
+                   help="command lines that produced the counter runs, kept as '#' lines")
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        for name, calls, avg, tot in kernel_stats(a.dir):
+            print(f"{calls:6d} calls  avg {avg / 1e3:11.2f} us  total {tot / 1e6:10.3f} ms  {name[:110]}")
+    elif a.cmd == "trace":
+        for name, grid, calls, avg in kernel_trace(a.dir):
+            print(f"{calls:6d} calls  grid {grid:9d}  avg {avg / 1e3:11.2f} us  {name[:100]}")
+    else:
+        r = traffic(a.fetch_dir, a.write_dir, a.kernel, a.copy_bytes, a.grid)
+        txt = json.dumps(r, indent=1)
+        if a.out:
+            with open(a.out, "w") as f:
+                for line in a.how:
+                    f.write("# " + line + "\n")
+                f.write(txt + "\n")
+        print(txt)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
