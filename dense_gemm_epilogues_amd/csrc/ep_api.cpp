@@ -17,14 +17,6 @@
 
 namespace ep {
 
-const TileCfg kTileCfgs[kNumTileCfgs] = {
-    {256, 256, 131072, 1, "256x256x32x4st"},
-    {128, 128, 131072, 1, "128x128x64x4st"},
-    {256, 128, 98304, 1, "256x128x32x4st"},
-    {128, 256, 98304, 1, "128x256x32x4st"},
-    {256, 256, 131072, 1, "256x256x64x2st"},
-};
-
 #define EP_DECL_TABLE(dt, lay, epi) extern const GemmLauncher kLaunch_##dt##_##lay##_##epi[kNumTileCfgs];
 #define EP_DECL_EPIS(dt, lay)                                                                    \
   EP_DECL_TABLE(dt, lay, 0) EP_DECL_TABLE(dt, lay, 1) EP_DECL_TABLE(dt, lay, 2)                  \
@@ -116,16 +108,19 @@ bool cfg_allowed(int cfg, bool dual, ep_b_layout lay) {
 
 int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   // Estimated time ~ rounds of resident tiles x work per tile / relative efficiency.
-  static const double kEff[kNumTileCfgs] = {1.0, 0.80, 0.92, 0.92, 0.99};
+  // Relative main-loop efficiency of each configuration, measured on MI355X at full-chip
+  // shapes (fp16/bf16, both B layouts, every epilog): 256x256x32 with 4 stages is the
+  // fastest wherever it fills the chip.
+  static const double kEff[kNumTileCfgs] = {1.0, 0.70, 0.80, 0.80, 0.85, 0.97, 0.80, 0.82};
   int best = 0;
   double best_t = 1e300;
   for (int c = 0; c < kNumTileCfgs; ++c) {
     if (!cfg_allowed(c, dual, lay)) continue;
     const int64_t bn = dual ? kTileCfgs[c].bnt / 2 : kTileCfgs[c].bnt;
     const int64_t tiles = ((m + kTileCfgs[c].bm - 1) / kTileCfgs[c].bm) * ((n + bn - 1) / bn);
-    const int64_t slots = (int64_t)cus * kTileCfgs[c].wgs_per_cu;
+    const int64_t slots = (int64_t)cus * kTileCfgs[c].occ;
     const int64_t rounds = (tiles + slots - 1) / slots;
-    const double t = (double)rounds * (double)(kTileCfgs[c].bm * bn) * kTileCfgs[c].wgs_per_cu / kEff[c];
+    const double t = (double)rounds * (double)(kTileCfgs[c].bm * bn) * kTileCfgs[c].occ / kEff[c];
     if (t < best_t * 0.999) {
       best_t = t;
       best = c;

@@ -12,11 +12,9 @@
 
 namespace ep {
 // Explicit kernel instantiations (emitted in the device pass).
-template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 0>(GemmArgs);
-template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 1>(GemmArgs);
-template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 2>(GemmArgs);
-template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 3>(GemmArgs);
-template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, 4>(GemmArgs);
+#define EP_INST(c) template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, c>(GemmArgs);
+EP_INST(0) EP_INST(1) EP_INST(2) EP_INST(3) EP_INST(4) EP_INST(5) EP_INST(6) EP_INST(7)
+static_assert(kNumTileCfgs == 8, "instantiate every tile configuration");
 
 #if !defined(__HIP_DEVICE_COMPILE__)
 // Host-side launcher table, indexed by tile configuration.
@@ -24,6 +22,7 @@ extern const GemmLauncher EP_TABLE_NAME(EP_DT, EP_LAY, EP_EPI)[kNumTileCfgs];
 const GemmLauncher EP_TABLE_NAME(EP_DT, EP_LAY, EP_EPI)[kNumTileCfgs] = {
     launch_gemm<EP_DT, EP_LAY, EP_EPI, 0>, launch_gemm<EP_DT, EP_LAY, EP_EPI, 1>,
     launch_gemm<EP_DT, EP_LAY, EP_EPI, 2>, launch_gemm<EP_DT, EP_LAY, EP_EPI, 3>,
-    launch_gemm<EP_DT, EP_LAY, EP_EPI, 4>};
+    launch_gemm<EP_DT, EP_LAY, EP_EPI, 4>, launch_gemm<EP_DT, EP_LAY, EP_EPI, 5>,
+    launch_gemm<EP_DT, EP_LAY, EP_EPI, 6>, launch_gemm<EP_DT, EP_LAY, EP_EPI, 7>};
 #endif
 }  // namespace ep

@@ -1,20 +1,23 @@
 // Fused GEMM + epilogue kernel for CDNA4 (gfx950).
 //
-// One workgroup (4 wave64s in a 2x2 grid) computes a BM x BN output tile:
-//   * A and B tiles of 64 k-values are staged in LDS, double buffered, in a k-contiguous
-//     layout (each row = 64 elements = 128 bytes = 8 chunks of 16 bytes) with chunk c of row
-//     r stored at chunk c ^ ((r ^ r>>3) & 7), so that every 8 (and 16) consecutive rows read
-//     by the MFMA fragment loads hit distinct banks.
-//   * Global loads are 16-byte buffer loads (hardware bounds checks give zeros past the
-//     matrix edges).  A B operand given K x N (N contiguous) is transposed in registers
-//     (8 k-rows x 8 columns per thread) before it is written to LDS, so both B layouts
-//     share one LDS layout and one fragment-read path.
+// One workgroup (4 wave64s in a 2x2 grid, one workgroup per CU) computes a BM x BN output
+// tile with fp32 accumulators held in registers:
+//   * A and B tiles of BK k-values move from global memory straight into LDS with 16-byte
+//     buffer loads that write LDS (no register staging), through a ring of NST stages; the
+//     loads of k-step kt + NST - 1 are spread evenly over k-step kt.  Hardware bounds checks
+//     turn offsets past the matrix edges into zeros.
+//   * k-contiguous tiles (A, and B given N x K) keep rows of BK elements with an XOR swizzle
+//     of their 16-byte chunks, so the MFMA fragment reads are free of bank conflicts.  B given
+//     K x N (N contiguous) is kept as [BK k][128 n] sub-tiles and read with the LDS transpose
+//     read (ds_read_b64_tr_b16), which hands each lane the k-run of one column.
 //   * The K loop issues v_mfma_f32_32x32x16_{f16,bf16}: lane l of a 32x32 block holds
-//     column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 of its 16 accumulator registers.
-//   * The epilogue runs on the float32 accumulators: each wave stages a 32-row slab through
+//     column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 of its 16 accumulator registers.  The
+//     order of MFMAs, fragment reads and loads inside a k-step is fixed explicitly, and the
+//     barrier between k-steps waits only for the stage needed next.
+//   * The epilogue runs on the fp32 accumulators: each wave stages a 32-row slab through
 //     LDS so that every lane owns 4 consecutive columns of one row, applies the epilog
 //     (bias, ReLU, mask packing, mask application + column sums, SiLU*mul, dSwiGLU) in
-//     float32 and writes each output once, with 8-byte row-contiguous stores.
+//     fp32 and writes each output once, with 8-byte row-contiguous stores.
 //
 // Epilogs follow "Fusing Matmul Epilogs with nvmath-python" (forward: RELU_BIAS,
 // RELU_AUX_BIAS; backward: DRELU_BGRAD), the hotdry.top cuBLASLt post (BIAS, the
@@ -37,11 +40,11 @@ constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every num_records we build
 
-// Tile configurations: workgroup rows, B-tile rows, k-step, LDS stages.
-constexpr int cfg_bm(int cfg) { return (cfg == 1 || cfg == 3) ? 128 : 256; }
-constexpr int cfg_bnt(int cfg) { return (cfg == 1 || cfg == 2) ? 128 : 256; }
-constexpr int cfg_bk(int cfg) { return (cfg == 1 || cfg == 4) ? 64 : 32; }
-constexpr int cfg_nst(int cfg) { return cfg == 4 ? 2 : 4; }
+constexpr int cfg_bm(int cfg) { return kTileCfgs[cfg].bm; }
+constexpr int cfg_bnt(int cfg) { return kTileCfgs[cfg].bnt; }
+constexpr int cfg_bk(int cfg) { return kTileCfgs[cfg].bk; }
+constexpr int cfg_nst(int cfg) { return kTileCfgs[cfg].nst; }
+constexpr int cfg_occ(int cfg) { return kTileCfgs[cfg].occ; }
 
 template <int DT>
 struct Elem;
@@ -119,11 +122,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// byte offset of 16-byte chunk `c` of row `r` in a k-contiguous LDS tile
-__device__ __forceinline__ uint32_t swz(int r, int c) {
-  return (uint32_t)(r * 128 + (((c ^ r ^ (r >> 3)) & 7) << 4));
-}
-
 // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a contiguous range
 // of the tile order so that tiles sharing A rows / B columns share that XCD's L2, and
 // walk tiles in groups of kGroupM tile-rows.
@@ -142,13 +140,13 @@ __device__ __forceinline__ void map_tile(int bid, int nblocks, int tiles_m, int 
 }
 
 // XOR swizzle of the 16-byte chunks of an LDS tile row (CPR chunks per row): chunk c of row r
-// is stored at chunk c ^ swf(r).  For 8 chunks (128-byte rows) every 8 and every 16
-// consecutive rows read at one logical chunk land on distinct banks; for 4 chunks (64-byte
-// rows) the same holds for (row mod 2, chunk) and (row mod 4, chunk) pairs.
+// is stored at chunk c ^ swf(r).  With this function the fragment reads (32 consecutive rows
+// at one logical chunk per half-wave, ds_read_b128) run without LDS bank conflicts for both
+// 64-byte and 128-byte rows on gfx950, as measured with SQ_LDS_BANK_CONFLICT; the variant
+// ((r >> 1) ^ (r >> 3)) & 3 for 64-byte rows doubled the LDS cycles of every read.
 template <int CPR>
 __device__ __forceinline__ int swf(int r) {
-  if constexpr (CPR == 8) return (r ^ (r >> 3)) & 7;
-  else return ((r >> 1) ^ (r >> 3)) & 3;
+  return (r ^ (r >> 3)) & (CPR - 1);
 }
 
 template <int DT, int LAY, int EPI, int CFG>
@@ -184,11 +182,11 @@ struct GemmTraits {
   static_assert(LPR >= 8 && LPR <= 64, "a relu_aux word must span whole lanes");
   static_assert(KS == 2 || KS == 4, "k-slices per step must be even");
   static_assert(A_SLOTS >= 1 && B_SLOTS >= 1, "tile too small for 1 KiB DMA slots");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(LDS_BYTES * cfg_occ(CFG) <= 160 * 1024, "LDS budget");
 };
 
 template <int DT, int LAY, int EPI, int CFG>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p) {
   using E = Elem<DT>;
   using TR = GemmTraits<DT, LAY, EPI, CFG>;
   constexpr bool DUAL = TR::DUAL;
@@ -513,8 +511,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
   }
   f32x4 colsum = {0.f, 0.f, 0.f, 0.f};
 
+  // Epilog inputs read per element are fetched for a whole 32-row slab before its
+  // accumulators are staged, so their latency overlaps the staging instead of stalling
+  // every row.  DSWIGLU: each lane's gate and up values.  DRELU_BGRAD: the slab's mask
+  // words (WPR per row) spread over the wave, NW per lane, and handed to the lanes that use
+  // them with a cross-lane read.
+  constexpr int WPR = WTN / 32;                   // mask words per staged row
+  constexpr int NW = WPR / 2 > 0 ? WPR / 2 : 1;   // mask words per lane per slab
+  constexpr int RPW = 64 / WPR;                   // slab rows covered by one word register
+  static_assert(EPI != E_DRELU_BGRAD || (WPR == 2 || WPR == 4), "mask prefetch layout");
+  constexpr int PF_GU = EPI == E_DSWIGLU ? TR::ITERS : 1;
+  uint32_t pf_w[NW];
+  u32x2 pf_g[PF_GU], pf_u[PF_GU];
+
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
+    if constexpr (EPI == E_DRELU_BGRAD) {
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        const int grow = m0 + wm * WTM + i * 32 + q * RPW + lane / WPR;
+        const int wcol = (n0 + wn * WTN) / 32 + lane % WPR;
+        const bool ok = grow < M && wcol * 32 < N;
+        pf_w[q] = ok ? p.aux_in[(int64_t)grow * p.ld_aux + wcol] : 0u;
+      }
+    } else if constexpr (EPI == E_DSWIGLU) {
+#pragma unroll
+      for (int it = 0; it < TR::ITERS; ++it) {
+        const int grow = m0 + wm * WTM + i * 32 + it * TR::RPI + lr;
+        const bool ok = colok && grow < M;
+        const int64_t go = ((int64_t)grow * p.ld_gu + gcol) * 2;
+        pf_g[it] = ok ? __builtin_nontemporal_load((const u32x2*)((const char*)p.gate + go)) : u32x2{0u, 0u};
+        pf_u[it] = ok ? __builtin_nontemporal_load((const u32x2*)((const char*)p.up + go)) : u32x2{0u, 0u};
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       float* arr = stg + (DUAL ? (j / NBO) * 32 * SP : 0);
@@ -526,7 +555,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
       }
     }
     __syncthreads();
-#pragma unroll 2
+    constexpr int EPI_UNROLL = EPI == E_DSWIGLU ? TR::ITERS : 2;
+#pragma unroll EPI_UNROLL
     for (int it = 0; it < TR::ITERS; ++it) {
       const int lrow = it * TR::RPI + lr;
       const int grow = m0 + wm * WTM + i * 32 + lrow;
@@ -556,7 +586,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
           if (ok && (lane & 7) == 0) p.aux_out[(int64_t)grow * p.ld_aux + (gcol >> 5)] = w;
         }
       } else if constexpr (EPI == E_DRELU_BGRAD) {
-        const uint32_t word = ok ? p.aux_in[(int64_t)grow * p.ld_aux + (gcol >> 5)] : 0u;
+        // word (row lrow, column word lc / 32) sits in register lrow / RPW of lane
+        // (lrow % RPW) * WPR + lc / 32; lrow / RPW is the same for every lane of an iteration
+        const int q = (it * TR::RPI) / RPW;
+        const uint32_t src = NW == 1 ? pf_w[0] : (q ? pf_w[NW - 1] : pf_w[0]);
+        const uint32_t word = (uint32_t)__shfl((int)src, (lrow % RPW) * WPR + (lc >> 5));
         const uint32_t bits = word >> (gcol & 31);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = ((bits >> e) & 1u) ? v[e] : 0.0f;
@@ -570,9 +604,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs p) {
         if (ok) *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(h);
       } else if constexpr (EPI == E_DSWIGLU) {
         if (ok) {
-          const int64_t go = ((int64_t)grow * p.ld_gu + gcol) * 2;
-          const f32x4 g = unpack4<DT>(*(const u32x2*)((const char*)p.gate + go));
-          const f32x4 u = unpack4<DT>(*(const u32x2*)((const char*)p.up + go));
+          const f32x4 g = unpack4<DT>(pf_g[it]);
+          const f32x4 u = unpack4<DT>(pf_u[it]);
           f32x4 dg, du;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -616,16 +649,5 @@ void launch_gemm(const GemmArgs& a, hipStream_t s) {
   const int nblocks = a.tiles_m * a.tiles_n;
   hipLaunchKernelGGL((gemm_kernel<DT, LAY, EPI, CFG>), dim3(nblocks), dim3(kThreads), 0, s, a);
 }
-
-#define EP_LAUNCH_ROW(DT, LAY, EPI) \
-  { launch_gemm<DT, LAY, EPI, 0>, launch_gemm<DT, LAY, EPI, 1>, launch_gemm<DT, LAY, EPI, 2>, launch_gemm<DT, LAY, EPI, 3> }
-
-#define EP_LAUNCH_TABLE(DT, LAY)                                                              \
-  {                                                                                           \
-    EP_LAUNCH_ROW(DT, LAY, E_DEFAULT), EP_LAUNCH_ROW(DT, LAY, E_BIAS),                        \
-        EP_LAUNCH_ROW(DT, LAY, E_RELU_BIAS), EP_LAUNCH_ROW(DT, LAY, E_RELU_AUX_BIAS),         \
-        EP_LAUNCH_ROW(DT, LAY, E_DRELU_BGRAD), EP_LAUNCH_ROW(DT, LAY, E_SWIGLU),              \
-        EP_LAUNCH_ROW(DT, LAY, E_DSWIGLU)                                                     \
-  }
 
 }  // namespace ep

@@ -43,7 +43,8 @@ def test_library_exports_every_declared_function(L):
 
 def test_abi_version_and_status_strings(L):
     assert L.ep_abi_version() == 1
-    assert L.ep_num_tile_cfgs() >= 1
+    from tests.test_parity_small_gpu import NUM_TILE_CFGS
+    assert L.ep_num_tile_cfgs() == NUM_TILE_CFGS
     for code, name in ep.STATUS.items():
         assert L.ep_status_string(code).decode() == name
     assert L.ep_status_string(99).decode() == "EP_ERR_UNKNOWN"

@@ -117,13 +117,19 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0):
     p.free()
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+# tile configurations 0-7 of the library; those with a 128-row B tile cannot hold the gate
+# and up sub-tiles of a K x N dual B operand
+NUM_TILE_CFGS = 8
+BNT128_CFGS = (1, 2, 6)
+
+
+@pytest.mark.parametrize("cfg", list(range(NUM_TILE_CFGS)))
 @pytest.mark.parametrize("layout", ["KN", "NK"])
 @pytest.mark.parametrize("dtname", ["f16", "bf16"])
 @pytest.mark.parametrize("epi", EPIS)
 def test_small_shapes_fused(epi, dtname, layout, cfg):
     require_gpu()
-    if epi == "SWIGLU" and layout == "KN" and cfg in (1, 2):
+    if epi == "SWIGLU" and layout == "KN" and cfg in BNT128_CFGS:
         import dense_gemm_epilogues_amd as ep
         dev = torch.device("cuda")
         a = torch.zeros((64, 64), dtype=DTYPES[dtname], device=dev)
