@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--no-large", action="store_true", help="skip the large-workload summary")
     ap.add_argument("--only", default=None,
                     help="profile helper: run only one workload's fused path "
-                         "(sq4096, h200, swiglu, down, dswiglu) and print its line")
+                         "(sq4096, h200, swiglu, dswiglu) and print its line")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="profile helper: first run one device-to-device copy of this many bytes "

@@ -29,8 +29,6 @@ FLAGS = [
 N_EPI = 7
 
 
-
-
 def _compile(args):
     src, obj, defines = args
     cmd = [HIPCC] + FLAGS + defines + ["-c", src, "-o", obj]

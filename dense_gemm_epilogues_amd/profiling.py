@@ -6,6 +6,11 @@
   python -m dense_gemm_epilogues_amd.profiling trace DIR
       per (kernel, grid size) call count and average duration from the kernel trace
       (reads *_kernel_trace.csv), so launches of one kernel at different shapes separate.
+  python -m dense_gemm_epilogues_amd.profiling counters PMC_DIR [PMC_DIR ...] --trace TRACE_DIR
+      per (kernel, grid size) averages of every counter in the `--pmc` runs, with the
+      sustained shader clock (GRBM_GUI_ACTIVE / XCDs / duration), the MFMA busy fraction
+      (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x SIMDs)) and the LDS bank-conflict fraction
+      (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE); durations come from the kernel trace.
   python -m dense_gemm_epilogues_amd.profiling traffic FETCH_DIR WRITE_DIR KERNEL_SUBSTR \
       --copy-bytes B [--grid G] [--out FILE]
       HBM bytes per launch of the kernel whose name contains KERNEL_SUBSTR (and, with
@@ -81,6 +86,44 @@ def pmc_dispatches(d, counter):
             for r in rows if r["Counter_Name"] == counter]
 
 
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU.  GRBM_GUI_ACTIVE counts busy cycles per XCD and
+# rocprofv3 sums it over the XCDs; SQ_VALU_MFMA_BUSY_CYCLES sums over every SIMD.
+XCDS, SIMDS = 8, 256 * 4
+
+
+def counters(pmc_dirs, trace_dir):
+    """[(name, grid, n, {counter: mean}, derived)] for every kernel in the counter runs."""
+    per = defaultdict(lambda: defaultdict(list))
+    for d in pmc_dirs:
+        disp = defaultdict(dict)
+        for r in csv.DictReader(open(_find(d, "*counter_collection.csv"))):
+            key = (r["Kernel_Name"], int(r["Grid_Size"]))
+            disp[(key, r["Dispatch_Id"])][r["Counter_Name"]] = float(r["Counter_Value"])
+        for (key, _), cs in disp.items():
+            for c, v in cs.items():
+                per[key][c].append(v)
+    dur = {(n, g): avg for (n, g, _, avg) in kernel_trace(trace_dir)}
+    out = []
+    for key, cs in per.items():
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        der = {}
+        t = dur.get(key)
+        if t and "GRBM_GUI_ACTIVE" in mean:
+            cyc = mean["GRBM_GUI_ACTIVE"] / XCDS
+            der["duration_us"] = t / 1e3
+            der["clock_GHz"] = cyc / t
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                der["mfma_busy"] = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS)
+        if mean.get("SQ_LDS_IDX_ACTIVE"):
+            der["lds_bank_conflict_frac"] = mean.get("SQ_LDS_BANK_CONFLICT", 0.0) / mean["SQ_LDS_IDX_ACTIVE"]
+        out.append((key[0], key[1], max(len(v) for v in cs.values()), mean, der))
+    return sorted(out, key=lambda x: -der_time(x))
+
+
+def der_time(x):
+    return x[4].get("duration_us", 0.0)
+
+
 def _mean(rows, substr, grid=None):
     vals = [v for (k, g, v) in rows if substr in k and (grid is None or g == grid)]
     if not vals:
@@ -122,6 +165,10 @@ def main(argv=None):
     s.add_argument("dir")
     tr = sub.add_parser("trace")
     tr.add_argument("dir")
+    c = sub.add_parser("counters")
+    c.add_argument("pmc_dirs", nargs="+")
+    c.add_argument("--trace", required=True)
+    c.add_argument("--only", default="gemm_kernel")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
@@ -135,6 +182,13 @@ def main(argv=None):
     if a.cmd == "stats":
         for name, calls, avg, tot in kernel_stats(a.dir):
             print(f"{calls:6d} calls  avg {avg / 1e3:11.2f} us  total {tot / 1e6:10.3f} ms  {name[:110]}")
+    elif a.cmd == "counters":
+        for name, grid, n, mean, der in counters(a.pmc_dirs, a.trace):
+            if a.only not in name:
+                continue
+            print(f"{name[:60]}  grid {grid}  dispatches {n}")
+            print("    " + "  ".join(f"{k}={v:.4g}" for k, v in der.items()))
+            print("    " + "  ".join(f"{k}={v:.4g}" for k, v in sorted(mean.items())))
     elif a.cmd == "trace":
         for name, grid, calls, avg in kernel_trace(a.dir):
             print(f"{calls:6d} calls  grid {grid:9d}  avg {avg / 1e3:11.2f} us  {name[:100]}")
