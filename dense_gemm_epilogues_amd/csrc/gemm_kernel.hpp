@@ -97,6 +97,15 @@ __device__ __forceinline__ f32x4 unpack4(u32x2 w) {
   return v;
 }
 
+// Copy of one accumulator register for VALU use.  The operand constraint keeps the
+// accumulators in AGPRs up to each use, so the epilogue copies them one at a time instead of
+// moving all of them into VGPRs when the K loop ends.
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 // Logistic function from its definition, 1 / (1 + e^-t), with e^-t = 2^(-t log2 e) on the
 // hardware exp2.  t -> -inf gives 2^(+inf) = inf and 1/inf = 0; t -> +inf gives 1.
 __device__ __forceinline__ float sigmoid_f(float t) {
@@ -171,15 +180,22 @@ struct GemmTraits {
   static constexpr int KN_SUB = BK * 256;        // bytes of one [BK k][128 n] sub-tile
   static constexpr int KN_SPS = BK / 4;          // DMA slots per sub-tile
   static constexpr int SPITCH = WTN + 8;         // staging pitch in floats
-  static constexpr int NARR = DUAL ? 2 : 1;
-  static constexpr int STG_FLOATS = NARR * 32 * SPITCH;  // per wave
+  static constexpr int STG_FLOATS = 32 * SPITCH;  // per wave: one 32-row slab of the output
   static constexpr int BG_OFF = 4 * STG_FLOATS * 4;      // bytes; cross-wave bgrad exchange
-  static constexpr int EPI_BYTES = BG_OFF + 2 * WTN * 4;
+  static constexpr int MASK_OFF = BG_OFF + 2 * WTN * 4;  // bytes; one slab's mask words per M-wave
+  static constexpr int WPT = BN_OUT / 32;                  // mask words per tile row
+  static constexpr int EPI_BYTES = MASK_OFF + 2 * 32 * WPT * 4;
   static constexpr int LDS_BYTES = (NST * STAGE > EPI_BYTES) ? NST * STAGE : EPI_BYTES;
   static constexpr int LPR = WTN / 4;            // lanes per staged row
   static constexpr int RPI = 64 / LPR;           // staged rows per iteration
   static constexpr int ITERS = 32 / RPI;
-  static_assert(LPR >= 8 && LPR <= 64, "a relu_aux word must span whole lanes");
+  static_assert(LPR >= 8 && LPR <= 64, "staged rows must span whole lanes");
+  static constexpr int NBO = DUAL ? NB / 2 : NB;  // accumulator blocks per output column range
+  static_assert(DUAL || NBO == 2 || NBO == 4, "mask words per slab row must be 2 or 4");
+  static_assert(!DUAL || NBO >= 1, "dual B needs a block per output column range");
+  // staged rows per chunk of the store loop: 8 rows read together where the epilog is a plain
+  // store; one row at a time where it has per-row inputs (measured faster on MI355X)
+  static constexpr int CH = (EPI == E_DSWIGLU || EPI == E_DRELU_BGRAD) ? 1 : (ITERS < 8 ? ITERS : 8);
   static_assert(KS == 2 || KS == 4, "k-slices per step must be even");
   static_assert(A_SLOTS >= 1 && B_SLOTS >= 1, "tile too small for 1 KiB DMA slots");
   static_assert(LDS_BYTES * cfg_occ(CFG) <= 160 * 1024, "LDS budget");
@@ -497,125 +513,175 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
+  // Accumulator layout: lane l of 32x32 block (i, j) holds column 32 j + l%32 of the wave's
+  // columns and, in register r, row 8 (r/4) + 4 (l/32) + r%4 of the block's 32 rows.
+  // Everything that needs only the column (bias, ReLU, the mask bits, SiLU*mul, the masked
+  // column sums) is applied to the accumulators in place; then each 32-row slab is staged
+  // through LDS so that every lane owns 4 consecutive columns of one row for the stores.
+  constexpr int NBO = TR::NBO;
+  constexpr bool HAS_BIAS = EPI == E_BIAS || EPI == E_RELU_BIAS || EPI == E_RELU_AUX_BIAS;
+  constexpr bool RELU = EPI == E_RELU_BIAS || EPI == E_RELU_AUX_BIAS;
+  const int l32 = lane & 31;
+  const int ccol0 = n0 + wn * WTN;  // first output column of the wave
   float* stg = (float*)smem + wave * TR::STG_FLOATS;
   constexpr int SP = TR::SPITCH;
-  constexpr int NBO = DUAL ? NB / 2 : NB;  // blocks per staged array
-  const int lr = lane / TR::LPR;           // row within an iteration
-  const int lc = (lane % TR::LPR) * 4;     // staged column
-  const int gcol = n0 + wn * WTN + lc;
+  const int lr = lane / TR::LPR;        // staged row within an iteration
+  const int lc = (lane % TR::LPR) * 4;  // staged column
+  const int gcol = ccol0 + lc;
   const bool colok = gcol < N;
 
-  f32x4 bias4 = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (EPI == E_BIAS || EPI == E_RELU_BIAS || EPI == E_RELU_AUX_BIAS) {
-    if (colok) bias4 = unpack4<DT>(*(const u32x2*)((const char*)p.bias + (int64_t)gcol * 2));
+  float bias_mf[NBO];
+#pragma unroll
+  for (int j = 0; j < NBO; ++j) {
+    bias_mf[j] = 0.0f;
+    if constexpr (HAS_BIAS) {
+      const int c = ccol0 + 32 * j + l32;
+      if (c < N) bias_mf[j] = E::to_f32(((const uint16_t*)p.bias)[c]);
+    }
   }
-  f32x4 colsum = {0.f, 0.f, 0.f, 0.f};
+  f32x4 colsum = {0.f, 0.f, 0.f, 0.f};  // DRELU_BGRAD: sums of the lane's 4 staged columns
 
-  // Epilog inputs read per element are fetched for a whole 32-row slab before its
-  // accumulators are staged, so their latency overlaps the staging instead of stalling
-  // every row.  DSWIGLU: each lane's gate and up values.  DRELU_BGRAD: the slab's mask
-  // words (WPR per row) spread over the wave, NW per lane, and handed to the lanes that use
-  // them with a cross-lane read.
-  constexpr int WPR = WTN / 32;                   // mask words per staged row
-  constexpr int NW = WPR / 2 > 0 ? WPR / 2 : 1;   // mask words per lane per slab
-  constexpr int RPW = 64 / WPR;                   // slab rows covered by one word register
-  static_assert(EPI != E_DRELU_BGRAD || (WPR == 2 || WPR == 4), "mask prefetch layout");
+  // DRELU_BGRAD: the slab's mask words (32 rows x WPR words) are fetched before it is staged,
+  // NW per lane: word (row, w) sits in register row / RPW of lane (row % RPW) * WPR + w.
+  constexpr int WPR = NBO;
+  constexpr int NW = WPR / 2 > 0 ? WPR / 2 : 1;
+  constexpr int RPW = 64 / WPR;
+  // DSWIGLU reads gate and up per element in the staged layout, for a whole slab before it
+  // is staged, so their latency overlaps the staging.
   constexpr int PF_GU = EPI == E_DSWIGLU ? TR::ITERS : 1;
-  uint32_t pf_w[NW];
   u32x2 pf_g[PF_GU], pf_u[PF_GU];
 
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
+    const int srow0 = m0 + wm * WTM + i * 32;  // first row of the slab
+    uint32_t pf_w[NW];
     if constexpr (EPI == E_DRELU_BGRAD) {
 #pragma unroll
       for (int q = 0; q < NW; ++q) {
-        const int grow = m0 + wm * WTM + i * 32 + q * RPW + lane / WPR;
-        const int wcol = (n0 + wn * WTN) / 32 + lane % WPR;
-        const bool ok = grow < M && wcol * 32 < N;
-        pf_w[q] = ok ? p.aux_in[(int64_t)grow * p.ld_aux + wcol] : 0u;
+        const int grow = srow0 + q * RPW + lane / WPR;
+        const int wc = ccol0 / 32 + lane % WPR;
+        pf_w[q] = (grow < M && wc * 32 < N) ? p.aux_in[(int64_t)grow * p.ld_aux + wc] : 0u;
       }
     } else if constexpr (EPI == E_DSWIGLU) {
 #pragma unroll
       for (int it = 0; it < TR::ITERS; ++it) {
-        const int grow = m0 + wm * WTM + i * 32 + it * TR::RPI + lr;
+        const int grow = srow0 + it * TR::RPI + lr;
         const bool ok = colok && grow < M;
         const int64_t go = ((int64_t)grow * p.ld_gu + gcol) * 2;
         pf_g[it] = ok ? __builtin_nontemporal_load((const u32x2*)((const char*)p.gate + go)) : u32x2{0u, 0u};
         pf_u[it] = ok ? __builtin_nontemporal_load((const u32x2*)((const char*)p.up + go)) : u32x2{0u, 0u};
       }
     }
+
+    // ---- accumulator space, then the slab is staged
+    uint32_t* mk = (uint32_t*)(smem + TR::MASK_OFF) + wm * 32 * TR::WPT;  // [32 rows][WPT words]
+    constexpr bool XFORM = HAS_BIAS || EPI == E_SWIGLU;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      float* arr = stg + (DUAL ? (j / NBO) * 32 * SP : 0);
-      const int col = (j % NBO) * 32 + (lane & 31);
+    for (int j = 0; j < NBO; ++j) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * hlf + (r & 3);
-        arr[row * SP + col] = acc[i][j][r];
+        const int r0 = 8 * (r >> 2) + (r & 3);  // block row held by lanes 0-31 (lanes 32-63: +4)
+        float v;
+        if constexpr (XFORM) v = acc_read(acc[i][j][r]);
+        else v = acc[i][j][r];
+        if constexpr (HAS_BIAS) v += bias_mf[j];
+        if constexpr (RELU) {
+          const bool pr = v > 0.0f;
+          v = pr ? v : 0.0f;
+          if constexpr (EPI == E_RELU_AUX_BIAS) {
+            // bit l of the ballot is column 32 j + l%32 of row r0 (l < 32) or r0 + 4 (l >= 32)
+            // (every lane writes the same wave-uniform word to the same LDS address)
+            const uint64_t b = __builtin_amdgcn_ballot_w64(pr);
+            mk[r0 * TR::WPT + wn * NBO + j] = (uint32_t)b;
+            mk[(r0 + 4) * TR::WPT + wn * NBO + j] = (uint32_t)(b >> 32);
+          }
+        } else if constexpr (EPI == E_SWIGLU) {
+          // block j holds the gate columns, block j + NB/2 the up columns of the same outputs
+          const float u = acc_read(acc[i][j + NB / 2][r]);
+          v = v * sigmoid_f(v) * u;
+        }
+        // staged right away (row 8 (r/4) + 4 (l/32) + r%4 of the slab, column 32 j + l%32)
+        stg[(r0 + 4 * hlf) * SP + j * 32 + l32] = v;
+        // one register at a time: otherwise the scheduler hoists every ballot / lane read
+        // of the slab and runs out of scalar registers
+        if constexpr (EPI == E_RELU_AUX_BIAS) __builtin_amdgcn_sched_barrier(0);
       }
     }
+
     __syncthreads();
-    constexpr int EPI_UNROLL = EPI == E_DSWIGLU ? TR::ITERS : 2;
-#pragma unroll EPI_UNROLL
-    for (int it = 0; it < TR::ITERS; ++it) {
-      const int lrow = it * TR::RPI + lr;
-      const int grow = m0 + wm * WTM + i * 32 + lrow;
-      const bool ok = colok && grow < M;
-      f32x4 v = *(const f32x4*)(stg + lrow * SP + lc);
-      const int64_t drow = (int64_t)grow * p.ldd;
-      if constexpr (EPI == E_DEFAULT) {
-        if (ok) *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(v);
-      } else if constexpr (EPI == E_BIAS) {
-        v += bias4;
-        if (ok) *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(v);
-      } else if constexpr (EPI == E_RELU_BIAS || EPI == E_RELU_AUX_BIAS) {
-        v += bias4;
-        uint32_t nib = 0;
+
+    if constexpr (EPI == E_RELU_AUX_BIAS) {
+      // the tile's words of the slab's 32 rows: one contiguous piece of WPT words per row,
+      // written by the wn = 0 wave (words past ceil(N / 32) are not part of the row)
+      if (wn == 0) {
+        constexpr int LPRW = TR::WPT / 4;  // lanes per row, 4 words (16 bytes) each
+        const int nw = (N + 31) / 32;
+        const bool vec = (((uintptr_t)p.aux_out | (uintptr_t)(p.ld_aux * 4)) & 15) == 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool pr = v[e] > 0.0f;
-          v[e] = pr ? v[e] : 0.0f;
-          nib |= (pr ? 1u : 0u) << e;
-        }
-        if (ok) *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(v);
-        if constexpr (EPI == E_RELU_AUX_BIAS) {
-          uint32_t w = (colok ? nib : 0u) << (4 * (lane & 7));
-          w |= (uint32_t)__shfl_xor((int)w, 1);
-          w |= (uint32_t)__shfl_xor((int)w, 2);
-          w |= (uint32_t)__shfl_xor((int)w, 4);
-          if (ok && (lane & 7) == 0) p.aux_out[(int64_t)grow * p.ld_aux + (gcol >> 5)] = w;
-        }
-      } else if constexpr (EPI == E_DRELU_BGRAD) {
-        // word (row lrow, column word lc / 32) sits in register lrow / RPW of lane
-        // (lrow % RPW) * WPR + lc / 32; lrow / RPW is the same for every lane of an iteration
-        const int q = (it * TR::RPI) / RPW;
-        const uint32_t src = NW == 1 ? pf_w[0] : (q ? pf_w[NW - 1] : pf_w[0]);
-        const uint32_t word = (uint32_t)__shfl((int)src, (lrow % RPW) * WPR + (lc >> 5));
-        const uint32_t bits = word >> (gcol & 31);
+        for (int pass = 0; pass < (32 * LPRW + 63) / 64; ++pass) {
+          const int t = pass * 64 + lane;
+          const int row = t / LPRW, part = t % LPRW;
+          const int grow = srow0 + row;
+          const int w0 = n0 / 32 + part * 4;
+          if (row < 32 && grow < M && w0 < nw) {
+            const u32x4 v = *(const u32x4*)(mk + row * TR::WPT + part * 4);
+            uint32_t* dst = p.aux_out + (int64_t)grow * p.ld_aux + w0;
+            if (vec && w0 + 4 <= nw) {
+              *(u32x4*)dst = v;
+            } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = ((bits >> e) & 1u) ? v[e] : 0.0f;
-        if (ok) *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(v);
-        colsum += v;
-      } else if constexpr (EPI == E_SWIGLU) {
-        const f32x4 u = *(const f32x4*)(stg + 32 * SP + lrow * SP + lc);
-        f32x4 h;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = v[e] * sigmoid_f(v[e]) * u[e];
-        if (ok) *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(h);
-      } else if constexpr (EPI == E_DSWIGLU) {
-        if (ok) {
-          const f32x4 g = unpack4<DT>(pf_g[it]);
-          const f32x4 u = unpack4<DT>(pf_u[it]);
-          f32x4 dg, du;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float s = sigmoid_f(g[e]);
-            const float t = v[e] * s;             // dh * s
-            du[e] = t * g[e];                     // dh * silu(g)
-            dg[e] = t * u[e] * (1.0f + g[e] * (1.0f - s));
+              for (int e = 0; e < 4; ++e)
+                if (w0 + e < nw) dst[e] = v[e];
+            }
           }
-          *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(dg);
-          *(u32x2*)((char*)p.d2 + ((int64_t)grow * p.ldd2 + gcol) * 2) = pack4<DT>(du);
+        }
+      }
+    }
+
+    // ---- stores: CH staged rows per chunk, their LDS reads issued together
+    constexpr int OUTER_UNROLL = EPI == E_DRELU_BGRAD ? 2 : TR::ITERS;
+#pragma unroll OUTER_UNROLL
+    for (int c0 = 0; c0 < TR::ITERS; c0 += TR::CH) {
+      f32x4 vv[TR::CH];
+#pragma unroll
+      for (int c = 0; c < TR::CH; ++c) vv[c] = *(const f32x4*)(stg + ((c0 + c) * TR::RPI + lr) * SP + lc);
+      if constexpr (EPI == E_DRELU_BGRAD) {
+        uint32_t wd[TR::CH];
+#pragma unroll
+        for (int c = 0; c < TR::CH; ++c) {
+          const int lrow = (c0 + c) * TR::RPI + lr;
+          const int q = ((c0 + c) * TR::RPI) / RPW;  // the same for every lane of the row group
+          const uint32_t src = NW == 1 ? pf_w[0] : (q ? pf_w[NW - 1] : pf_w[0]);
+          wd[c] = (uint32_t)__shfl((int)src, (lrow % RPW) * WPR + (lc >> 5)) >> (gcol & 31);
+        }
+#pragma unroll
+        for (int c = 0; c < TR::CH; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[c][e] = ((wd[c] >> e) & 1u) ? vv[c][e] : 0.0f;
+      }
+#pragma unroll
+      for (int c = 0; c < TR::CH; ++c) {
+        const int grow = srow0 + (c0 + c) * TR::RPI + lr;
+        const bool ok = colok && grow < M;
+        const int64_t drow = (int64_t)grow * p.ldd;
+        if constexpr (EPI == E_DSWIGLU) {
+          if (ok) {
+            const f32x4 g = unpack4<DT>(pf_g[c0 + c]);
+            const f32x4 u = unpack4<DT>(pf_u[c0 + c]);
+            f32x4 dg, du;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sg = sigmoid_f(g[e]);
+              const float t = vv[c][e] * sg;           // dh * s
+              du[e] = t * g[e];                        // dh * silu(g)
+              dg[e] = t * u[e] * (1.0f + g[e] * (1.0f - sg));
+            }
+            *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(dg);
+            *(u32x2*)((char*)p.d2 + ((int64_t)grow * p.ldd2 + gcol) * 2) = pack4<DT>(du);
+          }
+        } else {
+          if (ok) *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(vv[c]);
+          if constexpr (EPI == E_DRELU_BGRAD) colsum += vv[c];  // rows past M staged as 0
         }
       }
     }
@@ -623,17 +689,17 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   }
 
   if constexpr (EPI == E_DRELU_BGRAD) {
-    // lanes that share columns: lane, lane + LPR, ... (different rows)
+    // lanes that share columns: lane, lane + LPR, ... (different rows); then the other
+    // M-wave's sums through LDS; one partial per (M tile, column), or an atomic add
 #pragma unroll
-    for (int s = TR::LPR; s < 64; s <<= 1)
+    for (int sh = TR::LPR; sh < 64; sh <<= 1)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) colsum[e] += __shfl_xor(colsum[e], s);
+      for (int e = 0; e < 4; ++e) colsum[e] += __shfl_xor(colsum[e], sh);
     float* bg = (float*)(smem + TR::BG_OFF) + wn * WTN;
     if (wm == 1 && lane < TR::LPR) *(f32x4*)(bg + lc) = colsum;
     __syncthreads();
     if (wm == 0 && lane < TR::LPR && colok) {
-      const f32x4 other = *(const f32x4*)(bg + lc);
-      const f32x4 tot = colsum + other;
+      const f32x4 tot = colsum + *(const f32x4*)(bg + lc);
       if (p.bgrad_atomic) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) atomicAdd(p.bgrad_part + gcol + e, tot[e]);
