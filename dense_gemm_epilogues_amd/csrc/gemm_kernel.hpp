@@ -15,9 +15,9 @@
 //     order of MFMAs, fragment reads and loads inside a k-step is fixed explicitly, and the
 //     barrier between k-steps waits only for the stage needed next.
 //   * The epilogue runs on the fp32 accumulators: each wave stages a 32-row slab through
-//     LDS so that every lane owns 4 consecutive columns of one row, applies the epilog
+//     LDS so that every lane owns 8 consecutive columns of one row, applies the epilog
 //     (bias, ReLU, mask packing, mask application + column sums, SiLU*mul, dSwiGLU) in
-//     fp32 and writes each output once, with 8-byte row-contiguous stores.
+//     fp32 and writes each output once, with 16-byte row-contiguous stores.
 //
 // Epilogs follow "Fusing Matmul Epilogs with nvmath-python" (forward: RELU_BIAS,
 // RELU_AUX_BIAS; backward: DRELU_BGRAD), the hotdry.top cuBLASLt post (BIAS, the
@@ -84,6 +84,12 @@ __device__ __forceinline__ u32x2 pack4(f32x4 v) {
   r[0] = E::from_f32(v[0]) | (E::from_f32(v[1]) << 16);
   r[1] = E::from_f32(v[2]) | (E::from_f32(v[3]) << 16);
   return r;
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 pack8(f32x4 a, f32x4 b) {
+  const u32x2 x = pack4<DT>(a), y = pack4<DT>(b);
+  return u32x4{x[0], x[1], y[0], y[1]};
 }
 
 template <int DT>
@@ -186,10 +192,10 @@ struct GemmTraits {
   static constexpr int WPT = BN_OUT / 32;                  // mask words per tile row
   static constexpr int EPI_BYTES = MASK_OFF + 2 * 32 * WPT * 4;
   static constexpr int LDS_BYTES = (NST * STAGE > EPI_BYTES) ? NST * STAGE : EPI_BYTES;
-  static constexpr int LPR = WTN / 4;            // lanes per staged row
+  static constexpr int LPR = WTN / 8;            // lanes per staged row (8 columns each)
   static constexpr int RPI = 64 / LPR;           // staged rows per iteration
   static constexpr int ITERS = 32 / RPI;
-  static_assert(LPR >= 8 && LPR <= 64, "staged rows must span whole lanes");
+  static_assert(LPR >= 4 && LPR <= 64, "staged rows must span whole lanes");
   static constexpr int NBO = DUAL ? NB / 2 : NB;  // accumulator blocks per output column range
   static_assert(DUAL || NBO == 2 || NBO == 4, "mask words per slab row must be 2 or 4");
   static_assert(!DUAL || NBO >= 1, "dual B needs a block per output column range");
@@ -517,7 +523,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // columns and, in register r, row 8 (r/4) + 4 (l/32) + r%4 of the block's 32 rows.
   // Everything that needs only the column (bias, ReLU, the mask bits, SiLU*mul, the masked
   // column sums) is applied to the accumulators in place; then each 32-row slab is staged
-  // through LDS so that every lane owns 4 consecutive columns of one row for the stores.
+  // through LDS so that every lane owns 8 consecutive columns of one row for the stores.
   constexpr int NBO = TR::NBO;
   constexpr bool HAS_BIAS = EPI == E_BIAS || EPI == E_RELU_BIAS || EPI == E_RELU_AUX_BIAS;
   constexpr bool RELU = EPI == E_RELU_BIAS || EPI == E_RELU_AUX_BIAS;
@@ -526,7 +532,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   float* stg = (float*)smem + wave * TR::STG_FLOATS;
   constexpr int SP = TR::SPITCH;
   const int lr = lane / TR::LPR;        // staged row within an iteration
-  const int lc = (lane % TR::LPR) * 4;  // staged column
+  const int lc = (lane % TR::LPR) * 8;  // first of the lane's 8 staged columns
   const int gcol = ccol0 + lc;
   const bool colok = gcol < N;
 
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       if (c < N) bias_mf[j] = E::to_f32(((const uint16_t*)p.bias)[c]);
     }
   }
-  f32x4 colsum = {0.f, 0.f, 0.f, 0.f};  // DRELU_BGRAD: sums of the lane's 4 staged columns
+  f32x4 colsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // DRELU_BGRAD: the lane's 8 columns
 
   // DRELU_BGRAD: the slab's mask words (32 rows x WPR words) are fetched before it is staged,
   // NW per lane: word (row, w) sits in register row / RPW of lane (row % RPW) * WPR + w.
@@ -549,7 +555,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // DSWIGLU reads gate and up per element in the staged layout, for a whole slab before it
   // is staged, so their latency overlaps the staging.
   constexpr int PF_GU = EPI == E_DSWIGLU ? TR::ITERS : 1;
-  u32x2 pf_g[PF_GU], pf_u[PF_GU];
+  u32x4 pf_g[PF_GU], pf_u[PF_GU];
 
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
@@ -568,8 +574,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
         const int grow = srow0 + it * TR::RPI + lr;
         const bool ok = colok && grow < M;
         const int64_t go = ((int64_t)grow * p.ld_gu + gcol) * 2;
-        pf_g[it] = ok ? __builtin_nontemporal_load((const u32x2*)((const char*)p.gate + go)) : u32x2{0u, 0u};
-        pf_u[it] = ok ? __builtin_nontemporal_load((const u32x2*)((const char*)p.up + go)) : u32x2{0u, 0u};
+        pf_g[it] = ok ? __builtin_nontemporal_load((const u32x4*)((const char*)p.gate + go)) : u32x4{0u, 0u, 0u, 0u};
+        pf_u[it] = ok ? __builtin_nontemporal_load((const u32x4*)((const char*)p.up + go)) : u32x4{0u, 0u, 0u, 0u};
       }
     }
 
@@ -642,9 +648,13 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     constexpr int OUTER_UNROLL = EPI == E_DRELU_BGRAD ? 2 : TR::ITERS;
 #pragma unroll OUTER_UNROLL
     for (int c0 = 0; c0 < TR::ITERS; c0 += TR::CH) {
-      f32x4 vv[TR::CH];
+      f32x4 vv[TR::CH][2];
 #pragma unroll
-      for (int c = 0; c < TR::CH; ++c) vv[c] = *(const f32x4*)(stg + ((c0 + c) * TR::RPI + lr) * SP + lc);
+      for (int c = 0; c < TR::CH; ++c) {
+        const float* src = stg + ((c0 + c) * TR::RPI + lr) * SP + lc;
+        vv[c][0] = *(const f32x4*)src;
+        vv[c][1] = *(const f32x4*)(src + 4);
+      }
       if constexpr (EPI == E_DRELU_BGRAD) {
         uint32_t wd[TR::CH];
 #pragma unroll
@@ -657,7 +667,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 #pragma unroll
         for (int c = 0; c < TR::CH; ++c)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vv[c][e] = ((wd[c] >> e) & 1u) ? vv[c][e] : 0.0f;
+          for (int e = 0; e < 8; ++e) vv[c][e >> 2][e & 3] = ((wd[c] >> e) & 1u) ? vv[c][e >> 2][e & 3] : 0.0f;
       }
 #pragma unroll
       for (int c = 0; c < TR::CH; ++c) {
@@ -666,22 +676,28 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
         const int64_t drow = (int64_t)grow * p.ldd;
         if constexpr (EPI == E_DSWIGLU) {
           if (ok) {
-            const f32x4 g = unpack4<DT>(pf_g[c0 + c]);
-            const f32x4 u = unpack4<DT>(pf_u[c0 + c]);
-            f32x4 dg, du;
+            f32x4 dg[2], du[2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float sg = sigmoid_f(g[e]);
-              const float t = vv[c][e] * sg;           // dh * s
-              du[e] = t * g[e];                        // dh * silu(g)
-              dg[e] = t * u[e] * (1.0f + g[e] * (1.0f - sg));
+            for (int h = 0; h < 2; ++h) {
+              const f32x4 g = unpack4<DT>(u32x2{pf_g[c0 + c][2 * h], pf_g[c0 + c][2 * h + 1]});
+              const f32x4 u = unpack4<DT>(u32x2{pf_u[c0 + c][2 * h], pf_u[c0 + c][2 * h + 1]});
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float sg = sigmoid_f(g[e]);
+                const float t = vv[c][h][e] * sg;        // dh * s
+                du[h][e] = t * g[e];                     // dh * silu(g)
+                dg[h][e] = t * u[e] * (1.0f + g[e] * (1.0f - sg));
+              }
             }
-            *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(dg);
-            *(u32x2*)((char*)p.d2 + ((int64_t)grow * p.ldd2 + gcol) * 2) = pack4<DT>(du);
+            *(u32x4*)((char*)p.d + (drow + gcol) * 2) = pack8<DT>(dg[0], dg[1]);
+            *(u32x4*)((char*)p.d2 + ((int64_t)grow * p.ldd2 + gcol) * 2) = pack8<DT>(du[0], du[1]);
           }
         } else {
-          if (ok) *(u32x2*)((char*)p.d + (drow + gcol) * 2) = pack4<DT>(vv[c]);
-          if constexpr (EPI == E_DRELU_BGRAD) colsum += vv[c];  // rows past M staged as 0
+          if (ok) *(u32x4*)((char*)p.d + (drow + gcol) * 2) = pack8<DT>(vv[c][0], vv[c][1]);
+          if constexpr (EPI == E_DRELU_BGRAD) {  // rows past M are staged as 0
+            colsum[0] += vv[c][0];
+            colsum[1] += vv[c][1];
+          }
         }
       }
     }
@@ -694,17 +710,25 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 #pragma unroll
     for (int sh = TR::LPR; sh < 64; sh <<= 1)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) colsum[e] += __shfl_xor(colsum[e], sh);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) colsum[h][e] += __shfl_xor(colsum[h][e], sh);
     float* bg = (float*)(smem + TR::BG_OFF) + wn * WTN;
-    if (wm == 1 && lane < TR::LPR) *(f32x4*)(bg + lc) = colsum;
+    if (wm == 1 && lane < TR::LPR) {
+      *(f32x4*)(bg + lc) = colsum[0];
+      *(f32x4*)(bg + lc + 4) = colsum[1];
+    }
     __syncthreads();
     if (wm == 0 && lane < TR::LPR && colok) {
-      const f32x4 tot = colsum + *(const f32x4*)(bg + lc);
-      if (p.bgrad_atomic) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) atomicAdd(p.bgrad_part + gcol + e, tot[e]);
-      } else {
-        *(f32x4*)(p.bgrad_part + (int64_t)pm * N + gcol) = tot;
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 tot = colsum[h] + *(const f32x4*)(bg + lc + 4 * h);
+        if (p.bgrad_atomic) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) atomicAdd(p.bgrad_part + gcol + 4 * h + e, tot[e]);
+        } else {
+          *(f32x4*)(p.bgrad_part + (int64_t)pm * N + gcol + 4 * h) = tot;
+        }
       }
     }
   }
