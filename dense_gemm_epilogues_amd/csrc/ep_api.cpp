@@ -35,6 +35,32 @@ EP_DECL_EPIS(1, 1)
 static const GemmLauncher* const kTables[2][2][E_NUM] = {{EP_ROW(0, 0), EP_ROW(0, 1)},
                                                          {EP_ROW(1, 0), EP_ROW(1, 1)}};
 
+#define EP_DECL_P(dt, lay)                                                  \
+  extern const GemmLauncher kPartial_##dt##_##lay##_0[kNumTileCfgs]; \
+  extern const GemmLauncher kPartial_##dt##_##lay##_5[kNumTileCfgs];
+EP_DECL_P(0, 0) EP_DECL_P(0, 1) EP_DECL_P(1, 0) EP_DECL_P(1, 1)
+#define EP_DECL_F(dt) EP_DECL_TABLE_F(dt, 0) EP_DECL_TABLE_F(dt, 1) EP_DECL_TABLE_F(dt, 2) \
+  EP_DECL_TABLE_F(dt, 3) EP_DECL_TABLE_F(dt, 4) EP_DECL_TABLE_F(dt, 5) EP_DECL_TABLE_F(dt, 6)
+#define EP_DECL_TABLE_F(dt, epi) extern const GemmLauncher kFixup_##dt##_##epi[kNumTileCfgs];
+EP_DECL_F(0) EP_DECL_F(1)
+// [dtype][layout][single B, dual B]
+static const GemmLauncher* const kPartialTables[2][2][2] = {
+    {{kPartial_0_0_0, kPartial_0_0_5}, {kPartial_0_1_0, kPartial_0_1_5}},
+    {{kPartial_1_0_0, kPartial_1_0_5}, {kPartial_1_1_0, kPartial_1_1_5}}};
+static const GemmLauncher* const kFixupTables[2][E_NUM] = {
+    {kFixup_0_0, kFixup_0_1, kFixup_0_2, kFixup_0_3, kFixup_0_4, kFixup_0_5, kFixup_0_6},
+    {kFixup_1_0, kFixup_1_1, kFixup_1_2, kFixup_1_3, kFixup_1_4, kFixup_1_5, kFixup_1_6}};
+
+GemmLauncher gemm_partial_launcher(int dtype, int layout, bool dual, int cfg) {
+  if (dtype < 0 || dtype > 1 || layout < 0 || layout > 1 || cfg < 0 || cfg >= kNumTileCfgs) return nullptr;
+  return kPartialTables[dtype][layout][dual ? 1 : 0][cfg];
+}
+
+GemmLauncher gemm_fixup_launcher(int dtype, int epi, int cfg) {
+  if (dtype < 0 || dtype > 1 || epi < 0 || epi >= E_NUM || cfg < 0 || cfg >= kNumTileCfgs) return nullptr;
+  return kFixupTables[dtype][epi][cfg];
+}
+
 GemmLauncher gemm_launcher(int dtype, int layout, int epi, int cfg) {
   if (dtype < 0 || dtype > 1 || layout < 0 || layout > 1 || epi < 0 || epi >= E_NUM || cfg < 0 ||
       cfg >= kNumTileCfgs)
@@ -88,6 +114,8 @@ struct ep_plan_s {
   GemmArgs args;       // fused launch (or the DEFAULT GEMM of the unfused path)
   GemmArgs args2;      // unfused SwiGLU: the up-branch GEMM
   GemmLauncher launch;
+  GemmLauncher launch_partial, launch_fixup;  // split-K (splits > 1)
+  int splits;
   void* workspace;     // single allocation owned by the plan
   size_t workspace_bytes;
   float* part;         // bgrad partials (two-pass)
@@ -129,6 +157,28 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   return best;
 }
 
+// Split-K: how many K ranges per tile.  Only grids that leave CUs idle are split: the time
+// of one resident round of tiles scales as rounds(tiles * S) / S, and every split adds a
+// write and a read of the fp32 tile partials (BM * BNT * 4 bytes), priced at a CU's share of
+// HBM bandwidth (about 20 GB/s) against the tile's K loop (about 1 us per 32-deep k-step).
+int choose_splits(int64_t tiles, int slots, int kt, int cfg) {
+  if (tiles >= slots) return 1;
+  const double tile_us = kt * (kTileCfgs[cfg].bk / 32.0) * 1.0;
+  const double part_us = 2.0 * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * 4.0 / 20e3;  // bytes / (bytes/us)
+  int best = 1;
+  double best_t = 1.0;
+  for (int sp = 2; sp <= EP_MAX_SPLIT_K; ++sp) {
+    if (kt / sp < 16) break;
+    const double rounds = (double)((tiles * sp + slots - 1) / slots);
+    const double t = rounds / sp + sp * part_us / tile_us;
+    if (t < best_t * 0.97) {
+      best_t = t;
+      best = sp;
+    }
+  }
+  return best;
+}
+
 ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io,
                    const ep_options* opt) {
   if (!s) return fail(EP_ERR_INVALID_ARG, "shape is NULL");
@@ -148,6 +198,10 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
       return fail(EP_ERR_INVALID_ARG, "unknown bgrad mode %d", (int)opt->bgrad_mode);
     if (opt->tile_cfg < -1 || opt->tile_cfg >= kNumTileCfgs)
       return fail(EP_ERR_INVALID_ARG, "tile_cfg %d out of range", opt->tile_cfg);
+    if (opt->split_k < 0 || opt->split_k > EP_MAX_SPLIT_K)
+      return fail(EP_ERR_INVALID_ARG, "split_k %d out of range [0, %d]", opt->split_k, EP_MAX_SPLIT_K);
+    if (opt->path == EP_PATH_UNFUSED && opt->split_k > 1)
+      return fail(EP_ERR_UNSUPPORTED, "split_k applies to the fused path only");
   }
   // operand pointers
   if (!s->a || !s->b || !s->d) return fail(EP_ERR_INVALID_ARG, "a, b and d must be non-NULL");
@@ -257,7 +311,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   *out = nullptr;
   ep_status st = validate(s, dtype, epi, io, opt_in);
   if (st != EP_OK) return st;
-  ep_options opt = opt_in ? *opt_in : ep_options{EP_PATH_FUSED, EP_BGRAD_TWO_PASS, -1};
+  ep_options opt = opt_in ? *opt_in : ep_options{EP_PATH_FUSED, EP_BGRAD_TWO_PASS, -1, 0};
 
   // ---- first HIP call: the device must exist and be usable
   int dev = -1;
@@ -301,10 +355,35 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
     delete h;
     return fail(EP_ERR_INTERNAL, "no kernel instantiated for this combination");
   }
+  // split-K (fused path only)
+  const int kt_all = (int)((s->k + kTileCfgs[cfg].bk - 1) / kTileCfgs[cfg].bk);
+  int splits = 1;
+  if (!unfused) {
+    splits = opt.split_k > 0 ? opt.split_k
+                             : choose_splits((int64_t)a.tiles_m * a.tiles_n,
+                                             prop.multiProcessorCount * kTileCfgs[cfg].occ, kt_all, cfg);
+    if (splits > kt_all) splits = kt_all;
+  }
+  if (splits > 1) {
+    a.kt_per_split = (kt_all + splits - 1) / splits;
+    splits = (kt_all + a.kt_per_split - 1) / a.kt_per_split;  // no empty K range
+  }
+  h->splits = splits;
+  a.splits = splits;
+  if (splits > 1) {
+    h->launch_partial = gemm_partial_launcher((int)dtype, (int)s->b_layout, kernel_dual, cfg);
+    h->launch_fixup = gemm_fixup_launcher((int)dtype, (int)epi, cfg);
+    if (!h->launch_partial || !h->launch_fixup) {
+      delete h;
+      return fail(EP_ERR_INTERNAL, "no split-K kernel instantiated for this combination");
+    }
+  }
 
   // ---- workspace sizing
   const int64_t M = s->m, N = s->n;
-  size_t part_bytes = 0, z_bytes = 0, z2_bytes = 0;
+  size_t part_bytes = 0, z_bytes = 0, z2_bytes = 0, kpart_bytes = 0;
+  if (splits > 1)
+    kpart_bytes = (size_t)splits * a.tiles_m * a.tiles_n * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * sizeof(float);
   if (epi == EP_EPILOG_DRELU_BGRAD) {
     if (unfused) {
       h->colsum_rows = 256;
@@ -322,7 +401,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
     z2_bytes = z_bytes;
   }
   auto round_up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  h->workspace_bytes = round_up(part_bytes) + round_up(z_bytes) + round_up(z2_bytes);
+  h->workspace_bytes = round_up(part_bytes) + round_up(z_bytes) + round_up(z2_bytes) + round_up(kpart_bytes);
   if (h->workspace_bytes) {
     he = hipMalloc(&h->workspace, h->workspace_bytes);
     if (he != hipSuccess) {
@@ -334,7 +413,8 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
     char* w = (char*)h->workspace;
     if (part_bytes) { h->part = (float*)w; w += round_up(part_bytes); }
     if (z_bytes) { h->uf.z = w; w += round_up(z_bytes); }
-    if (z2_bytes) { h->uf.z2 = w; }
+    if (z2_bytes) { h->uf.z2 = w; w += round_up(z2_bytes); }
+    if (kpart_bytes) a.part = (float*)w;
     h->uf.ldz = N;
   }
 
@@ -371,9 +451,9 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
     }
   }
   if (getenv("EP_LOG")) {
-    fprintf(stderr, "[ep] plan m=%lld n=%lld k=%lld %s %s %s cfg=%s tiles=%dx%d ws=%zu\n", (long long)M,
+    fprintf(stderr, "[ep] plan m=%lld n=%lld k=%lld %s %s %s cfg=%s tiles=%dx%d splits=%d ws=%zu\n", (long long)M,
             (long long)N, (long long)s->k, dtype == EP_F16 ? "f16" : "bf16", s->b_layout == EP_B_KN ? "KN" : "NK",
-            kEpiNames[epi], kTileCfgs[cfg].name, a.tiles_m, a.tiles_n, h->workspace_bytes);
+            kEpiNames[epi], kTileCfgs[cfg].name, a.tiles_m, a.tiles_n, splits, h->workspace_bytes);
   }
   *out = h;
   return EP_OK;
@@ -396,8 +476,15 @@ ep_status ep_execute(ep_handle h, void* stream) {
     if (h->epilog == EP_EPILOG_DRELU_BGRAD && h->opt.bgrad_mode == EP_BGRAD_ATOMIC) {
       if (launch_fill_zero_f32(h->io.bgrad, N, s) != hipSuccess) return check_launch("fill_zero");
     }
-    h->launch(h->args, s);
-    if ((st = check_launch("fused gemm")) != EP_OK) return st;
+    if (h->splits > 1) {
+      h->launch_partial(h->args, s);
+      if ((st = check_launch("split-K partial gemm")) != EP_OK) return st;
+      h->launch_fixup(h->args, s);
+      if ((st = check_launch("split-K fixup + epilog")) != EP_OK) return st;
+    } else {
+      h->launch(h->args, s);
+      if ((st = check_launch("fused gemm")) != EP_OK) return st;
+    }
     if (h->epilog == EP_EPILOG_DRELU_BGRAD && h->opt.bgrad_mode == EP_BGRAD_TWO_PASS) {
       launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s);
       if ((st = check_launch("bgrad_reduce")) != EP_OK) return st;
@@ -465,6 +552,7 @@ ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
                      (h->opt.path == EP_PATH_FUSED ? kEpiNames[h->epilog] : "DEFAULT") + "," +
                      kTileCfgs[h->cfg].name + ">";
   std::string extra;
+  if (h->splits > 1) kern += " split-K x" + std::to_string(h->splits) + " (partial + fixup)";
   if (h->opt.path == EP_PATH_FUSED) {
     if (h->epilog == EP_EPILOG_DRELU_BGRAD)
       extra = h->opt.bgrad_mode == EP_BGRAD_TWO_PASS ? " + bgrad_reduce" : " (after fill_zero; atomic bgrad)";
@@ -481,10 +569,10 @@ ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
   }
   snprintf(buf, n,
            "epilog=%s path=%s dtype=%s layout=%s m=%lld n=%lld k=%lld tile=%s tile_cfg=%d grid=%dx%d "
-           "workspace_bytes=%zu kernels=%s%s",
+           "splits=%d workspace_bytes=%zu kernels=%s%s",
            kEpiNames[h->epilog], h->opt.path == EP_PATH_FUSED ? "fused" : "unfused", dt, lay, (long long)s.m,
            (long long)s.n, (long long)s.k, kTileCfgs[h->cfg].name, h->cfg, h->args.tiles_m, h->args.tiles_n,
-           h->workspace_bytes, kern.c_str(), extra.c_str());
+           h->splits, h->workspace_bytes, kern.c_str(), extra.c_str());
   return EP_OK;
 }
 

@@ -39,6 +39,10 @@ struct GemmArgs {
   int64_t ld_gu;
   void* d2;
   int64_t ldd2;
+  // split-K (see the MODE parameter of gemm_kernel): K-ranges per tile, K-steps per range,
+  // and the fp32 partial accumulators [splits][tiles][BM * BNT]
+  int splits, kt_per_split;
+  float* part;
 };
 
 // Tile configurations, shared by the kernels (compile-time parameters) and the planner.
@@ -62,6 +66,9 @@ typedef void (*GemmLauncher)(const GemmArgs&, hipStream_t);
 
 // [dtype][layout][epi][cfg]; null where not instantiated
 GemmLauncher gemm_launcher(int dtype, int layout, int epi, int cfg);
+// split-K: the partial kernel depends only on single or dual B, the fixup kernel not on the layout
+GemmLauncher gemm_partial_launcher(int dtype, int layout, bool dual, int cfg);
+GemmLauncher gemm_fixup_launcher(int dtype, int epi, int cfg);
 const char* gemm_kernel_name(int dtype, int layout, int epi, int cfg);
 
 // ---- unfused baseline and reduction kernels (elementwise.hip)

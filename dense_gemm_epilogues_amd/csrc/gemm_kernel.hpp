@@ -37,6 +37,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
+constexpr int kMaxSplits = 4;  // split-K ranges per tile
 constexpr int kGroupM = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every num_records we build
 
@@ -207,7 +208,11 @@ struct GemmTraits {
   static_assert(LDS_BYTES * cfg_occ(CFG) <= 160 * 1024, "LDS budget");
 };
 
-template <int DT, int LAY, int EPI, int CFG>
+// MODE 0: whole K range, then the epilog.  MODE 1 (split-K partial): block b computes the
+// K-steps [s * kt_per_split, (s + 1) * kt_per_split) of tile b % tiles, s = b / tiles, and stores
+// its fp32 accumulators to p.part.  MODE 2 (split-K fixup): block b sums the p.splits partials
+// of tile b in split order and runs the epilog (no K loop).
+template <int DT, int LAY, int EPI, int CFG, int MODE>
 __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p) {
   using E = Elem<DT>;
   using TR = GemmTraits<DT, LAY, EPI, CFG>;
@@ -224,12 +229,21 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int wm = wave >> 1, wn = wave & 1;
 
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int split = MODE == 1 ? (int)blockIdx.x / ntiles : 0;
+  const int tbid = (int)blockIdx.x - split * ntiles;  // tile index before the XCD remap
   int pm, pn;
-  map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, pm, pn);
+  map_tile(tbid, ntiles, p.tiles_m, p.tiles_n, pm, pn);
   const int m0 = pm * BM;
   const int n0 = pn * TR::BN_OUT;
   const int M = p.M, N = p.N, K = p.K;
-  const int KT = (K + BK - 1) / BK;
+  const int KT_ALL = (K + BK - 1) / BK;
+  // this block's K-steps: [KT0, KTE); local k-step kt loads global k-step KT0 + kt, and every
+  // k-step past KTE reads as zeros (its global index is replaced by KT_ALL, past K)
+  const int KT0 = MODE == 1 ? split * p.kt_per_split : 0;
+  const int KTE = MODE == 1 ? min(KT_ALL, KT0 + p.kt_per_split) : (MODE == 2 ? 0 : KT_ALL);
+  const int KT = KTE > KT0 ? KTE - KT0 : 0;
+  auto gkt = [&](int kt) { return KT0 + kt < KTE ? KT0 + kt : KT_ALL; };
 
   const char* Ag = (const char*)p.a;
   const char* Bg = (const char*)p.b;
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     uint32_t num;
   };
   auto kn_rsrc = [&](int kt) {
-    const int k0 = kt * BK;
+    const int k0 = gkt(kt) * BK;
     const int64_t bytes = ((int64_t)(K - k0) * p.ldb - (n0 + w_cbase)) * 2;
     KnSrc s;
     s.base = w_bsrc + ((int64_t)k0 * p.ldb + n0 + w_cbase) * 2;
@@ -306,7 +320,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // One DMA op = one 1 KiB slot of a stage (A slots first, then B slots).
   constexpr int N_DMA = A_SLOTS + B_SLOTS;
   auto dma_op = [&](int kt, char* As, int t, const KnSrc& kr) {
-    const int k0 = kt * BK;
+    const int k0 = gkt(kt) * BK;
     if (t < A_SLOTS) {
       const int q = t;
       const uint32_t off = (k0 < a_klim[q]) ? a_voff[q] + k0 * 2 : kOOB;
@@ -507,16 +521,58 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     slice(T_{}, GL{}, fa[L], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[0], fb[0]);
   };
 
+  if constexpr (MODE != 2) {
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue_tile(s, smem + s * TR::STAGE);
-  ring_barrier(std::integral_constant<int, VMC_PRO>{});
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags(smem, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < KT; ++kt) kstep(kt);
+    for (int s = 0; s < NST - 1; ++s) issue_tile(s, smem + s * TR::STAGE);
+    ring_barrier(std::integral_constant<int, VMC_PRO>{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(smem, 0, fa[0], fb[0]);
+    for (int kt = 0; kt < KT; ++kt) kstep(kt);
+  }
   // loads issued past the last k-step (they read as zeros) must land before LDS is reused
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lgkm_fence(fb[0]);
   __syncthreads();
+
+  // ---------------------------------------------------------------- split-K
+  // Partials are stored register-major: f32x4 number q of thread t of a tile's partial sits at
+  // float offset (q * 256 + t) * 4, so each store / load instruction covers 1 KiB contiguously.
+  constexpr int ACC4 = MB * NB * 4;  // f32x4 accumulator groups per thread
+  if constexpr (MODE == 1) {
+    float* dst = p.part + ((int64_t)split * ntiles + tbid) * (int64_t)(ACC4 * kThreads * 4);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int q = (i * NB + j) * 4 + g;
+          f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          __builtin_nontemporal_store(v, (f32x4*)(dst + ((int64_t)q * kThreads + tid) * 4));
+        }
+    return;
+  } else {
+  if constexpr (MODE == 2) {
+    // each f32x4 group is summed over the splits in split order (so the result does not
+    // depend on which split finished first) and written to the accumulators once
+    const float* src = p.part + (int64_t)tbid * (ACC4 * kThreads * 4);
+    const int64_t sstride = (int64_t)ntiles * (ACC4 * kThreads * 4);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int q = (i * NB + j) * 4 + g;
+          const float* sq = src + ((int64_t)q * kThreads + tid) * 4;
+          f32x4 v = __builtin_nontemporal_load((const f32x4*)sq);
+#pragma unroll
+          for (int sp = 1; sp < kMaxSplits; ++sp)
+            if (sp < p.splits) v += __builtin_nontemporal_load((const f32x4*)(sq + sp * sstride));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] = v[e];
+        }
+  }
 
   // ---------------------------------------------------------------- epilogue
   // Accumulator layout: lane l of 32x32 block (i, j) holds column 32 j + l%32 of the wave's
@@ -732,12 +788,13 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       }
     }
   }
+}  // MODE != 1
 }
 
-template <int DT, int LAY, int EPI, int CFG>
+template <int DT, int LAY, int EPI, int CFG, int MODE = 0>
 void launch_gemm(const GemmArgs& a, hipStream_t s) {
-  const int nblocks = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<DT, LAY, EPI, CFG>), dim3(nblocks), dim3(kThreads), 0, s, a);
+  const int nblocks = a.tiles_m * a.tiles_n * (MODE == 1 ? a.splits : 1);
+  hipLaunchKernelGGL((gemm_kernel<DT, LAY, EPI, CFG, MODE>), dim3(nblocks), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace ep

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 1
+#define EP_ABI_VERSION 2
 
 typedef struct ep_plan_s* ep_handle;
 
@@ -133,7 +133,15 @@ typedef struct {
   ep_bgrad_mode bgrad_mode;/* DRELU_BGRAD: deterministic two-pass reduction (default) or
                               float32 atomics into bgrad (order-dependent rounding) */
   int tile_cfg;            /* -1 = choose by shape; otherwise an index < ep_num_tile_cfgs() */
+  int split_k;             /* fused path: 0 = chosen by shape (split only when the output tiles
+                              leave CUs idle); 1 = never; 2..EP_MAX_SPLIT_K = split the K range of
+                              every tile into that many parts, each computed by its own
+                              workgroup into fp32 partials that a second launch sums (in a fixed
+                              order) before running the epilog.  Must be 0 or 1 for the unfused
+                              path. */
 } ep_options;
+
+#define EP_MAX_SPLIT_K 4
 
 /*
  * ep_plan: validate the request, pick a tile configuration, allocate the workspace and
@@ -148,7 +156,7 @@ typedef struct {
 ep_status ep_plan(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog,
                   const ep_epilog_io* io, ep_handle* out);
 
-/* ep_plan with options (opt may be NULL for the defaults {FUSED, TWO_PASS, -1}). */
+/* ep_plan with options (opt may be NULL for the defaults {FUSED, TWO_PASS, -1, 0}). */
 ep_status ep_plan_ex(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog,
                      const ep_epilog_io* io, const ep_options* opt, ep_handle* out);
 

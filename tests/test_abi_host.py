@@ -42,7 +42,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.ep_abi_version() == 1
+    assert L.ep_abi_version() == 2
     from tests.test_parity_small_gpu import NUM_TILE_CFGS
     assert L.ep_num_tile_cfgs() == NUM_TILE_CFGS
     for code, name in ep.STATUS.items():
@@ -117,6 +117,10 @@ CASES = [
     ("unfused with atomic bgrad", lambda L: plan(L, shape(lay=NK), E["DRELU_BGRAD"],
                                                  ep_epilog_io(relu_aux_in=X_PTR, bgrad=X_PTR + 4096),
                                                  opt=ep_options(path=1, bgrad_mode=1, tile_cfg=-1))[0], UNSUPPORTED),
+    ("split_k negative", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=-1))[0], INVALID),
+    ("split_k above 4", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=5))[0], INVALID),
+    ("unfused with split_k", lambda L: plan(L, shape(), opt=ep_options(path=1, bgrad_mode=0, tile_cfg=-1, split_k=2))[0],
+     UNSUPPORTED),
 ]
 
 

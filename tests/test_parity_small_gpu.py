@@ -51,7 +51,7 @@ def make_inputs(epi, dt, layout, m, n, k, seed, dev):
     return {kk: v.to(dev) for kk, v in ins.items()}
 
 
-def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0):
+def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split_k=0, bgrad_mode="two_pass"):
     import dense_gemm_epilogues_amd as ep
     dev = torch.device("cuda")
     dt = DTYPES[dtname]
@@ -74,14 +74,19 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0):
         epi_in["gate"], epi_in["up"] = ins["gate"], ins["up"]
         ubuf, uview = padded(m, n, dt, dev)
         aux_out["d_up"] = uview
-    say(f"case epi={epi} dt={dtname} layout={layout} m={m} n={n} k={k} cfg={cfg} path={path}")
+    say(f"case epi={epi} dt={dtname} layout={layout} m={m} n={n} k={k} cfg={cfg} path={path} split_k={split_k}")
     p = ep.Plan(ins["a"], ins["b"], epilog=epi, epilog_inputs=epi_in, b_layout=layout, out=out,
-                aux_out=aux_out, path=path, tile_cfg=cfg)
+                aux_out=aux_out, path=path, tile_cfg=cfg, split_k=split_k, bgrad_mode=bgrad_mode)
+    if split_k > 1:
+        kt = -(-k // (64 if cfg in (1, 4) else 32))
+        per = -(-kt // min(split_k, kt))
+        want = -(-kt // per)
+        assert f"splits={want} " in p.info(), p.info()
     p.execute()
     torch.cuda.synchronize()
 
     a64, b64 = f64(ins["a"]), f64(ins["b"])
-    what = f"{epi}/{dtname}/{layout}/{m}x{n}x{k}/cfg{cfg}/{path}"
+    what = f"{epi}/{dtname}/{layout}/{m}x{n}x{k}/cfg{cfg}/{path}/split{split_k}"
     if epi == "DEFAULT":
         assert_half(f64(out), oracle.matmul(a64, b64, layout), what)
     elif epi == "BIAS":
@@ -138,6 +143,27 @@ def test_small_shapes_fused(epi, dtname, layout, cfg):
         return
     for (m, n, k) in SHAPES:
         run_and_check(epi, dtname, layout, m, n, k, cfg)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 4])
+@pytest.mark.parametrize("layout", ["KN", "NK"])
+@pytest.mark.parametrize("epi", EPIS)
+def test_split_k(epi, layout, splits):
+    """K split over 2-4 workgroups per tile (fp32 partials, then a fixup launch that sums them
+    and runs the epilog): every epilog, both dtypes, three tile configurations, a K that
+    divides unevenly and a K too short for the requested number of ranges."""
+    require_gpu()
+    for cfg in (0, 1, 6):
+        if epi == "SWIGLU" and layout == "KN" and cfg in BNT128_CFGS:
+            continue
+        for dtname in ("f16", "bf16"):
+            for (m, n, k) in [(300, 200, 520), (130, 264, 136)]:
+                run_and_check(epi, dtname, layout, m, n, k, cfg, split_k=splits)
+
+
+def test_split_k_atomic_bgrad():
+    require_gpu()
+    run_and_check("DRELU_BGRAD", "f16", "NK", 300, 200, 520, 0, split_k=3, bgrad_mode="atomic")
 
 
 @pytest.mark.parametrize("layout", ["KN", "NK"])
