@@ -181,6 +181,106 @@ def dswiglu_bwd(c, steps, warmup, flush, dev):
     return {"fused": f, "unfused": u, "speedup": u["ms"] / f["ms"]}
 
 
+def swiglu_m_sweep(steps, warmup, flush, dev, ms=(2048, 4096, 8192, 16384)):
+    """Fused SWIGLU (both GEMMs and SiLU*mul in one kernel) against the unfused two GEMMs +
+    silu_mul at several token counts M, H 5120, I 17408 (the M range of the
+    gemm_swiglu_mlp_fusion.py docstring)."""
+    import dense_gemm_epilogues_amd as ep
+    import workloads as W
+    c = W.SWIGLU[4]
+    out = {}
+    for m in ms:
+        inp = W.swiglu_inputs(c, device=dev, m=m)
+        res = {}
+        for path in ("fused", "unfused"):
+            ps = ep.Plan(inp["x"], inp["wg"], "SWIGLU", {"b2": inp["wu"]}, b_layout="NK", path=path)
+            step_ms, _ = run_steps([ps.execute], steps, warmup, flush)
+            res[path] = float(np.mean(step_ms))
+            ps.free()
+        tf = 4.0 * m * c.h * c.i / (res["fused"] * 1e-3) / 1e12
+        out[f"M{m}"] = {"fused_ms": round(res["fused"], 4), "unfused_ms": round(res["unfused"], 4),
+                        "fused_tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_F16_TFLOPS, 2),
+                        "speedup": round(res["unfused"] / res["fused"], 4)}
+        del inp
+        torch.cuda.empty_cache()
+    return out
+
+
+def execute_overhead(dev):
+    """What one ep_execute costs apart from the kernels: the host time to enqueue it, the
+    end-to-end latency of a 256^3 fp16 GEMM (launch + kernel, synchronised every call; the
+    gemm_swiglu_mlp_fusion.py notes quote about 8 us per 256^3 execute on B200), and the fused
+    SwiGLU forward (SWIGLU + down GEMM, M 2048) replayed from a captured HIP graph against
+    eager launches."""
+    import dense_gemm_epilogues_amd as ep
+    import workloads as W
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    a = torch.randn(256, 256, device=dev, generator=g).half()
+    b = torch.randn(256, 256, device=dev, generator=g).half()
+    p = ep.Plan(a, b, "DEFAULT", b_layout="NK")
+    for _ in range(50):
+        p.execute()
+    torch.cuda.synchronize()
+    n = 2000
+    t0 = time.perf_counter()
+    for _ in range(n):
+        p.execute()
+    t1 = time.perf_counter()
+    torch.cuda.synchronize()
+    host_us = (t1 - t0) / n * 1e6
+    lat = []
+    for _ in range(200):
+        t0 = time.perf_counter()
+        p.execute()
+        torch.cuda.synchronize()
+        lat.append(time.perf_counter() - t0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        p.execute()
+    e1.record()
+    torch.cuda.synchronize()
+    gpu_us = e0.elapsed_time(e1) / n * 1e3
+    p.free()
+
+    c = W.SWIGLU[4]
+    inp = W.swiglu_inputs(c, device=dev)
+    ps = ep.Plan(inp["x"], inp["wg"], "SWIGLU", {"b2": inp["wu"]}, b_layout="NK")
+    hh, _ = ps.execute()
+    pd = ep.Plan(hh, inp["wd"], "DEFAULT", b_layout="NK")
+    step = lambda: (ps.execute(), pd.execute())
+    step()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()  # warm on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    reps = 50
+    times = {}
+    for name, fn in (("eager", step), ("graph", graph.replay)):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        times[name] = (time.perf_counter() - t0) / reps * 1e3
+    ps.free()
+    pd.free()
+    return {"host_us_per_execute": round(host_us, 2),
+            "gemm_256cubed_us_back_to_back": round(gpu_us, 2),
+            "gemm_256cubed_us_synchronised": round(float(np.median(lat)) * 1e6, 2),
+            "swiglu_fwd_M2048_eager_ms": round(times["eager"], 4),
+            "swiglu_fwd_M2048_graph_ms": round(times["graph"], 4)}
+
+
 def cpu_baseline(inputs, c):
     """The float64 oracle on the same inputs: one full forward + backward step of the square
     layer, repeated until about 10 s of CPU work (at least once)."""
@@ -211,8 +311,8 @@ def cpu_baseline(inputs, c):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of "
-                                   "this build (see the sharding notes in DESIGN.md)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the fused GEMM kernels run on one "
+                                   "device and no multi-GPU path is implemented", "n_gpus": args.gpus}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU available"}))
@@ -313,6 +413,9 @@ def main():
             "pct_peak": round(100 * r5["fused"]["tflops"] / PEAK_F16_TFLOPS, 2),
             "fused_ms": round(r5["fused"]["ms"], 4), "unfused_ms": round(r5["unfused"]["ms"], 4),
             "speedup": round(r5["speedup"], 4)}
+        torch.cuda.empty_cache()
+        large["swiglu_fwd_bf16_M_sweep_H5120_I17408"] = swiglu_m_sweep(s_l, w_l, flush, dev)
+        large["execute_overhead"] = execute_overhead(dev)
         line["configs"] = large
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r2["inputs"], c2)
