@@ -206,6 +206,33 @@ def swiglu_m_sweep(steps, warmup, flush, dev, ms=(2048, 4096, 8192, 16384)):
     return out
 
 
+def autotune_vs_model(steps, warmup, flush, dev):
+    """Plan-time tuning (ep_options.autotune) against the shape model's choice, on the square
+    forward and on the SwiGLU down projection (160 output tiles on 256 CUs)."""
+    import dense_gemm_epilogues_amd as ep
+    import workloads as W
+    out = {}
+    c2 = W.LINEAR[2]
+    li = W.linear_inputs(c2, device=dev)
+    c4 = W.SWIGLU[4]
+    si = W.swiglu_inputs(c4, device=dev)
+    h = torch.randn(c4.m, c4.i, device=dev).to(torch.bfloat16)
+    cases = {"square_fwd_relu_aux_bias": (li["x"], li["w"], "RELU_AUX_BIAS", {"bias": li["bias"]}, "KN"),
+             "swiglu_down_gemm": (h, si["wd"], "DEFAULT", {}, "NK")}
+    for name, (a, b, epi, ins, lay) in cases.items():
+        r = {}
+        for tuned in (False, True):
+            p = ep.Plan(a, b, epi, ins, b_layout=lay, autotune=tuned)
+            step_ms, _ = run_steps([p.execute], steps, warmup, flush)
+            info = p.info()
+            r["tuned" if tuned else "model"] = {
+                "ms": round(float(np.mean(step_ms)), 4),
+                "tile": info.split("tile=")[1].split()[0], "splits": int(info.split("splits=")[1].split()[0])}
+            p.free()
+        out[name] = r
+    return out
+
+
 def execute_overhead(dev):
     """What one ep_execute costs apart from the kernels: the host time to enqueue it, the
     end-to-end latency of a 256^3 fp16 GEMM (launch + kernel, synchronised every call; the
@@ -416,6 +443,7 @@ def main():
         torch.cuda.empty_cache()
         large["swiglu_fwd_bf16_M_sweep_H5120_I17408"] = swiglu_m_sweep(s_l, w_l, flush, dev)
         large["execute_overhead"] = execute_overhead(dev)
+        large["autotune_vs_model"] = autotune_vs_model(s_l, w_l, flush, dev)
         line["configs"] = large
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r2["inputs"], c2)

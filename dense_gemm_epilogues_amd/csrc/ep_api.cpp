@@ -9,8 +9,11 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <string>
+#include <tuple>
 
 #include "ep.h"
 #include "ep_internal.hpp"
@@ -202,6 +205,10 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
       return fail(EP_ERR_INVALID_ARG, "split_k %d out of range [0, %d]", opt->split_k, EP_MAX_SPLIT_K);
     if (opt->path == EP_PATH_UNFUSED && opt->split_k > 1)
       return fail(EP_ERR_UNSUPPORTED, "split_k applies to the fused path only");
+    if (opt->autotune != 0 && opt->autotune != 1)
+      return fail(EP_ERR_INVALID_ARG, "autotune must be 0 or 1");
+    if (opt->autotune && (opt->path != EP_PATH_FUSED || opt->tile_cfg >= 0 || opt->split_k != 0))
+      return fail(EP_ERR_INVALID_ARG, "autotune needs the fused path, tile_cfg -1 and split_k 0");
   }
   // operand pointers
   if (!s->a || !s->b || !s->d) return fail(EP_ERR_INVALID_ARG, "a, b and d must be non-NULL");
@@ -280,6 +287,81 @@ GemmArgs base_args(const ep_shape* s, int cfg, bool dual) {
 
 }  // namespace
 
+extern "C" ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io,
+                                const ep_options* opt_in, ep_handle* out);
+extern "C" ep_status ep_execute(ep_handle h, void* stream);
+extern "C" ep_status ep_free(ep_handle h);
+
+namespace {
+
+// Plan-time tuning: every allowed (tile configuration, split) pair is planned, run once to
+// warm up and three times under HIP events on the null stream, and the fastest is kept.
+// The choice is cached for the process under the problem's key.
+using TuneKey = std::tuple<int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int, int, int, int, int>;
+std::mutex g_tune_mu;
+std::map<TuneKey, std::pair<int, int>> g_tune_cache;
+
+ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io, ep_options& opt,
+                   int dev) {
+  const TuneKey key{s->m, s->n, s->k, s->lda, s->ldb, s->ldd, (int)s->b_layout, (int)dtype, (int)epi,
+                    (int)opt.bgrad_mode, dev};
+  {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    auto it = g_tune_cache.find(key);
+    if (it != g_tune_cache.end()) {
+      opt.tile_cfg = it->second.first;
+      opt.split_k = it->second.second;
+      opt.autotune = 0;
+      return EP_OK;
+    }
+  }
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
+    return fail(EP_ERR_HIP, "autotune: hipEventCreate failed");
+  float best_ms = 1e30f;
+  int best_cfg = -1, best_split = 1;
+  for (int c = 0; c < kNumTileCfgs; ++c) {
+    for (int sp : {1, 0}) {  // unsplit, then the split the shape model picks (if it splits)
+      ep_options o = opt;
+      o.autotune = 0;
+      o.tile_cfg = c;
+      o.split_k = sp;
+      ep_handle t = nullptr;
+      if (ep_plan_ex(s, dtype, epi, io, &o, &t) != EP_OK) continue;
+      const int got_split = t->splits;
+      if (sp == 0 && got_split == 1) {  // the model does not split: same as the unsplit run
+        ep_free(t);
+        continue;
+      }
+      float ms = 0.f;
+      bool ok = ep_execute(t, nullptr) == EP_OK && hipEventRecord(e0, nullptr) == hipSuccess;
+      for (int r = 0; ok && r < 3; ++r) ok = ep_execute(t, nullptr) == EP_OK;
+      ok = ok && hipEventRecord(e1, nullptr) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+           hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+      ep_free(t);
+      if (ok && ms < best_ms) {
+        best_ms = ms;
+        best_cfg = c;
+        best_split = got_split;
+      }
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (best_cfg < 0) return fail(EP_ERR_INTERNAL, "autotune: no candidate configuration ran");
+  {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    g_tune_cache[key] = {best_cfg, best_split};
+  }
+  t_last_error.clear();
+  opt.tile_cfg = best_cfg;
+  opt.split_k = best_split;
+  opt.autotune = 0;
+  return EP_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int ep_abi_version(void) { return EP_ABI_VERSION; }
@@ -311,7 +393,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   *out = nullptr;
   ep_status st = validate(s, dtype, epi, io, opt_in);
   if (st != EP_OK) return st;
-  ep_options opt = opt_in ? *opt_in : ep_options{EP_PATH_FUSED, EP_BGRAD_TWO_PASS, -1, 0};
+  ep_options opt = opt_in ? *opt_in : ep_options{EP_PATH_FUSED, EP_BGRAD_TWO_PASS, -1, 0, 0};
 
   // ---- first HIP call: the device must exist and be usable
   int dev = -1;
@@ -322,6 +404,11 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   if (he != hipSuccess) return fail(EP_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(he));
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(EP_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+
+  if (opt.autotune) {
+    st = autotune(s, dtype, epi, io, opt, dev);
+    if (st != EP_OK) return st;
+  }
 
   const bool dual = epi == EP_EPILOG_SWIGLU;
   const bool unfused = opt.path == EP_PATH_UNFUSED;

@@ -139,6 +139,13 @@ typedef struct {
                               workgroup into fp32 partials that a second launch sums (in a fixed
                               order) before running the epilog.  Must be 0 or 1 for the unfused
                               path. */
+  int autotune;            /* fused path, tile_cfg -1 and split_k 0 only: 1 = ep_plan times every
+                              allowed (tile configuration, split) pair on the bound buffers and
+                              keeps the fastest.  The buffers' contents are overwritten and
+                              ep_plan synchronizes the device.  The choice is cached per
+                              (m, n, k, leading dimensions, layout, dtype, epilog) for the
+                              process, so later plans of the same problem do not time again.
+                              0 = choose by the shape model (default). */
 } ep_options;
 
 #define EP_MAX_SPLIT_K 4
@@ -156,7 +163,7 @@ typedef struct {
 ep_status ep_plan(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog,
                   const ep_epilog_io* io, ep_handle* out);
 
-/* ep_plan with options (opt may be NULL for the defaults {FUSED, TWO_PASS, -1, 0}). */
+/* ep_plan with options (opt may be NULL for the defaults {FUSED, TWO_PASS, -1, 0, 0}). */
 ep_status ep_plan_ex(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog,
                      const ep_epilog_io* io, const ep_options* opt, ep_handle* out);
 

@@ -121,6 +121,13 @@ CASES = [
     ("split_k above 4", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=5))[0], INVALID),
     ("unfused with split_k", lambda L: plan(L, shape(), opt=ep_options(path=1, bgrad_mode=0, tile_cfg=-1, split_k=2))[0],
      UNSUPPORTED),
+    ("autotune not 0/1", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, autotune=2))[0], INVALID),
+    ("autotune with a fixed tile_cfg", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=0,
+                                                                                   autotune=1))[0], INVALID),
+    ("autotune with split_k", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=2,
+                                                                          autotune=1))[0], INVALID),
+    ("autotune on the unfused path", lambda L: plan(L, shape(), opt=ep_options(path=1, bgrad_mode=0, tile_cfg=-1,
+                                                                                 autotune=1))[0], INVALID),
 ]
 
 

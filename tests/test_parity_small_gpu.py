@@ -51,7 +51,8 @@ def make_inputs(epi, dt, layout, m, n, k, seed, dev):
     return {kk: v.to(dev) for kk, v in ins.items()}
 
 
-def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split_k=0, bgrad_mode="two_pass"):
+def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split_k=0, bgrad_mode="two_pass",
+                  autotune=False):
     import dense_gemm_epilogues_amd as ep
     dev = torch.device("cuda")
     dt = DTYPES[dtname]
@@ -76,7 +77,8 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
         aux_out["d_up"] = uview
     say(f"case epi={epi} dt={dtname} layout={layout} m={m} n={n} k={k} cfg={cfg} path={path} split_k={split_k}")
     p = ep.Plan(ins["a"], ins["b"], epilog=epi, epilog_inputs=epi_in, b_layout=layout, out=out,
-                aux_out=aux_out, path=path, tile_cfg=cfg, split_k=split_k, bgrad_mode=bgrad_mode)
+                aux_out=aux_out, path=path, tile_cfg=cfg, split_k=split_k, bgrad_mode=bgrad_mode,
+                autotune=autotune)
     if split_k > 1:
         kt = -(-k // (64 if cfg in (1, 4) else 32))
         per = -(-kt // min(split_k, kt))
@@ -159,6 +161,16 @@ def test_split_k(epi, layout, splits):
         for dtname in ("f16", "bf16"):
             for (m, n, k) in [(300, 200, 520), (130, 264, 136)]:
                 run_and_check(epi, dtname, layout, m, n, k, cfg, split_k=splits)
+
+
+@pytest.mark.parametrize("epi", EPIS)
+def test_autotune(epi):
+    """Plan-time tuning picks some (tile, split) pair; the tuned plan must still be exact, and a
+    second plan of the same problem reuses the cached choice."""
+    require_gpu()
+    for layout in ("KN", "NK"):
+        run_and_check(epi, "bf16", layout, 300, 200, 520, -1, autotune=True)
+        run_and_check(epi, "bf16", layout, 300, 200, 520, -1, autotune=True, seed=1)
 
 
 def test_split_k_atomic_bgrad():
