@@ -14,6 +14,7 @@ Sources, by page:
   * "nvmath-python wraps cuBLASLt: low-overhead matmul + bias fusion primitives for
     PyTorch" (hotdry.top blog post, paragraphs 3-7 and their listings).
   * "gemm_swiglu_mlp_fusion.py" (cudnn-frontend sample, module docstring and _demo).
+  * GELU: named (not defined) by the hotdry.top post; the exact erf form is used.
 
 Every function is pinned by a CPU test (exact rational brute force, closed forms,
 invariants, hand-derived fixtures under tests/golden/).  Nothing here is "parity
@@ -22,7 +23,7 @@ unpinned".
 from .core import (
     decode_f16, decode_bf16_bits, matmul, bias_epilog, relu_bias, relu_aux_bias,
     pack_relu_mask, unpack_relu_mask, drelu_bgrad, bgrad_all_ones_closed_form,
-    sigmoid, silu, silu_grad, swiglu, dswiglu,
+    sigmoid, silu, silu_grad, swiglu, dswiglu, gelu, gelu_grad, gelu_aux_bias, dgelu_bgrad,
 )
 from .compare import rel_l2, check_half_output, check_mask, check_bgrad, TOL
 from .sampling import sample_tiles, sample_columns
@@ -30,7 +31,7 @@ from .sampling import sample_tiles, sample_columns
 __all__ = [
     "decode_f16", "decode_bf16_bits", "matmul", "bias_epilog", "relu_bias", "relu_aux_bias",
     "pack_relu_mask", "unpack_relu_mask", "drelu_bgrad", "bgrad_all_ones_closed_form",
-    "sigmoid", "silu", "silu_grad", "swiglu", "dswiglu",
+    "sigmoid", "silu", "silu_grad", "swiglu", "dswiglu", "gelu", "gelu_grad", "gelu_aux_bias", "dgelu_bgrad",
     "rel_l2", "check_half_output", "check_mask", "check_bgrad", "TOL",
     "sample_tiles", "sample_columns",
 ]

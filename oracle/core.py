@@ -11,6 +11,7 @@ Conventions (shared with the library's C header only through this prose, not cod
     before any arithmetic; nothing is rounded afterwards.
 """
 import numpy as np
+from scipy.special import erf as _erf
 
 
 # ----------------------------------------------------------------------------- decoding
@@ -213,3 +214,39 @@ def dswiglu(dout, wd, gate, up, b_layout="KN"):
     gate = np.asarray(gate, dtype=np.float64)
     up = np.asarray(up, dtype=np.float64)
     return dh * up * silu_grad(gate), dh * silu(gate), dh
+
+
+# ---------------------------------------------------------------------------- GELU
+# The hotdry.top cuBLASLt post (its opening paragraph and the paragraph listing the
+# predefined epilogs) names GELU as a fusable activation and GELU_BIAS as an epilog but does
+# not say which GELU.  The exact form is used: gelu(t) = t * Phi(t), Phi the standard normal
+# CDF.  GELU_AUX_BIAS and DGELU_BGRAD follow the RELU_AUX_BIAS / DRELU_BGRAD pair: the forward
+# also returns its pre-activation, the backward scales dY W^T by gelu' of that stored
+# pre-activation and reduces the result over the batch into the bias gradient.
+
+def gelu(t):
+    """t * Phi(t) = t / 2 * (1 + erf(t / sqrt(2)))."""
+    t = np.asarray(t, dtype=np.float64)
+    return 0.5 * t * (1.0 + _erf(t / np.sqrt(2.0)))
+
+
+def gelu_grad(t):
+    """d gelu / dt = Phi(t) + t * phi(t), phi(t) = exp(-t^2 / 2) / sqrt(2 pi)."""
+    t = np.asarray(t, dtype=np.float64)
+    return 0.5 * (1.0 + _erf(t / np.sqrt(2.0))) + t * np.exp(-0.5 * t * t) / np.sqrt(2.0 * np.pi)
+
+
+def gelu_aux_bias(a, b, bias, b_layout):
+    """GELU_BIAS / GELU_AUX_BIAS epilog: (Y, P) with P = A B + bias (the pre-activation,
+    returned by GELU_AUX_BIAS as its auxiliary output) and Y = gelu(P)."""
+    p = bias_epilog(a, b, bias, b_layout)
+    return gelu(p), p
+
+
+def dgelu_bgrad(a, b, b_layout, p_aux):
+    """DGELU_BGRAD epilog: (dX, bgrad) with dX = (dY W^T) * gelu'(P) elementwise, P the stored
+    pre-activation of the forward (the exact values the GPU consumed), and bgrad the
+    column-wise sum over the batch of the unrounded dX."""
+    g = matmul(a, b, b_layout)
+    dx = g * gelu_grad(p_aux)
+    return dx, dx.sum(axis=0)

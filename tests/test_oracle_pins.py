@@ -385,3 +385,74 @@ def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
     wrong = oracle.matmul(a2, np.ascontiguousarray(b2.T), "KN")
     exact = _brute.exact_matmul(a2.tolist(), b2.tolist(), "KN")
     assert any(abs(Fraction(wrong[i, j]) - exact[i][j]) > Fraction(1, 2 ** 20) for i in range(3) for j in range(4))
+
+
+# ---------------------------------------------------------------------------- GELU
+def test_gelu_golden(golden_dir):
+    g = load(golden_dir, "gelu_aux_bias_dgelu_2x2x2.json")
+    x, w, bias = np.array(g["x"], float), np.array(g["w"], float), np.array(g["bias"], float)
+    y, p = oracle.gelu_aux_bias(x, w, bias, "KN")
+    assert np.allclose(p, g["p"], rtol=0, atol=1e-15)
+    assert np.allclose(y, g["y"], rtol=0, atol=1e-15)
+    dx, bg = oracle.dgelu_bgrad(np.array(g["dy"], float), np.array(g["w_bwd"], float), "NK", p)
+    assert np.allclose(dx, g["dx"], rtol=0, atol=1e-15)
+    assert np.allclose(bg, g["bgrad"], rtol=0, atol=1e-15)
+
+
+def test_gelu_identities_and_limits():
+    t = np.linspace(-8, 8, 321)
+    assert oracle.gelu(np.array([0.0]))[0] == 0.0
+    assert oracle.gelu_grad(np.array([0.0]))[0] == 0.5
+    # erf is odd, so gelu(t) - gelu(-t) = t
+    assert np.allclose(oracle.gelu(t) - oracle.gelu(-t), t, rtol=0, atol=1e-14)
+    # gelu(t) -> t for large t, -> 0 for very negative t; gelu' -> 1 and 0
+    big = oracle.gelu(np.array([40.0, -40.0]))
+    assert big[0] == 40.0 and abs(big[1]) < 1e-300
+    gb = oracle.gelu_grad(np.array([40.0, -40.0]))
+    assert gb[0] == 1.0 and abs(gb[1]) < 1e-300
+    # the minimum of gelu: gelu'(t*) = 0 near t* = -0.7518 (Phi(t) = -t phi(t))
+    tm = np.linspace(-0.76, -0.74, 2001)
+    t_star = tm[np.argmin(np.abs(oracle.gelu_grad(tm)))]
+    assert abs(t_star + 0.7518) < 2e-4
+
+
+def test_gelu_grad_central_differences():
+    t = np.linspace(-9, 9, 181)
+    h = 1e-5
+    fd = (oracle.gelu(t + h) - oracle.gelu(t - h)) / (2 * h)
+    assert np.allclose(oracle.gelu_grad(t), fd, rtol=0, atol=1e-9)
+
+
+def test_gelu_aux_bias_special_cases_and_bruteforce():
+    x, w, b = f16((5, 8)), f16((8, 6), 0.4), f16((6,), 0.2)
+    y, p = oracle.gelu_aux_bias(x, w, b, "KN")
+    pe = _brute.exact_matmul(x.tolist(), w.tolist(), "KN")
+    for i in range(5):
+        for j in range(6):
+            assert abs(p[i, j] - (float(pe[i][j]) + float(b[j]))) < 1e-12
+    assert np.allclose(y, oracle.gelu(p), rtol=0, atol=0)
+    # bias = 0 reduces to gelu of the plain product; the NK layout of W^T gives the same result
+    y0, _ = oracle.gelu_aux_bias(x, w, np.zeros(6), "KN")
+    assert np.allclose(y0, oracle.gelu(x.astype(float) @ w.astype(float)), rtol=0, atol=1e-15)
+    y1, _ = oracle.gelu_aux_bias(x, np.ascontiguousarray(w.T), b, "NK")
+    assert np.allclose(y1, y, rtol=0, atol=1e-15)
+
+
+def test_dgelu_bgrad_closed_form_and_gradient():
+    rng = np.random.default_rng(11)
+    dy, w = rng.standard_normal((7, 5)), rng.standard_normal((9, 5))   # w: N x K (NK)
+    # pre-activation 0 everywhere: gelu'(0) = 1/2, so dX = G / 2 and bgrad = colsum(dY) W^T / 2
+    dx, bg = oracle.dgelu_bgrad(dy, w, "NK", np.zeros((7, 9)))
+    assert np.allclose(dx, 0.5 * dy @ w.T, rtol=1e-14, atol=1e-14)
+    assert np.allclose(bg, 0.5 * oracle.bgrad_all_ones_closed_form(dy, w, "NK"), rtol=1e-13, atol=1e-13)
+    # dX is the gradient of sum(G * gelu(P)) with respect to P
+    p = 2 * rng.standard_normal((7, 9))
+    dx, bg = oracle.dgelu_bgrad(dy, w, "NK", p)
+    g = dy @ w.T
+    F = lambda q: float(np.sum(g * oracle.gelu(q)))
+    for _ in range(5):
+        d = rng.standard_normal((7, 9))
+        eps = 1e-6
+        fd = (F(p + eps * d) - F(p - eps * d)) / (2 * eps)
+        assert abs(fd - float(np.sum(dx * d))) <= 1e-6 * (1 + abs(fd))
+    assert np.allclose(bg, dx.sum(axis=0), rtol=0, atol=0)
