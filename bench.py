@@ -139,6 +139,33 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True):
     return out
 
 
+def gelu_layer(c, steps, warmup, flush, dev):
+    """Fused GELU_AUX_BIAS forward + DGELU_BGRAD backward (consuming the forward's saved
+    pre-activation) against the unfused GEMM + elementwise sequence, on a linear layer's inputs."""
+    import dense_gemm_epilogues_amd as ep
+    import workloads as W
+    inp = W.linear_inputs(c, device=dev)
+    x, w, bias, dy = inp["x"], inp["w"], inp["bias"], inp["dy"]
+    res = {}
+    for path in ("fused", "unfused"):
+        pf = ep.Plan(x, w, "GELU_AUX_BIAS", {"bias": bias}, b_layout="KN", path=path)
+        _, aux = pf.execute()
+        pb = ep.Plan(dy, w, "DGELU_BGRAD", {"gelu_aux": aux["gelu_aux"]}, b_layout="NK", path=path)
+        step_ms, per = run_steps([pf.execute, pb.execute], steps, warmup, flush)
+        res[path] = {"step_ms": float(np.mean(step_ms)), "fwd_ms": float(np.mean(per[0])),
+                     "bwd_ms": float(np.mean(per[1]))}
+        pf.free()
+        pb.free()
+    flop = 2.0 * c.m * c.n * c.k
+    f, u = res["fused"], res["unfused"]
+    return {"fused_step_tflops": round(2 * flop / (f["step_ms"] * 1e-3) / 1e12, 1),
+            "fwd_pct_peak": round(100 * flop / (f["fwd_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
+            "bwd_pct_peak": round(100 * flop / (f["bwd_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
+            "fused_fwd_ms": round(f["fwd_ms"], 5), "fused_bwd_ms": round(f["bwd_ms"], 5),
+            "unfused_fwd_ms": round(u["fwd_ms"], 5), "unfused_bwd_ms": round(u["bwd_ms"], 5),
+            "speedup_step": round(u["step_ms"] / f["step_ms"], 4)}
+
+
 def swiglu_fwd(c, steps, warmup, flush, dev):
     import dense_gemm_epilogues_amd as ep
     import workloads as W
@@ -442,6 +469,7 @@ def main():
             "speedup": round(r5["speedup"], 4)}
         torch.cuda.empty_cache()
         large["swiglu_fwd_bf16_M_sweep_H5120_I17408"] = swiglu_m_sweep(s_l, w_l, flush, dev)
+        large["gelu_layer_fp16_4096x4096x4096"] = gelu_layer(W.LINEAR[2], args.steps, args.warmup, flush, dev)
         large["execute_overhead"] = execute_overhead(dev)
         large["autotune_vs_model"] = autotune_vs_model(s_l, w_l, flush, dev)
         line["configs"] = large

@@ -28,6 +28,7 @@ library_path = os.path.join(_HERE, "libep.so")
 EPILOGS = {
     "DEFAULT": 0, "BIAS": 1, "RELU_BIAS": 2, "RELU_AUX_BIAS": 3,
     "DRELU_BGRAD": 4, "SWIGLU": 5, "DSWIGLU": 6,
+    "GELU_BIAS": 7, "GELU_AUX_BIAS": 8, "DGELU_BGRAD": 9,
 }
 _LAYOUTS = {"KN": 0, "NK": 1}
 _DTYPES = {torch.float16: 0, torch.bfloat16: 1}
@@ -49,7 +50,7 @@ class ep_epilog_io(ctypes.Structure):
                 ("relu_aux_in", ctypes.c_void_p), ("ld_aux", ctypes.c_int64),
                 ("bgrad", ctypes.c_void_p), ("b2", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("up", ctypes.c_void_p), ("ld_gu", ctypes.c_int64), ("d2", ctypes.c_void_p),
-                ("ldd2", ctypes.c_int64)]
+                ("ldd2", ctypes.c_int64), ("gelu_aux", ctypes.c_void_p), ("ld_gelu_aux", ctypes.c_int64)]
 
 
 class ep_options(ctypes.Structure):
@@ -135,6 +136,9 @@ class Plan:
       DRELU_BGRAD: {"relu_aux": (M, >= ceil(N/32)) int32 mask words}
       SWIGLU: {"b2": up weight, same layout as b}
       DSWIGLU: {"gate": (M, N), "up": (M, N)}
+      GELU_BIAS / GELU_AUX_BIAS: {"bias": (N,)}
+      DGELU_BGRAD: {"gelu_aux": (M, N) pre-activation saved by GELU_AUX_BIAS}
+    aux outputs (execute()'s second value): relu_aux, drelu_bgrad, d_up, gelu_aux, dgelu_bgrad.
     Outputs are allocated here with torch.empty unless `out` / `aux_out` are given and are
     reused by every execute().  Tensors are kept alive for the plan's lifetime.
     path "fused" | "unfused"; bgrad_mode "two_pass" | "atomic"; tile_cfg -1 (by shape) or an
@@ -160,8 +164,22 @@ class Plan:
         self.out = out
         self.aux = {}
         io = ep_epilog_io()
-        if epilog in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS"):
+        if epilog in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS", "GELU_AUX_BIAS"):
             io.bias = _ptr(epilog_inputs["bias"])
+        if epilog == "GELU_AUX_BIAS":
+            ga = aux_out.get("gelu_aux")
+            if ga is None:
+                ga = torch.empty((m, n), dtype=a.dtype, device=a.device)
+            io.gelu_aux, io.ld_gelu_aux = _ptr(ga), ga.stride(0)
+            self.aux["gelu_aux"] = ga
+        if epilog == "DGELU_BGRAD":
+            gi = epilog_inputs["gelu_aux"]
+            io.gelu_aux, io.ld_gelu_aux = _ptr(gi), gi.stride(0)
+            bg = aux_out.get("dgelu_bgrad")
+            if bg is None:
+                bg = torch.empty((n,), dtype=torch.float32, device=a.device)
+            io.bgrad = _ptr(bg)
+            self.aux["dgelu_bgrad"] = bg
         if epilog == "RELU_AUX_BIAS":
             ra = aux_out.get("relu_aux")
             if ra is None:

@@ -196,6 +196,50 @@ __global__ void dswiglu_kernel(const char* dh, int64_t lddh, const char* gate, c
   }
 }
 
+// exact GELU t Phi(t) and its derivative Phi(t) + t phi(t) (exp on the hardware exp2)
+__device__ __forceinline__ float ew_gelu(float t) { return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f)); }
+__device__ __forceinline__ float ew_gelu_grad(float t) {
+  return 0.5f * (1.0f + erff(t * 0.70710678118654752f)) +
+         t * 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * t * t);
+}
+
+// unfused GELU forward, in place: aux = z (when aux is given), z = gelu(z)
+template <int DT>
+__global__ void gelu_apply_kernel(char* z, int64_t ldz, char* aux, int64_t ld_aux, int M, int N) {
+  const int gpr = N / 8;
+  const int64_t total = (int64_t)M * gpr;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = i / gpr;
+    const int col = (int)(i - row * gpr) * 8;
+    const u32x4 raw = *(const u32x4*)(z + (row * ldz + col) * 2);
+    if (aux) *(u32x4*)(aux + (row * ld_aux + col) * 2) = raw;
+    float f[8];
+    unpack8<DT>(raw, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = ew_gelu(f[e]);
+    *(u32x4*)(z + (row * ldz + col) * 2) = pack8<DT>(f);
+  }
+}
+
+// unfused GELU backward, in place: g = g * gelu'(aux)
+template <int DT>
+__global__ void dgelu_apply_kernel(char* g, int64_t ldg, const char* aux, int64_t ld_aux, int M, int N) {
+  const int gpr = N / 8;
+  const int64_t total = (int64_t)M * gpr;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = i / gpr;
+    const int col = (int)(i - row * gpr) * 8;
+    float fg[8], fa[8];
+    unpack8<DT>(*(const u32x4*)(g + (row * ldg + col) * 2), fg);
+    unpack8<DT>(*(const u32x4*)(aux + (row * ld_aux + col) * 2), fa);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fg[e] *= ew_gelu_grad(fa[e]);
+    *(u32x4*)(g + (row * ldg + col) * 2) = pack8<DT>(fg);
+  }
+}
+
 constexpr int kEwThreads = 256;
 
 inline int ew_blocks(int64_t work) {
@@ -273,6 +317,22 @@ hipError_t launch_dswiglu(int dtype, const void* dh, int64_t lddh, const void* g
   EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(dswiglu_kernel<DTV>, dim3(nb), dim3(kEwThreads), 0, s, (const char*)dh,
                                            lddh, (const char*)gate, (const char*)up, ld_gu, (char*)dg, lddg, (char*)du,
                                            lddu, M, N));
+  return hipGetLastError();
+}
+
+hipError_t launch_gelu_apply(int dtype, void* z, int64_t ldz, void* aux, int64_t ld_aux, int M, int N,
+                             hipStream_t s) {
+  const int nb = ew_blocks((int64_t)M * (N / 8));
+  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(gelu_apply_kernel<DTV>, dim3(nb), dim3(kEwThreads), 0, s, (char*)z, ldz,
+                                           (char*)aux, ld_aux, M, N));
+  return hipGetLastError();
+}
+
+hipError_t launch_dgelu_apply(int dtype, void* g, int64_t ldg, const void* aux, int64_t ld_aux, int M, int N,
+                              hipStream_t s) {
+  const int nb = ew_blocks((int64_t)M * (N / 8));
+  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(dgelu_apply_kernel<DTV>, dim3(nb), dim3(kEwThreads), 0, s, (char*)g, ldg,
+                                           (const char*)aux, ld_aux, M, N));
   return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ namespace ep {
 #define EP_DECL_TABLE(dt, lay, epi) extern const GemmLauncher kLaunch_##dt##_##lay##_##epi[kNumTileCfgs];
 #define EP_DECL_EPIS(dt, lay)                                                                    \
   EP_DECL_TABLE(dt, lay, 0) EP_DECL_TABLE(dt, lay, 1) EP_DECL_TABLE(dt, lay, 2)                  \
-  EP_DECL_TABLE(dt, lay, 3) EP_DECL_TABLE(dt, lay, 4) EP_DECL_TABLE(dt, lay, 5) EP_DECL_TABLE(dt, lay, 6)
+  EP_DECL_TABLE(dt, lay, 3) EP_DECL_TABLE(dt, lay, 4) EP_DECL_TABLE(dt, lay, 5) EP_DECL_TABLE(dt, lay, 6)  \
+  EP_DECL_TABLE(dt, lay, 7) EP_DECL_TABLE(dt, lay, 8) EP_DECL_TABLE(dt, lay, 9)
 EP_DECL_EPIS(0, 0)
 EP_DECL_EPIS(0, 1)
 EP_DECL_EPIS(1, 0)
@@ -33,7 +34,8 @@ EP_DECL_EPIS(1, 1)
   {                                                                                              \
     kLaunch_##dt##_##lay##_0, kLaunch_##dt##_##lay##_1, kLaunch_##dt##_##lay##_2,                \
         kLaunch_##dt##_##lay##_3, kLaunch_##dt##_##lay##_4, kLaunch_##dt##_##lay##_5,            \
-        kLaunch_##dt##_##lay##_6                                                                 \
+        kLaunch_##dt##_##lay##_6, kLaunch_##dt##_##lay##_7, kLaunch_##dt##_##lay##_8,            \
+        kLaunch_##dt##_##lay##_9                                                                 \
   }
 static const GemmLauncher* const kTables[2][2][E_NUM] = {{EP_ROW(0, 0), EP_ROW(0, 1)},
                                                          {EP_ROW(1, 0), EP_ROW(1, 1)}};
@@ -43,7 +45,8 @@ static const GemmLauncher* const kTables[2][2][E_NUM] = {{EP_ROW(0, 0), EP_ROW(0
   extern const GemmLauncher kPartial_##dt##_##lay##_5[kNumTileCfgs];
 EP_DECL_P(0, 0) EP_DECL_P(0, 1) EP_DECL_P(1, 0) EP_DECL_P(1, 1)
 #define EP_DECL_F(dt) EP_DECL_TABLE_F(dt, 0) EP_DECL_TABLE_F(dt, 1) EP_DECL_TABLE_F(dt, 2) \
-  EP_DECL_TABLE_F(dt, 3) EP_DECL_TABLE_F(dt, 4) EP_DECL_TABLE_F(dt, 5) EP_DECL_TABLE_F(dt, 6)
+  EP_DECL_TABLE_F(dt, 3) EP_DECL_TABLE_F(dt, 4) EP_DECL_TABLE_F(dt, 5) EP_DECL_TABLE_F(dt, 6) \
+  EP_DECL_TABLE_F(dt, 7) EP_DECL_TABLE_F(dt, 8) EP_DECL_TABLE_F(dt, 9)
 #define EP_DECL_TABLE_F(dt, epi) extern const GemmLauncher kFixup_##dt##_##epi[kNumTileCfgs];
 EP_DECL_F(0) EP_DECL_F(1)
 // [dtype][layout][single B, dual B]
@@ -51,8 +54,10 @@ static const GemmLauncher* const kPartialTables[2][2][2] = {
     {{kPartial_0_0_0, kPartial_0_0_5}, {kPartial_0_1_0, kPartial_0_1_5}},
     {{kPartial_1_0_0, kPartial_1_0_5}, {kPartial_1_1_0, kPartial_1_1_5}}};
 static const GemmLauncher* const kFixupTables[2][E_NUM] = {
-    {kFixup_0_0, kFixup_0_1, kFixup_0_2, kFixup_0_3, kFixup_0_4, kFixup_0_5, kFixup_0_6},
-    {kFixup_1_0, kFixup_1_1, kFixup_1_2, kFixup_1_3, kFixup_1_4, kFixup_1_5, kFixup_1_6}};
+    {kFixup_0_0, kFixup_0_1, kFixup_0_2, kFixup_0_3, kFixup_0_4, kFixup_0_5, kFixup_0_6, kFixup_0_7, kFixup_0_8,
+     kFixup_0_9},
+    {kFixup_1_0, kFixup_1_1, kFixup_1_2, kFixup_1_3, kFixup_1_4, kFixup_1_5, kFixup_1_6, kFixup_1_7, kFixup_1_8,
+     kFixup_1_9}};
 
 GemmLauncher gemm_partial_launcher(int dtype, int layout, bool dual, int cfg) {
   if (dtype < 0 || dtype > 1 || layout < 0 || layout > 1 || cfg < 0 || cfg >= kNumTileCfgs) return nullptr;
@@ -71,8 +76,8 @@ GemmLauncher gemm_launcher(int dtype, int layout, int epi, int cfg) {
   return kTables[dtype][layout][epi][cfg];
 }
 
-static const char* kEpiNames[E_NUM] = {"DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS",
-                                       "DRELU_BGRAD", "SWIGLU", "DSWIGLU"};
+static const char* kEpiNames[E_NUM] = {"DEFAULT", "BIAS",     "RELU_BIAS",     "RELU_AUX_BIAS", "DRELU_BGRAD",
+                                       "SWIGLU",  "DSWIGLU", "GELU_BIAS",     "GELU_AUX_BIAS", "DGELU_BGRAD"};
 
 }  // namespace ep
 
@@ -222,9 +227,12 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   if (s->ldd < s->n || s->ldd % 8 || s->ldd >= kMaxLd)
     return fail(EP_ERR_INVALID_ARG, "ldd must be a multiple of 8 in [n, 2^22)");
 
-  const bool wants_bias = epi == EP_EPILOG_BIAS || epi == EP_EPILOG_RELU_BIAS || epi == EP_EPILOG_RELU_AUX_BIAS;
+  const bool wants_bias = epi == EP_EPILOG_BIAS || epi == EP_EPILOG_RELU_BIAS || epi == EP_EPILOG_RELU_AUX_BIAS ||
+                          epi == EP_EPILOG_GELU_BIAS || epi == EP_EPILOG_GELU_AUX_BIAS;
   const bool wants_aux_out = epi == EP_EPILOG_RELU_AUX_BIAS;
   const bool wants_aux_in = epi == EP_EPILOG_DRELU_BGRAD;
+  const bool wants_bgrad = epi == EP_EPILOG_DRELU_BGRAD || epi == EP_EPILOG_DGELU_BGRAD;
+  const bool wants_gaux = epi == EP_EPILOG_GELU_AUX_BIAS || epi == EP_EPILOG_DGELU_BGRAD;
   const bool wants_b2 = epi == EP_EPILOG_SWIGLU;
   const bool wants_gu = epi == EP_EPILOG_DSWIGLU;
   if (wants_bias != (io->bias != nullptr))
@@ -233,8 +241,19 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
     return fail(EP_ERR_INVALID_ARG, wants_aux_out ? "relu_aux output is required" : "relu_aux must be NULL");
   if (wants_aux_in != (io->relu_aux_in != nullptr))
     return fail(EP_ERR_INVALID_ARG, wants_aux_in ? "relu_aux_in is required" : "relu_aux_in must be NULL");
-  if (wants_aux_in != (io->bgrad != nullptr))
-    return fail(EP_ERR_INVALID_ARG, wants_aux_in ? "bgrad output is required" : "bgrad must be NULL");
+  if (wants_bgrad != (io->bgrad != nullptr))
+    return fail(EP_ERR_INVALID_ARG, wants_bgrad ? "bgrad output is required" : "bgrad must be NULL");
+  if (wants_gaux != (io->gelu_aux != nullptr))
+    return fail(EP_ERR_INVALID_ARG, wants_gaux ? "gelu_aux is required" : "gelu_aux must be NULL for this epilog");
+  if (wants_gaux && !aligned(io->gelu_aux, 16)) return fail(EP_ERR_INVALID_ARG, "gelu_aux must be 16-byte aligned");
+  if (wants_bgrad && !aligned(io->bgrad, 16)) return fail(EP_ERR_INVALID_ARG, "bgrad must be 16-byte aligned");
+  if (wants_gaux) {
+    const int64_t ld = io->ld_gelu_aux == 0 ? s->n : io->ld_gelu_aux;
+    if (ld < s->n || ld % 8 || ld >= kMaxLd)
+      return fail(EP_ERR_INVALID_ARG, "ld_gelu_aux must be a multiple of 8 in [n, 2^22)");
+  } else if (io->ld_gelu_aux != 0) {
+    return fail(EP_ERR_INVALID_ARG, "ld_gelu_aux must be 0 for this epilog");
+  }
   if (wants_b2 != (io->b2 != nullptr))
     return fail(EP_ERR_INVALID_ARG, wants_b2 ? "b2 (up weight) is required" : "b2 must be NULL");
   if (wants_gu != (io->gate != nullptr) || wants_gu != (io->up != nullptr) || wants_gu != (io->d2 != nullptr))
@@ -431,6 +450,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   if (h->io.ld_aux == 0) h->io.ld_aux = (s->n + 31) / 32;
   if (h->io.ld_gu == 0) h->io.ld_gu = s->n;
   if (h->io.ldd2 == 0) h->io.ldd2 = s->ldd;
+  if (h->io.ld_gelu_aux == 0) h->io.ld_gelu_aux = s->n;
   h->opt = opt;
   h->device = dev;
   h->cfg = cfg;
@@ -471,7 +491,8 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   size_t part_bytes = 0, z_bytes = 0, z2_bytes = 0, kpart_bytes = 0;
   if (splits > 1)
     kpart_bytes = (size_t)splits * a.tiles_m * a.tiles_n * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * sizeof(float);
-  if (epi == EP_EPILOG_DRELU_BGRAD) {
+  const bool bgrad_epi = epi == EP_EPILOG_DRELU_BGRAD || epi == EP_EPILOG_DGELU_BGRAD;
+  if (bgrad_epi) {
     if (unfused) {
       h->colsum_rows = 256;
       h->nparts = (int)((M + h->colsum_rows - 1) / h->colsum_rows);
@@ -517,7 +538,9 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
     a.ld_gu = h->io.ld_gu;
     a.d2 = io->d2;
     a.ldd2 = h->io.ldd2;
-    if (epi == EP_EPILOG_DRELU_BGRAD) {
+    a.gaux = io->gelu_aux;
+    a.ld_gaux = h->io.ld_gelu_aux;
+    if (bgrad_epi) {
       a.bgrad_atomic = opt.bgrad_mode == EP_BGRAD_ATOMIC;
       a.bgrad_part = a.bgrad_atomic ? io->bgrad : h->part;
     }
@@ -559,8 +582,9 @@ ep_status ep_execute(ep_handle h, void* stream) {
   const int dt = (int)h->dtype;
   const int M = (int)sh.m, N = (int)sh.n;
   ep_status st;
+  const bool bgrad_epi = h->epilog == EP_EPILOG_DRELU_BGRAD || h->epilog == EP_EPILOG_DGELU_BGRAD;
   if (h->opt.path == EP_PATH_FUSED) {
-    if (h->epilog == EP_EPILOG_DRELU_BGRAD && h->opt.bgrad_mode == EP_BGRAD_ATOMIC) {
+    if (bgrad_epi && h->opt.bgrad_mode == EP_BGRAD_ATOMIC) {
       if (launch_fill_zero_f32(h->io.bgrad, N, s) != hipSuccess) return check_launch("fill_zero");
     }
     if (h->splits > 1) {
@@ -572,7 +596,7 @@ ep_status ep_execute(ep_handle h, void* stream) {
       h->launch(h->args, s);
       if ((st = check_launch("fused gemm")) != EP_OK) return st;
     }
-    if (h->epilog == EP_EPILOG_DRELU_BGRAD && h->opt.bgrad_mode == EP_BGRAD_TWO_PASS) {
+    if (bgrad_epi && h->opt.bgrad_mode == EP_BGRAD_TWO_PASS) {
       launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s);
       if ((st = check_launch("bgrad_reduce")) != EP_OK) return st;
     }
@@ -610,6 +634,20 @@ ep_status ep_execute(ep_handle h, void* stream) {
       launch_dswiglu(dt, sh.d, sh.ldd, h->io.gate, h->io.up, h->io.ld_gu, sh.d, sh.ldd, h->io.d2, h->io.ldd2, M,
                      N, s);
       break;
+    case EP_EPILOG_GELU_BIAS:
+    case EP_EPILOG_GELU_AUX_BIAS:
+      launch_bias_add(dt, sh.d, sh.ldd, h->io.bias, M, N, s);
+      if ((st = check_launch("bias_add")) != EP_OK) return st;
+      launch_gelu_apply(dt, sh.d, sh.ldd, h->epilog == EP_EPILOG_GELU_AUX_BIAS ? h->io.gelu_aux : nullptr,
+                        h->io.ld_gelu_aux, M, N, s);
+      break;
+    case EP_EPILOG_DGELU_BGRAD:
+      launch_dgelu_apply(dt, sh.d, sh.ldd, h->io.gelu_aux, h->io.ld_gelu_aux, M, N, s);
+      if ((st = check_launch("dgelu_apply")) != EP_OK) return st;
+      launch_colsum_partial(dt, sh.d, sh.ldd, h->part, M, N, h->colsum_rows, s);
+      if ((st = check_launch("colsum")) != EP_OK) return st;
+      launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s);
+      break;
   }
   return check_launch("unfused epilogue");
 }
@@ -641,7 +679,7 @@ ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
   std::string extra;
   if (h->splits > 1) kern += " split-K x" + std::to_string(h->splits) + " (partial + fixup)";
   if (h->opt.path == EP_PATH_FUSED) {
-    if (h->epilog == EP_EPILOG_DRELU_BGRAD)
+    if (h->epilog == EP_EPILOG_DRELU_BGRAD || h->epilog == EP_EPILOG_DGELU_BGRAD)
       extra = h->opt.bgrad_mode == EP_BGRAD_TWO_PASS ? " + bgrad_reduce" : " (after fill_zero; atomic bgrad)";
   } else {
     switch (h->epilog) {
@@ -651,6 +689,9 @@ ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
       case EP_EPILOG_DRELU_BGRAD: extra = " + mask_apply + colsum + bgrad_reduce"; break;
       case EP_EPILOG_SWIGLU: extra = " x2 + silu_mul"; break;
       case EP_EPILOG_DSWIGLU: extra = " + dswiglu"; break;
+      case EP_EPILOG_GELU_BIAS: extra = " + bias_add + gelu"; break;
+      case EP_EPILOG_GELU_AUX_BIAS: extra = " + bias_add + gelu (aux)"; break;
+      case EP_EPILOG_DGELU_BGRAD: extra = " + dgelu_apply + colsum + bgrad_reduce"; break;
       default: break;
     }
   }

@@ -13,7 +13,10 @@ enum Epi : int {
   E_DRELU_BGRAD = 4,
   E_SWIGLU = 5,
   E_DSWIGLU = 6,
-  E_NUM = 7
+  E_GELU_BIAS = 7,
+  E_GELU_AUX_BIAS = 8,
+  E_DGELU_BGRAD = 9,
+  E_NUM = 10
 };
 
 enum Layout : int { L_KN = 0, L_NK = 1 };
@@ -43,6 +46,8 @@ struct GemmArgs {
   // and the fp32 partial accumulators [splits][tiles][BM * BNT]
   int splits, kt_per_split;
   float* part;
+  void* gaux;           // GELU_AUX_BIAS output / DGELU_BGRAD input: pre-activation, element type
+  int64_t ld_gaux;
 };
 
 // Tile configurations, shared by the kernels (compile-time parameters) and the planner.
@@ -83,6 +88,10 @@ hipError_t launch_bgrad_reduce(const float* part, int nparts, float* bgrad, int 
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_silu_mul(int dtype, const void* g, const void* u, int64_t ldgu, void* h, int64_t ldh,
                            int M, int N, hipStream_t s);
+hipError_t launch_gelu_apply(int dtype, void* z, int64_t ldz, void* aux, int64_t ld_aux, int M, int N,
+                             hipStream_t s);
+hipError_t launch_dgelu_apply(int dtype, void* g, int64_t ldg, const void* aux, int64_t ld_aux, int M, int N,
+                              hipStream_t s);
 hipError_t launch_dswiglu(int dtype, const void* dh, int64_t lddh, const void* gate, const void* up,
                           int64_t ld_gu, void* dg, int64_t lddg, void* du, int64_t lddu, int M, int N,
                           hipStream_t s);

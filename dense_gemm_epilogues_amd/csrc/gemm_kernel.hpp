@@ -113,6 +113,14 @@ __device__ __forceinline__ float acc_read(float a) {
   return v;
 }
 
+// GELU in its exact form, gelu(t) = t Phi(t) = t/2 (1 + erf(t / sqrt 2)), and its derivative
+// Phi(t) + t phi(t) with phi(t) = exp(-t^2/2) / sqrt(2 pi) (exp on the hardware exp2).
+__device__ __forceinline__ float gelu_f(float t) { return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_grad_f(float t) {
+  const float phi = 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * t * t);
+  return 0.5f * (1.0f + erff(t * 0.70710678118654752f)) + t * phi;
+}
+
 // Logistic function from its definition, 1 / (1 + e^-t), with e^-t = 2^(-t log2 e) on the
 // hardware exp2.  t -> -inf gives 2^(+inf) = inf and 1/inf = 0; t -> +inf gives 1.
 __device__ __forceinline__ float sigmoid_f(float t) {
@@ -202,7 +210,8 @@ struct GemmTraits {
   static_assert(!DUAL || NBO >= 1, "dual B needs a block per output column range");
   // staged rows per chunk of the store loop: 8 rows read together where the epilog is a plain
   // store; one row at a time where it has per-row inputs (measured faster on MI355X)
-  static constexpr int CH = (EPI == E_DSWIGLU || EPI == E_DRELU_BGRAD) ? 1 : (ITERS < 8 ? ITERS : 8);
+  static constexpr int CH =
+      (EPI == E_DSWIGLU || EPI == E_DRELU_BGRAD || EPI == E_DGELU_BGRAD) ? 1 : (ITERS < 8 ? ITERS : 8);
   static_assert(KS == 2 || KS == 4, "k-slices per step must be even");
   static_assert(A_SLOTS >= 1 && B_SLOTS >= 1, "tile too small for 1 KiB DMA slots");
   static_assert(LDS_BYTES * cfg_occ(CFG) <= 160 * 1024, "LDS budget");
@@ -581,7 +590,9 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // column sums) is applied to the accumulators in place; then each 32-row slab is staged
   // through LDS so that every lane owns 8 consecutive columns of one row for the stores.
   constexpr int NBO = TR::NBO;
-  constexpr bool HAS_BIAS = EPI == E_BIAS || EPI == E_RELU_BIAS || EPI == E_RELU_AUX_BIAS;
+  constexpr bool HAS_BIAS = EPI == E_BIAS || EPI == E_RELU_BIAS || EPI == E_RELU_AUX_BIAS ||
+                           EPI == E_GELU_BIAS || EPI == E_GELU_AUX_BIAS;
+  constexpr bool BGRAD = EPI == E_DRELU_BGRAD || EPI == E_DGELU_BGRAD;
   constexpr bool RELU = EPI == E_RELU_BIAS || EPI == E_RELU_AUX_BIAS;
   const int l32 = lane & 31;
   const int ccol0 = n0 + wn * WTN;  // first output column of the wave
@@ -601,7 +612,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       if (c < N) bias_mf[j] = E::to_f32(((const uint16_t*)p.bias)[c]);
     }
   }
-  f32x4 colsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // DRELU_BGRAD: the lane's 8 columns
+  f32x4 colsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // bias gradients: the lane's 8 columns
 
   // DRELU_BGRAD: the slab's mask words (32 rows x WPR words) are fetched before it is staged,
   // NW per lane: word (row, w) sits in register row / RPW of lane (row % RPW) * WPR + w.
@@ -610,7 +621,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr int RPW = 64 / WPR;
   // DSWIGLU reads gate and up per element in the staged layout, for a whole slab before it
   // is staged, so their latency overlaps the staging.
-  constexpr int PF_GU = EPI == E_DSWIGLU ? TR::ITERS : 1;
+  constexpr int PF_GU = (EPI == E_DSWIGLU || EPI == E_DGELU_BGRAD) ? TR::ITERS : 1;
   u32x4 pf_g[PF_GU], pf_u[PF_GU];
 
 #pragma unroll
@@ -623,6 +634,14 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
         const int grow = srow0 + q * RPW + lane / WPR;
         const int wc = ccol0 / 32 + lane % WPR;
         pf_w[q] = (grow < M && wc * 32 < N) ? p.aux_in[(int64_t)grow * p.ld_aux + wc] : 0u;
+      }
+    } else if constexpr (EPI == E_DGELU_BGRAD) {
+#pragma unroll
+      for (int it = 0; it < TR::ITERS; ++it) {
+        const int grow = srow0 + it * TR::RPI + lr;
+        const bool ok = colok && grow < M;
+        const int64_t go = ((int64_t)grow * p.ld_gaux + gcol) * 2;
+        pf_g[it] = ok ? __builtin_nontemporal_load((const u32x4*)((const char*)p.gaux + go)) : u32x4{0u, 0u, 0u, 0u};
       }
     } else if constexpr (EPI == E_DSWIGLU) {
 #pragma unroll
@@ -748,9 +767,28 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
             *(u32x4*)((char*)p.d + (drow + gcol) * 2) = pack8<DT>(dg[0], dg[1]);
             *(u32x4*)((char*)p.d2 + ((int64_t)grow * p.ldd2 + gcol) * 2) = pack8<DT>(du[0], du[1]);
           }
+        } else if constexpr (EPI == E_GELU_BIAS || EPI == E_GELU_AUX_BIAS) {
+          if (ok) {
+            if constexpr (EPI == E_GELU_AUX_BIAS)
+              *(u32x4*)((char*)p.gaux + ((int64_t)grow * p.ld_gaux + gcol) * 2) = pack8<DT>(vv[c][0], vv[c][1]);
+            f32x4 y[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) y[h][e] = gelu_f(vv[c][h][e]);
+            *(u32x4*)((char*)p.d + (drow + gcol) * 2) = pack8<DT>(y[0], y[1]);
+          }
         } else {
+          if constexpr (EPI == E_DGELU_BGRAD) {  // rows past M: aux read as 0, staged value 0
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const f32x4 pa = unpack4<DT>(u32x2{pf_g[c0 + c][2 * h], pf_g[c0 + c][2 * h + 1]});
+#pragma unroll
+              for (int e = 0; e < 4; ++e) vv[c][h][e] *= gelu_grad_f(pa[e]);
+            }
+          }
           if (ok) *(u32x4*)((char*)p.d + (drow + gcol) * 2) = pack8<DT>(vv[c][0], vv[c][1]);
-          if constexpr (EPI == E_DRELU_BGRAD) {  // rows past M are staged as 0
+          if constexpr (BGRAD) {  // rows past M are staged as 0
             colsum[0] += vv[c][0];
             colsum[1] += vv[c][1];
           }
@@ -760,7 +798,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     __syncthreads();
   }
 
-  if constexpr (EPI == E_DRELU_BGRAD) {
+  if constexpr (BGRAD) {
     // lanes that share columns: lane, lane + LPR, ... (different rows); then the other
     // M-wave's sums through LDS; one partial per (M tile, column), or an atomic add
 #pragma unroll

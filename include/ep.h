@@ -83,6 +83,15 @@ typedef enum { EP_B_KN = 0, EP_B_NK = 1 } ep_b_layout;
  *                          D2 = d_up = dh .* gate .* s;  gate and up are M x N inputs in
  *                          the element type (row stride ld_gu).  gemm_swiglu_mlp_fusion.py,
  *                          module docstring (backward dSwiGLU as a matmul epilogue).
+ * EP_EPILOG_GELU_BIAS      D = gelu(A.B + bias) with the exact GELU, gelu(t) = t Phi(t) =
+ *                          t/2 (1 + erf(t / sqrt 2)) (hotdry.top post: GELU_BIAS among the
+ *                          predefined epilogs; the post does not fix the GELU variant).
+ * EP_EPILOG_GELU_AUX_BIAS  as GELU_BIAS, and also writes gelu_aux = A.B + bias, the
+ *                          pre-activation rounded to the element type (M x N, row stride
+ *                          ld_gelu_aux), for the backward.
+ * EP_EPILOG_DGELU_BGRAD    D = (A.B) .* gelu'(P) with P read from gelu_aux (M x N, element
+ *                          type), gelu'(t) = Phi(t) + t phi(t), and bgrad[j] = sum_i D[i][j]
+ *                          in float32 over the unrounded values, as DRELU_BGRAD.
  */
 typedef enum {
   EP_EPILOG_DEFAULT = 0,
@@ -91,7 +100,10 @@ typedef enum {
   EP_EPILOG_RELU_AUX_BIAS = 3,
   EP_EPILOG_DRELU_BGRAD = 4,
   EP_EPILOG_SWIGLU = 5,
-  EP_EPILOG_DSWIGLU = 6
+  EP_EPILOG_DSWIGLU = 6,
+  EP_EPILOG_GELU_BIAS = 7,
+  EP_EPILOG_GELU_AUX_BIAS = 8,
+  EP_EPILOG_DGELU_BGRAD = 9
 } ep_epilog;
 
 /* The GEMM operands, bound at plan time. Sizes and leading dimensions are in elements. */
@@ -113,13 +125,16 @@ typedef struct {
   uint32_t* relu_aux;          /* RELU_AUX_BIAS output: m rows of ld_aux words */
   const uint32_t* relu_aux_in; /* DRELU_BGRAD input: m rows of ld_aux words */
   int64_t ld_aux;              /* words per mask row; 0 means ceil(n/32) */
-  float* bgrad;                /* DRELU_BGRAD output: n floats */
+  float* bgrad;                /* DRELU_BGRAD / DGELU_BGRAD output: n floats */
   const void* b2;              /* SWIGLU: the up weight, same layout/ldb as b */
   const void* gate;            /* DSWIGLU inputs: m x n, row stride ld_gu */
   const void* up;
   int64_t ld_gu;               /* 0 means n */
   void* d2;                    /* DSWIGLU output d_up: m x n, row stride ldd2 (0 means ldd) */
   int64_t ldd2;
+  void* gelu_aux;              /* GELU_AUX_BIAS output / DGELU_BGRAD input: the pre-activation,
+                                  m x n in the element type, row stride ld_gelu_aux */
+  int64_t ld_gelu_aux;         /* 0 means n */
 } ep_epilog_io;
 
 typedef enum { EP_PATH_FUSED = 0, EP_PATH_UNFUSED = 1 } ep_path;

@@ -83,7 +83,7 @@ CASES = [
     ("k not multiple of 8", lambda L: plan(L, shape(k=60, lda=64))[0], UNSUPPORTED),
     ("m >= 2^31", lambda L: plan(L, shape(m=1 << 31))[0], UNSUPPORTED),
     ("unknown dtype", lambda L: plan(L, shape(), dtype=7)[0], UNSUPPORTED),
-    ("unknown epilog", lambda L: plan(L, shape(), epi=9)[0], UNSUPPORTED),
+    ("unknown epilog", lambda L: plan(L, shape(), epi=10)[0], UNSUPPORTED),
     ("unknown layout", lambda L: plan(L, shape(lay=3))[0], UNSUPPORTED),
     ("null a", lambda L: plan(L, shape(a=0))[0], INVALID),
     ("misaligned b", lambda L: plan(L, shape(b=B_PTR + 8))[0], INVALID),
@@ -121,6 +121,19 @@ CASES = [
     ("split_k above 4", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=5))[0], INVALID),
     ("unfused with split_k", lambda L: plan(L, shape(), opt=ep_options(path=1, bgrad_mode=0, tile_cfg=-1, split_k=2))[0],
      UNSUPPORTED),
+    ("GELU_BIAS without bias", lambda L: plan(L, shape(), E["GELU_BIAS"])[0], INVALID),
+    ("GELU_AUX_BIAS without gelu_aux", lambda L: plan(L, shape(), E["GELU_AUX_BIAS"], ep_epilog_io(bias=X_PTR))[0], INVALID),
+    ("GELU_BIAS with a stray gelu_aux", lambda L: plan(L, shape(), E["GELU_BIAS"],
+                                                       ep_epilog_io(bias=X_PTR, gelu_aux=X_PTR + 8192))[0], INVALID),
+    ("misaligned gelu_aux", lambda L: plan(L, shape(), E["GELU_AUX_BIAS"],
+                                           ep_epilog_io(bias=X_PTR, gelu_aux=X_PTR + 8200))[0], INVALID),
+    ("ld_gelu_aux too small", lambda L: plan(L, shape(), E["GELU_AUX_BIAS"],
+                                             ep_epilog_io(bias=X_PTR, gelu_aux=X_PTR + 8192, ld_gelu_aux=56))[0], INVALID),
+    ("ld_gelu_aux not multiple of 8", lambda L: plan(L, shape(), E["GELU_AUX_BIAS"],
+                                                     ep_epilog_io(bias=X_PTR, gelu_aux=X_PTR + 8192, ld_gelu_aux=68))[0], INVALID),
+    ("DGELU_BGRAD without bgrad", lambda L: plan(L, shape(lay=NK), E["DGELU_BGRAD"], ep_epilog_io(gelu_aux=X_PTR))[0], INVALID),
+    ("DGELU_BGRAD without gelu_aux", lambda L: plan(L, shape(lay=NK), E["DGELU_BGRAD"], ep_epilog_io(bgrad=X_PTR))[0], INVALID),
+    ("ld_gelu_aux on a non-GELU epilog", lambda L: plan(L, shape(), E["DEFAULT"], ep_epilog_io(ld_gelu_aux=64))[0], INVALID),
     ("autotune not 0/1", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, autotune=2))[0], INVALID),
     ("autotune with a fixed tile_cfg", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=0,
                                                                                    autotune=1))[0], INVALID),

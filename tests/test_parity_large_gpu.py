@@ -203,3 +203,37 @@ def test_dswiglu_backward_sampled():
         assert_half(f64(du[r0:r1, c0:c1]), dur, f"dswiglu d_up tile {(r0, c0)}")
     assert bool(torch.isfinite(dg.float()).all()) and bool(torch.isfinite(du.float()).all())
     p.free()
+
+
+# ------------------------------------------------------------------ GELU layer (square 4096)
+def test_square_gelu_layer_full():
+    """GELU_AUX_BIAS forward and DGELU_BGRAD backward on the square fp16 layer's inputs,
+    compared in full; the backward consumes the pre-activation the GPU forward saved."""
+    require_gpu()
+    ep = _ep()
+    c = W.LINEAR[2]
+    dev = torch.device("cuda")
+    say("case square GELU layer 4096^3 fp16: forward GELU_AUX_BIAS, backward DGELU_BGRAD")
+    inp = W.linear_inputs(c, device=dev)
+    x, w, bias, dy = inp["x"], inp["w"], inp["bias"], inp["dy"]
+    pf = ep.Plan(x, w, "GELU_AUX_BIAS", {"bias": bias}, b_layout="KN")
+    y, aux = pf.execute()
+    pb = ep.Plan(dy, w, "DGELU_BGRAD", {"gelu_aux": aux["gelu_aux"]}, b_layout="NK")
+    dx, auxb = pb.execute()
+    torch.cuda.synchronize()
+    x64, w64, b64, dy64 = f64(x), f64(w), f64(bias), f64(dy)
+    yref, pref = oracle.gelu_aux_bias(x64, w64, b64, "KN")
+    assert_half(f64(y), yref, "square gelu fwd Y")
+    assert_half(f64(aux["gelu_aux"]), pref, "square gelu fwd pre-activation")
+    dxref, bgref = oracle.dgelu_bgrad(dy64, w64, "NK", f64(aux["gelu_aux"]))
+    assert_half(f64(dx), dxref, "square gelu bwd dX")
+    assert_bgrad(auxb["dgelu_bgrad"].cpu().numpy(), bgref, "square gelu bwd bgrad")
+    # a zero pre-activation: gelu'(0) = 1/2, so bgrad is half the all-ones closed form
+    zeros = torch.zeros_like(aux["gelu_aux"])
+    p0 = ep.Plan(dy, w, "DGELU_BGRAD", {"gelu_aux": zeros}, b_layout="NK")
+    _, aux0 = p0.execute()
+    torch.cuda.synchronize()
+    cf = 0.5 * oracle.bgrad_all_ones_closed_form(dy64, w64, "NK")
+    assert_bgrad(aux0["dgelu_bgrad"].cpu().numpy(), cf, "square gelu bwd, zero pre-activation closed form")
+    for p in (pf, pb, p0):
+        p.free()

@@ -15,7 +15,8 @@ from tests._gpu import assert_bgrad, assert_half, assert_mask, f64, require_gpu,
 
 pytestmark = pytest.mark.gpu
 
-EPIS = ["DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "DRELU_BGRAD", "SWIGLU", "DSWIGLU"]
+EPIS = ["DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "DRELU_BGRAD", "SWIGLU", "DSWIGLU",
+        "GELU_BIAS", "GELU_AUX_BIAS", "DGELU_BGRAD"]
 SHAPES = [(300, 200, 136), (37, 8, 8), (130, 264, 520), (1, 64, 72)]
 DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
 SENT16 = -1  # 0xFFFF, a NaN pattern in both half types
@@ -38,8 +39,10 @@ def make_inputs(epi, dt, layout, m, n, k, seed, dev):
     x = rn(m, k)
     b = rn(k, n, scale=k ** -0.5) if layout == "KN" else rn(n, k, scale=k ** -0.5)
     ins = {"a": x, "b": b}
-    if epi in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS"):
+    if epi in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS", "GELU_AUX_BIAS"):
         ins["bias"] = rn(n, scale=0.5)
+    if epi == "DGELU_BGRAD":
+        ins["gaux"] = rn(m, n, scale=1.5)  # a saved pre-activation
     if epi == "DRELU_BGRAD":
         p = torch.randn(m, n, generator=g).numpy()
         ins["mask"] = torch.from_numpy(oracle.pack_relu_mask(p > 0).view(np.int32).copy())
@@ -60,8 +63,15 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
     obuf, out = padded(m, n, dt, dev)
     aux_out, epi_in = {}, {}
     nw = (n + 31) // 32
-    if epi in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS"):
+    if epi in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS", "GELU_AUX_BIAS"):
         epi_in["bias"] = ins["bias"]
+    if epi == "GELU_AUX_BIAS":
+        gabuf, gaview = padded(m, n, dt, dev)
+        aux_out["gelu_aux"] = gaview
+    if epi == "DGELU_BGRAD":
+        epi_in["gelu_aux"] = ins["gaux"]
+        gbuf = torch.full((n + 4,), float("nan"), dtype=torch.float32, device=dev)
+        aux_out["dgelu_bgrad"] = gbuf[:n]
     if epi == "RELU_AUX_BIAS":
         abuf = torch.full((m + 1, nw + 1), SENT32, dtype=torch.int32, device=dev)
         aux_out["relu_aux"] = abuf[:m, :nw]
@@ -119,6 +129,18 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
         assert_half(f64(aux_out["d_up"]), du, what)
         ub = ubuf.view(torch.int16).cpu().numpy()
         assert np.all(ub[m, :] == -1) and np.all(ub[:, n:] == -1), f"{what}: d_up padding written"
+    elif epi in ("GELU_BIAS", "GELU_AUX_BIAS"):
+        y, pre = oracle.gelu_aux_bias(a64, b64, f64(ins["bias"]), layout)
+        assert_half(f64(out), y, what)
+        if epi == "GELU_AUX_BIAS":
+            assert_half(f64(aux_out["gelu_aux"]), pre, what)
+            gb = gabuf.view(torch.int16).cpu().numpy()
+            assert np.all(gb[m, :] == -1) and np.all(gb[:, n:] == -1), f"{what}: gelu_aux padding written"
+    elif epi == "DGELU_BGRAD":
+        dx, bg = oracle.dgelu_bgrad(a64, b64, layout, f64(ins["gaux"]))
+        assert_half(f64(out), dx, what)
+        assert_bgrad(aux_out["dgelu_bgrad"].cpu().numpy(), bg, what)
+        assert torch.isnan(gbuf[n:]).all(), f"{what}: bgrad padding written"
     ob = obuf.view(torch.int16).cpu().numpy()
     assert np.all(ob[m, :] == -1) and np.all(ob[:, n:] == -1), f"{what}: output padding written"
     p.free()
