@@ -42,7 +42,7 @@ class ep_shape(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("b_layout", ctypes.c_int), ("a", ctypes.c_void_p), ("lda", ctypes.c_int64),
                 ("b", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("d", ctypes.c_void_p),
-                ("ldd", ctypes.c_int64)]
+                ("ldd", ctypes.c_int64), ("a_layout", ctypes.c_int)]
 
 
 class ep_epilog_io(ctypes.Structure):
@@ -131,7 +131,8 @@ def _stream_handle(stream):
 class Plan:
     """A planned fused GEMM + epilog (the C library's ep_handle).
 
-    a: M x K.  b: K x N (b_layout "KN") or N x K ("NK").  epilog_inputs:
+    a: M x K (a_layout "MK"), or K x M ("KM": the GEMM uses a's transpose; DEFAULT epilog only,
+    as in a weight gradient X^T dY).  b: K x N (b_layout "KN") or N x K ("NK").  epilog_inputs:
       BIAS / RELU_BIAS / RELU_AUX_BIAS: {"bias": (N,)}
       DRELU_BGRAD: {"relu_aux": (M, >= ceil(N/32)) int32 mask words}
       SWIGLU: {"b2": up weight, same layout as b}
@@ -148,7 +149,8 @@ class Plan:
     """
 
     def __init__(self, a, b, epilog="DEFAULT", epilog_inputs=None, b_layout="KN", out=None,
-                 aux_out=None, path="fused", bgrad_mode="two_pass", tile_cfg=-1, split_k=0, autotune=False):
+                 aux_out=None, path="fused", bgrad_mode="two_pass", tile_cfg=-1, split_k=0, autotune=False,
+                 a_layout="MK"):
         L = lib()
         epilog_inputs = dict(epilog_inputs or {})
         aux_out = dict(aux_out or {})
@@ -156,7 +158,9 @@ class Plan:
             raise ValueError(f"unknown epilog {epilog!r}")
         if a.dtype not in _DTYPES or b.dtype != a.dtype:
             raise ValueError("a and b must both be float16 or both bfloat16")
-        m, k = a.shape
+        if a_layout not in ("MK", "KM"):
+            raise ValueError(f"unknown a_layout {a_layout!r}")
+        m, k = a.shape if a_layout == "MK" else (a.shape[1], a.shape[0])
         n = b.shape[1] if b_layout == "KN" else b.shape[0]
         if out is None:
             out = torch.empty((m, n), dtype=a.dtype, device=a.device)
@@ -209,7 +213,7 @@ class Plan:
             io.d2, io.ldd2 = _ptr(d2), d2.stride(0)
             self.aux["d_up"] = d2
         shape = ep_shape(m=m, n=n, k=k, b_layout=_LAYOUTS[b_layout], a=_ptr(a), lda=_ld(a),
-                         b=_ptr(b), ldb=_ld(b), d=_ptr(out), ldd=_ld(out))
+                         b=_ptr(b), ldb=_ld(b), d=_ptr(out), ldd=_ld(out), a_layout=0 if a_layout == "MK" else 1)
         opt = ep_options(path=_PATHS[path], bgrad_mode=_BGRAD[bgrad_mode], tile_cfg=tile_cfg, split_k=split_k,
                          autotune=int(bool(autotune)))
         handle = ctypes.c_void_p()

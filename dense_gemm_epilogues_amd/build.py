@@ -43,9 +43,10 @@ def build(verbose=False, jobs=None):
     os.makedirs(BUILD, exist_ok=True)
     tasks = []
     inst = os.path.join(CSRC, "gemm_inst.hip")
+    # layouts 0/1: A M x K with B K x N / N x K, every epilog; 2/3: A given K x M, DEFAULT only
     for dt in (0, 1):
-        for lay in (0, 1):
-            for epi in range(N_EPI):
+        for lay in (0, 1, 2, 3):
+            for epi in (range(N_EPI) if lay < 2 else (0,)):
                 obj = os.path.join(BUILD, f"gemm_{dt}_{lay}_{epi}.o")
                 tasks.append((inst, obj, [f"-DEP_DT={dt}", f"-DEP_LAY={lay}", f"-DEP_EPI={epi}"]))
     tasks.append((os.path.join(CSRC, "elementwise.hip"), os.path.join(BUILD, "elementwise.o"), []))

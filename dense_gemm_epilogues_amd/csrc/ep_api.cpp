@@ -29,6 +29,9 @@ EP_DECL_EPIS(0, 0)
 EP_DECL_EPIS(0, 1)
 EP_DECL_EPIS(1, 0)
 EP_DECL_EPIS(1, 1)
+// K x M A (layouts 2 and 3): DEFAULT only
+EP_DECL_TABLE(0, 2, 0) EP_DECL_TABLE(0, 3, 0) EP_DECL_TABLE(1, 2, 0) EP_DECL_TABLE(1, 3, 0)
+static const GemmLauncher* const kTablesAKM[2][2] = {{kLaunch_0_2_0, kLaunch_0_3_0}, {kLaunch_1_2_0, kLaunch_1_3_0}};
 
 #define EP_ROW(dt, lay)                                                                          \
   {                                                                                              \
@@ -44,6 +47,12 @@ static const GemmLauncher* const kTables[2][2][E_NUM] = {{EP_ROW(0, 0), EP_ROW(0
   extern const GemmLauncher kPartial_##dt##_##lay##_0[kNumTileCfgs]; \
   extern const GemmLauncher kPartial_##dt##_##lay##_5[kNumTileCfgs];
 EP_DECL_P(0, 0) EP_DECL_P(0, 1) EP_DECL_P(1, 0) EP_DECL_P(1, 1)
+extern const GemmLauncher kPartial_0_2_0[kNumTileCfgs];
+extern const GemmLauncher kPartial_0_3_0[kNumTileCfgs];
+extern const GemmLauncher kPartial_1_2_0[kNumTileCfgs];
+extern const GemmLauncher kPartial_1_3_0[kNumTileCfgs];
+static const GemmLauncher* const kPartialAKM[2][2] = {{kPartial_0_2_0, kPartial_0_3_0},
+                                                      {kPartial_1_2_0, kPartial_1_3_0}};
 #define EP_DECL_F(dt) EP_DECL_TABLE_F(dt, 0) EP_DECL_TABLE_F(dt, 1) EP_DECL_TABLE_F(dt, 2) \
   EP_DECL_TABLE_F(dt, 3) EP_DECL_TABLE_F(dt, 4) EP_DECL_TABLE_F(dt, 5) EP_DECL_TABLE_F(dt, 6) \
   EP_DECL_TABLE_F(dt, 7) EP_DECL_TABLE_F(dt, 8) EP_DECL_TABLE_F(dt, 9)
@@ -60,7 +69,8 @@ static const GemmLauncher* const kFixupTables[2][E_NUM] = {
      kFixup_1_9}};
 
 GemmLauncher gemm_partial_launcher(int dtype, int layout, bool dual, int cfg) {
-  if (dtype < 0 || dtype > 1 || layout < 0 || layout > 1 || cfg < 0 || cfg >= kNumTileCfgs) return nullptr;
+  if (dtype < 0 || dtype > 1 || layout < 0 || layout > 3 || cfg < 0 || cfg >= kNumTileCfgs) return nullptr;
+  if (layout >= 2) return dual ? nullptr : kPartialAKM[dtype][layout - 2][cfg];
   return kPartialTables[dtype][layout][dual ? 1 : 0][cfg];
 }
 
@@ -70,9 +80,10 @@ GemmLauncher gemm_fixup_launcher(int dtype, int epi, int cfg) {
 }
 
 GemmLauncher gemm_launcher(int dtype, int layout, int epi, int cfg) {
-  if (dtype < 0 || dtype > 1 || layout < 0 || layout > 1 || epi < 0 || epi >= E_NUM || cfg < 0 ||
+  if (dtype < 0 || dtype > 1 || layout < 0 || layout > 3 || epi < 0 || epi >= E_NUM || cfg < 0 ||
       cfg >= kNumTileCfgs)
     return nullptr;
+  if (layout >= 2) return epi == E_DEFAULT ? kTablesAKM[dtype][layout - 2][cfg] : nullptr;
   return kTables[dtype][layout][epi][cfg];
 }
 
@@ -195,10 +206,15 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   if ((int)epi < 0 || (int)epi >= E_NUM) return fail(EP_ERR_UNSUPPORTED, "unknown epilog %d", (int)epi);
   if (s->b_layout != EP_B_KN && s->b_layout != EP_B_NK)
     return fail(EP_ERR_UNSUPPORTED, "unknown B layout %d", (int)s->b_layout);
+  if (s->a_layout != EP_A_MK && s->a_layout != EP_A_KM)
+    return fail(EP_ERR_UNSUPPORTED, "unknown A layout %d", (int)s->a_layout);
+  if (s->a_layout == EP_A_KM && epi != EP_EPILOG_DEFAULT)
+    return fail(EP_ERR_UNSUPPORTED, "a K x M A operand is supported with the DEFAULT epilog only");
   if (s->m < 1 || s->n < 1 || s->k < 1) return fail(EP_ERR_INVALID_ARG, "m, n, k must be >= 1");
   if (s->m >= kMaxDim || s->n >= kMaxDim || s->k >= kMaxDim)
     return fail(EP_ERR_UNSUPPORTED, "m, n, k must be < 2^31");
   if (s->n % 8 || s->k % 8) return fail(EP_ERR_UNSUPPORTED, "n and k must be multiples of 8");
+  if (s->a_layout == EP_A_KM && s->m % 8) return fail(EP_ERR_UNSUPPORTED, "a K x M A needs m % 8 == 0");
   if (opt) {
     if (opt->path != EP_PATH_FUSED && opt->path != EP_PATH_UNFUSED)
       return fail(EP_ERR_INVALID_ARG, "unknown path %d", (int)opt->path);
@@ -220,8 +236,9 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   if (!aligned(s->a, 16) || !aligned(s->b, 16) || !aligned(s->d, 16))
     return fail(EP_ERR_INVALID_ARG, "a, b and d must be 16-byte aligned");
   const int64_t brow = s->b_layout == EP_B_KN ? s->n : s->k;
-  if (s->lda < s->k || s->lda % 8 || s->lda >= kMaxLd)
-    return fail(EP_ERR_INVALID_ARG, "lda must be a multiple of 8 in [k, 2^22)");
+  const int64_t arow = s->a_layout == EP_A_KM ? s->m : s->k;
+  if (s->lda < arow || s->lda % 8 || s->lda >= kMaxLd)
+    return fail(EP_ERR_INVALID_ARG, "lda must be a multiple of 8 in [row length, 2^22)");
   if (s->ldb < brow || s->ldb % 8 || s->ldb >= kMaxLd)
     return fail(EP_ERR_INVALID_ARG, "ldb must be a multiple of 8 in [row length, 2^22)");
   if (s->ldd < s->n || s->ldd % 8 || s->ldd >= kMaxLd)
@@ -322,8 +339,8 @@ std::map<TuneKey, std::pair<int, int>> g_tune_cache;
 
 ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io, ep_options& opt,
                    int dev) {
-  const TuneKey key{s->m, s->n, s->k, s->lda, s->ldb, s->ldd, (int)s->b_layout, (int)dtype, (int)epi,
-                    (int)opt.bgrad_mode, dev};
+  const TuneKey key{s->m, s->n, s->k, s->lda, s->ldb, s->ldd, (int)s->b_layout + 2 * (int)s->a_layout,
+                    (int)dtype, (int)epi, (int)opt.bgrad_mode, dev};
   {
     std::lock_guard<std::mutex> lk(g_tune_mu);
     auto it = g_tune_cache.find(key);
@@ -457,7 +474,8 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
 
   GemmArgs a = base_args(s, cfg, kernel_dual);
   const int fused_epi = unfused ? (int)E_DEFAULT : (int)epi;
-  h->launch = gemm_launcher((int)dtype, (int)s->b_layout, fused_epi, cfg);
+  const int klay = (int)s->b_layout + (s->a_layout == EP_A_KM ? 2 : 0);  // kernel layout index
+  h->launch = gemm_launcher((int)dtype, klay, fused_epi, cfg);
   if (!h->launch) {
     delete h;
     return fail(EP_ERR_INTERNAL, "no kernel instantiated for this combination");
@@ -478,7 +496,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   h->splits = splits;
   a.splits = splits;
   if (splits > 1) {
-    h->launch_partial = gemm_partial_launcher((int)dtype, (int)s->b_layout, kernel_dual, cfg);
+    h->launch_partial = gemm_partial_launcher((int)dtype, klay, kernel_dual, cfg);
     h->launch_fixup = gemm_fixup_launcher((int)dtype, (int)epi, cfg);
     if (!h->launch_partial || !h->launch_fixup) {
       delete h;
@@ -672,7 +690,8 @@ ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
   if (!buf || n == 0) return fail(EP_ERR_INVALID_ARG, "buffer is NULL or empty");
   const ep_shape& s = h->shape;
   const char* dt = h->dtype == EP_F16 ? "f16" : "bf16";
-  const char* lay = s.b_layout == EP_B_KN ? "KN" : "NK";
+  const char* lay = s.a_layout == EP_A_KM ? (s.b_layout == EP_B_KN ? "A^T,KN" : "A^T,NK")
+                                          : (s.b_layout == EP_B_KN ? "KN" : "NK");
   std::string kern = std::string("gemm_kernel<") + dt + "," + lay + "," +
                      (h->opt.path == EP_PATH_FUSED ? kEpiNames[h->epilog] : "DEFAULT") + "," +
                      kTileCfgs[h->cfg].name + ">";

@@ -225,6 +225,11 @@ template <int DT, int LAY, int EPI, int CFG, int MODE>
 __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p) {
   using E = Elem<DT>;
   using TR = GemmTraits<DT, LAY, EPI, CFG>;
+  // LAY: bit 0 = B layout (L_KN / L_NK); LAY >= 2: A is given K x M (M contiguous) and the
+  // GEMM uses its transpose, staged like a K x N B operand
+  constexpr int BLAY = LAY & 1;
+  constexpr bool AKM = LAY >= 2;
+  static_assert(!AKM || EPI == E_DEFAULT, "a K x M A operand is instantiated for DEFAULT only");
   constexpr bool DUAL = TR::DUAL;
   constexpr int BM = TR::BM, BNT = TR::BNT, BK = TR::BK, NST = TR::NST;
   constexpr int MB = TR::MB, NB = TR::NB, WTM = TR::WTM, WTB = TR::WTB, WTN = TR::WTN;
@@ -271,12 +276,23 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(Ag + (int64_t)m0 * p.lda * 2, (int64_t)(M - m0) * p.lda * 2);
   uint32_t a_voff[A_SLOTS];
   int a_klim[A_SLOTS];  // the k-step offset k0 is valid for this lane iff k0 < klim
+  // K x M A: BM/128 sub-tiles of [BK k][128 m]; each wave's slots lie in one sub-tile
+  const int wa_mbase = ((wave * A_SLOTS) / TR::KN_SPS) * 128;
 #pragma unroll
   for (int q = 0; q < A_SLOTS; ++q) {
-    const int row = (wave * A_SLOTS + q) * RPS + lane / CPR;
-    const int c = (lane % CPR) ^ swf<CPR>(row);
-    a_voff[q] = (uint32_t)(row * p.lda * 2) + c * 16;
-    a_klim[q] = K - c * 8;
+    if constexpr (AKM) {
+      const int t = (wave * A_SLOTS + q) % TR::KN_SPS;
+      const int k = 4 * t + (lane >> 4);
+      const int pch = lane & 15;
+      const int ml = (((pch >> 2) ^ (k & 3)) << 5) + ((pch & 3) << 3);
+      a_voff[q] = (m0 + wa_mbase + ml < M) ? (uint32_t)(k * p.lda * 2) + ml * 2 : kOOB;
+      a_klim[q] = 0;
+    } else {
+      const int row = (wave * A_SLOTS + q) * RPS + lane / CPR;
+      const int c = (lane % CPR) ^ swf<CPR>(row);
+      a_voff[q] = (uint32_t)(row * p.lda * 2) + c * 16;
+      a_klim[q] = K - c * 8;
+    }
   }
   // Each wave's B slots come from a single source: for N x K the wave loads BNT/4 rows
   // (DUAL: waves 0-1 the gate rows, waves 2-3 the up rows); for K x N the wave's slots lie in
@@ -285,7 +301,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   const bool w_second = DUAL && wave >= 2;
   const int w_sub = (wave * B_SLOTS) / TR::KN_SPS;  // K x N sub-tile of this wave
   const int w_cbase = DUAL ? 0 : w_sub * 128;
-  const char* w_bsrc = (DUAL && (LAY == L_NK ? w_second : w_sub == 1)) ? B2g : Bg;
+  const char* w_bsrc = (DUAL && (BLAY == L_NK ? w_second : w_sub == 1)) ? B2g : Bg;
   const __amdgpu_buffer_rsrc_t rB_nk =
       make_rsrc(w_bsrc + (int64_t)n0 * p.ldb * 2, (int64_t)(N - n0) * p.ldb * 2);
   uint32_t b_voff[B_SLOTS];
@@ -293,7 +309,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 #pragma unroll
   for (int q = 0; q < B_SLOTS; ++q) {
     const int s = wave * B_SLOTS + q;
-    if constexpr (LAY == L_NK) {
+    if constexpr (BLAY == L_NK) {
       const int row = s * RPS + lane / CPR;
       const int c = (lane % CPR) ^ swf<CPR>(row);
       const int srow = DUAL ? (row % (BNT / 2)) : row;
@@ -314,15 +330,24 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // K x N: base and clamped extent of this wave's sub-tile for the k-step being loaded
   // (descriptor values are not passed between functions: the host pass cannot take them)
   struct KnSrc {
-    const char* base;
+    const char* base;   // K x N B: this wave's sub-tile for the k-step
     uint32_t num;
+    const char* abase;  // K x M A: the same for A
+    uint32_t anum;
   };
   auto kn_rsrc = [&](int kt) {
     const int k0 = gkt(kt) * BK;
-    const int64_t bytes = ((int64_t)(K - k0) * p.ldb - (n0 + w_cbase)) * 2;
     KnSrc s;
+    const int64_t bytes = ((int64_t)(K - k0) * p.ldb - (n0 + w_cbase)) * 2;
     s.base = w_bsrc + ((int64_t)k0 * p.ldb + n0 + w_cbase) * 2;
     s.num = bytes <= 0 ? 0u : (bytes >= 0x7fffffffLL ? 0x7fffffffu : (uint32_t)bytes);
+    s.abase = Ag;
+    s.anum = 0u;
+    if constexpr (AKM) {
+      const int64_t abytes = ((int64_t)(K - k0) * p.lda - (m0 + wa_mbase)) * 2;
+      s.abase = Ag + ((int64_t)k0 * p.lda + m0 + wa_mbase) * 2;
+      s.anum = abytes <= 0 ? 0u : (abytes >= 0x7fffffffLL ? 0x7fffffffu : (uint32_t)abytes);
+    }
     return s;
   };
 
@@ -332,13 +357,19 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     const int k0 = gkt(kt) * BK;
     if (t < A_SLOTS) {
       const int q = t;
-      const uint32_t off = (k0 < a_klim[q]) ? a_voff[q] + k0 * 2 : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rA, (__attribute__((address_space(3))) void*)(As + (wave * A_SLOTS + q) * 1024), 16, (int)off, 0, 0, 0);
+      if constexpr (AKM) {
+        const __amdgpu_buffer_rsrc_t rka = make_rsrc_raw(kr.abase, kr.anum);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rka, (__attribute__((address_space(3))) void*)(As + (wave * A_SLOTS + q) * 1024), 16, (int)a_voff[q], 0, 0, 0);
+      } else {
+        const uint32_t off = (k0 < a_klim[q]) ? a_voff[q] + k0 * 2 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rA, (__attribute__((address_space(3))) void*)(As + (wave * A_SLOTS + q) * 1024), 16, (int)off, 0, 0, 0);
+      }
     } else {
       const int q = t - A_SLOTS;
       char* Bs = As + TR::A_BYTES;
-      if constexpr (LAY == L_NK) {
+      if constexpr (BLAY == L_NK) {
         const uint32_t off = (k0 < b_klim[q]) ? b_voff[q] + k0 * 2 : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rB_nk, (__attribute__((address_space(3))) void*)(Bs + (wave * B_SLOTS + q) * 1024), 16, (int)off, 0, 0, 0);
@@ -359,11 +390,25 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   const int hlf = lane >> 5;
   uint32_t a_rd[MB], b_rd[NB];
   int a_f[MB], b_f[NB];
+  // transpose-read address of a 32-wide block at column (row) base `base` of a [BK][128]
+  // sub-tile layout: within each 16-lane group g, lane i fetches 4 columns of k-row
+  // kbase + i/4; the hardware hands lane i the 4 k-values of column i
+  auto tr_addr = [&](int base) {
+    const int g = lane >> 4, i = lane & 15;
+    const int u = base >> 7, cb = base & 127;
+    return (uint32_t)(u * TR::KN_SUB + (8 * (g >> 1) + (i >> 2)) * 256 + ((((cb >> 5) ^ (i >> 2)) & 3) << 6) +
+                      32 * (g & 1) + 8 * (i & 3));
+  };
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const int row = wm * WTM + i * 32 + (lane & 31);
-    a_rd[i] = row * ROWB;
-    a_f[i] = swf<CPR>(row);
+    if constexpr (AKM) {
+      a_rd[i] = tr_addr(wm * WTM + i * 32);
+      a_f[i] = 0;
+    } else {
+      const int row = wm * WTM + i * 32 + (lane & 31);
+      a_rd[i] = row * ROWB;
+      a_f[i] = swf<CPR>(row);
+    }
   }
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
@@ -373,17 +418,12 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     } else {
       brow = wn * WTB + j * 32;
     }
-    if constexpr (LAY == L_NK) {
+    if constexpr (BLAY == L_NK) {
       const int row = brow + (lane & 31);
       b_rd[j] = row * ROWB;
       b_f[j] = swf<CPR>(row);
     } else {
-      // transpose reads: within each 16-lane group g, lane i fetches 4 columns of k-row
-      // kbase + i/4; the hardware hands lane i the 4 k-values of column i.
-      const int g = lane >> 4, i = lane & 15;
-      const int u = brow >> 7, cb = brow & 127;
-      b_rd[j] = u * TR::KN_SUB + (8 * (g >> 1) + (i >> 2)) * 256 + ((((cb >> 5) ^ (i >> 2)) & 3) << 6) +
-                32 * (g & 1) + 8 * (i & 3);
+      b_rd[j] = tr_addr(brow);
       b_f[j] = 0;
     }
   }
@@ -400,46 +440,57 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   u32x4 fa[2][MB], fb[2][NB];
   // One read op = one LDS fragment read: A blocks first, then B blocks (K x N: two
   // transpose reads of 4 k-values each per block).
-  constexpr int B_OPS = (LAY == L_NK) ? NB : 2 * NB;
-  constexpr int N_RD = MB + B_OPS;
+  constexpr int A_OPS = AKM ? 2 * MB : MB;
+  constexpr int B_OPS = (BLAY == L_NK) ? NB : 2 * NB;
+  constexpr int N_RD = A_OPS + B_OPS;
+  // Transpose reads are issued as inline asm: the compiler's LDS-DMA alias check would
+  // otherwise make every one wait for all in-flight loads of later stages (which never
+  // alias the stage being read).  Completion is awaited explicitly (lgkm_fence) before use.
+  auto tr_read = [&](uint32_t addr, u32x4& dst, int half) {
+    u32x2 w;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(w) : "v"(addr));
+    dst[2 * half] = w[0];
+    dst[2 * half + 1] = w[1];
+  };
   auto read_op = [&](const char* As, int ks, int r, u32x4* A, u32x4* B) {
-    if (r < MB) {
-      A[r] = *(const u32x4*)(As + a_rd[r] + ((((ks * 2 + hlf) ^ a_f[r]) & (CPR - 1)) << 4));
+    if (r < A_OPS) {
+      if constexpr (AKM) {
+        const int i = r >> 1, half = r & 1;
+        tr_read(lds_addr(As + a_rd[i]) + ks * 4096 + half * 1024, A[i], half);
+      } else {
+        A[r] = *(const u32x4*)(As + a_rd[r] + ((((ks * 2 + hlf) ^ a_f[r]) & (CPR - 1)) << 4));
+      }
       return;
     }
     const char* Bs = As + TR::A_BYTES;
-    if constexpr (LAY == L_NK) {
-      const int j = r - MB;
+    if constexpr (BLAY == L_NK) {
+      const int j = r - A_OPS;
       B[j] = *(const u32x4*)(Bs + b_rd[j] + ((((ks * 2 + hlf) ^ b_f[j]) & (CPR - 1)) << 4));
     } else {
-      // Issued as inline asm: the compiler's LDS-DMA alias check would otherwise make every
-      // transpose read wait for all in-flight loads of later stages (which never alias the
-      // stage being read).  Completion is awaited explicitly (lgkm_fence) before use.
-      const int j = (r - MB) >> 1, half = (r - MB) & 1;
-      const uint32_t addr = lds_addr(Bs + b_rd[j]) + ks * 4096 + half * 1024;
-      u32x2 w;
-      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(w) : "v"(addr));
-      B[j][2 * half] = w[0];
-      B[j][2 * half + 1] = w[1];
+      const int j = (r - A_OPS) >> 1, half = (r - A_OPS) & 1;
+      tr_read(lds_addr(Bs + b_rd[j]) + ks * 4096 + half * 1024, B[j], half);
     }
   };
   auto read_frags = [&](const char* As, int ks, u32x4* A, u32x4* B) {
 #pragma unroll
     for (int r = 0; r < N_RD; ++r) read_op(As, ks, r, A, B);
   };
-  // Wait for every outstanding LDS read and tie the wait to the B fragments, so no MFMA that
-  // consumes them can be scheduled above it.
-  auto lgkm_fence = [&](u32x4* B) {
-    if constexpr (LAY == L_KN) {
-      if constexpr (NB == 4) {
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B[0]), "+v"(B[1]), "+v"(B[2]), "+v"(B[3]));
-      } else if constexpr (NB == 2) {
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B[0]), "+v"(B[1]));
-      } else {
-        static_assert(NB == 1 || NB == 2 || NB == 4, "unsupported NB");
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(B[0]));
-      }
+  // Wait for every outstanding LDS read and tie the wait to the fragments the transpose
+  // reads wrote, so no MFMA that consumes them can be scheduled above it.
+  auto tie4 = [&](u32x4* F, auto n_c) {
+    constexpr int NF = decltype(n_c)::value;
+    static_assert(NF == 1 || NF == 2 || NF == 4, "unsupported fragment count");
+    if constexpr (NF == 4) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F[0]), "+v"(F[1]), "+v"(F[2]), "+v"(F[3]));
+    } else if constexpr (NF == 2) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F[0]), "+v"(F[1]));
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F[0]));
     }
+  };
+  auto lgkm_fence = [&](u32x4* A, u32x4* B) {
+    if constexpr (AKM) tie4(A, std::integral_constant<int, MB>{});
+    if constexpr (BLAY == L_KN) tie4(B, std::integral_constant<int, NB>{});
   };
   // The instruction order inside a k-step is fixed explicitly: every sched_barrier below
   // stops the scheduler from moving instructions across it.  Each MFMA is followed by its
@@ -511,7 +562,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     for (int ks = 0; ks < KS - 1; ++ks) {
       u32x4* A = fa[ks & 1];
       u32x4* B = fb[ks & 1];
-      lgkm_fence(B);
+      lgkm_fence(A, B);
       __builtin_amdgcn_sched_barrier(0);
       if (ks == 0)
         slice(T_{}, std::integral_constant<int, 0>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, fa[1], fb[1]);
@@ -522,7 +573,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     }
     constexpr int L = (KS - 1) & 1;  // buffer of the last slice
     using GL = std::integral_constant<int, (KS - 1) * NMMA>;
-    lgkm_fence(fb[L]);
+    lgkm_fence(fa[L], fb[L]);
     __builtin_amdgcn_sched_barrier(0);
     slice(F_{}, GL{}, fa[L], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[0], fb[0]);
     ring_barrier(std::integral_constant<int, VMC_LOOP>{});
@@ -540,7 +591,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   }
   // loads issued past the last k-step (they read as zeros) must land before LDS is reused
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  lgkm_fence(fb[0]);
+  lgkm_fence(fa[0], fb[0]);
   __syncthreads();
 
   // ---------------------------------------------------------------- split-K

@@ -53,6 +53,12 @@ typedef enum { EP_F16 = 0, EP_BF16 = 1 } ep_dtype;
 
 typedef enum { EP_B_KN = 0, EP_B_NK = 1 } ep_b_layout;
 
+/* EP_A_MK (default): A is row-major M x K.  EP_A_KM: A is given row-major K x M (M
+ * contiguous, row stride lda >= m) and the GEMM uses its transpose, as the weight gradient
+ * of a linear layer needs (dW = X^T dY contracts over the batch).  EP_A_KM requires m % 8 == 0
+ * and the DEFAULT epilog. */
+typedef enum { EP_A_MK = 0, EP_A_KM = 1 } ep_a_layout;
+
 /*
  * Epilogs.  Each is applied to the float32 accumulator tile inside the GEMM kernel before
  * the single store to HBM.
@@ -110,12 +116,13 @@ typedef enum {
 typedef struct {
   int64_t m, n, k;        /* 1 <= m, n, k < 2^31; n and k multiples of 8 */
   ep_b_layout b_layout;
-  const void* a;          /* M x K, lda >= k */
+  const void* a;          /* M x K, lda >= k (EP_A_KM: K x M, lda >= m) */
   int64_t lda;
   const void* b;          /* K x N (ldb >= n) or N x K (ldb >= k) */
   int64_t ldb;
   void* d;                /* M x N output, ldd >= n */
   int64_t ldd;
+  ep_a_layout a_layout;   /* EP_A_MK (0) unless the transpose of a K x M A is wanted */
 } ep_shape;
 
 /* Epilog inputs and auxiliary outputs (the epilog_inputs dictionary and the aux dictionary

@@ -58,9 +58,10 @@ def test_free_null_and_execute_null(L):
     assert L.ep_plan_info(None, buf, 64) == INVALID
 
 
-def shape(m=64, n=64, k=64, lay=KN, a=A_PTR, b=B_PTR, d=D_PTR, lda=None, ldb=None, ldd=None):
-    return ep_shape(m=m, n=n, k=k, b_layout=lay, a=a, lda=k if lda is None else lda, b=b,
-                    ldb=(n if lay == KN else k) if ldb is None else ldb, d=d, ldd=n if ldd is None else ldd)
+def shape(m=64, n=64, k=64, lay=KN, a=A_PTR, b=B_PTR, d=D_PTR, lda=None, ldb=None, ldd=None, alay=0):
+    return ep_shape(m=m, n=n, k=k, b_layout=lay, a=a, lda=(m if alay else k) if lda is None else lda, b=b,
+                    ldb=(n if lay == KN else k) if ldb is None else ldb, d=d, ldd=n if ldd is None else ldd,
+                    a_layout=alay)
 
 
 def plan(L, s, epi=E["DEFAULT"], io=None, dtype=F16, opt=None, out=True):
@@ -121,6 +122,11 @@ CASES = [
     ("split_k above 4", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=5))[0], INVALID),
     ("unfused with split_k", lambda L: plan(L, shape(), opt=ep_options(path=1, bgrad_mode=0, tile_cfg=-1, split_k=2))[0],
      UNSUPPORTED),
+    ("unknown A layout", lambda L: plan(L, shape(alay=2))[0], UNSUPPORTED),
+    ("K x M A with a non-DEFAULT epilog", lambda L: plan(L, shape(alay=1), E["BIAS"], ep_epilog_io(bias=X_PTR))[0],
+     UNSUPPORTED),
+    ("K x M A with m not a multiple of 8", lambda L: plan(L, shape(m=60, alay=1, lda=64))[0], UNSUPPORTED),
+    ("K x M A with lda < m", lambda L: plan(L, shape(m=128, alay=1, lda=64))[0], INVALID),
     ("GELU_BIAS without bias", lambda L: plan(L, shape(), E["GELU_BIAS"])[0], INVALID),
     ("GELU_AUX_BIAS without gelu_aux", lambda L: plan(L, shape(), E["GELU_AUX_BIAS"], ep_epilog_io(bias=X_PTR))[0], INVALID),
     ("GELU_BIAS with a stray gelu_aux", lambda L: plan(L, shape(), E["GELU_BIAS"],

@@ -237,3 +237,67 @@ def test_square_gelu_layer_full():
     assert_bgrad(aux0["dgelu_bgrad"].cpu().numpy(), cf, "square gelu bwd, zero pre-activation closed form")
     for p in (pf, pb, p0):
         p.free()
+
+
+# ------------------------------------------------------------------ SwiGLU-MLP training step
+def test_swiglu_mlp_training_step_all_gradients():
+    """The whole SwiGLU MLP forward and backward with this library only, M 2048:
+      forward  [g | u] = x W_gu^T (DEFAULT, W_gu = [Wg; Wu]), h = SWIGLU(x; Wg, Wu), out = h Wd^T;
+      backward [d_gate | d_up] = DSWIGLU(dout, Wd; g, u) into one M x 2I buffer,
+               dx = [d_gate | d_up] . W_gu  (one GEMM over the concatenated K = 2I),
+               [dWg; dWu] = [d_gate | d_up]^T . x and dWd = dout^T . h (transposed-A GEMMs).
+    Every step is compared with the oracle applied to the same inputs the GPU step consumed
+    (the previous GPU step's output), so each kernel is checked on its own."""
+    require_gpu()
+    ep = _ep()
+    dev = torch.device("cuda")
+    c = W.SWIGLU[4]
+    m, hd, idim = c.m, c.h, c.i
+    say("case SwiGLU-MLP training step bf16 M2048 H5120 I17408: all four gradients")
+    inp = W.swiglu_inputs(c, device=dev)
+    x, wg, wu, wd = inp["x"], inp["wg"], inp["wu"], inp["wd"]
+    w_gu = torch.cat([wg, wu], dim=0).contiguous()                     # 2I x H
+    dout = W.randn((m, hd), W.seed_of(c.cfg, 6), 1.0, torch.bfloat16, dev)
+    plans = []
+
+    def run(*args, **kw):
+        p = ep.Plan(*args, **kw)
+        plans.append(p)  # kept until the device is synchronised
+        return p.execute()[0]
+
+    # forward
+    gu = run(x, w_gu, "DEFAULT", b_layout="NK")                          # M x 2I = [g | u]
+    h = run(x, w_gu[:idim], "SWIGLU", {"b2": w_gu[idim:]}, b_layout="NK")
+    out = run(h, wd, "DEFAULT", b_layout="NK")
+    # backward
+    dgu = torch.empty((m, 2 * idim), dtype=torch.bfloat16, device=dev)
+    run(dout, wd, "DSWIGLU", {"gate": gu[:, :idim], "up": gu[:, idim:]}, b_layout="KN",
+        out=dgu[:, :idim], aux_out={"d_up": dgu[:, idim:]})
+    dx = run(dgu, w_gu, "DEFAULT", b_layout="KN")                        # M x H, K = 2I
+    dw_gu = run(dgu, x, "DEFAULT", b_layout="KN", a_layout="KM")         # 2I x H
+    dwd = run(dout, h, "DEFAULT", b_layout="KN", a_layout="KM")          # H x I
+    torch.cuda.synchronize()
+
+    x64, wg64, wu64, wd64, dout64 = f64(x), f64(wg), f64(wu), f64(wd), f64(dout)
+    # forward pieces
+    rows = slice(0, 512)  # the oracle's full-width products on a row block (the kernels tile rows identically)
+    assert_half(f64(gu[rows, :idim]), oracle.matmul(x64[rows], wg64, "NK"), "g")
+    assert_half(f64(gu[rows, idim:]), oracle.matmul(x64[rows], wu64, "NK"), "u")
+    href, _, _ = oracle.swiglu(x64[rows], wg64, wu64)
+    assert_half(f64(h[rows]), href, "h")
+    h64 = f64(h)
+    assert_half(f64(out[rows]), oracle.matmul(h64[rows], wd64, "NK"), "out")
+    # backward pieces, each on the GPU's own inputs
+    gu64 = f64(gu)
+    dg_ref, du_ref, _ = oracle.dswiglu(dout64[rows], wd64, gu64[rows, :idim], gu64[rows, idim:])
+    assert_half(f64(dgu[rows, :idim]), dg_ref, "d_gate")
+    assert_half(f64(dgu[rows, idim:]), du_ref, "d_up")
+    dgu64 = f64(dgu)
+    w_gu64 = f64(w_gu)
+    assert_half(f64(dx[rows]), oracle.matmul(dgu64[rows], w_gu64, "KN"), "dx = d_gate Wg + d_up Wu")
+    # weight gradients: full contraction over the batch, checked on column blocks
+    cols = slice(0, 640)
+    assert_half(f64(dw_gu[:, cols]), dgu64.T @ x64[:, cols], "[dWg; dWu] = [d_gate | d_up]^T x")
+    assert_half(f64(dwd[:, :640]), dout64.T @ h64[:, :640], "dWd = dout^T h")
+    for p in plans:
+        p.free()

@@ -195,6 +195,35 @@ def test_autotune(epi):
         run_and_check(epi, "bf16", layout, 300, 200, 520, -1, autotune=True, seed=1)
 
 
+@pytest.mark.parametrize("layout", ["KN", "NK"])
+@pytest.mark.parametrize("dtname", ["f16", "bf16"])
+def test_transposed_a(dtname, layout):
+    """A given K x M (the GEMM uses its transpose, as a weight gradient X^T dY does), DEFAULT
+    epilog: every tile configuration, unsplit and split, with ragged M, N and K tails."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev = torch.device("cuda")
+    dt = DTYPES[dtname]
+    for (m, n, k) in [(296, 200, 136), (40, 8, 8), (136, 264, 520), (8, 64, 72)]:
+        g = torch.Generator().manual_seed(m + n + k)
+        at = (torch.randn(k, m, generator=g)).to(dt).to(dev)          # K x M
+        b = (torch.randn(k, n, generator=g) * k ** -0.5).to(dt) if layout == "KN" else \
+            (torch.randn(n, k, generator=g) * k ** -0.5).to(dt)
+        b = b.to(dev)
+        ref = oracle.matmul(f64(at).T, f64(b), layout)
+        for cfg in range(NUM_TILE_CFGS):
+            for split in (1, 2):
+                obuf, out = padded(m, n, dt, dev)
+                say(f"case A^T dt={dtname} layout={layout} m={m} n={n} k={k} cfg={cfg} split={split}")
+                p = ep.Plan(at, b, "DEFAULT", b_layout=layout, out=out, tile_cfg=cfg, split_k=split, a_layout="KM")
+                p.execute()
+                torch.cuda.synchronize()
+                assert_half(f64(out), ref, f"A^T {dtname}/{layout}/{m}x{n}x{k}/cfg{cfg}/split{split}")
+                ob = obuf.view(torch.int16).cpu().numpy()
+                assert np.all(ob[m, :] == -1) and np.all(ob[:, n:] == -1), "output padding written"
+                p.free()
+
+
 def test_split_k_atomic_bgrad():
     require_gpu()
     run_and_check("DRELU_BGRAD", "f16", "NK", 300, 200, 520, 0, split_k=3, bgrad_mode="atomic")
