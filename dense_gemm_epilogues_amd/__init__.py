@@ -28,7 +28,7 @@ library_path = os.path.join(_HERE, "libep.so")
 EPILOGS = {
     "DEFAULT": 0, "BIAS": 1, "RELU_BIAS": 2, "RELU_AUX_BIAS": 3,
     "DRELU_BGRAD": 4, "SWIGLU": 5, "DSWIGLU": 6,
-    "GELU_BIAS": 7, "GELU_AUX_BIAS": 8, "DGELU_BGRAD": 9,
+    "GELU_BIAS": 7, "GELU_AUX_BIAS": 8, "DGELU_BGRAD": 9, "SWIGLU_AUX": 10,
 }
 _LAYOUTS = {"KN": 0, "NK": 1}
 _DTYPES = {torch.float16: 0, torch.bfloat16: 1}
@@ -135,11 +135,12 @@ class Plan:
     as in a weight gradient X^T dY).  b: K x N (b_layout "KN") or N x K ("NK").  epilog_inputs:
       BIAS / RELU_BIAS / RELU_AUX_BIAS: {"bias": (N,)}
       DRELU_BGRAD: {"relu_aux": (M, >= ceil(N/32)) int32 mask words}
-      SWIGLU: {"b2": up weight, same layout as b}
+      SWIGLU / SWIGLU_AUX: {"b2": up weight, same layout as b}; SWIGLU_AUX also returns "gu", the
+        (M, 2N) pre-activations [gate | up] that DSWIGLU can take as its gate and up
       DSWIGLU: {"gate": (M, N), "up": (M, N)}
       GELU_BIAS / GELU_AUX_BIAS: {"bias": (N,)}
       DGELU_BGRAD: {"gelu_aux": (M, N) pre-activation saved by GELU_AUX_BIAS}
-    aux outputs (execute()'s second value): relu_aux, drelu_bgrad, d_up, gelu_aux, dgelu_bgrad.
+    aux outputs (execute()'s second value): relu_aux, drelu_bgrad, d_up, gelu_aux, dgelu_bgrad, gu.
     Outputs are allocated here with torch.empty unless `out` / `aux_out` are given and are
     reused by every execute().  Tensors are kept alive for the plan's lifetime.
     path "fused" | "unfused"; bgrad_mode "two_pass" | "atomic"; tile_cfg -1 (by shape) or an
@@ -200,8 +201,14 @@ class Plan:
                 bg = torch.empty((n,), dtype=torch.float32, device=a.device)
             io.bgrad = _ptr(bg)
             self.aux["drelu_bgrad"] = bg
-        if epilog == "SWIGLU":
+        if epilog in ("SWIGLU", "SWIGLU_AUX"):
             io.b2 = _ptr(epilog_inputs["b2"])
+        if epilog == "SWIGLU_AUX":
+            gu = aux_out.get("gu")
+            if gu is None:
+                gu = torch.empty((m, 2 * n), dtype=a.dtype, device=a.device)
+            io.d2, io.ldd2 = _ptr(gu), gu.stride(0)
+            self.aux["gu"] = gu
         if epilog == "DSWIGLU":
             g, u = epilog_inputs["gate"], epilog_inputs["up"]
             if g.stride(0) != u.stride(0):

@@ -26,7 +26,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", CSRC, "-I", INCLUDE,
 ]
-N_EPI = 10
+N_EPI = 11
 
 
 def _compile(args):

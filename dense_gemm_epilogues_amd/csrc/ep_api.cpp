@@ -24,7 +24,7 @@ namespace ep {
 #define EP_DECL_EPIS(dt, lay)                                                                    \
   EP_DECL_TABLE(dt, lay, 0) EP_DECL_TABLE(dt, lay, 1) EP_DECL_TABLE(dt, lay, 2)                  \
   EP_DECL_TABLE(dt, lay, 3) EP_DECL_TABLE(dt, lay, 4) EP_DECL_TABLE(dt, lay, 5) EP_DECL_TABLE(dt, lay, 6)  \
-  EP_DECL_TABLE(dt, lay, 7) EP_DECL_TABLE(dt, lay, 8) EP_DECL_TABLE(dt, lay, 9)
+  EP_DECL_TABLE(dt, lay, 7) EP_DECL_TABLE(dt, lay, 8) EP_DECL_TABLE(dt, lay, 9) EP_DECL_TABLE(dt, lay, 10)
 EP_DECL_EPIS(0, 0)
 EP_DECL_EPIS(0, 1)
 EP_DECL_EPIS(1, 0)
@@ -38,7 +38,7 @@ static const GemmLauncher* const kTablesAKM[2][2] = {{kLaunch_0_2_0, kLaunch_0_3
     kLaunch_##dt##_##lay##_0, kLaunch_##dt##_##lay##_1, kLaunch_##dt##_##lay##_2,                \
         kLaunch_##dt##_##lay##_3, kLaunch_##dt##_##lay##_4, kLaunch_##dt##_##lay##_5,            \
         kLaunch_##dt##_##lay##_6, kLaunch_##dt##_##lay##_7, kLaunch_##dt##_##lay##_8,            \
-        kLaunch_##dt##_##lay##_9                                                                 \
+        kLaunch_##dt##_##lay##_9, kLaunch_##dt##_##lay##_10                                      \
   }
 static const GemmLauncher* const kTables[2][2][E_NUM] = {{EP_ROW(0, 0), EP_ROW(0, 1)},
                                                          {EP_ROW(1, 0), EP_ROW(1, 1)}};
@@ -55,7 +55,7 @@ static const GemmLauncher* const kPartialAKM[2][2] = {{kPartial_0_2_0, kPartial_
                                                       {kPartial_1_2_0, kPartial_1_3_0}};
 #define EP_DECL_F(dt) EP_DECL_TABLE_F(dt, 0) EP_DECL_TABLE_F(dt, 1) EP_DECL_TABLE_F(dt, 2) \
   EP_DECL_TABLE_F(dt, 3) EP_DECL_TABLE_F(dt, 4) EP_DECL_TABLE_F(dt, 5) EP_DECL_TABLE_F(dt, 6) \
-  EP_DECL_TABLE_F(dt, 7) EP_DECL_TABLE_F(dt, 8) EP_DECL_TABLE_F(dt, 9)
+  EP_DECL_TABLE_F(dt, 7) EP_DECL_TABLE_F(dt, 8) EP_DECL_TABLE_F(dt, 9) EP_DECL_TABLE_F(dt, 10)
 #define EP_DECL_TABLE_F(dt, epi) extern const GemmLauncher kFixup_##dt##_##epi[kNumTileCfgs];
 EP_DECL_F(0) EP_DECL_F(1)
 // [dtype][layout][single B, dual B]
@@ -64,9 +64,9 @@ static const GemmLauncher* const kPartialTables[2][2][2] = {
     {{kPartial_1_0_0, kPartial_1_0_5}, {kPartial_1_1_0, kPartial_1_1_5}}};
 static const GemmLauncher* const kFixupTables[2][E_NUM] = {
     {kFixup_0_0, kFixup_0_1, kFixup_0_2, kFixup_0_3, kFixup_0_4, kFixup_0_5, kFixup_0_6, kFixup_0_7, kFixup_0_8,
-     kFixup_0_9},
+     kFixup_0_9, kFixup_0_10},
     {kFixup_1_0, kFixup_1_1, kFixup_1_2, kFixup_1_3, kFixup_1_4, kFixup_1_5, kFixup_1_6, kFixup_1_7, kFixup_1_8,
-     kFixup_1_9}};
+     kFixup_1_9, kFixup_1_10}};
 
 GemmLauncher gemm_partial_launcher(int dtype, int layout, bool dual, int cfg) {
   if (dtype < 0 || dtype > 1 || layout < 0 || layout > 3 || cfg < 0 || cfg >= kNumTileCfgs) return nullptr;
@@ -88,7 +88,8 @@ GemmLauncher gemm_launcher(int dtype, int layout, int epi, int cfg) {
 }
 
 static const char* kEpiNames[E_NUM] = {"DEFAULT", "BIAS",     "RELU_BIAS",     "RELU_AUX_BIAS", "DRELU_BGRAD",
-                                       "SWIGLU",  "DSWIGLU", "GELU_BIAS",     "GELU_AUX_BIAS", "DGELU_BGRAD"};
+                                       "SWIGLU",  "DSWIGLU", "GELU_BIAS",     "GELU_AUX_BIAS", "DGELU_BGRAD",
+                                       "SWIGLU_AUX"};
 
 }  // namespace ep
 
@@ -250,8 +251,9 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   const bool wants_aux_in = epi == EP_EPILOG_DRELU_BGRAD;
   const bool wants_bgrad = epi == EP_EPILOG_DRELU_BGRAD || epi == EP_EPILOG_DGELU_BGRAD;
   const bool wants_gaux = epi == EP_EPILOG_GELU_AUX_BIAS || epi == EP_EPILOG_DGELU_BGRAD;
-  const bool wants_b2 = epi == EP_EPILOG_SWIGLU;
+  const bool wants_b2 = epi == EP_EPILOG_SWIGLU || epi == EP_EPILOG_SWIGLU_AUX;
   const bool wants_gu = epi == EP_EPILOG_DSWIGLU;
+  const bool wants_d2 = wants_gu || epi == EP_EPILOG_SWIGLU_AUX;
   if (wants_bias != (io->bias != nullptr))
     return fail(EP_ERR_INVALID_ARG, wants_bias ? "bias is required" : "bias must be NULL for this epilog");
   if (wants_aux_out != (io->relu_aux != nullptr))
@@ -273,8 +275,11 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   }
   if (wants_b2 != (io->b2 != nullptr))
     return fail(EP_ERR_INVALID_ARG, wants_b2 ? "b2 (up weight) is required" : "b2 must be NULL");
-  if (wants_gu != (io->gate != nullptr) || wants_gu != (io->up != nullptr) || wants_gu != (io->d2 != nullptr))
-    return fail(EP_ERR_INVALID_ARG, wants_gu ? "gate, up and d2 are required" : "gate, up, d2 must be NULL");
+  if (wants_gu != (io->gate != nullptr) || wants_gu != (io->up != nullptr))
+    return fail(EP_ERR_INVALID_ARG, wants_gu ? "gate and up are required" : "gate and up must be NULL");
+  if (wants_d2 != (io->d2 != nullptr))
+    return fail(EP_ERR_INVALID_ARG, wants_d2 ? "d2 is required" : "d2 must be NULL for this epilog");
+  if (wants_d2 && !aligned(io->d2, 16)) return fail(EP_ERR_INVALID_ARG, "d2 must be 16-byte aligned");
   if (wants_bias && !aligned(io->bias, 16)) return fail(EP_ERR_INVALID_ARG, "bias must be 16-byte aligned");
   if (wants_b2 && !aligned(io->b2, 16)) return fail(EP_ERR_INVALID_ARG, "b2 must be 16-byte aligned");
   if (wants_gu && (!aligned(io->gate, 16) || !aligned(io->up, 16) || !aligned(io->d2, 16)))
@@ -291,11 +296,17 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   }
   if (wants_gu) {
     const int64_t ldgu = io->ld_gu == 0 ? s->n : io->ld_gu;
-    const int64_t ldd2 = io->ldd2 == 0 ? s->ldd : io->ldd2;
     if (ldgu < s->n || ldgu % 8 || ldgu >= kMaxLd) return fail(EP_ERR_INVALID_ARG, "ld_gu must be a multiple of 8 in [n, 2^22)");
-    if (ldd2 < s->n || ldd2 % 8 || ldd2 >= kMaxLd) return fail(EP_ERR_INVALID_ARG, "ldd2 must be a multiple of 8 in [n, 2^22)");
-  } else if (io->ld_gu != 0 || io->ldd2 != 0) {
-    return fail(EP_ERR_INVALID_ARG, "ld_gu and ldd2 must be 0 for this epilog");
+  } else if (io->ld_gu != 0) {
+    return fail(EP_ERR_INVALID_ARG, "ld_gu must be 0 for this epilog");
+  }
+  if (wants_d2) {
+    const int64_t d2w = wants_gu ? s->n : 2 * s->n;  // DSWIGLU: d_up; SWIGLU_AUX: [gate | up]
+    const int64_t ldd2 = io->ldd2 == 0 ? (wants_gu ? s->ldd : d2w) : io->ldd2;
+    if (ldd2 < d2w || ldd2 % 8 || ldd2 >= kMaxLd)
+      return fail(EP_ERR_INVALID_ARG, "ldd2 must be a multiple of 8 in [d2 row length, 2^22)");
+  } else if (io->ldd2 != 0) {
+    return fail(EP_ERR_INVALID_ARG, "ldd2 must be 0 for this epilog");
   }
   if (opt && opt->bgrad_mode == EP_BGRAD_ATOMIC && opt->path == EP_PATH_UNFUSED)
     return fail(EP_ERR_UNSUPPORTED, "the unfused path uses the two-pass bias-gradient reduction only");
@@ -446,7 +457,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
     if (st != EP_OK) return st;
   }
 
-  const bool dual = epi == EP_EPILOG_SWIGLU;
+  const bool dual = epi == EP_EPILOG_SWIGLU || epi == EP_EPILOG_SWIGLU_AUX;
   const bool unfused = opt.path == EP_PATH_UNFUSED;
   // the unfused path runs plain DEFAULT GEMMs (single-B) into intermediates
   const bool kernel_dual = dual && !unfused;
@@ -466,7 +477,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   h->io = *io;
   if (h->io.ld_aux == 0) h->io.ld_aux = (s->n + 31) / 32;
   if (h->io.ld_gu == 0) h->io.ld_gu = s->n;
-  if (h->io.ldd2 == 0) h->io.ldd2 = s->ldd;
+  if (h->io.ldd2 == 0) h->io.ldd2 = epi == EP_EPILOG_SWIGLU_AUX ? 2 * s->n : s->ldd;
   if (h->io.ld_gelu_aux == 0) h->io.ld_gelu_aux = s->n;
   h->opt = opt;
   h->device = dev;
@@ -520,7 +531,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
       part_bytes = (size_t)h->nparts * N * sizeof(float);
     }
   }
-  if (unfused && dual) {
+  if (unfused && epi == EP_EPILOG_SWIGLU) {
     // the two branch GEMMs of the unfused SwiGLU need intermediates; every other unfused
     // sequence runs its elementwise passes in place on the output
     z_bytes = (size_t)M * N * 2;
@@ -566,15 +577,19 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   } else {
     // unfused: the GEMM writes its DEFAULT result straight to d (or, for SwiGLU, to the
     // two branch intermediates)
-    if (dual) {
+    // (SWIGLU_AUX: the two branch results go straight to their halves of d2)
+    if (epi == EP_EPILOG_SWIGLU) {
       a.d = h->uf.z;
       a.ldd = h->uf.ldz;
+    } else if (epi == EP_EPILOG_SWIGLU_AUX) {
+      a.d = io->d2;
+      a.ldd = h->io.ldd2;
     }
     h->args = a;
     if (dual) {
       GemmArgs a2 = a;
       a2.b = io->b2;
-      a2.d = h->uf.z2;
+      a2.d = epi == EP_EPILOG_SWIGLU ? h->uf.z2 : (void*)((char*)io->d2 + N * 2);
       h->args2 = a2;
     }
   }
@@ -648,6 +663,11 @@ ep_status ep_execute(ep_handle h, void* stream) {
       if ((st = check_launch("gemm up")) != EP_OK) return st;
       launch_silu_mul(dt, h->uf.z, h->uf.z2, h->uf.ldz, sh.d, sh.ldd, M, N, s);
       break;
+    case EP_EPILOG_SWIGLU_AUX:
+      h->launch(h->args2, s);
+      if ((st = check_launch("gemm up")) != EP_OK) return st;
+      launch_silu_mul(dt, h->io.d2, (const char*)h->io.d2 + N * 2, h->io.ldd2, sh.d, sh.ldd, M, N, s);
+      break;
     case EP_EPILOG_DSWIGLU:
       launch_dswiglu(dt, sh.d, sh.ldd, h->io.gate, h->io.up, h->io.ld_gu, sh.d, sh.ldd, h->io.d2, h->io.ldd2, M,
                      N, s);
@@ -707,6 +727,7 @@ ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
       case EP_EPILOG_RELU_AUX_BIAS: extra = " + bias_add + relu_pack"; break;
       case EP_EPILOG_DRELU_BGRAD: extra = " + mask_apply + colsum + bgrad_reduce"; break;
       case EP_EPILOG_SWIGLU: extra = " x2 + silu_mul"; break;
+      case EP_EPILOG_SWIGLU_AUX: extra = " x2 (into d2) + silu_mul"; break;
       case EP_EPILOG_DSWIGLU: extra = " + dswiglu"; break;
       case EP_EPILOG_GELU_BIAS: extra = " + bias_add + gelu"; break;
       case EP_EPILOG_GELU_AUX_BIAS: extra = " + bias_add + gelu (aux)"; break;

@@ -16,7 +16,8 @@ enum Epi : int {
   E_GELU_BIAS = 7,
   E_GELU_AUX_BIAS = 8,
   E_DGELU_BGRAD = 9,
-  E_NUM = 10
+  E_SWIGLU_AUX = 10,
+  E_NUM = 11
 };
 
 enum Layout : int { L_KN = 0, L_NK = 1 };

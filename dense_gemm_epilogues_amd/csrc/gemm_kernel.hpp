@@ -176,7 +176,7 @@ __device__ __forceinline__ int swf(int r) {
 template <int DT, int LAY, int EPI, int CFG>
 struct GemmTraits {
   static constexpr int BM = cfg_bm(CFG), BNT = cfg_bnt(CFG), BK = cfg_bk(CFG), NST = cfg_nst(CFG);
-  static constexpr bool DUAL = EPI == E_SWIGLU;
+  static constexpr bool DUAL = EPI == E_SWIGLU || EPI == E_SWIGLU_AUX;
   static constexpr int WTM = BM / 2;             // rows per wave
   static constexpr int WTB = BNT / 2;            // B-tile rows per wave
   static constexpr int MB = WTM / 32;            // 32x32 blocks per wave along M
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 
     // ---- accumulator space, then the slab is staged
     uint32_t* mk = (uint32_t*)(smem + TR::MASK_OFF) + wm * 32 * TR::WPT;  // [32 rows][WPT words]
-    constexpr bool XFORM = HAS_BIAS || EPI == E_SWIGLU;
+    constexpr bool XFORM = HAS_BIAS || DUAL;
 #pragma unroll
     for (int j = 0; j < NBO; ++j) {
 #pragma unroll
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
             mk[r0 * TR::WPT + wn * NBO + j] = (uint32_t)b;
             mk[(r0 + 4) * TR::WPT + wn * NBO + j] = (uint32_t)(b >> 32);
           }
-        } else if constexpr (EPI == E_SWIGLU) {
+        } else if constexpr (DUAL) {
           // block j holds the gate columns, block j + NB/2 the up columns of the same outputs
           const float u = acc_read(acc[i][j + NB / 2][r]);
           v = v * sigmoid_f(v) * u;
@@ -847,6 +847,31 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       }
     }
     __syncthreads();
+
+    if constexpr (EPI == E_SWIGLU_AUX) {
+      // the gate (pass 0) and up (pass 1) pre-activations of the slab, still in the
+      // accumulators, go to d2 columns [0, N) and [N, 2N)
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int j = 0; j < NBO; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int r0 = 8 * (r >> 2) + (r & 3);
+            stg[(r0 + 4 * hlf) * SP + j * 32 + l32] = pass == 0 ? acc[i][j][r] : acc[i][j + NB / 2][r];
+          }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < TR::ITERS; ++it) {
+          const int grow = srow0 + it * TR::RPI + lr;
+          const float* src = stg + (it * TR::RPI + lr) * SP + lc;
+          const f32x4 v0 = *(const f32x4*)src, v1 = *(const f32x4*)(src + 4);
+          if (colok && grow < M)
+            *(u32x4*)((char*)p.d2 + ((int64_t)grow * p.ldd2 + pass * N + gcol) * 2) = pack8<DT>(v0, v1);
+        }
+        __syncthreads();
+      }
+    }
   }
 
   if constexpr (BGRAD) {

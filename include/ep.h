@@ -89,6 +89,11 @@ typedef enum { EP_A_MK = 0, EP_A_KM = 1 } ep_a_layout;
  *                          D2 = d_up = dh .* gate .* s;  gate and up are M x N inputs in
  *                          the element type (row stride ld_gu).  gemm_swiglu_mlp_fusion.py,
  *                          module docstring (backward dSwiGLU as a matmul epilogue).
+ * EP_EPILOG_SWIGLU_AUX     as SWIGLU, and also writes the two pre-activations to d2 (M x 2N,
+ *                          row stride ldd2 >= 2N): columns [0, N) = A.B (gate), [N, 2N) =
+ *                          A.B2 (up), rounded to the element type; the layout DSWIGLU reads
+ *                          with gate = d2, up = d2 + N, ld_gu = ldd2 (save instead of
+ *                          recompute for the backward; gemm_swiglu_mlp_fusion.py docstring).
  * EP_EPILOG_GELU_BIAS      D = gelu(A.B + bias) with the exact GELU, gelu(t) = t Phi(t) =
  *                          t/2 (1 + erf(t / sqrt 2)) (hotdry.top post: GELU_BIAS among the
  *                          predefined epilogs; the post does not fix the GELU variant).
@@ -109,7 +114,8 @@ typedef enum {
   EP_EPILOG_DSWIGLU = 6,
   EP_EPILOG_GELU_BIAS = 7,
   EP_EPILOG_GELU_AUX_BIAS = 8,
-  EP_EPILOG_DGELU_BGRAD = 9
+  EP_EPILOG_DGELU_BGRAD = 9,
+  EP_EPILOG_SWIGLU_AUX = 10
 } ep_epilog;
 
 /* The GEMM operands, bound at plan time. Sizes and leading dimensions are in elements. */
@@ -137,7 +143,9 @@ typedef struct {
   const void* gate;            /* DSWIGLU inputs: m x n, row stride ld_gu */
   const void* up;
   int64_t ld_gu;               /* 0 means n */
-  void* d2;                    /* DSWIGLU output d_up: m x n, row stride ldd2 (0 means ldd) */
+  void* d2;                    /* DSWIGLU output d_up: m x n, row stride ldd2 (0 means ldd);
+                                  SWIGLU_AUX output [gate | up]: m x 2n, row stride ldd2
+                                  (0 means 2n) */
   int64_t ldd2;
   void* gelu_aux;              /* GELU_AUX_BIAS output / DGELU_BGRAD input: the pre-activation,
                                   m x n in the element type, row stride ld_gelu_aux */

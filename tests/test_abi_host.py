@@ -84,7 +84,12 @@ CASES = [
     ("k not multiple of 8", lambda L: plan(L, shape(k=60, lda=64))[0], UNSUPPORTED),
     ("m >= 2^31", lambda L: plan(L, shape(m=1 << 31))[0], UNSUPPORTED),
     ("unknown dtype", lambda L: plan(L, shape(), dtype=7)[0], UNSUPPORTED),
-    ("unknown epilog", lambda L: plan(L, shape(), epi=10)[0], UNSUPPORTED),
+    ("unknown epilog", lambda L: plan(L, shape(), epi=11)[0], UNSUPPORTED),
+    ("SWIGLU_AUX without d2", lambda L: plan(L, shape(lay=NK), E["SWIGLU_AUX"], ep_epilog_io(b2=X_PTR))[0], INVALID),
+    ("SWIGLU_AUX ldd2 below 2n", lambda L: plan(L, shape(lay=NK), E["SWIGLU_AUX"],
+                                                ep_epilog_io(b2=X_PTR, d2=X_PTR + 8192, ldd2=64))[0], INVALID),
+    ("SWIGLU with a stray d2", lambda L: plan(L, shape(lay=NK), E["SWIGLU"], ep_epilog_io(b2=X_PTR, d2=X_PTR + 8192))[0],
+     INVALID),
     ("unknown layout", lambda L: plan(L, shape(lay=3))[0], UNSUPPORTED),
     ("null a", lambda L: plan(L, shape(a=0))[0], INVALID),
     ("misaligned b", lambda L: plan(L, shape(b=B_PTR + 8))[0], INVALID),

@@ -242,7 +242,8 @@ def test_square_gelu_layer_full():
 # ------------------------------------------------------------------ SwiGLU-MLP training step
 def test_swiglu_mlp_training_step_all_gradients():
     """The whole SwiGLU MLP forward and backward with this library only, M 2048:
-      forward  [g | u] = x W_gu^T (DEFAULT, W_gu = [Wg; Wu]), h = SWIGLU(x; Wg, Wu), out = h Wd^T;
+      forward  h and the saved [g | u] = SWIGLU_AUX(x; Wg, Wu) (W_gu = [Wg; Wu]), out = h Wd^T, and
+               the recompute alternative [g | u] = x W_gu^T (one DEFAULT GEMM) as a cross-check;
       backward [d_gate | d_up] = DSWIGLU(dout, Wd; g, u) into one M x 2I buffer,
                dx = [d_gate | d_up] . W_gu  (one GEMM over the concatenated K = 2I),
                [dWg; dWu] = [d_gate | d_up]^T . x and dWd = dout^T . h (transposed-A GEMMs).
@@ -265,9 +266,12 @@ def test_swiglu_mlp_training_step_all_gradients():
         plans.append(p)  # kept until the device is synchronised
         return p.execute()[0]
 
-    # forward
-    gu = run(x, w_gu, "DEFAULT", b_layout="NK")                          # M x 2I = [g | u]
-    h = run(x, w_gu[:idim], "SWIGLU", {"b2": w_gu[idim:]}, b_layout="NK")
+    # forward (saving): h and [g | u] from one kernel
+    ps = ep.Plan(x, w_gu[:idim], "SWIGLU_AUX", {"b2": w_gu[idim:]}, b_layout="NK")
+    plans.append(ps)
+    h, aux = ps.execute()
+    gu = aux["gu"]                                                       # M x 2I = [g | u]
+    gu_re = run(x, w_gu, "DEFAULT", b_layout="NK")                       # recompute alternative
     out = run(h, wd, "DEFAULT", b_layout="NK")
     # backward
     dgu = torch.empty((m, 2 * idim), dtype=torch.bfloat16, device=dev)
@@ -281,8 +285,9 @@ def test_swiglu_mlp_training_step_all_gradients():
     x64, wg64, wu64, wd64, dout64 = f64(x), f64(wg), f64(wu), f64(wd), f64(dout)
     # forward pieces
     rows = slice(0, 512)  # the oracle's full-width products on a row block (the kernels tile rows identically)
-    assert_half(f64(gu[rows, :idim]), oracle.matmul(x64[rows], wg64, "NK"), "g")
-    assert_half(f64(gu[rows, idim:]), oracle.matmul(x64[rows], wu64, "NK"), "u")
+    assert_half(f64(gu[rows, :idim]), oracle.matmul(x64[rows], wg64, "NK"), "saved g")
+    assert_half(f64(gu[rows, idim:]), oracle.matmul(x64[rows], wu64, "NK"), "saved u")
+    assert_half(f64(gu_re[rows]), f64(gu[rows]), "recomputed [g | u] against the saved one")
     href, _, _ = oracle.swiglu(x64[rows], wg64, wu64)
     assert_half(f64(h[rows]), href, "h")
     h64 = f64(h)

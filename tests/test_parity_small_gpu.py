@@ -16,7 +16,7 @@ from tests._gpu import assert_bgrad, assert_half, assert_mask, f64, require_gpu,
 pytestmark = pytest.mark.gpu
 
 EPIS = ["DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "DRELU_BGRAD", "SWIGLU", "DSWIGLU",
-        "GELU_BIAS", "GELU_AUX_BIAS", "DGELU_BGRAD"]
+        "GELU_BIAS", "GELU_AUX_BIAS", "DGELU_BGRAD", "SWIGLU_AUX"]
 SHAPES = [(300, 200, 136), (37, 8, 8), (130, 264, 520), (1, 64, 72)]
 DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
 SENT16 = -1  # 0xFFFF, a NaN pattern in both half types
@@ -46,7 +46,7 @@ def make_inputs(epi, dt, layout, m, n, k, seed, dev):
     if epi == "DRELU_BGRAD":
         p = torch.randn(m, n, generator=g).numpy()
         ins["mask"] = torch.from_numpy(oracle.pack_relu_mask(p > 0).view(np.int32).copy())
-    if epi == "SWIGLU":
+    if epi in ("SWIGLU", "SWIGLU_AUX"):
         ins["b2"] = rn(*b.shape, scale=k ** -0.5)
     if epi == "DSWIGLU":
         ins["gate"] = rn(m, n, scale=1.5)
@@ -79,8 +79,11 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
         epi_in["relu_aux"] = ins["mask"]
         gbuf = torch.full((n + 4,), float("nan"), dtype=torch.float32, device=dev)
         aux_out["drelu_bgrad"] = gbuf[:n]
-    if epi == "SWIGLU":
+    if epi in ("SWIGLU", "SWIGLU_AUX"):
         epi_in["b2"] = ins["b2"]
+    if epi == "SWIGLU_AUX":
+        gubuf, guview = padded(m, 2 * n, dt, dev)
+        aux_out["gu"] = guview
     if epi == "DSWIGLU":
         epi_in["gate"], epi_in["up"] = ins["gate"], ins["up"]
         ubuf, uview = padded(m, n, dt, dev)
@@ -120,9 +123,14 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
         assert_half(f64(out), dx, what)
         assert_bgrad(aux_out["drelu_bgrad"].cpu().numpy(), bg, what)
         assert torch.isnan(gbuf[n:]).all(), f"{what}: bgrad padding written"
-    elif epi == "SWIGLU":
-        h, _, _ = oracle.swiglu(a64, b64, f64(ins["b2"]), layout)
+    elif epi in ("SWIGLU", "SWIGLU_AUX"):
+        h, g, u = oracle.swiglu(a64, b64, f64(ins["b2"]), layout)
         assert_half(f64(out), h, what)
+        if epi == "SWIGLU_AUX":
+            assert_half(f64(aux_out["gu"][:, :n]), g, what + " gate")
+            assert_half(f64(aux_out["gu"][:, n:]), u, what + " up")
+            gb = gubuf.view(torch.int16).cpu().numpy()
+            assert np.all(gb[m, :] == -1) and np.all(gb[:, 2 * n:] == -1), f"{what}: gu padding written"
     elif epi == "DSWIGLU":
         dg, du, _ = oracle.dswiglu(a64, b64, f64(ins["gate"]), f64(ins["up"]), layout)
         assert_half(f64(out), dg, what)
@@ -158,12 +166,12 @@ BNT128_CFGS = (1, 2, 6)
 @pytest.mark.parametrize("epi", EPIS)
 def test_small_shapes_fused(epi, dtname, layout, cfg):
     require_gpu()
-    if epi == "SWIGLU" and layout == "KN" and cfg in BNT128_CFGS:
+    if epi in ("SWIGLU", "SWIGLU_AUX") and layout == "KN" and cfg in BNT128_CFGS:
         import dense_gemm_epilogues_amd as ep
         dev = torch.device("cuda")
         a = torch.zeros((64, 64), dtype=DTYPES[dtname], device=dev)
         with pytest.raises(ep.EPError, match="EP_ERR_UNSUPPORTED"):
-            ep.Plan(a, a, "SWIGLU", {"b2": a}, b_layout="KN", tile_cfg=cfg)
+            ep.Plan(a, a, epi, {"b2": a}, b_layout="KN", tile_cfg=cfg)
         return
     for (m, n, k) in SHAPES:
         run_and_check(epi, dtname, layout, m, n, k, cfg)
@@ -178,7 +186,7 @@ def test_split_k(epi, layout, splits):
     divides unevenly and a K too short for the requested number of ranges."""
     require_gpu()
     for cfg in (0, 1, 6):
-        if epi == "SWIGLU" and layout == "KN" and cfg in BNT128_CFGS:
+        if epi in ("SWIGLU", "SWIGLU_AUX") and layout == "KN" and cfg in BNT128_CFGS:
             continue
         for dtname in ("f16", "bf16"):
             for (m, n, k) in [(300, 200, 520), (130, 264, 136)]:
@@ -234,7 +242,7 @@ def test_split_k_atomic_bgrad():
 def test_small_shapes_unfused(epi, layout):
     require_gpu()
     for (m, n, k) in SHAPES:
-        run_and_check(epi, "f16" if epi not in ("SWIGLU", "DSWIGLU") else "bf16", layout, m, n, k, -1,
+        run_and_check(epi, "f16" if epi not in ("SWIGLU", "DSWIGLU", "SWIGLU_AUX") else "bf16", layout, m, n, k, -1,
                       path="unfused")
 
 
