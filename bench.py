@@ -8,7 +8,10 @@ GEMM throughput in TFLOP/s (2*M*N*K per GEMM; epilog flops not counted).  The sa
 carries the unfused-path step time (same GEMM core, DEFAULT epilog, separate kernels
 through HBM) and, under "configs", the fused/unfused timings of the large workloads:
 the H200-shape fp16 layer (65536 x 16384 x 8192), the bf16 SwiGLU forward
-(M 2048, H 5120, I 17408) and the GEMM + dSwiGLU backward (M 16384).
+(M 2048, H 5120, I 17408), the GEMM + dSwiGLU backward (M 16384), a whole SwiGLU-MLP
+training step, an M sweep, the GELU layer, launch overhead and plan-time tuning.  Where
+stated, torch (hipBLASLt GEMMs plus elementwise ops) runs the same step as a vendor-library
+reference.
 
 Timing: HIP events on the stream the kernels run on, around each step; a 512 MiB
 buffer is overwritten between steps (outside the events) so no step starts with its
@@ -39,7 +42,7 @@ def parse():
     ap.add_argument("--no-large", action="store_true", help="skip the large-workload summary")
     ap.add_argument("--only", default=None,
                     help="profile helper: run only one workload's fused path "
-                         "(sq4096, h200, swiglu, dswiglu) and print its line")
+                         "(sq4096, h200, swiglu, dswiglu, mlp_step, gelu) and print its line")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="profile helper: first run one device-to-device copy of this many bytes "
@@ -123,6 +126,19 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True):
                      "bwd_ms": float(np.mean(per[1])), "fwd_info": pf.info(), "bwd_info": pb.info()}
         pf.free()
         pb.free()
+    if with_unfused:
+        # vendor-library reference: hipBLASLt GEMMs + torch elementwise, byte mask instead of bits
+        if mask_bwd is not None:  # the separate backward mask (M x K bits) as bytes, unpacked untimed
+            bits = torch.arange(32, device=dev, dtype=torch.int32)
+            keep_b = ((mask_bwd.unsqueeze(-1) >> bits) & 1).to(torch.bool).reshape(m, k)
+
+        def torch_step():
+            y = torch.addmm(bias, x, w).relu_()
+            keep = y > 0
+            (dy @ w.t()) * (keep if mask_bwd is None else keep_b)
+            dy.float().sum(0)
+        step_ms, _ = run_steps([torch_step], steps, warmup, flush)
+        res["torch"] = {"step_ms": float(np.mean(step_ms))}
     flop = 2.0 * m * n * k
     out = {"flop_per_gemm": flop, "fused": res["fused"]}
     f = res["fused"]
@@ -135,6 +151,8 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True):
         out["speedup_step"] = u["step_ms"] / f["step_ms"]
         out["speedup_fwd"] = u["fwd_ms"] / f["fwd_ms"]
         out["speedup_bwd"] = u["bwd_ms"] / f["bwd_ms"]
+        out["torch"] = res["torch"]
+        out["speedup_vs_torch"] = res["torch"]["step_ms"] / f["step_ms"]
     out["inputs"] = {"x": x, "w": w, "bias": bias, "dy": dy}
     return out
 
@@ -206,6 +224,70 @@ def dswiglu_bwd(c, steps, warmup, flush, dev):
     f, u = res["fused"], res["unfused"]
     f["tflops"] = flop / (f["ms"] * 1e-3) / 1e12
     return {"fused": f, "unfused": u, "speedup": u["ms"] / f["ms"]}
+
+
+def mlp_training_step(c, steps, warmup, flush, dev):
+    """One SwiGLU-MLP training step (forward and all four gradients) with this library:
+      forward  h, [g | u] = SWIGLU_AUX(x; Wg, Wu); out = h Wd^T
+      backward [d_gate | d_up] = DSWIGLU(dout, Wd; g, u); dx = [d_gate | d_up] [Wg; Wu];
+               [dWg; dWu] = [d_gate | d_up]^T x and dWd = dout^T h (transposed-A GEMMs).
+    The fused path runs 6 kernels; the unfused path replaces SWIGLU_AUX and DSWIGLU by
+    their GEMM + elementwise sequences.  torch (hipBLASLt GEMMs and elementwise ops) runs the
+    same step as a vendor-library reference.  FLOP per step: 18 M H I."""
+    import dense_gemm_epilogues_amd as ep
+    import workloads as W
+    inp = W.swiglu_inputs(c, device=dev)
+    x, wg, wu, wd = inp["x"], inp["wg"], inp["wu"], inp["wd"]
+    m, hd, idim = c.m, c.h, c.i
+    w_gu = torch.cat([wg, wu], dim=0).contiguous()
+    dout = W.randn((m, hd), W.seed_of(c.cfg, 6), 1.0, torch.bfloat16, dev)
+    dgu = torch.empty((m, 2 * idim), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for path in ("fused", "unfused"):
+        ps = ep.Plan(x, w_gu[:idim], "SWIGLU_AUX", {"b2": w_gu[idim:]}, b_layout="NK", path=path)
+        h, aux = ps.execute()
+        gu = aux["gu"]
+        pd = ep.Plan(h, wd, "DEFAULT", b_layout="NK")
+        pds = ep.Plan(dout, wd, "DSWIGLU", {"gate": gu[:, :idim], "up": gu[:, idim:]}, b_layout="KN",
+                      out=dgu[:, :idim], aux_out={"d_up": dgu[:, idim:]}, path=path)
+        pdx = ep.Plan(dgu, w_gu, "DEFAULT", b_layout="KN")
+        pwgu = ep.Plan(dgu, x, "DEFAULT", b_layout="KN", a_layout="KM")
+        pwd = ep.Plan(dout, h, "DEFAULT", b_layout="KN", a_layout="KM")
+        fns = [ps.execute, pd.execute, pds.execute, pdx.execute, pwgu.execute, pwd.execute]
+        step_ms, per = run_steps(fns, steps, warmup, flush)
+        res[path] = {"step_ms": float(np.mean(step_ms)), "per_ms": [float(np.mean(v)) for v in per]}
+        for p in (ps, pd, pds, pdx, pwgu, pwd):
+            p.free()
+    # vendor-library reference: the same step with torch ops (GEMMs via hipBLASLt)
+    wgt, wut, wdt = wg.t(), wu.t(), wd.t()
+
+    def torch_step():
+        g = x @ wgt
+        u = x @ wut
+        hh = torch.nn.functional.silu(g.float()).mul_(u.float()).to(torch.bfloat16)
+        hh @ wdt
+        dh = (dout @ wd).float()
+        gf, uf = g.float(), u.float()
+        sg = torch.sigmoid(gf)
+        dsilu = sg * (1 + gf * (1 - sg))
+        dg = (dh * uf * dsilu).to(torch.bfloat16)
+        du = (dh * gf * sg).to(torch.bfloat16)
+        dg @ wg + du @ wu
+        dg.t() @ x
+        du.t() @ x
+        dout.t() @ hh
+    step_ms, _ = run_steps([torch_step], steps, warmup, flush)
+    res["torch"] = {"step_ms": float(np.mean(step_ms))}
+    flop = 18.0 * m * hd * idim
+    names = ["swiglu_aux_fwd", "down_gemm", "dswiglu", "dx_gemm_K2I", "dw_gate_up_gemm_AKM", "dw_down_gemm_AKM"]
+    f, u = res["fused"], res["unfused"]
+    return {"fused_step_ms": round(f["step_ms"], 4), "unfused_step_ms": round(u["step_ms"], 4),
+            "torch_step_ms": round(res["torch"]["step_ms"], 4),
+            "fused_step_tflops": round(flop / (f["step_ms"] * 1e-3) / 1e12, 1),
+            "step_pct_peak": round(100 * flop / (f["step_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
+            "speedup_vs_unfused": round(u["step_ms"] / f["step_ms"], 4),
+            "speedup_vs_torch": round(res["torch"]["step_ms"] / f["step_ms"], 4),
+            "fused_kernel_ms": {n: round(v, 4) for n, v in zip(names, f["per_ms"])}}
 
 
 def swiglu_m_sweep(steps, warmup, flush, dev, ms=(2048, 4096, 8192, 16384)):
@@ -394,6 +476,10 @@ def main():
             r.pop("inputs")
         elif args.only == "swiglu":
             r = swiglu_fwd(W.SWIGLU[4], st, wu, flush, dev)
+        elif args.only == "gelu":
+            r = gelu_layer(W.LINEAR[2], st, wu, flush, dev)
+        elif args.only == "mlp_step":
+            r = mlp_training_step(W.SWIGLU[4], st, wu, flush, dev)
         elif args.only == "dswiglu":
             r = dswiglu_bwd(W.SWIGLU[5], st, wu, flush, dev)
         else:
@@ -426,6 +512,8 @@ def main():
         "pct_peak": round(100.0 * f2["tflops_step"] / PEAK_F16_TFLOPS, 2),
         "speedup_vs_unfused": round(r2["speedup_step"], 4),
         "unfused_ms_per_step": round(r2["unfused"]["step_ms"], 5),
+        "torch_ms_per_step": round(r2["torch"]["step_ms"], 5),
+        "speedup_vs_torch": round(r2["speedup_vs_torch"], 4),
         "fwd_ms": round(f2["fwd_ms"], 5), "bwd_ms": round(f2["bwd_ms"], 5),
         "roofline": {"bound": "mfma", "kernel": f2["fwd_info"].split("kernels=")[1],
                      "achieved": round(fwd_tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
@@ -450,7 +538,8 @@ def main():
             "bwd_pct_peak": round(100 * r3["fused"]["tflops_bwd"] / PEAK_F16_TFLOPS, 2),
             "fused_fwd_ms": round(r3["fused"]["fwd_ms"], 4), "fused_bwd_ms": round(r3["fused"]["bwd_ms"], 4),
             "unfused_fwd_ms": round(r3["unfused"]["fwd_ms"], 4), "unfused_bwd_ms": round(r3["unfused"]["bwd_ms"], 4),
-            "speedup_fwd": round(r3["speedup_fwd"], 4), "speedup_bwd": round(r3["speedup_bwd"], 4)}
+            "speedup_fwd": round(r3["speedup_fwd"], 4), "speedup_bwd": round(r3["speedup_bwd"], 4),
+            "torch_step_ms": round(r3["torch"]["step_ms"], 4), "speedup_step_vs_torch": round(r3["speedup_vs_torch"], 4)}
         torch.cuda.empty_cache()
         r4 = swiglu_fwd(W.SWIGLU[4], args.steps, args.warmup, flush, dev)
         large["swiglu_fwd_bf16_M2048_H5120_I17408"] = {
@@ -469,6 +558,8 @@ def main():
             "speedup": round(r5["speedup"], 4)}
         torch.cuda.empty_cache()
         large["swiglu_fwd_bf16_M_sweep_H5120_I17408"] = swiglu_m_sweep(s_l, w_l, flush, dev)
+        large["swiglu_mlp_training_step_bf16_M2048_H5120_I17408"] = mlp_training_step(W.SWIGLU[4], s_l, w_l, flush, dev)
+        torch.cuda.empty_cache()
         large["gelu_layer_fp16_4096x4096x4096"] = gelu_layer(W.LINEAR[2], args.steps, args.warmup, flush, dev)
         large["execute_overhead"] = execute_overhead(dev)
         large["autotune_vs_model"] = autotune_vs_model(s_l, w_l, flush, dev)

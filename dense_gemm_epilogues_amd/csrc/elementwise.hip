@@ -8,6 +8,7 @@
 // kernel is a plain HBM-bound pass: 16-byte row-contiguous accesses, one element group of
 // 8 per thread, grid-stride loops.
 #include "ep_internal.hpp"
+#include "normal_dist.hpp"
 
 namespace ep {
 namespace {
@@ -196,12 +197,6 @@ __global__ void dswiglu_kernel(const char* dh, int64_t lddh, const char* gate, c
   }
 }
 
-// exact GELU t Phi(t) and its derivative Phi(t) + t phi(t) (exp on the hardware exp2)
-__device__ __forceinline__ float ew_gelu(float t) { return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f)); }
-__device__ __forceinline__ float ew_gelu_grad(float t) {
-  return 0.5f * (1.0f + erff(t * 0.70710678118654752f)) +
-         t * 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * t * t);
-}
 
 // unfused GELU forward, in place: aux = z (when aux is given), z = gelu(z)
 template <int DT>
@@ -217,7 +212,7 @@ __global__ void gelu_apply_kernel(char* z, int64_t ldz, char* aux, int64_t ld_au
     float f[8];
     unpack8<DT>(raw, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = ew_gelu(f[e]);
+    for (int e = 0; e < 8; ++e) f[e] = gelu_f(f[e]);
     *(u32x4*)(z + (row * ldz + col) * 2) = pack8<DT>(f);
   }
 }
@@ -235,7 +230,7 @@ __global__ void dgelu_apply_kernel(char* g, int64_t ldg, const char* aux, int64_
     unpack8<DT>(*(const u32x4*)(g + (row * ldg + col) * 2), fg);
     unpack8<DT>(*(const u32x4*)(aux + (row * ld_aux + col) * 2), fa);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) fg[e] *= ew_gelu_grad(fa[e]);
+    for (int e = 0; e < 8; ++e) fg[e] *= gelu_grad_f(fa[e]);
     *(u32x4*)(g + (row * ldg + col) * 2) = pack8<DT>(fg);
   }
 }

@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "ep_internal.hpp"
+#include "normal_dist.hpp"
 
 namespace ep {
 
@@ -111,14 +112,6 @@ __device__ __forceinline__ float acc_read(float a) {
   float v;
   asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
   return v;
-}
-
-// GELU in its exact form, gelu(t) = t Phi(t) = t/2 (1 + erf(t / sqrt 2)), and its derivative
-// Phi(t) + t phi(t) with phi(t) = exp(-t^2/2) / sqrt(2 pi) (exp on the hardware exp2).
-__device__ __forceinline__ float gelu_f(float t) { return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f)); }
-__device__ __forceinline__ float gelu_grad_f(float t) {
-  const float phi = 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * t * t);
-  return 0.5f * (1.0f + erff(t * 0.70710678118654752f)) + t * phi;
 }
 
 // Logistic function from its definition, 1 / (1 + e^-t), with e^-t = 2^(-t log2 e) on the
