@@ -177,6 +177,19 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   return best;
 }
 
+// Rows of a k-contiguous operand whose stride is a multiple of 32 KiB fall into few L2 sets:
+// the 256 rows of one k-step evict each other.  A 32-deep k-step reads 64 bytes of each row,
+// half a 128-byte line, and the other half, read one k-step later, is fetched again.  With
+// both operands k-contiguous (B given N x K) at such strides, 65536 x 8192 x 16384 fetched
+// twice the bytes of a padded stride and ran 18 % slower; 64-deep k-steps read whole lines
+// and recover most of it.  With B given K x N only A's rows are affected and the 32-deep
+// 4-stage ring stays faster (14.75 against 15.69 ms for the same shape).
+bool strides_conflict(const ep_shape* s) {
+  const int64_t es = 2;  // bytes per fp16 / bf16 element
+  const bool b_kc = s->b_layout == EP_B_NK && (s->ldb * es) % 32768 == 0;
+  return s->k >= 4096 && b_kc;
+}
+
 // Split-K: how many K ranges per tile.  Only grids that leave CUs idle are split: the time
 // of one resident round of tiles scales as rounds(tiles * S) / S, and every split adds a
 // write and a read of the fp32 tile partials (BM * BNT * 4 bytes), priced at a CU's share of
@@ -464,8 +477,9 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   if (opt.tile_cfg >= 0 && !cfg_allowed(opt.tile_cfg, kernel_dual, s->b_layout))
     return fail(EP_ERR_UNSUPPORTED, "tile_cfg %d cannot run SWIGLU with a K x N weight (needs a 256-row B tile)",
                 opt.tile_cfg);
-  const int cfg = opt.tile_cfg >= 0 ? opt.tile_cfg
-                                    : choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount);
+  int cfg = opt.tile_cfg >= 0 ? opt.tile_cfg
+                              : choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount);
+  if (opt.tile_cfg < 0 && cfg == 0 && strides_conflict(s)) cfg = 4;  // same tile, 64-deep k-steps
 
   ep_plan_s* h = new (std::nothrow) ep_plan_s;
   if (!h) return fail(EP_ERR_OUT_OF_MEMORY, "host allocation failed");

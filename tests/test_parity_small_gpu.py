@@ -232,6 +232,33 @@ def test_transposed_a(dtname, layout):
                 p.free()
 
 
+@pytest.mark.parametrize("layout,ld_extra,want_cfg", [("NK", 0, 4), ("NK", 64, 0), ("KN", 0, 0)])
+def test_strided_rows_pick_deep_k_steps(layout, ld_extra, want_cfg):
+    """At a full-chip shape the planner's default is the 256x256 tile with 32-deep k-steps,
+    except for a k-contiguous B (N x K) whose row stride is a multiple of 32 KiB (here 16384
+    elements): then 64-deep k-steps.  A padded stride, or B given K x N, keeps the default.
+    Row blocks at the start, middle and end are checked against the oracle."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev = torch.device("cuda")
+    m = n = k = 4096
+    g = torch.Generator().manual_seed(5)
+    a = torch.randn(m, k, generator=g).half().to(dev)
+    if layout == "NK":
+        b = ((torch.randn(n, 16384 + ld_extra, generator=g) * k ** -0.5).half().to(dev))[:, :k]
+    else:
+        b = (torch.randn(k, n, generator=g) * k ** -0.5).half().to(dev)
+    say(f"case strided rows layout={layout} ldb={b.stride(0)} {m}x{n}x{k}")
+    p = ep.Plan(a, b, "DEFAULT", b_layout=layout)
+    assert f"tile_cfg={want_cfg} " in p.info(), p.info()
+    out, _ = p.execute()
+    torch.cuda.synchronize()
+    rows = np.r_[0:32, 2040:2072, 4064:4096]
+    b64 = f64(b)
+    assert_half(f64(out)[rows], oracle.matmul(f64(a)[rows], b64, layout), f"strided {layout}/{ld_extra}")
+    p.free()
+
+
 def test_split_k_atomic_bgrad():
     require_gpu()
     run_and_check("DRELU_BGRAD", "f16", "NK", 300, 200, 520, 0, split_k=3, bgrad_mode="atomic")
