@@ -141,12 +141,22 @@ __global__ void colsum_partial_kernel(const char* x, int64_t ldx, float* part, i
   *(f32x4*)(o + 4) = f32x4{s[4], s[5], s[6], s[7]};
 }
 
-// bgrad[n] = sum_t part[t][n], in order of t (deterministic)
+// bgrad[n] = sum_t part[t][n], in order of t (deterministic).  The loads of 8 partials are
+// issued together and then added in order, so the latency of one round trip is paid per 8
+// partials instead of per partial.
 __global__ void bgrad_reduce_kernel(const float* part, int nparts, float* bgrad, int N) {
   const int col = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (col >= N) return;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int t = 0; t < nparts; ++t) s += *(const f32x4*)(part + (int64_t)t * N + col);
+  for (int t0 = 0; t0 < nparts; t0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (t0 + u < nparts) v[u] = *(const f32x4*)(part + (int64_t)(t0 + u) * N + col);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (t0 + u < nparts) s += v[u];
+  }
   *(f32x4*)(bgrad + col) = s;
 }
 

@@ -79,13 +79,24 @@ struct Elem<T_BF16> {
   }
 };
 
+// Two floats to one word of two elements (lo in bits 0-15), rounded to nearest even: a
+// two-element vector conversion, which gfx950 does in one v_cvt_pk_{f16,bf16}_f32.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == T_F16) {
+    const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ u32x2 pack4(f32x4 v) {
-  using E = Elem<DT>;
-  u32x2 r;
-  r[0] = E::from_f32(v[0]) | (E::from_f32(v[1]) << 16);
-  r[1] = E::from_f32(v[2]) | (E::from_f32(v[3]) << 16);
-  return r;
+  return u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
 }
 
 template <int DT>
@@ -103,6 +114,15 @@ __device__ __forceinline__ f32x4 unpack4(u32x2 w) {
   v[2] = E::to_f32(w[1] & 0xffffu);
   v[3] = E::to_f32(w[1] >> 16);
   return v;
+}
+
+// a & b in one v_and_b32 the compiler cannot see through (it would turn an AND with a
+// sign-extended bit back into a compare and a select, two instructions and a hazard wait
+// where a bit-field extract and this AND are two)
+__device__ __forceinline__ uint32_t and_opaque(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // Copy of one accumulator register for VALU use.  The operand constraint keeps the
@@ -764,6 +784,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     }
 
     // ---- stores: CH staged rows per chunk, their LDS reads issued together
+    // (the lane's output address of staged row 0; staged row t is t * ldd elements further)
+    char* const dslab = (char*)p.d + ((int64_t)(srow0 + lr) * p.ldd + gcol) * 2;
     constexpr int OUTER_UNROLL = EPI == E_DRELU_BGRAD ? 2 : TR::ITERS;
 #pragma unroll OUTER_UNROLL
     for (int c0 = 0; c0 < TR::ITERS; c0 += TR::CH) {
@@ -786,13 +808,19 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 #pragma unroll
         for (int c = 0; c < TR::CH; ++c)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) vv[c][e >> 2][e & 3] = ((wd[c] >> e) & 1u) ? vv[c][e >> 2][e & 3] : 0.0f;
+          for (int e = 0; e < 8; ++e) {
+            // bit e of the word, sign-extended to all ones or zero, keeps the value or makes it
+            // +0 (the element is copied out first: a bit cast of a vector-element lvalue reads
+            // the vector's first element)
+            const uint32_t keep = (uint32_t)((int32_t)(wd[c] << (31 - e)) >> 31);
+            vv[c][e >> 2][e & 3] = __uint_as_float(and_opaque(__float_as_uint(vv[c][e >> 2][e & 3]), keep));
+          }
       }
 #pragma unroll
       for (int c = 0; c < TR::CH; ++c) {
         const int grow = srow0 + (c0 + c) * TR::RPI + lr;
         const bool ok = colok && grow < M;
-        const int64_t drow = (int64_t)grow * p.ldd;
+        char* const dptr = dslab + (int64_t)((c0 + c) * TR::RPI) * p.ldd * 2;
         if constexpr (EPI == E_DSWIGLU) {
           if (ok) {
             f32x4 dg[2], du[2];
@@ -808,7 +836,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
                 dg[h][e] = t * u[e] * (1.0f + g[e] * (1.0f - sg));
               }
             }
-            *(u32x4*)((char*)p.d + (drow + gcol) * 2) = pack8<DT>(dg[0], dg[1]);
+            *(u32x4*)dptr = pack8<DT>(dg[0], dg[1]);
             *(u32x4*)((char*)p.d2 + ((int64_t)grow * p.ldd2 + gcol) * 2) = pack8<DT>(du[0], du[1]);
           }
         } else if constexpr (EPI == E_GELU_BIAS || EPI == E_GELU_AUX_BIAS) {
@@ -820,7 +848,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
             for (int h = 0; h < 2; ++h)
 #pragma unroll
               for (int e = 0; e < 4; ++e) y[h][e] = gelu_f(vv[c][h][e]);
-            *(u32x4*)((char*)p.d + (drow + gcol) * 2) = pack8<DT>(y[0], y[1]);
+            *(u32x4*)dptr = pack8<DT>(y[0], y[1]);
           }
         } else {
           if constexpr (EPI == E_DGELU_BGRAD) {  // rows past M: aux read as 0, staged value 0
@@ -831,7 +859,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
               for (int e = 0; e < 4; ++e) vv[c][h][e] *= gelu_grad_f(pa[e]);
             }
           }
-          if (ok) *(u32x4*)((char*)p.d + (drow + gcol) * 2) = pack8<DT>(vv[c][0], vv[c][1]);
+          if (ok) *(u32x4*)dptr = pack8<DT>(vv[c][0], vv[c][1]);
           if constexpr (BGRAD) {  // rows past M are staged as 0
             colsum[0] += vv[c][0];
             colsum[1] += vv[c][1];
