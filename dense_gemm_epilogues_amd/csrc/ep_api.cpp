@@ -159,11 +159,12 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   // Relative main-loop efficiency of each configuration, measured on MI355X at full-chip
   // shapes (fp16/bf16, both B layouts, every epilog): 256x256x32 with 4 stages is the
   // fastest wherever it fills the chip.
-  static const double kEff[kNumTileCfgs] = {1.0, 0.70, 0.80, 0.80, 0.85, 0.97, 0.80, 0.82};
+  // (the register-staged configuration is chosen by pick_cfg's rule, not by this model)
+  static const double kEff[kNumTileCfgs] = {1.0, 0.70, 0.80, 0.80, 0.85, 0.97, 0.80, 0.82, 0.0};
   int best = 0;
   double best_t = 1e300;
   for (int c = 0; c < kNumTileCfgs; ++c) {
-    if (!cfg_allowed(c, dual, lay)) continue;
+    if (!cfg_allowed(c, dual, lay) || kEff[c] <= 0.0) continue;
     const int64_t bn = dual ? kTileCfgs[c].bnt / 2 : kTileCfgs[c].bnt;
     const int64_t tiles = ((m + kTileCfgs[c].bm - 1) / kTileCfgs[c].bm) * ((n + bn - 1) / bn);
     const int64_t slots = (int64_t)cus * kTileCfgs[c].occ;
@@ -179,15 +180,27 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
 
 // Rows of a k-contiguous operand whose stride is a multiple of 32 KiB fall into few L2 sets:
 // the 256 rows of one k-step evict each other.  A 32-deep k-step reads 64 bytes of each row,
-// half a 128-byte line, and the other half, read one k-step later, is fetched again.  With
-// both operands k-contiguous (B given N x K) at such strides, 65536 x 8192 x 16384 fetched
-// twice the bytes of a padded stride and ran 18 % slower; 64-deep k-steps read whole lines
-// and recover most of it.  With B given K x N only A's rows are affected and the 32-deep
-// 4-stage ring stays faster (14.75 against 15.69 ms for the same shape).
+// half a 128-byte line, and the other half, read one k-step later, is fetched again (65536 x
+// 8192 x 16384 with both operands at such strides fetched twice the bytes of a padded stride
+// and ran 18 % slower).  A 64-deep k-step reads whole lines.
 bool strides_conflict(const ep_shape* s) {
   const int64_t es = 2;  // bytes per fp16 / bf16 element
   const bool b_kc = s->b_layout == EP_B_NK && (s->ldb * es) % 32768 == 0;
   return s->k >= 4096 && b_kc;
+}
+
+// With B given N x K both operands arrive as 64-byte row pieces at 32-deep k-steps, twice
+// the address work per byte of K x N, and the loads stall in the texture addresser.  The
+// 64-deep register-staged configuration (whole 128-byte lines, loads a full k-step ahead)
+// measured faster on MI355X for every N x K shape from 1 to 16 rounds of resident tiles
+// (4096^3: 141 -> 126 us; 4096^2 x 8192: 272 -> 243 us; 16384^2 x 4096: 1.89 -> 1.84 ms), but
+// slower at 64 rounds (65536 x 16384 x 8192: 15.6 -> 16.4 ms), so larger grids keep the
+// 32-deep ring unless their strides conflict.  With B given K x N the 32-deep ring is faster.
+constexpr int kVstCfg = 8;
+int pick_cfg(const ep_shape* s, int model_cfg, int cus) {
+  if (model_cfg != 0 || s->b_layout != EP_B_NK || s->a_layout != EP_A_MK) return model_cfg;
+  const int64_t tiles = ((s->m + 255) / 256) * ((s->n + 255) / 256);
+  return (tiles <= 16LL * cus || strides_conflict(s)) ? kVstCfg : model_cfg;
 }
 
 // Split-K: how many K ranges per tile.  Only grids that leave CUs idle are split: the time
@@ -477,9 +490,10 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   if (opt.tile_cfg >= 0 && !cfg_allowed(opt.tile_cfg, kernel_dual, s->b_layout))
     return fail(EP_ERR_UNSUPPORTED, "tile_cfg %d cannot run SWIGLU with a K x N weight (needs a 256-row B tile)",
                 opt.tile_cfg);
-  int cfg = opt.tile_cfg >= 0 ? opt.tile_cfg
-                              : choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount);
-  if (opt.tile_cfg < 0 && cfg == 0 && strides_conflict(s)) cfg = 4;  // same tile, 64-deep k-steps
+  const int cfg = opt.tile_cfg >= 0
+                      ? opt.tile_cfg
+                      : pick_cfg(s, choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount),
+                                 prop.multiProcessorCount);
 
   ep_plan_s* h = new (std::nothrow) ep_plan_s;
   if (!h) return fail(EP_ERR_OUT_OF_MEMORY, "host allocation failed");

@@ -55,17 +55,20 @@ struct GemmArgs {
 //   bm  = workgroup rows; bnt = rows of the B tile held in LDS (output columns per workgroup
 //         are bnt, or bnt/2 for the dual-B SwiGLU kernel); bk = k-values per LDS stage;
 //   nst = LDS ring stages; occ = workgroups resident per CU (the kernel is compiled so that
-//         occ workgroups fit the register file, and its LDS ring fits 160 KiB / occ).
+//         occ workgroups fit the register file, and its LDS ring fits 160 KiB / occ);
+//   vst = 1: tiles go global -> registers -> LDS, one k-step ahead of the LDS ring (2 stages
+//         only); 0: global -> LDS directly.
 struct TileCfg {
-  int bm, bnt, bk, nst, occ;
+  int bm, bnt, bk, nst, occ, vst;
   const char* name;
 };
-constexpr int kNumTileCfgs = 8;
+constexpr int kNumTileCfgs = 9;
 constexpr TileCfg kTileCfgs[kNumTileCfgs] = {
-    {256, 256, 32, 4, 1, "256x256x32x4st"},   {128, 128, 64, 4, 1, "128x128x64x4st"},
-    {256, 128, 32, 4, 1, "256x128x32x4st"},   {128, 256, 32, 4, 1, "128x256x32x4st"},
-    {256, 256, 64, 2, 1, "256x256x64x2st"},   {256, 256, 32, 5, 1, "256x256x32x5st"},
-    {256, 128, 32, 3, 2, "256x128x32x3st_2wg"}, {128, 256, 32, 3, 2, "128x256x32x3st_2wg"},
+    {256, 256, 32, 4, 1, 0, "256x256x32x4st"},   {128, 128, 64, 4, 1, 0, "128x128x64x4st"},
+    {256, 128, 32, 4, 1, 0, "256x128x32x4st"},   {128, 256, 32, 4, 1, 0, "128x256x32x4st"},
+    {256, 256, 64, 2, 1, 0, "256x256x64x2st"},   {256, 256, 32, 5, 1, 0, "256x256x32x5st"},
+    {256, 128, 32, 3, 2, 0, "256x128x32x3st_2wg"}, {128, 256, 32, 3, 2, 0, "128x256x32x3st_2wg"},
+    {256, 256, 64, 2, 1, 1, "256x256x64x2st_vst"},
 };
 
 typedef void (*GemmLauncher)(const GemmArgs&, hipStream_t);

@@ -47,6 +47,7 @@ constexpr int cfg_bnt(int cfg) { return kTileCfgs[cfg].bnt; }
 constexpr int cfg_bk(int cfg) { return kTileCfgs[cfg].bk; }
 constexpr int cfg_nst(int cfg) { return kTileCfgs[cfg].nst; }
 constexpr int cfg_occ(int cfg) { return kTileCfgs[cfg].occ; }
+constexpr bool cfg_vst(int cfg) { return kTileCfgs[cfg].vst != 0; }
 
 template <int DT>
 struct Elem;
@@ -399,6 +400,37 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     for (int t = 0; t < N_DMA; ++t) dma_op(kt, As, t, kr);
   };
 
+  // Register staging (vst configurations): the same 16 bytes per lane as dma_op, loaded into
+  // registers (sreg[t]) one k-step ahead and written to the lane's 16 bytes of the slot later.
+  constexpr bool VST = cfg_vst(CFG);
+  static_assert(!VST || NST == 2, "register staging feeds a 2-stage LDS ring");
+  u32x4 sreg[VST ? N_DMA : 1];
+  auto gload = [&](int kt, int t, const KnSrc& kr) -> u32x4 {
+    const int k0 = gkt(kt) * BK;
+    if (t < A_SLOTS) {
+      const int q = t;
+      if constexpr (AKM) {
+        return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc_raw(kr.abase, kr.anum), (int)a_voff[q], 0, 0);
+      } else {
+        const uint32_t off = (k0 < a_klim[q]) ? a_voff[q] + k0 * 2 : kOOB;
+        return __builtin_amdgcn_raw_buffer_load_b128(rA, (int)off, 0, 0);
+      }
+    } else {
+      const int q = t - A_SLOTS;
+      if constexpr (BLAY == L_NK) {
+        const uint32_t off = (k0 < b_klim[q]) ? b_voff[q] + k0 * 2 : kOOB;
+        return __builtin_amdgcn_raw_buffer_load_b128(rB_nk, (int)off, 0, 0);
+      } else {
+        return __builtin_amdgcn_raw_buffer_load_b128(make_rsrc_raw(kr.base, kr.num), (int)b_voff[q], 0, 0);
+      }
+    }
+  };
+  auto lput = [&](char* As, int t) {
+    char* slot = t < A_SLOTS ? As + (wave * A_SLOTS + t) * 1024
+                             : As + TR::A_BYTES + (wave * B_SLOTS + (t - A_SLOTS)) * 1024;
+    *(u32x4*)(slot + lane * 16) = sreg[t];
+  };
+
   // fragment-read addresses
   const int hlf = lane >> 5;
   uint32_t a_rd[MB], b_rd[NB];
@@ -535,7 +567,14 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       if (g % DSTRIDE == 0) {
 #pragma unroll
         for (int d = (g / DSTRIDE) * DPER; d < (g / DSTRIDE + 1) * DPER; ++d)
-          if (d < N_DMA) dma_op(kt, dst, d, kr);
+          if (d < N_DMA) {
+            if constexpr (VST) {
+              lput(dst, d);              // k-step kt - 1 (loaded one k-step ago) into its stage
+              sreg[d] = gload(kt, d, kr);  // k-step kt into the freed register
+            } else {
+              dma_op(kt, dst, d, kr);
+            }
+          }
       }
       if constexpr (RD) {
 #pragma unroll
@@ -562,14 +601,19 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   static_assert(NST >= 2, "the ring needs at least 2 stages");
   static_assert(VMC_LOOP <= 63 && VMC_PRO <= 63, "vmcnt range");
   auto ring_barrier = [&](auto vmc_c) {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(decltype(vmc_c)::value) : "memory");
+    if constexpr (VST)  // the stage was written from registers: only LDS traffic to wait for
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(decltype(vmc_c)::value) : "memory");
   };
   // Loads for k-step kt + NST - 1 are issued during k-step kt.
   auto kstep = [&](int kt) {
     const char* cur = smem + (kt % NST) * TR::STAGE;
     const char* nxt = smem + ((kt + 1) % NST) * TR::STAGE;
     char* dst = smem + ((kt + NST - 1) % NST) * TR::STAGE;
-    const int kl = kt + NST - 1;
+    // the k-step whose loads are issued: NST - 1 ahead (register staging: one more, the
+    // registers holding k-step kt + 1 on their way to dst)
+    const int kl = VST ? kt + 2 : kt + NST - 1;
     const KnSrc kr = kn_rsrc(kl);
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) {
@@ -595,8 +639,20 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   };
 
   if constexpr (MODE != 2) {
+    if constexpr (VST) {
+      // k-step 0 through the registers into stage 0, then k-step 1 into the registers
+      const KnSrc k0 = kn_rsrc(0);
 #pragma unroll
-    for (int s = 0; s < NST - 1; ++s) issue_tile(s, smem + s * TR::STAGE);
+      for (int t = 0; t < N_DMA; ++t) sreg[t] = gload(0, t, k0);
+#pragma unroll
+      for (int t = 0; t < N_DMA; ++t) lput(smem, t);
+      const KnSrc k1 = kn_rsrc(1);
+#pragma unroll
+      for (int t = 0; t < N_DMA; ++t) sreg[t] = gload(1, t, k1);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NST - 1; ++s) issue_tile(s, smem + s * TR::STAGE);
+    }
     ring_barrier(std::integral_constant<int, VMC_PRO>{});
     __builtin_amdgcn_sched_barrier(0);
     read_frags(smem, 0, fa[0], fb[0]);

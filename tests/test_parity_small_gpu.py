@@ -156,7 +156,7 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
 
 # tile configurations 0-7 of the library; those with a 128-row B tile cannot hold the gate
 # and up sub-tiles of a K x N dual B operand
-NUM_TILE_CFGS = 8
+NUM_TILE_CFGS = 9
 BNT128_CFGS = (1, 2, 6)
 
 
@@ -232,30 +232,39 @@ def test_transposed_a(dtname, layout):
                 p.free()
 
 
-@pytest.mark.parametrize("layout,ld_extra,want_cfg", [("NK", 0, 4), ("NK", 64, 0), ("KN", 0, 0)])
-def test_strided_rows_pick_deep_k_steps(layout, ld_extra, want_cfg):
-    """At a full-chip shape the planner's default is the 256x256 tile with 32-deep k-steps,
-    except for a k-contiguous B (N x K) whose row stride is a multiple of 32 KiB (here 16384
-    elements): then 64-deep k-steps.  A padded stride, or B given K x N, keeps the default.
-    Row blocks at the start, middle and end are checked against the oracle."""
+@pytest.mark.parametrize("m,n,layout,ld_extra,want_cfg", [
+    (4096, 4096, "NK", 64, 8),      # one round of 256x256 tiles, N x K B: register-staged, 64 deep
+    (4096, 4096, "KN", 0, 0),       # K x N B: the 32-deep ring
+    (16384, 32768, "NK", 64, 0),    # 32 rounds: the 32-deep ring
+    (16384, 32768, "NK", 0, 8),     # 32 rounds, B rows 32 KiB apart: 64 deep (whole lines)
+])
+def test_planner_tile_choice(m, n, layout, ld_extra, want_cfg):
+    """The planner's default tile configuration at full-chip shapes (256 CUs), B rows 16384
+    (+ ld_extra) elements apart when B is N x K; the result is checked against the oracle on
+    sampled rows and columns."""
     require_gpu()
     import dense_gemm_epilogues_amd as ep
     dev = torch.device("cuda")
-    m = n = k = 4096
-    g = torch.Generator().manual_seed(5)
-    a = torch.randn(m, k, generator=g).half().to(dev)
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the expected choices assume 256 CUs")
+    k = 4096
+    g = torch.Generator(device=dev)
+    g.manual_seed(m + n + ld_extra)
+    a = torch.randn(m, k, device=dev, generator=g).half()
     if layout == "NK":
-        b = ((torch.randn(n, 16384 + ld_extra, generator=g) * k ** -0.5).half().to(dev))[:, :k]
+        b = (torch.randn(n, 16384 + ld_extra, device=dev, generator=g) * k ** -0.5).half()[:, :k]
     else:
-        b = (torch.randn(k, n, generator=g) * k ** -0.5).half().to(dev)
-    say(f"case strided rows layout={layout} ldb={b.stride(0)} {m}x{n}x{k}")
+        b = (torch.randn(k, n, device=dev, generator=g) * k ** -0.5).half()
+    say(f"case planner choice layout={layout} ldb={b.stride(0)} {m}x{n}x{k}")
     p = ep.Plan(a, b, "DEFAULT", b_layout=layout)
     assert f"tile_cfg={want_cfg} " in p.info(), p.info()
     out, _ = p.execute()
     torch.cuda.synchronize()
-    rows = np.r_[0:32, 2040:2072, 4064:4096]
-    b64 = f64(b)
-    assert_half(f64(out)[rows], oracle.matmul(f64(a)[rows], b64, layout), f"strided {layout}/{ld_extra}")
+    rows = torch.tensor(np.r_[0:32, m // 2 - 8:m // 2 + 24, m - 32:m], device=dev)
+    cols = torch.tensor(np.r_[0:64, n // 2:n // 2 + 64, n - 64:n], device=dev)
+    bsel = b[cols] if layout == "NK" else b[:, cols]
+    ref = oracle.matmul(f64(a[rows]), f64(bsel), layout)
+    assert_half(f64(out[rows][:, cols]), ref, f"planner {layout}/{m}x{n}/{ld_extra}")
     p.free()
 
 
