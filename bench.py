@@ -287,7 +287,8 @@ def mlp_training_step(c, steps, warmup, flush, dev):
             "step_pct_peak": round(100 * flop / (f["step_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
             "speedup_vs_unfused": round(u["step_ms"] / f["step_ms"], 4),
             "speedup_vs_torch": round(res["torch"]["step_ms"] / f["step_ms"], 4),
-            "fused_kernel_ms": {n: round(v, 4) for n, v in zip(names, f["per_ms"])}}
+            "fused_kernel_ms": {n: round(v, 4) for n, v in zip(names, f["per_ms"])},
+            "unfused_kernel_ms": {n: round(v, 4) for n, v in zip(names, u["per_ms"])}}
 
 
 def swiglu_m_sweep(steps, warmup, flush, dev, ms=(2048, 4096, 8192, 16384)):
@@ -558,7 +559,7 @@ def main():
             "speedup": round(r5["speedup"], 4)}
         torch.cuda.empty_cache()
         large["swiglu_fwd_bf16_M_sweep_H5120_I17408"] = swiglu_m_sweep(s_l, w_l, flush, dev)
-        large["swiglu_mlp_training_step_bf16_M2048_H5120_I17408"] = mlp_training_step(W.SWIGLU[4], s_l, w_l, flush, dev)
+        large["swiglu_mlp_training_step_bf16_M2048_H5120_I17408"] = mlp_training_step(W.SWIGLU[4], args.steps, args.warmup, flush, dev)
         torch.cuda.empty_cache()
         large["gelu_layer_fp16_4096x4096x4096"] = gelu_layer(W.LINEAR[2], args.steps, args.warmup, flush, dev)
         large["execute_overhead"] = execute_overhead(dev)

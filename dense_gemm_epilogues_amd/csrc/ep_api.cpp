@@ -5,6 +5,7 @@
 // configuration and allocates once; execution only enqueues kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -14,6 +15,7 @@
 #include <new>
 #include <string>
 #include <tuple>
+#include <vector>
 
 #include "ep.h"
 #include "ep_internal.hpp"
@@ -388,11 +390,15 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
       return EP_OK;
     }
   }
-  hipEvent_t e0, e1;
-  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
-    return fail(EP_ERR_HIP, "autotune: hipEventCreate failed");
-  float best_ms = 1e30f;
-  int best_cfg = -1, best_split = 1;
+  // Every candidate plan is built first and run once; then the candidates are timed in turn,
+  // kRounds rounds of one execute each, so that clock and power drift during tuning affect
+  // them alike; the median of each candidate's rounds decides.
+  struct Cand {
+    ep_handle h;
+    int cfg, split;
+    std::vector<float> ms;
+  };
+  std::vector<Cand> cands;
   for (int c = 0; c < kNumTileCfgs; ++c) {
     for (int sp : {1, 0}) {  // unsplit, then the split the shape model picks (if it splits)
       ep_options o = opt;
@@ -401,26 +407,45 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
       o.split_k = sp;
       ep_handle t = nullptr;
       if (ep_plan_ex(s, dtype, epi, io, &o, &t) != EP_OK) continue;
-      const int got_split = t->splits;
-      if (sp == 0 && got_split == 1) {  // the model does not split: same as the unsplit run
+      if (sp == 0 && t->splits == 1) {  // the model does not split: same as the unsplit run
         ep_free(t);
         continue;
       }
-      float ms = 0.f;
-      bool ok = ep_execute(t, nullptr) == EP_OK && hipEventRecord(e0, nullptr) == hipSuccess;
-      for (int r = 0; ok && r < 3; ++r) ok = ep_execute(t, nullptr) == EP_OK;
-      ok = ok && hipEventRecord(e1, nullptr) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
-           hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
-      ep_free(t);
-      if (ok && ms < best_ms) {
-        best_ms = ms;
-        best_cfg = c;
-        best_split = got_split;
-      }
+      cands.push_back({t, c, t->splits, {}});
     }
   }
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
+  constexpr int kRounds = 5;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  bool ok = hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess;
+  for (auto& cd : cands) ok = ok && ep_execute(cd.h, nullptr) == EP_OK;
+  ok = ok && hipDeviceSynchronize() == hipSuccess;
+  for (int r = 0; ok && r < kRounds; ++r) {
+    for (auto& cd : cands) {
+      float ms = 0.f;
+      ok = hipEventRecord(e0, nullptr) == hipSuccess && ep_execute(cd.h, nullptr) == EP_OK &&
+           hipEventRecord(e1, nullptr) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+           hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+      if (!ok) break;
+      cd.ms.push_back(ms);
+    }
+  }
+  float best_ms = 1e30f;
+  int best_cfg = -1, best_split = 1;
+  for (auto& cd : cands) {
+    if (ok && (int)cd.ms.size() == kRounds) {
+      std::sort(cd.ms.begin(), cd.ms.end());
+      const float med = cd.ms[kRounds / 2];
+      if (med < best_ms) {
+        best_ms = med;
+        best_cfg = cd.cfg;
+        best_split = cd.split;
+      }
+    }
+    ep_free(cd.h);
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (!ok) return fail(EP_ERR_HIP, "autotune: timing a candidate failed");
   if (best_cfg < 0) return fail(EP_ERR_INTERNAL, "autotune: no candidate configuration ran");
   {
     std::lock_guard<std::mutex> lk(g_tune_mu);
