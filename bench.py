@@ -15,7 +15,8 @@ reference.
 
 Timing: HIP events on the stream the kernels run on, one pair around each step; a 512 MiB
 buffer is overwritten between steps (outside the events) so no step starts with its
-operands in L2 / Infinity Cache.  An event record costs about 6 us of GPU time before the
+operands in L2 / Infinity Cache.  Compared variants (fused, unfused, torch) alternate step
+by step, so clock and power drift over the run reach each of them alike.  An event record costs about 6 us of GPU time before the
 next launch, so per-kernel durations (the roofline's average launch) come from launches run
 back to back between a single event pair.  Inputs are seeded synthetic tensors generated on the
 device.  The CPU oracle (float64 numpy) is timed on this host as a baseline only.
@@ -85,32 +86,38 @@ def flush_cache(buf):
         buf.zero_()
 
 
-def run_steps(fns, steps, warmup, flush, per_fn=True):
-    """fns: list of callables forming one step.  Returns per-step ms and per-fn ms lists.
-
-    Each event record costs about 6 us of GPU time before the next launch on MI355X, so the
-    per-function split (an event after every function) inflates the step; per_fn=False times
-    each step with a single event pair (per-fn list then empty)."""
+def run_interleaved(variants, steps, warmup, flush, per_fn=False):
+    """variants: {name: [fns forming one step]}.  The variants' steps alternate (a flushed
+    step of each in turn), so that clock and power drift over the run reach every variant
+    alike.  Returns {name: (step_ms list, per-fn lists or [])}."""
+    names = list(variants)
     for _ in range(warmup):
-        flush_cache(flush)
-        for f in fns:
-            f()
+        for nm in names:
+            flush_cache(flush)
+            for f in variants[nm]:
+                f()
     torch.cuda.synchronize()
-    n = len(fns) if per_fn else 1
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
-    for s in range(steps):
-        flush_cache(flush)
-        marks[s][0].record()
-        for i, f in enumerate(fns):
-            f()
-            if per_fn:
-                marks[s][i + 1].record()
-        if not per_fn:
-            marks[s][1].record()
+    marks = {nm: [[torch.cuda.Event(enable_timing=True) for _ in range((len(variants[nm]) if per_fn else 1) + 1)]
+                  for _ in range(steps)] for nm in names}
+    for st in range(steps):
+        for nm in names:
+            flush_cache(flush)
+            m = marks[nm][st]
+            m[0].record()
+            for i, f in enumerate(variants[nm]):
+                f()
+                if per_fn:
+                    m[i + 1].record()
+            if not per_fn:
+                m[1].record()
     torch.cuda.synchronize()
-    step_ms = [m[0].elapsed_time(m[n]) for m in marks]
-    per = [[m[i].elapsed_time(m[i + 1]) for m in marks] for i in range(n)] if per_fn else []
-    return step_ms, per
+    out = {}
+    for nm in names:
+        ms = marks[nm]
+        n = len(ms[0]) - 1
+        out[nm] = ([m[0].elapsed_time(m[n]) for m in ms],
+                   [[m[i].elapsed_time(m[i + 1]) for m in ms] for i in range(n)] if per_fn else [])
+    return out
 
 
 def launch_avg_ms(fn, reps=20):
@@ -142,16 +149,14 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True):
     else:
         mask_bwd = None
     res = {}
+    plans = {}
     for path in (["fused", "unfused"] if with_unfused else ["fused"]):
         pf = ep.Plan(x, w, "RELU_AUX_BIAS", {"bias": bias}, b_layout="KN", path=path)
         y, aux = pf.execute()
         mb = aux["relu_aux"] if mask_bwd is None else mask_bwd
         pb = ep.Plan(dy, w, "DRELU_BGRAD", {"relu_aux": mb}, b_layout="NK", path=path)
-        step_ms, _ = run_steps([pf.execute, pb.execute], steps, warmup, flush, per_fn=False)
-        res[path] = {"step_ms": float(np.mean(step_ms)), "fwd_ms": launch_avg_ms(pf.execute),
-                     "bwd_ms": launch_avg_ms(pb.execute), "fwd_info": pf.info(), "bwd_info": pb.info()}
-        pf.free()
-        pb.free()
+        plans[path] = (pf, pb)
+    variants = {path: [pf.execute, pb.execute] for path, (pf, pb) in plans.items()}
     if with_unfused:
         # vendor-library reference: hipBLASLt GEMMs + torch elementwise, byte mask instead of bits
         if mask_bwd is not None:  # the separate backward mask (M x K bits) as bytes, unpacked untimed
@@ -159,12 +164,22 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True):
             keep_b = ((mask_bwd.unsqueeze(-1) >> bits) & 1).to(torch.bool).reshape(m, k)
 
         def torch_step():
-            y = torch.addmm(bias, x, w).relu_()
-            keep = y > 0
+            yy = torch.addmm(bias, x, w).relu_()
+            keep = yy > 0
             (dy @ w.t()) * (keep if mask_bwd is None else keep_b)
             dy.float().sum(0)
-        step_ms, _ = run_steps([torch_step], steps, warmup, flush)
-        res["torch"] = {"step_ms": float(np.mean(step_ms))}
+        variants["torch"] = [torch_step]
+    timed = run_interleaved(variants, steps, warmup, flush)
+    for path, (pf, pb) in plans.items():
+        st = timed[path][0]
+        res[path] = {"step_ms": float(np.mean(st)), "step_ms_median": float(np.median(st)),
+                     "step_ms_min": float(np.min(st)), "step_ms_max": float(np.max(st)),
+                     "fwd_ms": launch_avg_ms(pf.execute), "bwd_ms": launch_avg_ms(pb.execute),
+                     "fwd_info": pf.info(), "bwd_info": pb.info()}
+        pf.free()
+        pb.free()
+    if with_unfused:
+        res["torch"] = {"step_ms": float(np.mean(timed["torch"][0]))}
     flop = 2.0 * m * n * k
     out = {"flop_per_gemm": flop, "fused": res["fused"]}
     f = res["fused"]
@@ -190,14 +205,17 @@ def gelu_layer(c, steps, warmup, flush, dev):
     import workloads as W
     inp = W.linear_inputs(c, device=dev)
     x, w, bias, dy = inp["x"], inp["w"], inp["bias"], inp["dy"]
-    res = {}
+    plans = {}
     for path in ("fused", "unfused"):
         pf = ep.Plan(x, w, "GELU_AUX_BIAS", {"bias": bias}, b_layout="KN", path=path)
         _, aux = pf.execute()
         pb = ep.Plan(dy, w, "DGELU_BGRAD", {"gelu_aux": aux["gelu_aux"]}, b_layout="NK", path=path)
-        step_ms, per = run_steps([pf.execute, pb.execute], steps, warmup, flush)
-        res[path] = {"step_ms": float(np.mean(step_ms)), "fwd_ms": float(np.mean(per[0])),
-                     "bwd_ms": float(np.mean(per[1]))}
+        plans[path] = (pf, pb)
+    timed = run_interleaved({p_: [pf.execute, pb.execute] for p_, (pf, pb) in plans.items()}, steps, warmup, flush)
+    res = {}
+    for path, (pf, pb) in plans.items():
+        res[path] = {"step_ms": float(np.mean(timed[path][0])), "fwd_ms": launch_avg_ms(pf.execute),
+                     "bwd_ms": launch_avg_ms(pb.execute)}
         pf.free()
         pb.free()
     flop = 2.0 * c.m * c.n * c.k
@@ -216,14 +234,17 @@ def swiglu_fwd(c, steps, warmup, flush, dev):
     inp = W.swiglu_inputs(c, device=dev)
     x, wg, wu, wd = inp["x"], inp["wg"], inp["wu"], inp["wd"]
     m, h, i = c.m, c.h, c.i
-    res = {}
+    plans = {}
     for path in ("fused", "unfused"):
         ps = ep.Plan(x, wg, "SWIGLU", {"b2": wu}, b_layout="NK", path=path)
         hh, _ = ps.execute()
         pd = ep.Plan(hh, wd, "DEFAULT", b_layout="NK")
-        step_ms, per = run_steps([ps.execute, pd.execute], steps, warmup, flush)
-        res[path] = {"step_ms": float(np.mean(step_ms)), "swiglu_ms": float(np.mean(per[0])),
-                     "down_ms": float(np.mean(per[1])), "swiglu_info": ps.info(), "down_info": pd.info()}
+        plans[path] = (ps, pd)
+    timed = run_interleaved({p_: [ps.execute, pd.execute] for p_, (ps, pd) in plans.items()}, steps, warmup, flush)
+    res = {}
+    for path, (ps, pd) in plans.items():
+        res[path] = {"step_ms": float(np.mean(timed[path][0])), "swiglu_ms": launch_avg_ms(ps.execute),
+                     "down_ms": launch_avg_ms(pd.execute), "swiglu_info": ps.info(), "down_info": pd.info()}
         ps.free()
         pd.free()
     f, u = res["fused"], res["unfused"]
@@ -239,12 +260,12 @@ def dswiglu_bwd(c, steps, warmup, flush, dev):
     import dense_gemm_epilogues_amd as ep
     import workloads as W
     inp = W.dswiglu_inputs(c, device=dev)
+    plans = {path: ep.Plan(inp["dout"], inp["wd"], "DSWIGLU", {"gate": inp["gate"], "up": inp["up"]},
+                           b_layout="KN", path=path) for path in ("fused", "unfused")}
+    timed = run_interleaved({p_: [p.execute] for p_, p in plans.items()}, steps, warmup, flush)
     res = {}
-    for path in ("fused", "unfused"):
-        p = ep.Plan(inp["dout"], inp["wd"], "DSWIGLU", {"gate": inp["gate"], "up": inp["up"]},
-                    b_layout="KN", path=path)
-        step_ms, per = run_steps([p.execute], steps, warmup, flush)
-        res[path] = {"ms": float(np.mean(step_ms)), "info": p.info()}
+    for path, p in plans.items():
+        res[path] = {"ms": float(np.mean(timed[path][0])), "info": p.info()}
         p.free()
     flop = 2.0 * c.m * c.h * c.i
     f, u = res["fused"], res["unfused"]
@@ -259,7 +280,9 @@ def mlp_training_step(c, steps, warmup, flush, dev):
                [dWg; dWu] = [d_gate | d_up]^T x and dWd = dout^T h (transposed-A GEMMs).
     The fused path runs 6 kernels; the unfused path replaces SWIGLU_AUX and DSWIGLU by
     their GEMM + elementwise sequences.  torch (hipBLASLt GEMMs and elementwise ops) runs the
-    same step as a vendor-library reference.  FLOP per step: 18 M H I."""
+    same step as a vendor-library reference.  The three alternate step by step, each step
+    timed with an event after every kernel (about 6 us each, alike for all).  FLOP per step:
+    18 M H I."""
     import dense_gemm_epilogues_amd as ep
     import workloads as W
     inp = W.swiglu_inputs(c, device=dev)
@@ -268,7 +291,7 @@ def mlp_training_step(c, steps, warmup, flush, dev):
     w_gu = torch.cat([wg, wu], dim=0).contiguous()
     dout = W.randn((m, hd), W.seed_of(c.cfg, 6), 1.0, torch.bfloat16, dev)
     dgu = torch.empty((m, 2 * idim), dtype=torch.bfloat16, device=dev)
-    res = {}
+    plans = {}
     for path in ("fused", "unfused"):
         ps = ep.Plan(x, w_gu[:idim], "SWIGLU_AUX", {"b2": w_gu[idim:]}, b_layout="NK", path=path)
         h, aux = ps.execute()
@@ -279,11 +302,7 @@ def mlp_training_step(c, steps, warmup, flush, dev):
         pdx = ep.Plan(dgu, w_gu, "DEFAULT", b_layout="KN")
         pwgu = ep.Plan(dgu, x, "DEFAULT", b_layout="KN", a_layout="KM")
         pwd = ep.Plan(dout, h, "DEFAULT", b_layout="KN", a_layout="KM")
-        fns = [ps.execute, pd.execute, pds.execute, pdx.execute, pwgu.execute, pwd.execute]
-        step_ms, per = run_steps(fns, steps, warmup, flush)
-        res[path] = {"step_ms": float(np.mean(step_ms)), "per_ms": [float(np.mean(v)) for v in per]}
-        for p in (ps, pd, pds, pdx, pwgu, pwd):
-            p.free()
+        plans[path] = (ps, pd, pds, pdx, pwgu, pwd)
     # vendor-library reference: the same step with torch ops (GEMMs via hipBLASLt)
     wgt, wut, wdt = wg.t(), wu.t(), wd.t()
 
@@ -302,8 +321,16 @@ def mlp_training_step(c, steps, warmup, flush, dev):
         dg.t() @ x
         du.t() @ x
         dout.t() @ hh
-    step_ms, _ = run_steps([torch_step], steps, warmup, flush)
-    res["torch"] = {"step_ms": float(np.mean(step_ms))}
+    variants = {path: [p_.execute for p_ in pl] for path, pl in plans.items()}
+    variants["torch"] = [torch_step]
+    timed = run_interleaved(variants, steps, warmup, flush, per_fn=True)
+    res = {}
+    for path, pl in plans.items():
+        res[path] = {"step_ms": float(np.mean(timed[path][0])),
+                     "per_ms": [float(np.mean(v)) for v in timed[path][1]]}
+        for p_ in pl:
+            p_.free()
+    res["torch"] = {"step_ms": float(np.mean(timed["torch"][0]))}
     flop = 18.0 * m * hd * idim
     names = ["swiglu_aux_fwd", "down_gemm", "dswiglu", "dx_gemm_K2I", "dw_gate_up_gemm_AKM", "dw_down_gemm_AKM"]
     f, u = res["fused"], res["unfused"]
@@ -327,12 +354,12 @@ def swiglu_m_sweep(steps, warmup, flush, dev, ms=(2048, 4096, 8192, 16384)):
     out = {}
     for m in ms:
         inp = W.swiglu_inputs(c, device=dev, m=m)
-        res = {}
-        for path in ("fused", "unfused"):
-            ps = ep.Plan(inp["x"], inp["wg"], "SWIGLU", {"b2": inp["wu"]}, b_layout="NK", path=path)
-            step_ms, _ = run_steps([ps.execute], steps, warmup, flush)
-            res[path] = float(np.mean(step_ms))
-            ps.free()
+        plans = {path: ep.Plan(inp["x"], inp["wg"], "SWIGLU", {"b2": inp["wu"]}, b_layout="NK", path=path)
+                 for path in ("fused", "unfused")}
+        timed = run_interleaved({p_: [p.execute] for p_, p in plans.items()}, steps, warmup, flush)
+        res = {path: float(np.mean(timed[path][0])) for path in plans}
+        for p in plans.values():
+            p.free()
         tf = 4.0 * m * c.h * c.i / (res["fused"] * 1e-3) / 1e12
         out[f"M{m}"] = {"fused_ms": round(res["fused"], 4), "unfused_ms": round(res["unfused"], 4),
                         "fused_tflops": round(tf, 1), "pct_peak": round(100 * tf / PEAK_F16_TFLOPS, 2),
@@ -356,14 +383,14 @@ def autotune_vs_model(steps, warmup, flush, dev):
     cases = {"square_fwd_relu_aux_bias": (li["x"], li["w"], "RELU_AUX_BIAS", {"bias": li["bias"]}, "KN"),
              "swiglu_down_gemm": (h, si["wd"], "DEFAULT", {}, "NK")}
     for name, (a, b, epi, ins, lay) in cases.items():
+        plans = {"model": ep.Plan(a, b, epi, ins, b_layout=lay),
+                 "tuned": ep.Plan(a, b, epi, ins, b_layout=lay, autotune=True)}
+        timed = run_interleaved({k: [p.execute] for k, p in plans.items()}, steps, warmup, flush)
         r = {}
-        for tuned in (False, True):
-            p = ep.Plan(a, b, epi, ins, b_layout=lay, autotune=tuned)
-            step_ms, _ = run_steps([p.execute], steps, warmup, flush)
+        for k, p in plans.items():
             info = p.info()
-            r["tuned" if tuned else "model"] = {
-                "ms": round(float(np.mean(step_ms)), 4),
-                "tile": info.split("tile=")[1].split()[0], "splits": int(info.split("splits=")[1].split()[0])}
+            r[k] = {"ms": round(float(np.mean(timed[k][0])), 4),
+                    "tile": info.split("tile=")[1].split()[0], "splits": int(info.split("splits=")[1].split()[0])}
             p.free()
         out[name] = r
     return out
@@ -536,6 +563,8 @@ def main():
                                "(X 4096x4096 . W 4096x4096 + bias) then fused DRELU_BGRAD backward "
                                "(dY . W^T masked by the forward relu_aux, + bgrad)",
                    "m": c2.m, "n": c2.n, "k": c2.k, "cache": "flushed between steps" if flush is not None else "warm"},
+        "ms_per_step_median": round(f2["step_ms_median"], 5),
+        "ms_per_step_min": round(f2["step_ms_min"], 5), "ms_per_step_max": round(f2["step_ms_max"], 5),
         "pct_peak": round(100.0 * f2["tflops_step"] / PEAK_F16_TFLOPS, 2),
         "speedup_vs_unfused": round(r2["speedup_step"], 4),
         "unfused_ms_per_step": round(r2["unfused"]["step_ms"], 5),

@@ -46,57 +46,83 @@ __device__ __forceinline__ float sigmoid_f(float t) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * t));
 }
 
-// groups of 8 consecutive columns; N % 8 == 0
+// Row-tiled launch shape shared by the elementwise kernels: blockIdx.y walks rows (grid-stride
+// past 65535), blockIdx.x covers a row's 8-column groups, kGroups groups per thread, kEwThreads
+// apart (each thread loads all of its groups before using any).  No integer division.
+constexpr int kEwThreads = 256;
+constexpr int kGroups = 2;
+
+__device__ __forceinline__ int group_of(int u) {
+  return (blockIdx.x * kGroups + u) * kEwThreads + threadIdx.x;
+}
+
 template <int DT>
 __global__ void bias_add_kernel(char* z, int64_t ldz, const char* bias, int M, int N) {
   const int gpr = N / 8;
-  const int64_t total = (int64_t)M * gpr;
-  for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < total;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = g / gpr;
-    const int col = (int)(g - row * gpr) * 8;
-    u32x4* p = (u32x4*)(z + (row * ldz + col) * 2);
-    float f[8], b[8];
-    unpack8<DT>(*p, f);
-    unpack8<DT>(*(const u32x4*)(bias + (int64_t)col * 2), b);
+  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+    char* zr = z + (int64_t)row * ldz * 2;
+    u32x4 w[kGroups], bw[kGroups];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] += b[e];
-    *p = pack8<DT>(f);
+    for (int u = 0; u < kGroups; ++u) {
+      const int g = group_of(u);
+      if (g < gpr) {
+        w[u] = *(const u32x4*)(zr + g * 16);
+        bw[u] = *(const u32x4*)(bias + g * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+      const int g = group_of(u);
+      if (g < gpr) {
+        float f[8], b[8];
+        unpack8<DT>(w[u], f);
+        unpack8<DT>(bw[u], b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] += b[e];
+        *(u32x4*)(zr + g * 16) = pack8<DT>(f);
+      }
+    }
   }
 }
 
 // Y = relu(Z); with_mask: also the relu_aux words.  One thread per 8 columns; the 4 threads
-// of a 32-column word combine their bytes with lane shuffles.  Block = 256 threads, and a
-// row's groups are laid out so that a word's 4 threads are consecutive lanes.
+// of a 32-column word are consecutive lanes (kEwThreads is a multiple of 4) and combine their
+// bytes with lane shuffles.  Groups run to a whole number of words per row (gpr = 4 nw).
 template <int DT>
 __global__ void relu_pack_kernel(const char* z, int64_t ldz, char* y, int64_t ldy, uint32_t* aux,
                                  int64_t ld_aux, int M, int N, int with_mask) {
   const int nw = (N + 31) / 32;
-  const int gpr = nw * 4;  // 8-column groups per row, padded to whole words
-  const int64_t total = (int64_t)M * gpr;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;  // multiple of 4
-  for (int64_t g0 = blockIdx.x * (int64_t)blockDim.x; g0 < total; g0 += stride) {
-    const int64_t g = g0 + threadIdx.x;
-    const bool valid = g < total;
-    const int64_t row = valid ? g / gpr : 0;
-    const int col = valid ? (int)(g - row * gpr) * 8 : N;
-    uint32_t byte = 0;
-    if (valid && col < N) {
-      float f[8];
-      unpack8<DT>(*(const u32x4*)(z + (row * ldz + col) * 2), f);
+  const int gpr = nw * 4;
+  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+    const char* zr = z + (int64_t)row * ldz * 2;
+    char* yr = y + (int64_t)row * ldy * 2;
+    u32x4 w[kGroups];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool pr = f[e] > 0.0f;
-        byte |= (pr ? 1u : 0u) << e;
-        f[e] = pr ? f[e] : 0.0f;
-      }
-      *(u32x4*)(y + (row * ldy + col) * 2) = pack8<DT>(f);
+    for (int u = 0; u < kGroups; ++u) {
+      const int g = group_of(u);
+      if (g < gpr && g * 8 < N) w[u] = *(const u32x4*)(zr + g * 16);
     }
-    if (with_mask) {
-      uint32_t w = byte << (8 * (threadIdx.x & 3));
-      w |= (uint32_t)__shfl_xor((int)w, 1);
-      w |= (uint32_t)__shfl_xor((int)w, 2);
-      if (valid && (threadIdx.x & 3) == 0) aux[row * ld_aux + (col >> 5)] = w;
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+      const int g = group_of(u);
+      uint32_t byte = 0;
+      if (g < gpr && g * 8 < N) {
+        float f[8];
+        unpack8<DT>(w[u], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool pr = f[e] > 0.0f;
+          byte |= (pr ? 1u : 0u) << e;
+          f[e] = pr ? f[e] : 0.0f;
+        }
+        *(u32x4*)(yr + g * 16) = pack8<DT>(f);
+      }
+      if (with_mask) {  // every lane takes part in the shuffles
+        uint32_t mw = byte << (8 * (threadIdx.x & 3));
+        mw |= (uint32_t)__shfl_xor((int)mw, 1);
+        mw |= (uint32_t)__shfl_xor((int)mw, 2);
+        if (g < gpr && (threadIdx.x & 3) == 0) aux[(int64_t)row * ld_aux + (g >> 2)] = mw;
+      }
     }
   }
 }
@@ -105,24 +131,38 @@ template <int DT>
 __global__ void mask_apply_kernel(const char* gsrc, int64_t ldg, const uint32_t* aux, int64_t ld_aux,
                                   char* dx, int64_t lddx, int M, int N) {
   const int gpr = N / 8;
-  const int64_t total = (int64_t)M * gpr;
-  for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < total;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = g / gpr;
-    const int col = (int)(g - row * gpr) * 8;
-    const uint32_t bits = aux[row * ld_aux + (col >> 5)] >> (col & 31);
-    u32x4 w = *(const u32x4*)(gsrc + (row * ldg + col) * 2);
+  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+    const char* gr = gsrc + (int64_t)row * ldg * 2;
+    const uint32_t* ar = aux + (int64_t)row * ld_aux;
+    u32x4 w[kGroups];
+    uint32_t mw[kGroups];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = ((bits >> (2 * q)) & 1u) ? 0x0000ffffu : 0u;
-      const uint32_t hi = ((bits >> (2 * q + 1)) & 1u) ? 0xffff0000u : 0u;
-      w[q] &= lo | hi;  // masked-out elements become +0
+    for (int u = 0; u < kGroups; ++u) {
+      const int g = group_of(u);
+      if (g < gpr) {
+        w[u] = *(const u32x4*)(gr + g * 16);
+        mw[u] = ar[g >> 2];
+      }
     }
-    *(u32x4*)(dx + (row * lddx + col) * 2) = w;
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+      const int g = group_of(u);
+      if (g < gpr) {
+        const uint32_t bits = mw[u] >> ((g & 3) * 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = ((bits >> (2 * q)) & 1u) ? 0x0000ffffu : 0u;
+          const uint32_t hi = ((bits >> (2 * q + 1)) & 1u) ? 0xffff0000u : 0u;
+          w[u][q] &= lo | hi;  // masked-out elements become +0
+        }
+        *(u32x4*)(dx + (int64_t)row * lddx * 2 + g * 16) = w[u];
+      }
+    }
   }
 }
 
-// part[blockIdx.y][col] = sum of rows [y*rpb, (y+1)*rpb) of column col; one thread per 8 cols
+// part[blockIdx.y][col] = sum of rows [y*rpb, (y+1)*rpb) of column col, in row order; one
+// thread per 8 columns, 8 rows loaded at a time and then added in order
 template <int DT>
 __global__ void colsum_partial_kernel(const char* x, int64_t ldx, float* part, int M, int N, int rpb) {
   const int col = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
@@ -130,11 +170,20 @@ __global__ void colsum_partial_kernel(const char* x, int64_t ldx, float* part, i
   const int r0 = blockIdx.y * rpb;
   const int r1 = min(M, r0 + rpb);
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r = r0; r < r1; ++r) {
-    float f[8];
-    unpack8<DT>(*(const u32x4*)(x + ((int64_t)r * ldx + col) * 2), f);
+  for (int rb = r0; rb < r1; rb += 8) {
+    u32x4 w[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] += f[e];
+    for (int u = 0; u < 8; ++u)
+      if (rb + u < r1) w[u] = *(const u32x4*)(x + ((int64_t)(rb + u) * ldx + col) * 2);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (rb + u < r1) {
+        float f[8];
+        unpack8<DT>(w[u], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += f[e];
+      }
+    }
   }
   float* o = part + (int64_t)blockIdx.y * N + col;
   *(f32x4*)o = f32x4{s[0], s[1], s[2], s[3]};
@@ -168,17 +217,29 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
 template <int DT>
 __global__ void silu_mul_kernel(const char* g, const char* u, int64_t ldgu, char* h, int64_t ldh, int M, int N) {
   const int gpr = N / 8;
-  const int64_t total = (int64_t)M * gpr;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = i / gpr;
-    const int col = (int)(i - row * gpr) * 8;
-    float fg[8], fu[8];
-    unpack8<DT>(*(const u32x4*)(g + (row * ldgu + col) * 2), fg);
-    unpack8<DT>(*(const u32x4*)(u + (row * ldgu + col) * 2), fu);
+  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+    const int64_t ro = (int64_t)row * ldgu * 2;
+    u32x4 wg[kGroups], wu[kGroups];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) fg[e] = fg[e] * sigmoid_f(fg[e]) * fu[e];
-    *(u32x4*)(h + (row * ldh + col) * 2) = pack8<DT>(fg);
+    for (int q = 0; q < kGroups; ++q) {
+      const int c = group_of(q);
+      if (c < gpr) {
+        wg[q] = *(const u32x4*)(g + ro + c * 16);
+        wu[q] = *(const u32x4*)(u + ro + c * 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      const int c = group_of(q);
+      if (c < gpr) {
+        float fg[8], fu[8];
+        unpack8<DT>(wg[q], fg);
+        unpack8<DT>(wu[q], fu);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fg[e] = fg[e] * sigmoid_f(fg[e]) * fu[e];
+        *(u32x4*)(h + (int64_t)row * ldh * 2 + c * 16) = pack8<DT>(fg);
+      }
+    }
   }
 }
 
@@ -186,44 +247,63 @@ template <int DT>
 __global__ void dswiglu_kernel(const char* dh, int64_t lddh, const char* gate, const char* up, int64_t ld_gu,
                                char* dg, int64_t lddg, char* du, int64_t lddu, int M, int N) {
   const int gpr = N / 8;
-  const int64_t total = (int64_t)M * gpr;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = i / gpr;
-    const int col = (int)(i - row * gpr) * 8;
-    float fd[8], fg[8], fu[8], og[8], ou[8];
-    unpack8<DT>(*(const u32x4*)(dh + (row * lddh + col) * 2), fd);
-    unpack8<DT>(*(const u32x4*)(gate + (row * ld_gu + col) * 2), fg);
-    unpack8<DT>(*(const u32x4*)(up + (row * ld_gu + col) * 2), fu);
+  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+    u32x4 wd[kGroups], wg[kGroups], wu[kGroups];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float s = sigmoid_f(fg[e]);
-      const float t = fd[e] * s;
-      ou[e] = t * fg[e];
-      og[e] = t * fu[e] * (1.0f + fg[e] * (1.0f - s));
+    for (int q = 0; q < kGroups; ++q) {
+      const int c = group_of(q);
+      if (c < gpr) {
+        wd[q] = *(const u32x4*)(dh + (int64_t)row * lddh * 2 + c * 16);
+        wg[q] = *(const u32x4*)(gate + (int64_t)row * ld_gu * 2 + c * 16);
+        wu[q] = *(const u32x4*)(up + (int64_t)row * ld_gu * 2 + c * 16);
+      }
     }
-    *(u32x4*)(dg + (row * lddg + col) * 2) = pack8<DT>(og);
-    *(u32x4*)(du + (row * lddu + col) * 2) = pack8<DT>(ou);
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      const int c = group_of(q);
+      if (c < gpr) {
+        float fd[8], fg[8], fu[8], og[8], ou[8];
+        unpack8<DT>(wd[q], fd);
+        unpack8<DT>(wg[q], fg);
+        unpack8<DT>(wu[q], fu);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sg = sigmoid_f(fg[e]);
+          const float t = fd[e] * sg;
+          ou[e] = t * fg[e];
+          og[e] = t * fu[e] * (1.0f + fg[e] * (1.0f - sg));
+        }
+        *(u32x4*)(dg + (int64_t)row * lddg * 2 + c * 16) = pack8<DT>(og);
+        *(u32x4*)(du + (int64_t)row * lddu * 2 + c * 16) = pack8<DT>(ou);
+      }
+    }
   }
 }
-
 
 // unfused GELU forward, in place: aux = z (when aux is given), z = gelu(z)
 template <int DT>
 __global__ void gelu_apply_kernel(char* z, int64_t ldz, char* aux, int64_t ld_aux, int M, int N) {
   const int gpr = N / 8;
-  const int64_t total = (int64_t)M * gpr;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = i / gpr;
-    const int col = (int)(i - row * gpr) * 8;
-    const u32x4 raw = *(const u32x4*)(z + (row * ldz + col) * 2);
-    if (aux) *(u32x4*)(aux + (row * ld_aux + col) * 2) = raw;
-    float f[8];
-    unpack8<DT>(raw, f);
+  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+    char* zr = z + (int64_t)row * ldz * 2;
+    u32x4 w[kGroups];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = gelu_f(f[e]);
-    *(u32x4*)(z + (row * ldz + col) * 2) = pack8<DT>(f);
+    for (int q = 0; q < kGroups; ++q) {
+      const int c = group_of(q);
+      if (c < gpr) w[q] = *(const u32x4*)(zr + c * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      const int c = group_of(q);
+      if (c < gpr) {
+        if (aux) *(u32x4*)(aux + (int64_t)row * ld_aux * 2 + c * 16) = w[q];
+        float f[8];
+        unpack8<DT>(w[q], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = gelu_f(f[e]);
+        *(u32x4*)(zr + c * 16) = pack8<DT>(f);
+      }
+    }
   }
 }
 
@@ -231,26 +311,42 @@ __global__ void gelu_apply_kernel(char* z, int64_t ldz, char* aux, int64_t ld_au
 template <int DT>
 __global__ void dgelu_apply_kernel(char* g, int64_t ldg, const char* aux, int64_t ld_aux, int M, int N) {
   const int gpr = N / 8;
-  const int64_t total = (int64_t)M * gpr;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = i / gpr;
-    const int col = (int)(i - row * gpr) * 8;
-    float fg[8], fa[8];
-    unpack8<DT>(*(const u32x4*)(g + (row * ldg + col) * 2), fg);
-    unpack8<DT>(*(const u32x4*)(aux + (row * ld_aux + col) * 2), fa);
+  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+    char* gr = g + (int64_t)row * ldg * 2;
+    u32x4 wg[kGroups], wa[kGroups];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) fg[e] *= gelu_grad_f(fa[e]);
-    *(u32x4*)(g + (row * ldg + col) * 2) = pack8<DT>(fg);
+    for (int q = 0; q < kGroups; ++q) {
+      const int c = group_of(q);
+      if (c < gpr) {
+        wg[q] = *(const u32x4*)(gr + c * 16);
+        wa[q] = *(const u32x4*)(aux + (int64_t)row * ld_aux * 2 + c * 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      const int c = group_of(q);
+      if (c < gpr) {
+        float fg[8], fa[8];
+        unpack8<DT>(wg[q], fg);
+        unpack8<DT>(wa[q], fa);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fg[e] *= gelu_grad_f(fa[e]);
+        *(u32x4*)(gr + c * 16) = pack8<DT>(fg);
+      }
+    }
   }
 }
 
-constexpr int kEwThreads = 256;
-
 inline int ew_blocks(int64_t work) {
-  // enough resident waves to saturate HBM (256 CUs x 8 blocks), capped by the work
+  // grid-stride kernels (fill, bgrad reduction): enough resident waves to saturate HBM
   int64_t b = (work + kEwThreads - 1) / kEwThreads;
   return (int)(b < 2048 ? (b < 1 ? 1 : b) : 2048);
+}
+
+// row-tiled grid for `gpr` 8-column groups per row
+inline dim3 row_grid(int M, int gpr) {
+  const int gx = (gpr + kEwThreads * kGroups - 1) / (kEwThreads * kGroups);
+  return dim3(gx < 1 ? 1 : gx, M < 65535 ? (M < 1 ? 1 : M) : 65535);
 }
 
 }  // namespace
@@ -267,24 +363,21 @@ inline int ew_blocks(int64_t work) {
   } while (0)
 
 hipError_t launch_bias_add(int dtype, void* z, int64_t ldz, const void* bias, int M, int N, hipStream_t s) {
-  const int nb = ew_blocks((int64_t)M * (N / 8));
-  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(bias_add_kernel<DTV>, dim3(nb), dim3(kEwThreads), 0, s, (char*)z, ldz,
+  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(bias_add_kernel<DTV>, row_grid(M, N / 8), dim3(kEwThreads), 0, s, (char*)z, ldz,
                                            (const char*)bias, M, N));
   return hipGetLastError();
 }
 
 hipError_t launch_relu_pack(int dtype, const void* z, int64_t ldz, void* y, int64_t ldy, uint32_t* aux,
                             int64_t ld_aux, int M, int N, int with_mask, hipStream_t s) {
-  const int nb = ew_blocks((int64_t)M * ((N + 31) / 32) * 4);
-  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(relu_pack_kernel<DTV>, dim3(nb), dim3(kEwThreads), 0, s, (const char*)z,
+  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(relu_pack_kernel<DTV>, row_grid(M, (N + 31) / 32 * 4), dim3(kEwThreads), 0, s, (const char*)z,
                                            ldz, (char*)y, ldy, aux, ld_aux, M, N, with_mask));
   return hipGetLastError();
 }
 
 hipError_t launch_mask_apply(int dtype, const void* g, int64_t ldg, const uint32_t* aux, int64_t ld_aux, void* dx,
                              int64_t lddx, int M, int N, hipStream_t s) {
-  const int nb = ew_blocks((int64_t)M * (N / 8));
-  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(mask_apply_kernel<DTV>, dim3(nb), dim3(kEwThreads), 0, s,
+  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(mask_apply_kernel<DTV>, row_grid(M, N / 8), dim3(kEwThreads), 0, s,
                                            (const char*)g, ldg, aux, ld_aux, (char*)dx, lddx, M, N));
   return hipGetLastError();
 }
@@ -310,16 +403,14 @@ hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t s) {
 
 hipError_t launch_silu_mul(int dtype, const void* g, const void* u, int64_t ldgu, void* h, int64_t ldh, int M, int N,
                            hipStream_t s) {
-  const int nb = ew_blocks((int64_t)M * (N / 8));
-  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(silu_mul_kernel<DTV>, dim3(nb), dim3(kEwThreads), 0, s, (const char*)g,
+  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(silu_mul_kernel<DTV>, row_grid(M, N / 8), dim3(kEwThreads), 0, s, (const char*)g,
                                            (const char*)u, ldgu, (char*)h, ldh, M, N));
   return hipGetLastError();
 }
 
 hipError_t launch_dswiglu(int dtype, const void* dh, int64_t lddh, const void* gate, const void* up, int64_t ld_gu,
                           void* dg, int64_t lddg, void* du, int64_t lddu, int M, int N, hipStream_t s) {
-  const int nb = ew_blocks((int64_t)M * (N / 8));
-  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(dswiglu_kernel<DTV>, dim3(nb), dim3(kEwThreads), 0, s, (const char*)dh,
+  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(dswiglu_kernel<DTV>, row_grid(M, N / 8), dim3(kEwThreads), 0, s, (const char*)dh,
                                            lddh, (const char*)gate, (const char*)up, ld_gu, (char*)dg, lddg, (char*)du,
                                            lddu, M, N));
   return hipGetLastError();
@@ -327,16 +418,14 @@ hipError_t launch_dswiglu(int dtype, const void* dh, int64_t lddh, const void* g
 
 hipError_t launch_gelu_apply(int dtype, void* z, int64_t ldz, void* aux, int64_t ld_aux, int M, int N,
                              hipStream_t s) {
-  const int nb = ew_blocks((int64_t)M * (N / 8));
-  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(gelu_apply_kernel<DTV>, dim3(nb), dim3(kEwThreads), 0, s, (char*)z, ldz,
+  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(gelu_apply_kernel<DTV>, row_grid(M, N / 8), dim3(kEwThreads), 0, s, (char*)z, ldz,
                                            (char*)aux, ld_aux, M, N));
   return hipGetLastError();
 }
 
 hipError_t launch_dgelu_apply(int dtype, void* g, int64_t ldg, const void* aux, int64_t ld_aux, int M, int N,
                               hipStream_t s) {
-  const int nb = ew_blocks((int64_t)M * (N / 8));
-  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(dgelu_apply_kernel<DTV>, dim3(nb), dim3(kEwThreads), 0, s, (char*)g, ldg,
+  EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(dgelu_apply_kernel<DTV>, row_grid(M, N / 8), dim3(kEwThreads), 0, s, (char*)g, ldg,
                                            (const char*)aux, ld_aux, M, N));
   return hipGetLastError();
 }

@@ -415,6 +415,15 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
     }
   }
   constexpr int kRounds = 5;
+  // Before each timed execute a 512 MiB scratch buffer is overwritten (outside the events),
+  // so that no candidate finds its operands in L2 or the Infinity Cache.  Without the buffer
+  // (allocation failed) the candidates are timed warm.
+  constexpr size_t kFlushBytes = size_t(512) << 20;
+  void* flush = nullptr;
+  if (hipMalloc(&flush, kFlushBytes) != hipSuccess) {
+    flush = nullptr;
+    (void)hipGetLastError();
+  }
   hipEvent_t e0 = nullptr, e1 = nullptr;
   bool ok = hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess;
   for (auto& cd : cands) ok = ok && ep_execute(cd.h, nullptr) == EP_OK;
@@ -422,7 +431,8 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   for (int r = 0; ok && r < kRounds; ++r) {
     for (auto& cd : cands) {
       float ms = 0.f;
-      ok = hipEventRecord(e0, nullptr) == hipSuccess && ep_execute(cd.h, nullptr) == EP_OK &&
+      if (flush && hipMemsetAsync(flush, r, kFlushBytes, nullptr) != hipSuccess) ok = false;
+      ok = ok && hipEventRecord(e0, nullptr) == hipSuccess && ep_execute(cd.h, nullptr) == EP_OK &&
            hipEventRecord(e1, nullptr) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
            hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
       if (!ok) break;
@@ -445,6 +455,7 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   }
   if (e0) (void)hipEventDestroy(e0);
   if (e1) (void)hipEventDestroy(e1);
+  if (flush) (void)hipFree(flush);
   if (!ok) return fail(EP_ERR_HIP, "autotune: timing a candidate failed");
   if (best_cfg < 0) return fail(EP_ERR_INTERNAL, "autotune: no candidate configuration ran");
   {
@@ -576,7 +587,12 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   const bool bgrad_epi = epi == EP_EPILOG_DRELU_BGRAD || epi == EP_EPILOG_DGELU_BGRAD;
   if (bgrad_epi) {
     if (unfused) {
-      h->colsum_rows = 256;
+      // rows per column-sum block: about 1024 blocks of 2048 columns over the matrix, so
+      // that every CU streams, within 32..256 rows (a multiple of 8)
+      const int64_t col_blocks = (N + 2047) / 2048;
+      int64_t rows = (M * col_blocks / 1024) / 8 * 8;
+      rows = rows < 32 ? 32 : (rows > 256 ? 256 : rows);
+      h->colsum_rows = (int)rows;
       h->nparts = (int)((M + h->colsum_rows - 1) / h->colsum_rows);
       part_bytes = (size_t)h->nparts * N * sizeof(float);
     } else if (opt.bgrad_mode == EP_BGRAD_TWO_PASS) {

@@ -172,9 +172,11 @@ typedef struct {
   int autotune;            /* fused path, tile_cfg -1 and split_k 0 only: 1 = ep_plan times every
                               allowed (tile configuration, split) pair on the bound buffers and
                               keeps the one with the lowest median of 5 executes (candidates
-                              timed in turn, round by round).  The buffers' contents are
-                              overwritten, every candidate's workspace is allocated at once,
-                              and ep_plan synchronizes the device.  The choice is cached per
+                              timed in turn, round by round, each execute after a 512 MiB
+                              scratch buffer was overwritten so that caches start cold).  The
+                              buffers' contents are overwritten, every candidate's workspace
+                              and the scratch buffer are allocated at once (temporarily), and
+                              ep_plan synchronizes the device.  The choice is cached per
                               (m, n, k, leading dimensions, layout, dtype, epilog) for the
                               process, so later plans of the same problem do not time again.
                               0 = choose by the shape model (default). */
