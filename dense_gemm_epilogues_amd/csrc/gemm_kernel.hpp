@@ -548,7 +548,10 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr int TOT = KS * NMMA;                       // MFMAs per k-step
   // With only 2 stages the loads of the next stage must land before this k-step's barrier,
   // so they are issued in the first half of the k-step; with more stages, over all of it.
-  constexpr int DWIN = NST == 2 ? TOT / 2 : TOT;
+  // Register staging writes the next stage from registers, which must happen before the
+  // barrier (GBAR below): spread over the first three quarters (measured 1-2.5 % faster than
+  // the first half, whose LDS writes crowd the fragment reads).
+  constexpr int DWIN = VST ? (TOT * 3) / 4 : (NST == 2 ? TOT / 2 : TOT);
   constexpr int DSTRIDE = DWIN / N_DMA > 0 ? DWIN / N_DMA : 1;
   constexpr int DPER = (N_DMA + DWIN - 1) / DWIN;      // DMA ops per issue point
   auto slice = [&](auto rd_c, auto g0_c, const u32x4* A, const u32x4* B, auto t0_c, auto t1_c, int kt,
@@ -590,6 +593,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   using W_ = std::integral_constant<int, NMMA>;
   // DMA ops of the current k-step issued before its barrier
   constexpr int GBAR = (KS - 1) * NMMA + HB;
+  static_assert(!VST || DWIN <= GBAR, "register-staged writes must precede the k-step barrier");
   constexpr int DPRE_RAW = ((GBAR + DSTRIDE - 1) / DSTRIDE) * DPER;
   constexpr int DPRE = DPRE_RAW < N_DMA ? DPRE_RAW : N_DMA;
   // Workgroup barrier that does not drain the DMA ring: wait until this wave's loads of the
