@@ -197,10 +197,12 @@ bool strides_conflict(const ep_shape* s) {
 // measured faster on MI355X for every N x K shape from 1 to 16 rounds of resident tiles
 // (4096^3: 141 -> 126 us; 4096^2 x 8192: 272 -> 243 us; 16384^2 x 4096: 1.89 -> 1.84 ms), but
 // slower at 64 rounds (65536 x 16384 x 8192: 15.6 -> 16.4 ms), so larger grids keep the
-// 32-deep ring unless their strides conflict.  With B given K x N the 32-deep ring is faster.
+// 32-deep ring unless their strides conflict.  With B given K x N the 32-deep ring is faster
+// (DSWIGLU included: register-staged it was no faster with weights of the workloads' scale).
+// The unfused path's GEMM takes the tile the fused epilog would.
 constexpr int kVstCfg = 8;
 int pick_cfg(const ep_shape* s, int model_cfg, int cus) {
-  if (model_cfg != 0 || s->b_layout != EP_B_NK || s->a_layout != EP_A_MK) return model_cfg;
+  if (model_cfg != 0 || s->a_layout != EP_A_MK || s->b_layout != EP_B_NK) return model_cfg;
   const int64_t tiles = ((s->m + 255) / 256) * ((s->n + 255) / 256);
   return (tiles <= 16LL * cus || strides_conflict(s)) ? kVstCfg : model_cfg;
 }
