@@ -282,6 +282,15 @@ def test_small_shapes_unfused(epi, layout):
                       path="unfused")
 
 
+@pytest.mark.parametrize("epi", EPIS)
+def test_unfused_rows_past_grid_limit(epi):
+    """The unfused path's elementwise kernels launch at most 65535 row-blocks and loop over the
+    remaining rows: M = 70001 rows (ragged N and K) against the oracle in full."""
+    require_gpu()
+    run_and_check(epi, "f16" if epi not in ("SWIGLU", "DSWIGLU", "SWIGLU_AUX") else "bf16", "NK", 70001, 72, 40, -1,
+                  path="unfused")
+
+
 def test_tiny_linear_layer_config():
     """The tiny fp16 linear layer: X 32x128, W 128x64, bias 64; backward dY 32x64 masked by a
     separate 32x128 pre-activation's relu_aux."""
