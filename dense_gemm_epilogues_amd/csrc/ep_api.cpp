@@ -682,6 +682,19 @@ static ep_status check_launch(const char* what) {
 ep_status ep_execute(ep_handle h, void* stream) {
   if (!h || h->magic != kMagic) return fail(EP_ERR_INVALID_ARG, "invalid or freed handle");
   hipStream_t s = (hipStream_t)stream;
+  // The launches go to the stream's device (the calling thread's current device for the null
+  // stream); the plan's pointers and workspace live on the device it was planned on.
+  int dev = -1;
+  if (s == nullptr) {
+    if (hipGetDevice(&dev) != hipSuccess) return fail(EP_ERR_HIP, "hipGetDevice failed");
+  } else {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(s, &sd) != hipSuccess) return fail(EP_ERR_INVALID_ARG, "the stream is not valid");
+    dev = (int)sd;
+  }
+  if (dev != h->device)
+    return fail(EP_ERR_INVALID_ARG, "the stream's device (%d) is not the device the plan was made on (%d)", dev,
+                h->device);
   const ep_shape& sh = h->shape;
   const int dt = (int)h->dtype;
   const int M = (int)sh.m, N = (int)sh.n;

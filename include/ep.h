@@ -203,10 +203,12 @@ ep_status ep_plan_ex(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog,
 
 /*
  * ep_execute: enqueue the planned computation on `stream` (a hipStream_t; NULL = the null
- * stream) and return without synchronizing.  Does no validation beyond the handle check
- * and no allocation.  A handle may be executed any number of times, on any stream, but
- * not concurrently on two streams (they would share its workspace).  Returns
- * EP_ERR_INVALID_ARG for a NULL or freed handle and EP_ERR_HIP if a launch fails.
+ * stream of the calling thread's current device) and return without synchronizing.  Checks
+ * only the handle and that the stream's device is the one the plan was made on; no
+ * allocation.  A handle may be executed any number of times, on any stream of its device,
+ * but not concurrently on two streams (they would share its workspace).  Returns
+ * EP_ERR_INVALID_ARG for a NULL or freed handle or a stream of another device (nothing is
+ * launched) and EP_ERR_HIP if a launch fails.
  */
 ep_status ep_execute(ep_handle h, void* stream);
 
