@@ -120,6 +120,60 @@ def run_interleaved(variants, steps, warmup, flush, per_fn=False):
     return out
 
 
+def clock_under_load(fns, seconds=1.5, period_s=0.01):
+    """Sustained shader clock and socket power while the step `fns` runs back to back for
+    `seconds` (batches of 50 steps, synchronised), sampled with amdsmi every `period_s` from a
+    second thread.  None when amdsmi is not available."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+    import threading
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, (int, float))]
+                pw = m.get("current_socket_power")
+                if clks:
+                    samples.append((sum(clks) / len(clks), pw if isinstance(pw, (int, float)) else None))
+            except Exception:
+                pass
+            time.sleep(period_s)
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    steps = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        steps += 50
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not samples:
+        return None
+    clk = [c for c, _ in samples]
+    pw = [w for _, w in samples if w is not None]
+    return {"gfxclk_mhz_mean": round(float(np.mean(clk)), 1), "gfxclk_mhz_min": round(float(np.min(clk)), 1),
+            "gfxclk_mhz_max": round(float(np.max(clk)), 1),
+            "socket_power_w_mean": round(float(np.mean(pw)), 1) if pw else None, "samples": len(samples),
+            "steps": steps, "how": "amdsmi current_gfxclks (mean over XCDs) and current_socket_power, every "
+                                  "10 ms while the fused step runs back to back without cache flushes"}
+
+
 def launch_avg_ms(fn, reps=20):
     """Average duration of fn's launches run back to back between one event pair (operands
     stay in the caches between launches; the event overhead is spread over reps)."""
@@ -135,7 +189,7 @@ def launch_avg_ms(fn, reps=20):
     return e0.elapsed_time(e1) / reps
 
 
-def linear_layer(c, steps, warmup, flush, dev, with_unfused=True):
+def linear_layer(c, steps, warmup, flush, dev, with_unfused=True, with_clock=False):
     """Fused fwd RELU_AUX_BIAS + bwd DRELU_BGRAD (mask chained from the forward).  The step
     is timed with one event pair (cache flushed before it); fwd_ms / bwd_ms are the averages
     of back-to-back launches of each half."""
@@ -176,6 +230,9 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True):
                      "step_ms_min": float(np.min(st)), "step_ms_max": float(np.max(st)),
                      "fwd_ms": launch_avg_ms(pf.execute), "bwd_ms": launch_avg_ms(pb.execute),
                      "fwd_info": pf.info(), "bwd_info": pb.info()}
+    # last, since 1.5 s of continuous load warms the card
+    clock = clock_under_load([plans["fused"][0].execute, plans["fused"][1].execute]) if with_clock else None
+    for pf, pb in plans.values():
         pf.free()
         pb.free()
     if with_unfused:
@@ -195,6 +252,7 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True):
         out["torch"] = res["torch"]
         out["speedup_vs_torch"] = res["torch"]["step_ms"] / f["step_ms"]
     out["inputs"] = {"x": x, "w": w, "bias": bias, "dy": dy}
+    out["clock"] = clock
     return out
 
 
@@ -543,7 +601,7 @@ def main():
 
     c2 = W.LINEAR[2]
     t_start = time.time()
-    r2 = linear_layer(c2, args.steps, args.warmup, flush, dev)
+    r2 = linear_layer(c2, args.steps, args.warmup, flush, dev, with_clock=True)
     f2 = r2["fused"]
     fwd_tflops = f2["tflops_fwd"]
     line = {
@@ -580,6 +638,7 @@ def main():
                      "avg_launch_how": "20 back-to-back launches of the forward between one HIP event pair "
                                        "on the launch stream"},
     }
+    line["clock_under_load"] = r2["clock"]
     tr = measured_traffic()
     if tr is not None:
         line["roofline"]["traffic"] = round(tr["traffic_bytes_per_launch"])
