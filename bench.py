@@ -13,13 +13,15 @@ training step, an M sweep, the GELU layer, launch overhead and plan-time tuning.
 stated, torch (hipBLASLt GEMMs plus elementwise ops) runs the same step as a vendor-library
 reference.
 
-Timing: HIP events on the stream the kernels run on, one pair around each step; a 512 MiB
-buffer is overwritten between steps (outside the events) so no step starts with its
-operands in L2 / Infinity Cache.  Compared variants (fused, unfused, torch) alternate step
-by step, so clock and power drift over the run reach each of them alike.  An event record costs about 6 us of GPU time before the
-next launch, so per-kernel durations (the roofline's average launch) come from launches run
-back to back between a single event pair.  Inputs are seeded synthetic tensors generated on the
-device.  The CPU oracle (float64 numpy) is timed on this host as a baseline only.
+Timing: HIP events on the stream the kernels run on.  The headline layer runs its steps back
+to back over several copies of its inputs that together exceed the 256 MB Infinity Cache, so
+no step finds its operands cached, with one event pair around each block of steps; fused,
+unfused and torch blocks alternate, so clock and power drift over the run reach each alike.
+The other workloads time one event pair per step, with a 512 MiB buffer overwritten between
+steps (outside the events), the variants alternating step by step.  An event record costs
+about 6 us of GPU time before the next launch, so per-kernel durations (the roofline's
+average launch) come from launches run back to back between a single event pair.  Inputs are
+seeded synthetic tensors generated on the device.  The CPU oracle (float64 numpy) is timed on this host as a baseline only.
 """
 import argparse
 import json
@@ -120,6 +122,38 @@ def run_interleaved(variants, steps, warmup, flush, per_fn=False):
     return out
 
 
+def run_rotating(variants, steps, warmup):
+    """variants: {name: [one step's fns for input set 0, for set 1, ...]}.  Exactly `steps`
+    steps of each variant are timed, back to back, cycling through its input sets (whose
+    total exceeds the Infinity Cache, so every step reads its operands from HBM), in 4 blocks
+    of steps/4 with one event pair each (one block if steps is not a multiple of 4); the
+    variants' blocks alternate, so that clock drift reaches each alike.  Returns {name:
+    per-step ms of each block}."""
+    names = list(variants)
+    for nm in names:
+        for st in range(warmup):
+            for f in variants[nm][st % len(variants[nm])]:
+                f()
+    torch.cuda.synchronize()
+    blocks = 4 if steps % 4 == 0 and steps >= 8 else 1
+    per = steps // blocks
+    ev = {nm: [] for nm in names}
+    idx = {nm: 0 for nm in names}
+    for _ in range(blocks):
+        for nm in names:
+            sets = variants[nm]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(per):
+                for f in sets[idx[nm] % len(sets)]:
+                    f()
+                idx[nm] += 1
+            e1.record()
+            ev[nm].append((e0, e1))
+    torch.cuda.synchronize()
+    return {nm: [a.elapsed_time(b) / per for a, b in ev[nm]] for nm in names}
+
+
 def clock_under_load(fns, seconds=1.5, period_s=0.01):
     """Sustained shader clock and socket power while the step `fns` runs back to back for
     `seconds` (batches of 50 steps, synchronised), sampled with amdsmi every `period_s` from a
@@ -190,53 +224,62 @@ def launch_avg_ms(fn, reps=20):
 
 
 def linear_layer(c, steps, warmup, flush, dev, with_unfused=True, with_clock=False):
-    """Fused fwd RELU_AUX_BIAS + bwd DRELU_BGRAD (mask chained from the forward).  The step
-    is timed with one event pair (cache flushed before it); fwd_ms / bwd_ms are the averages
-    of back-to-back launches of each half."""
+    """Fused fwd RELU_AUX_BIAS + bwd DRELU_BGRAD (mask chained from the forward), against the
+    unfused path and torch.  Steps run back to back over copies of the inputs that together
+    exceed the Infinity Cache (see run_rotating); fwd_ms / bwd_ms are the averages of
+    back-to-back launches of each half on one input set."""
     import dense_gemm_epilogues_amd as ep
     import workloads as W
     inp = W.linear_inputs(c, device=dev)
-    x, w, bias, dy = inp["x"], inp["w"], inp["bias"], inp["dy"]
     m, n, k = c.m, c.n, c.k
-    if c.mask_from == "separate":
-        mask_bwd = inp["mask_in"]
-    else:
-        mask_bwd = None
-    res = {}
-    plans = {}
-    for path in (["fused", "unfused"] if with_unfused else ["fused"]):
-        pf = ep.Plan(x, w, "RELU_AUX_BIAS", {"bias": bias}, b_layout="KN", path=path)
-        y, aux = pf.execute()
-        mb = aux["relu_aux"] if mask_bwd is None else mask_bwd
-        pb = ep.Plan(dy, w, "DRELU_BGRAD", {"relu_aux": mb}, b_layout="NK", path=path)
-        plans[path] = (pf, pb)
-    variants = {path: [pf.execute, pb.execute] for path, (pf, pb) in plans.items()}
+    separate = c.mask_from == "separate"
+    names = ["x", "w", "bias", "dy"] + (["mask_in"] if separate else [])
+    set_bytes = sum(inp[nm].numel() * inp[nm].element_size() for nm in names) + m * n * 2 + m * k * 2
+    nsets = int(min(8, max(1, -(-(768 << 20) // set_bytes))))
+    sets = [inp] + [{nm: inp[nm].clone() for nm in names} for _ in range(nsets - 1)]
+    paths = ["fused", "unfused"] if with_unfused else ["fused"]
+    plans = {path: [] for path in paths}
+    for ins in sets:
+        for path in paths:
+            pf = ep.Plan(ins["x"], ins["w"], "RELU_AUX_BIAS", {"bias": ins["bias"]}, b_layout="KN", path=path)
+            _, aux = pf.execute()
+            mb = ins["mask_in"] if separate else aux["relu_aux"]
+            pb = ep.Plan(ins["dy"], ins["w"], "DRELU_BGRAD", {"relu_aux": mb}, b_layout="NK", path=path)
+            plans[path].append((pf, pb))
+    variants = {path: [[pf.execute, pb.execute] for pf, pb in plans[path]] for path in paths}
     if with_unfused:
         # vendor-library reference: hipBLASLt GEMMs + torch elementwise, byte mask instead of bits
-        if mask_bwd is not None:  # the separate backward mask (M x K bits) as bytes, unpacked untimed
-            bits = torch.arange(32, device=dev, dtype=torch.int32)
-            keep_b = ((mask_bwd.unsqueeze(-1) >> bits) & 1).to(torch.bool).reshape(m, k)
+        def torch_step_of(ins):
+            x, w, bias, dy = ins["x"], ins["w"], ins["bias"], ins["dy"]
+            if separate:  # the separate backward mask (M x K bits) as bytes, unpacked untimed
+                bits = torch.arange(32, device=dev, dtype=torch.int32)
+                keep_b = ((ins["mask_in"].unsqueeze(-1) >> bits) & 1).to(torch.bool).reshape(m, k)
 
-        def torch_step():
-            yy = torch.addmm(bias, x, w).relu_()
-            keep = yy > 0
-            (dy @ w.t()) * (keep if mask_bwd is None else keep_b)
-            dy.float().sum(0)
-        variants["torch"] = [torch_step]
-    timed = run_interleaved(variants, steps, warmup, flush)
-    for path, (pf, pb) in plans.items():
-        st = timed[path][0]
+            def torch_step():
+                yy = torch.addmm(bias, x, w).relu_()
+                keep = yy > 0
+                (dy @ w.t()) * (keep_b if separate else keep)
+                dy.float().sum(0)
+            return torch_step
+        variants["torch"] = [[torch_step_of(ins)] for ins in sets]
+    timed = run_rotating(variants, steps, warmup)
+    res = {}
+    for path in paths:
+        st = timed[path]
+        pf, pb = plans[path][0]
         res[path] = {"step_ms": float(np.mean(st)), "step_ms_median": float(np.median(st)),
                      "step_ms_min": float(np.min(st)), "step_ms_max": float(np.max(st)),
                      "fwd_ms": launch_avg_ms(pf.execute), "bwd_ms": launch_avg_ms(pb.execute),
-                     "fwd_info": pf.info(), "bwd_info": pb.info()}
+                     "fwd_info": pf.info(), "bwd_info": pb.info(), "input_sets": nsets}
     # last, since 1.5 s of continuous load warms the card
-    clock = clock_under_load([plans["fused"][0].execute, plans["fused"][1].execute]) if with_clock else None
-    for pf, pb in plans.values():
-        pf.free()
-        pb.free()
+    clock = clock_under_load([plans["fused"][0][0].execute, plans["fused"][0][1].execute]) if with_clock else None
+    for path in paths:
+        for pf, pb in plans[path]:
+            pf.free()
+            pb.free()
     if with_unfused:
-        res["torch"] = {"step_ms": float(np.mean(timed["torch"][0]))}
+        res["torch"] = {"step_ms": float(np.mean(timed["torch"]))}
+    x, w, bias, dy = inp["x"], inp["w"], inp["bias"], inp["dy"]
     flop = 2.0 * m * n * k
     out = {"flop_per_gemm": flop, "fused": res["fused"]}
     f = res["fused"]
@@ -620,7 +663,11 @@ def main():
         "config": {"workload": "square ReLU linear layer, fp16 in / fp32 acc: fused RELU_AUX_BIAS forward "
                                "(X 4096x4096 . W 4096x4096 + bias) then fused DRELU_BGRAD backward "
                                "(dY . W^T masked by the forward relu_aux, + bgrad)",
-                   "m": c2.m, "n": c2.n, "k": c2.k, "cache": "flushed between steps" if flush is not None else "warm"},
+                   "m": c2.m, "n": c2.n, "k": c2.k,
+                   "cache": f"cold: steps rotate over {f2['input_sets']} copies of the inputs (more than the "
+                            "256 MB Infinity Cache together)"},
+        "timing": "4 blocks of steps/4 back-to-back steps per variant, one HIP event pair per block, "
+                  "fused / unfused / torch blocks alternating; median/min/max are over the blocks",
         "ms_per_step_median": round(f2["step_ms_median"], 5),
         "ms_per_step_min": round(f2["step_ms_min"], 5), "ms_per_step_max": round(f2["step_ms_max"], 5),
         "pct_peak": round(100.0 * f2["tflops_step"] / PEAK_F16_TFLOPS, 2),

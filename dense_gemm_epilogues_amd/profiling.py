@@ -6,6 +6,10 @@
   python -m dense_gemm_epilogues_amd.profiling trace DIR
       per (kernel, grid size) call count and average duration from the kernel trace
       (reads *_kernel_trace.csv), so launches of one kernel at different shapes separate.
+  python -m dense_gemm_epilogues_amd.profiling runs DIR KERNEL_SUBSTR [--grid G] [--min N]
+      every run of at least N consecutive dispatches (in start-time order, no other kernel
+      in between) of the kernel whose name contains KERNEL_SUBSTR, with its mean duration:
+      picks out the back-to-back launches a benchmark times between one event pair.
   python -m dense_gemm_epilogues_amd.profiling counters PMC_DIR [PMC_DIR ...] --trace TRACE_DIR
       per (kernel, grid size) averages of every counter in the `--pmc` runs, with the
       sustained shader clock (GRBM_GUI_ACTIVE / XCDs / duration), the MFMA busy fraction
@@ -81,6 +85,28 @@ def kernel_trace(d):
         acc[(r["Kernel_Name"], g)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     out = [(k[0], k[1], len(v), sum(v) / len(v)) for k, v in acc.items()]
     return sorted(out, key=lambda x: -x[2] * x[3])
+
+
+def dispatch_runs(d, kernel, grid=None, min_len=20):
+    """[(first dispatch index, length, avg_ns)] for each run of >= min_len consecutive
+    dispatches of one kernel (name contains `kernel`, grid size `grid` if given)."""
+    rows = list(csv.DictReader(open(_find(d, "*kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out, cur = [], []
+
+    def close(i):
+        if len(cur) >= min_len:
+            out.append((i - len(cur), len(cur), sum(cur) / len(cur)))
+
+    for i, r in enumerate(rows):
+        g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        if kernel in r["Kernel_Name"] and (grid is None or g == grid):
+            cur.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        else:
+            close(i)
+            cur = []
+    close(len(rows))
+    return out
 
 
 def pmc_dispatches(d, counter):
@@ -169,6 +195,11 @@ def main(argv=None):
     s.add_argument("dir")
     tr = sub.add_parser("trace")
     tr.add_argument("dir")
+    ru = sub.add_parser("runs")
+    ru.add_argument("dir")
+    ru.add_argument("kernel")
+    ru.add_argument("--grid", type=int, default=None)
+    ru.add_argument("--min", type=int, default=20)
     c = sub.add_parser("counters")
     c.add_argument("pmc_dirs", nargs="+")
     c.add_argument("--trace", required=True)
@@ -193,6 +224,9 @@ def main(argv=None):
             print(f"{name[:60]}  grid {grid}  dispatches {n}")
             print("    " + "  ".join(f"{k}={v:.4g}" for k, v in der.items()))
             print("    " + "  ".join(f"{k}={v:.4g}" for k, v in sorted(mean.items())))
+    elif a.cmd == "runs":
+        for first, n, avg in dispatch_runs(a.dir, a.kernel, a.grid, a.min):
+            print(f"dispatch {first:7d}  run of {n:6d}  avg {avg / 1e3:11.2f} us")
     elif a.cmd == "trace":
         for name, grid, calls, avg in kernel_trace(a.dir):
             print(f"{calls:6d} calls  grid {grid:9d}  avg {avg / 1e3:11.2f} us  {name[:100]}")
