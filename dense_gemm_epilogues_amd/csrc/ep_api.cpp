@@ -161,8 +161,9 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   // Relative main-loop efficiency of each configuration, measured on MI355X at full-chip
   // shapes (fp16/bf16, both B layouts, every epilog): 256x256x32 with 4 stages is the
   // fastest wherever it fills the chip.
-  // (the register-staged configuration is chosen by pick_cfg's rule, not by this model)
-  static const double kEff[kNumTileCfgs] = {1.0, 0.70, 0.80, 0.80, 0.85, 0.97, 0.80, 0.82, 0.0};
+  // (the configuration run for a 256x256 tile, 16x16x32 or register-staged, is chosen by
+  // pick_cfg's rule, not by this model)
+  static const double kEff[kNumTileCfgs] = {1.0, 0.70, 0.80, 0.80, 0.85, 0.97, 0.80, 0.82, 0.0, 0.0};
   int best = 0;
   double best_t = 1e300;
   for (int c = 0; c < kNumTileCfgs; ++c) {
@@ -180,31 +181,23 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   return best;
 }
 
-// Rows of a k-contiguous operand whose stride is a multiple of 32 KiB fall into few L2 sets:
-// the 256 rows of one k-step evict each other.  A 32-deep k-step reads 64 bytes of each row,
-// half a 128-byte line, and the other half, read one k-step later, is fetched again (65536 x
-// 8192 x 16384 with both operands at such strides fetched twice the bytes of a padded stride
-// and ran 18 % slower).  A 64-deep k-step reads whole lines.
-bool strides_conflict(const ep_shape* s) {
-  const int64_t es = 2;  // bytes per fp16 / bf16 element
-  const bool b_kc = s->b_layout == EP_B_NK && (s->ldb * es) % 32768 == 0;
-  return s->k >= 4096 && b_kc;
-}
-
-// With B given N x K both operands arrive as 64-byte row pieces at 32-deep k-steps, twice
-// the address work per byte of K x N, and the loads stall in the texture addresser.  The
-// 64-deep register-staged configuration (whole 128-byte lines, loads a full k-step ahead)
-// measured faster on MI355X for every N x K shape from 1 to 16 rounds of resident tiles
-// (4096^3: 141 -> 126 us; 4096^2 x 8192: 272 -> 243 us; 16384^2 x 4096: 1.89 -> 1.84 ms), but
-// slower at 64 rounds (65536 x 16384 x 8192: 15.6 -> 16.4 ms), so larger grids keep the
-// 32-deep ring unless their strides conflict.  With B given K x N the 32-deep ring is faster
-// (DSWIGLU included: register-staged it was no faster with weights of the workloads' scale).
-// The unfused path's GEMM takes the tile the fused epilog would.
+// The 256x256 tile is run with 16x16x32 MFMAs (configuration 9): on MI355X the card runs
+// these at a higher clock for the same power, and the kernel measured 2-7 % faster than the
+// 32x32x16 form for both B layouts, every workload shape from one round of tiles (4096^3) to
+// 64 (65536 x 8192 x 16384), N x K operands whose 32 KiB row stride makes L2 sets conflict,
+// the split-K down GEMM and the dSwiGLU GEMM.  The exception is the dual-B SwiGLU GEMM with
+// N x K weights at up to 16 rounds (M 2048, I 17408: 0.624 vs 0.638 ms): there the 64-deep
+// register-staged 32x32 configuration, whose loads arrive as whole 128-byte lines one
+// k-step ahead, stays ahead.  The unfused path's GEMM takes the tile the fused epilog would.
 constexpr int kVstCfg = 8;
-int pick_cfg(const ep_shape* s, int model_cfg, int cus) {
-  if (model_cfg != 0 || s->a_layout != EP_A_MK || s->b_layout != EP_B_NK) return model_cfg;
-  const int64_t tiles = ((s->m + 255) / 256) * ((s->n + 255) / 256);
-  return (tiles <= 16LL * cus || strides_conflict(s)) ? kVstCfg : model_cfg;
+constexpr int kM16Cfg = 9;
+int pick_cfg(const ep_shape* s, int model_cfg, int cus, bool dual) {
+  if (model_cfg != 0) return model_cfg;
+  if (dual && s->a_layout == EP_A_MK && s->b_layout == EP_B_NK) {
+    const int64_t tiles = ((s->m + 255) / 256) * ((s->n + 127) / 128);
+    if (tiles <= 16LL * cus) return kVstCfg;
+  }
+  return kM16Cfg;
 }
 
 // Split-K: how many K ranges per tile.  Only grids that leave CUs idle are split: the time
@@ -531,7 +524,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   const int cfg = opt.tile_cfg >= 0
                       ? opt.tile_cfg
                       : pick_cfg(s, choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount),
-                                 prop.multiProcessorCount);
+                                 prop.multiProcessorCount, kernel_dual);
 
   ep_plan_s* h = new (std::nothrow) ep_plan_s;
   if (!h) return fail(EP_ERR_OUT_OF_MEMORY, "host allocation failed");

@@ -10,10 +10,15 @@
 //     of their 16-byte chunks, so the MFMA fragment reads are free of bank conflicts.  B given
 //     K x N (N contiguous) is kept as [BK k][128 n] sub-tiles and read with the LDS transpose
 //     read (ds_read_b64_tr_b16), which hands each lane the k-run of one column.
-//   * The K loop issues v_mfma_f32_32x32x16_{f16,bf16}: lane l of a 32x32 block holds
-//     column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 of its 16 accumulator registers.  The
-//     order of MFMAs, fragment reads and loads inside a k-step is fixed explicitly, and the
-//     barrier between k-steps waits only for the stage needed next.
+//   * The K loop issues v_mfma_f32_32x32x16_{f16,bf16} (lane l of a 32x32 block holds column
+//     l%32 and rows 8*(r/4) + 4*(l/32) + r%4 of its 16 accumulator registers) or, in the m16
+//     configurations, v_mfma_f32_16x16x32_{f16,bf16} (lane l of a 16x16 block holds column
+//     l%16 and rows 4*(l/16) + r of its 4 registers; its operands are the 8 k-values
+//     8*(l/16) .. +7 of row / column l%16).  Under sustained load the 16x16x32 form moves a
+//     quarter of the accumulator data per instruction for half the FLOP, and the card, which
+//     is limited by power there, sustains about 13% more FLOP/s with it.  The order of MFMAs,
+//     fragment reads and loads inside a k-step is fixed explicitly, and the barrier between
+//     k-steps waits only for the stage needed next.
 //   * The epilogue runs on the fp32 accumulators: each wave stages a 32-row slab through
 //     LDS so that every lane owns 8 consecutive columns of one row, applies the epilog
 //     (bias, ReLU, mask packing, mask application + column sums, SiLU*mul, dSwiGLU) in
@@ -48,7 +53,19 @@ constexpr int cfg_bk(int cfg) { return kTileCfgs[cfg].bk; }
 constexpr int cfg_nst(int cfg) { return kTileCfgs[cfg].nst; }
 constexpr int cfg_occ(int cfg) { return kTileCfgs[cfg].occ; }
 constexpr bool cfg_vst(int cfg) { return kTileCfgs[cfg].vst != 0; }
+constexpr int cfg_mf(int cfg) { return kTileCfgs[cfg].mf; }
 
+// The 16x16x32 MFMAs are issued as inline asm whose accumulator operand must sit in AGPRs:
+// with the builtin, the register allocator spreads the 64 four-register accumulators of a
+// wave over both register files and copies them back and forth inside the K loop.  Inline
+// asm hides the instruction from the compiler's hazard tracking, so a configuration using it
+// must not spill or move registers around the MFMAs (the build's resource usage shows none
+// for the one 16x16x32 configuration; a register-staged variant spilled and computed wrong
+// sums).  Then the hazards are covered: an accumulator feeds the next MFMA on it a whole
+// k-slice (64 MFMAs) later, explicit wait states separate the zeroed accumulators from the
+// first MFMA and the last MFMA from the first reads of its results (mfma_drain), and
+// fragments come from LDS reads, whose waits the compiler inserts for asm operands as for
+// any other use.
 template <int DT>
 struct Elem;
 
@@ -64,6 +81,11 @@ struct Elem<T_F16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+  // 16x16x32 with the accumulator pinned to AGPRs (see mfma_acc below)
+  static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    return c;
+  }
 };
 
 template <>
@@ -77,6 +99,10 @@ struct Elem<T_BF16> {
   static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    return c;
   }
 };
 
@@ -120,6 +146,10 @@ __device__ __forceinline__ f32x4 unpack4(u32x2 w) {
 // a & b in one v_and_b32 the compiler cannot see through (it would turn an AND with a
 // sign-extended bit back into a compare and a select, two instructions and a hazard wait
 // where a bit-field extract and this AND are two)
+// Wait states between the last MFMA of the K loop and the first VALU / LDS read of its
+// results: more than any MFMA form in this kernel needs (18 for a 16-pass result).
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 __device__ __forceinline__ uint32_t and_opaque(uint32_t a, uint32_t b) {
   uint32_t r;
   asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
@@ -187,17 +217,36 @@ __device__ __forceinline__ int swf(int r) {
   return (r ^ (r >> 3)) & (CPR - 1);
 }
 
+// 16x16 blocks, reading window [T0, T1) of a k-slice: the B fragment reads are spread over
+// the first half of the window (RPMB per MFMA), and A fragment i (APF reads) is read at MFMA
+// max(T0, (i + 1) NB - 1), after the B reads of that MFMA.  Returns the number of A reads
+// issued after the last B read.
+constexpr int reads_after_b(int T0, int T1, int MB, int NB, int B_OPS, int APF) {
+  const int bspan = (T1 - T0) / 2 > 0 ? (T1 - T0) / 2 : 1;
+  const int rpmb = (B_OPS + bspan - 1) / bspan;
+  const int tb = T0 + (B_OPS - 1) / rpmb;
+  int n = 0;
+  for (int i = 0; i < MB; ++i) {
+    const int at = (i + 1) * NB - 1 > T0 ? (i + 1) * NB - 1 : T0;
+    if (at >= tb) n += APF;
+  }
+  return n;
+}
+
 template <int DT, int LAY, int EPI, int CFG>
 struct GemmTraits {
   static constexpr int BM = cfg_bm(CFG), BNT = cfg_bnt(CFG), BK = cfg_bk(CFG), NST = cfg_nst(CFG);
   static constexpr bool DUAL = EPI == E_SWIGLU || EPI == E_SWIGLU_AUX;
   static constexpr int WTM = BM / 2;             // rows per wave
   static constexpr int WTB = BNT / 2;            // B-tile rows per wave
-  static constexpr int MB = WTM / 32;            // 32x32 blocks per wave along M
-  static constexpr int NB = WTB / 32;            // ... along the B tile
+  static constexpr int MF = cfg_mf(CFG);         // MFMA block edge (32 or 16)
+  static constexpr int KMF = MF == 32 ? 16 : 32;  // k per MFMA
+  static constexpr int ACC_R = MF * MF / 64;     // accumulator registers per block and lane
+  static constexpr int MB = WTM / MF;            // MFMA blocks per wave along M
+  static constexpr int NB = WTB / MF;            // ... along the B tile
   static constexpr int BN_OUT = DUAL ? BNT / 2 : BNT;
   static constexpr int WTN = DUAL ? WTB / 2 : WTB;  // output columns per wave
-  static constexpr int KS = BK / 16;             // MFMA k-slices per k-step
+  static constexpr int KS = BK / KMF;            // MFMA k-slices per k-step
   static constexpr int ROWB = BK * 2;            // bytes per k-contiguous tile row
   static constexpr int CPR = BK / 8;             // 16-byte chunks per row
   static constexpr int A_BYTES = BM * ROWB;
@@ -220,13 +269,15 @@ struct GemmTraits {
   static constexpr int ITERS = 32 / RPI;
   static_assert(LPR >= 4 && LPR <= 64, "staged rows must span whole lanes");
   static constexpr int NBO = DUAL ? NB / 2 : NB;  // accumulator blocks per output column range
-  static_assert(DUAL || NBO == 2 || NBO == 4, "mask words per slab row must be 2 or 4");
+  static constexpr int WPR = WTN / 32;            // mask words per wave row
+  static_assert(DUAL || WPR == 2 || WPR == 4, "mask words per slab row must be 2 or 4");
   static_assert(!DUAL || NBO >= 1, "dual B needs a block per output column range");
   // staged rows per chunk of the store loop: 8 rows read together where the epilog is a plain
   // store; one row at a time where it has per-row inputs (measured faster on MI355X)
   static constexpr int CH =
       (EPI == E_DSWIGLU || EPI == E_DRELU_BGRAD || EPI == E_DGELU_BGRAD) ? 1 : (ITERS < 8 ? ITERS : 8);
-  static_assert(KS == 2 || KS == 4, "k-slices per step must be even");
+  static_assert(KS == 1 || KS == 2 || KS == 4, "k-slices per step: 1, 2 or 4");
+  static_assert(MF == 32 || MF == 16, "MFMA block edge");
   static_assert(A_SLOTS >= 1 && B_SLOTS >= 1, "tile too small for 1 KiB DMA slots");
   static_assert(LDS_BYTES * cfg_occ(CFG) <= 160 * 1024, "LDS budget");
 };
@@ -247,6 +298,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr bool DUAL = TR::DUAL;
   constexpr int BM = TR::BM, BNT = TR::BNT, BK = TR::BK, NST = TR::NST;
   constexpr int MB = TR::MB, NB = TR::NB, WTM = TR::WTM, WTB = TR::WTB, WTN = TR::WTN;
+  constexpr int MF = TR::MF, KMF = TR::KMF, ACC_R = TR::ACC_R;
+  using AccT = std::conditional_t<MF == 32, f32x16, f32x4>;
   constexpr int KS = TR::KS, ROWB = TR::ROWB, CPR = TR::CPR, RPS = TR::RPS;
   constexpr int A_SLOTS = TR::A_SLOTS, B_SLOTS = TR::B_SLOTS;
 
@@ -349,7 +402,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     const char* abase;  // K x M A: the same for A
     uint32_t anum;
   };
-  auto kn_rsrc = [&](int kt) {
+  auto kn_rsrc = [&](int kt) __attribute__((always_inline)) {
     const int k0 = gkt(kt) * BK;
     KnSrc s;
     const int64_t bytes = ((int64_t)(K - k0) * p.ldb - (n0 + w_cbase)) * 2;
@@ -367,7 +420,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 
   // One DMA op = one 1 KiB slot of a stage (A slots first, then B slots).
   constexpr int N_DMA = A_SLOTS + B_SLOTS;
-  auto dma_op = [&](int kt, char* As, int t, const KnSrc& kr) {
+  auto dma_op = [&](int kt, char* As, int t, const KnSrc& kr) __attribute__((always_inline)) {
     const int k0 = gkt(kt) * BK;
     if (t < A_SLOTS) {
       const int q = t;
@@ -394,7 +447,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       }
     }
   };
-  auto issue_tile = [&](int kt, char* As) {
+  auto issue_tile = [&](int kt, char* As) __attribute__((always_inline)) {
     const KnSrc kr = kn_rsrc(kt);
 #pragma unroll
     for (int t = 0; t < N_DMA; ++t) dma_op(kt, As, t, kr);
@@ -405,7 +458,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr bool VST = cfg_vst(CFG);
   static_assert(!VST || NST == 2, "register staging feeds a 2-stage LDS ring");
   u32x4 sreg[VST ? N_DMA : 1];
-  auto gload = [&](int kt, int t, const KnSrc& kr) -> u32x4 {
+  auto gload = [&](int kt, int t, const KnSrc& kr) __attribute__((always_inline)) -> u32x4 {
     const int k0 = gkt(kt) * BK;
     if (t < A_SLOTS) {
       const int q = t;
@@ -425,7 +478,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       }
     }
   };
-  auto lput = [&](char* As, int t) {
+  auto lput = [&](char* As, int t) __attribute__((always_inline)) {
     char* slot = t < A_SLOTS ? As + (wave * A_SLOTS + t) * 1024
                              : As + TR::A_BYTES + (wave * B_SLOTS + (t - A_SLOTS)) * 1024;
     *(u32x4*)(slot + lane * 16) = sreg[t];
@@ -433,24 +486,31 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 
   // fragment-read addresses
   const int hlf = lane >> 5;
+  // the lane's 8-element k-chunk within a k-slice: 32x32x16 takes k 8*(l/32) .. +7 of 16,
+  // 16x16x32 k 8*(l/16) .. +7 of 32; CPS 16-byte chunks per k-slice
+  const int kq = MF == 32 ? hlf : (lane >> 4);
+  constexpr int CPS = KMF / 8;
   uint32_t a_rd[MB], b_rd[NB];
   int a_f[MB], b_f[NB];
-  // transpose-read address of a 32-wide block at column (row) base `base` of a [BK][128]
+  // transpose-read address of an MF-wide block at column (row) base `base` of a [BK][128]
   // sub-tile layout: within each 16-lane group g, lane i fetches 4 columns of k-row
-  // kbase + i/4; the hardware hands lane i the 4 k-values of column i
-  auto tr_addr = [&](int base) {
+  // kbase + i/4; the hardware hands lane i the 4 k-values of column i.  32-wide blocks:
+  // groups 0-1 read k 0-7, groups 2-3 k 8-15, odd groups the block's columns 16-31;
+  // 16-wide blocks: group g reads k 8g .. 8g+7 of the block's 16 columns.
+  auto tr_addr = [&](int base) __attribute__((always_inline)) {
     const int g = lane >> 4, i = lane & 15;
     const int u = base >> 7, cb = base & 127;
-    return (uint32_t)(u * TR::KN_SUB + (8 * (g >> 1) + (i >> 2)) * 256 + ((((cb >> 5) ^ (i >> 2)) & 3) << 6) +
-                      32 * (g & 1) + 8 * (i & 3));
+    const int krow = MF == 32 ? 8 * (g >> 1) + (i >> 2) : 8 * g + (i >> 2);
+    const int cbyte = MF == 32 ? 32 * (g & 1) : 2 * (cb & 31);
+    return (uint32_t)(u * TR::KN_SUB + krow * 256 + ((((cb >> 5) ^ (i >> 2)) & 3) << 6) + cbyte + 8 * (i & 3));
   };
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     if constexpr (AKM) {
-      a_rd[i] = tr_addr(wm * WTM + i * 32);
+      a_rd[i] = tr_addr(wm * WTM + i * MF);
       a_f[i] = 0;
     } else {
-      const int row = wm * WTM + i * 32 + (lane & 31);
+      const int row = wm * WTM + i * MF + (lane & (MF - 1));
       a_rd[i] = row * ROWB;
       a_f[i] = swf<CPR>(row);
     }
@@ -459,12 +519,12 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   for (int j = 0; j < NB; ++j) {
     int brow;
     if constexpr (DUAL) {
-      brow = (j < NB / 2) ? wn * (WTB / 2) + j * 32 : BNT / 2 + wn * (WTB / 2) + (j - NB / 2) * 32;
+      brow = (j < NB / 2) ? wn * (WTB / 2) + j * MF : BNT / 2 + wn * (WTB / 2) + (j - NB / 2) * MF;
     } else {
-      brow = wn * WTB + j * 32;
+      brow = wn * WTB + j * MF;
     }
     if constexpr (BLAY == L_NK) {
-      const int row = brow + (lane & 31);
+      const int row = brow + (lane & (MF - 1));
       b_rd[j] = row * ROWB;
       b_f[j] = swf<CPR>(row);
     } else {
@@ -473,16 +533,28 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     }
   }
 
-  f32x16 acc[MB][NB];
+  AccT acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < ACC_R; ++r) acc[i][j][r] = 0.0f;
+  if constexpr (MF == 16) {
+    // the zeros are in the AGPRs, with wait states after them, before the first asm MFMA
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) asm volatile("" : "+a"(acc[i][j]));
+    mfma_drain();
+  }
 
   // ---------------------------------------------------------------- main loop
-  u32x4 fa[2][MB], fb[2][NB];
+  // 16x16 blocks: one set of A fragments (fragment i of the next k-slice replaces A[i] as
+  // soon as block row i is done; the MFMAs run row by row), two sets of B fragments.
+  // 32x32 blocks: two sets of each.
+  constexpr int NFA = MF == 16 ? 1 : 2;
+  u32x4 fa[NFA][MB], fb[2][NB];
   // One read op = one LDS fragment read: A blocks first, then B blocks (K x N: two
   // transpose reads of 4 k-values each per block).
   constexpr int A_OPS = AKM ? 2 * MB : MB;
@@ -491,51 +563,64 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // Transpose reads are issued as inline asm: the compiler's LDS-DMA alias check would
   // otherwise make every one wait for all in-flight loads of later stages (which never
   // alias the stage being read).  Completion is awaited explicitly (lgkm_fence) before use.
-  auto tr_read = [&](uint32_t addr, u32x4& dst, int half) {
+  auto tr_read = [&](uint32_t addr, u32x4& dst, int half) __attribute__((always_inline)) {
     u32x2 w;
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(w) : "v"(addr));
     dst[2 * half] = w[0];
     dst[2 * half + 1] = w[1];
   };
-  auto read_op = [&](const char* As, int ks, int r, u32x4* A, u32x4* B) {
+  // (a k-slice of a [BK][128] sub-tile is KMF k-rows of 256 bytes; the second transpose
+  // read of a fragment is 4 k-rows further)
+  auto read_op = [&](const char* As, int ks, int r, u32x4* A, u32x4* B) __attribute__((always_inline)) {
     if (r < A_OPS) {
       if constexpr (AKM) {
         const int i = r >> 1, half = r & 1;
-        tr_read(lds_addr(As + a_rd[i]) + ks * 4096 + half * 1024, A[i], half);
+        tr_read(lds_addr(As + a_rd[i]) + ks * KMF * 256 + half * 1024, A[i], half);
       } else {
-        A[r] = *(const u32x4*)(As + a_rd[r] + ((((ks * 2 + hlf) ^ a_f[r]) & (CPR - 1)) << 4));
+        A[r] = *(const u32x4*)(As + a_rd[r] + ((((ks * CPS + kq) ^ a_f[r]) & (CPR - 1)) << 4));
       }
       return;
     }
     const char* Bs = As + TR::A_BYTES;
     if constexpr (BLAY == L_NK) {
       const int j = r - A_OPS;
-      B[j] = *(const u32x4*)(Bs + b_rd[j] + ((((ks * 2 + hlf) ^ b_f[j]) & (CPR - 1)) << 4));
+      B[j] = *(const u32x4*)(Bs + b_rd[j] + ((((ks * CPS + kq) ^ b_f[j]) & (CPR - 1)) << 4));
     } else {
       const int j = (r - A_OPS) >> 1, half = (r - A_OPS) & 1;
-      tr_read(lds_addr(Bs + b_rd[j]) + ks * 4096 + half * 1024, B[j], half);
+      tr_read(lds_addr(Bs + b_rd[j]) + ks * KMF * 256 + half * 1024, B[j], half);
     }
   };
-  auto read_frags = [&](const char* As, int ks, u32x4* A, u32x4* B) {
+  // (16x16 blocks: B first, so that the A reads are the youngest, as in the K loop)
+  auto read_frags = [&](const char* As, int ks, u32x4* A, u32x4* B) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < N_RD; ++r) read_op(As, ks, r, A, B);
+    for (int q = 0; q < N_RD; ++q) read_op(As, ks, MF == 16 ? (q + A_OPS) % N_RD : q, A, B);
   };
   // Wait for every outstanding LDS read and tie the wait to the fragments the transpose
   // reads wrote, so no MFMA that consumes them can be scheduled above it.
-  auto tie4 = [&](u32x4* F, auto n_c) {
+  // (LDS reads complete in issue order: waiting until at most NL are outstanding completes
+  // all but the NL youngest; no scalar memory load is in flight inside the K loop)
+  auto tie4 = [&](u32x4* F, auto n_c, auto nl_c) __attribute__((always_inline)) {
     constexpr int NF = decltype(n_c)::value;
-    static_assert(NF == 1 || NF == 2 || NF == 4, "unsupported fragment count");
-    if constexpr (NF == 4) {
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F[0]), "+v"(F[1]), "+v"(F[2]), "+v"(F[3]));
+    constexpr int NL = decltype(nl_c)::value;
+    static_assert(NF == 1 || NF == 2 || NF == 4 || NF == 8, "unsupported fragment count");
+    static_assert(NL >= 0 && NL <= 15, "lgkmcnt range");
+    if constexpr (NF == 8) {
+      asm volatile("s_waitcnt lgkmcnt(%8)"
+                   : "+v"(F[0]), "+v"(F[1]), "+v"(F[2]), "+v"(F[3]), "+v"(F[4]), "+v"(F[5]), "+v"(F[6]), "+v"(F[7])
+                   : "n"(NL));
+    } else if constexpr (NF == 4) {
+      asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(F[0]), "+v"(F[1]), "+v"(F[2]), "+v"(F[3]) : "n"(NL));
     } else if constexpr (NF == 2) {
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F[0]), "+v"(F[1]));
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(F[0]), "+v"(F[1]) : "n"(NL));
     } else {
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F[0]));
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(F[0]) : "n"(NL));
     }
   };
-  auto lgkm_fence = [&](u32x4* A, u32x4* B) {
-    if constexpr (AKM) tie4(A, std::integral_constant<int, MB>{});
-    if constexpr (BLAY == L_KN) tie4(B, std::integral_constant<int, NB>{});
+  // NL: LDS reads issued after the last transpose read of B that may stay in flight (the
+  // A fragments of 16x16 blocks that are read after B, see reads_after_b)
+  auto lgkm_fence = [&](u32x4* A, u32x4* B, auto nl_c) __attribute__((always_inline)) {
+    if constexpr (AKM) tie4(A, std::integral_constant<int, MB>{}, std::integral_constant<int, 0>{});
+    if constexpr (BLAY == L_KN) tie4(B, std::integral_constant<int, NB>{}, nl_c);
   };
   // The instruction order inside a k-step is fixed explicitly: every sched_barrier below
   // stops the scheduler from moving instructions across it.  Each MFMA is followed by its
@@ -551,11 +636,14 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // Register staging writes the next stage from registers, which must happen before the
   // barrier (GBAR below): spread over the first three quarters (measured 1-2.5 % faster than
   // the first half, whose LDS writes crowd the fragment reads).
-  constexpr int DWIN = VST ? (TOT * 3) / 4 : (NST == 2 ? TOT / 2 : TOT);
+  constexpr int HB = NMMA >= 8 ? NMMA / 4 : NMMA / 2;  // MFMAs of the last slice before the barrier
+  // DMA ops of the current k-step issued before its barrier
+  constexpr int GBAR = (KS - 1) * NMMA + HB;
+  constexpr int DWIN = VST ? ((TOT * 3) / 4 < GBAR ? (TOT * 3) / 4 : GBAR) : (NST == 2 ? TOT / 2 : TOT);
   constexpr int DSTRIDE = DWIN / N_DMA > 0 ? DWIN / N_DMA : 1;
   constexpr int DPER = (N_DMA + DWIN - 1) / DWIN;      // DMA ops per issue point
   auto slice = [&](auto rd_c, auto g0_c, const u32x4* A, const u32x4* B, auto t0_c, auto t1_c, int kt,
-                   char* dst, const KnSrc& kr, const char* rstage, int rks, u32x4* RA, u32x4* RB) {
+                   char* dst, const KnSrc& kr, const char* rstage, int rks, u32x4* RA, u32x4* RB) __attribute__((always_inline)) {
     constexpr bool RD = decltype(rd_c)::value;
     constexpr int G0 = decltype(g0_c)::value;        // k-step MFMA index of MFMA t = 0
     constexpr int T0 = decltype(t0_c)::value, T1 = decltype(t1_c)::value;
@@ -563,6 +651,11 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     // before the end of the slice
     constexpr int RSPAN = (T1 - T0) > 8 ? (T1 - T0) - 4 : (T1 - T0);
     constexpr int RPM = (N_RD + RSPAN - 1) / RSPAN;
+    // 16x16 blocks: the B reads spread over the first half of the window, and A fragment i
+    // read right after the last MFMA of block row i (at the window's start if that is earlier)
+    constexpr int BSPAN = (T1 - T0) / 2 > 0 ? (T1 - T0) / 2 : 1;
+    constexpr int RPMB = (B_OPS + BSPAN - 1) / BSPAN;
+    constexpr int APF = A_OPS / MB;  // read ops per A fragment
 #pragma unroll
     for (int t = T0; t < T1; ++t) {
       acc[t / NB][t % NB] = E::mfma(A[t / NB], B[t % NB], acc[t / NB][t % NB]);
@@ -579,20 +672,35 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
             }
           }
       }
-      if constexpr (RD) {
+      if constexpr (RD && MF == 32) {
 #pragma unroll
         for (int r = (t - T0) * RPM; r < (t - T0 + 1) * RPM; ++r)
           if (r < N_RD) read_op(rstage, rks, r, RA, RB);
+      } else if constexpr (RD) {
+#pragma unroll
+        for (int r = (t - T0) * RPMB; r < (t - T0 + 1) * RPMB; ++r)
+          if (r < B_OPS) read_op(rstage, rks, A_OPS + r, RA, RB);
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int at = (i + 1) * NB - 1 > T0 ? (i + 1) * NB - 1 : T0;
+          if (at == t) {
+#pragma unroll
+            for (int h = 0; h < APF; ++h) read_op(rstage, rks, i * APF + h, RA, RB);
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   using Z_ = std::integral_constant<int, 0>;
-  constexpr int HB = NMMA >= 8 ? NMMA / 4 : NMMA / 2;  // MFMAs of the last slice before the barrier
   using H_ = std::integral_constant<int, HB>;
+  // A reads issued after the last B read of a reading window [T0, NMMA) (16x16 blocks with a
+  // K x N B; 0 otherwise): the fence before the next slice leaves them in flight
+  using NLH_ = std::integral_constant<int, (MF == 16 && !AKM && BLAY == L_KN)
+                                                ? reads_after_b(HB, NMMA, MB, NB, B_OPS, A_OPS / MB) : 0>;
+  using NL0_ = std::integral_constant<int, (MF == 16 && !AKM && BLAY == L_KN)
+                                                ? reads_after_b(0, NMMA, MB, NB, B_OPS, A_OPS / MB) : 0>;
   using W_ = std::integral_constant<int, NMMA>;
-  // DMA ops of the current k-step issued before its barrier
-  constexpr int GBAR = (KS - 1) * NMMA + HB;
   static_assert(!VST || DWIN <= GBAR, "register-staged writes must precede the k-step barrier");
   constexpr int DPRE_RAW = ((GBAR + DSTRIDE - 1) / DSTRIDE) * DPER;
   constexpr int DPRE = DPRE_RAW < N_DMA ? DPRE_RAW : N_DMA;
@@ -604,14 +712,18 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr int VMC_PRO = N_DMA * (NST - 2);           // after the prologue
   static_assert(NST >= 2, "the ring needs at least 2 stages");
   static_assert(VMC_LOOP <= 63 && VMC_PRO <= 63, "vmcnt range");
-  auto ring_barrier = [&](auto vmc_c) {
+  auto ring_barrier = [&](auto vmc_c) __attribute__((always_inline)) {
     if constexpr (VST)  // the stage was written from registers: only LDS traffic to wait for
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(decltype(vmc_c)::value) : "memory");
   };
-  // Loads for k-step kt + NST - 1 are issued during k-step kt.
-  auto kstep = [&](int kt) {
+  // Loads for k-step kt + NST - 1 are issued during k-step kt.  Slice ks of a k-step consumes
+  // fragment buffer (B0 + ks) & 1 and reads the next slice into the other one; with an odd
+  // number of slices per k-step (one) the buffers alternate between k-steps, so k-steps come
+  // in pairs of parity 0 and 1 (B0 = parity * KS).
+  auto kstep = [&](int kt, auto par_c) __attribute__((always_inline)) {
+    constexpr int B0 = (decltype(par_c)::value * KS) & 1;
     const char* cur = smem + (kt % NST) * TR::STAGE;
     const char* nxt = smem + ((kt + 1) % NST) * TR::STAGE;
     char* dst = smem + ((kt + NST - 1) % NST) * TR::STAGE;
@@ -621,26 +733,32 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     const KnSrc kr = kn_rsrc(kl);
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) {
-      u32x4* A = fa[ks & 1];
-      u32x4* B = fb[ks & 1];
-      lgkm_fence(A, B);
+      u32x4* A = fa[((B0 + ks) & 1) % NFA];
+      u32x4* B = fb[(B0 + ks) & 1];
+      u32x4* RA = fa[((B0 + ks + 1) & 1) % NFA];
+      u32x4* RB = fb[(B0 + ks + 1) & 1];
+      if (ks == 0) lgkm_fence(A, B, NLH_{});
+      else lgkm_fence(A, B, NL0_{});
       __builtin_amdgcn_sched_barrier(0);
       if (ks == 0)
-        slice(T_{}, std::integral_constant<int, 0>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, fa[1], fb[1]);
+        slice(T_{}, std::integral_constant<int, 0>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB);
       else if (ks == 1)
-        slice(T_{}, std::integral_constant<int, NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, fa[0], fb[0]);
+        slice(T_{}, std::integral_constant<int, NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB);
       else
-        slice(T_{}, std::integral_constant<int, 2 * NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, fa[1], fb[1]);
+        slice(T_{}, std::integral_constant<int, 2 * NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB);
     }
-    constexpr int L = (KS - 1) & 1;  // buffer of the last slice
+    constexpr int L = (B0 + KS - 1) & 1;  // buffer of the last slice
+    constexpr int NX = (B0 + KS) & 1;     // buffer of the next k-step's first slice
     using GL = std::integral_constant<int, (KS - 1) * NMMA>;
-    lgkm_fence(fa[L], fb[L]);
+    lgkm_fence(fa[L % NFA], fb[L], std::conditional_t<KS == 1, NLH_, NL0_>{});
     __builtin_amdgcn_sched_barrier(0);
-    slice(F_{}, GL{}, fa[L], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[0], fb[0]);
+    slice(F_{}, GL{}, fa[L % NFA], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[NX % NFA], fb[NX]);
     ring_barrier(std::integral_constant<int, VMC_LOOP>{});
     __builtin_amdgcn_sched_barrier(0);
-    slice(T_{}, GL{}, fa[L], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[0], fb[0]);
+    slice(T_{}, GL{}, fa[L % NFA], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[NX % NFA], fb[NX]);
   };
+  using P0_ = std::integral_constant<int, 0>;
+  using P1_ = std::integral_constant<int, 1>;
 
   if constexpr (MODE != 2) {
     if constexpr (VST) {
@@ -660,17 +778,29 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     ring_barrier(std::integral_constant<int, VMC_PRO>{});
     __builtin_amdgcn_sched_barrier(0);
     read_frags(smem, 0, fa[0], fb[0]);
-    for (int kt = 0; kt < KT; ++kt) kstep(kt);
+    if constexpr (KS % 2 == 0) {
+      for (int kt = 0; kt < KT; ++kt) kstep(kt, P0_{});
+    } else {
+      // k-steps in pairs; an odd count gets one more k-step, whose loads lie past the block's
+      // K range and read as zeros, so that the loop has a single body (a separate last k-step
+      // makes the register allocator move the accumulators between register files)
+      for (int kt = 0; kt < KT; kt += 2) {
+        kstep(kt, P0_{});
+        kstep(kt + 1, P1_{});
+      }
+    }
   }
   // loads issued past the last k-step (they read as zeros) must land before LDS is reused
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  lgkm_fence(fa[0], fb[0]);
+  if constexpr (MF == 16) mfma_drain();
+  lgkm_fence(fa[0], fb[0], std::integral_constant<int, 0>{});
+  lgkm_fence(fa[NFA - 1], fb[1], std::integral_constant<int, 0>{});
   __syncthreads();
 
   // ---------------------------------------------------------------- split-K
   // Partials are stored register-major: f32x4 number q of thread t of a tile's partial sits at
   // float offset (q * 256 + t) * 4, so each store / load instruction covers 1 KiB contiguously.
-  constexpr int ACC4 = MB * NB * 4;  // f32x4 accumulator groups per thread
+  constexpr int ACC4 = MB * NB * (ACC_R / 4);  // f32x4 accumulator groups per thread
   if constexpr (MODE == 1) {
     float* dst = p.part + ((int64_t)split * ntiles + tbid) * (int64_t)(ACC4 * kThreads * 4);
 #pragma unroll
@@ -678,8 +808,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int q = (i * NB + j) * 4 + g;
+        for (int g = 0; g < ACC_R / 4; ++g) {
+          const int q = (i * NB + j) * (ACC_R / 4) + g;
           f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
           __builtin_nontemporal_store(v, (f32x4*)(dst + ((int64_t)q * kThreads + tid) * 4));
         }
@@ -695,8 +825,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int q = (i * NB + j) * 4 + g;
+        for (int g = 0; g < ACC_R / 4; ++g) {
+          const int q = (i * NB + j) * (ACC_R / 4) + g;
           const float* sq = src + ((int64_t)q * kThreads + tid) * 4;
           f32x4 v = __builtin_nontemporal_load((const f32x4*)sq);
 #pragma unroll
@@ -709,7 +839,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 
   // ---------------------------------------------------------------- epilogue
   // Accumulator layout: lane l of 32x32 block (i, j) holds column 32 j + l%32 of the wave's
-  // columns and, in register r, row 8 (r/4) + 4 (l/32) + r%4 of the block's 32 rows.
+  // columns and, in register r, row 8 (r/4) + 4 (l/32) + r%4 of the block's 32 rows; lane l
+  // of 16x16 block (i, j) holds column 16 j + l%16 and, in register r, row 4 (l/16) + r.
   // Everything that needs only the column (bias, ReLU, the mask bits, SiLU*mul, the masked
   // column sums) is applied to the accumulators in place; then each 32-row slab is staged
   // through LDS so that every lane owns 8 consecutive columns of one row for the stores.
@@ -719,6 +850,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr bool BGRAD = EPI == E_DRELU_BGRAD || EPI == E_DGELU_BGRAD;
   constexpr bool RELU = EPI == E_RELU_BIAS || EPI == E_RELU_AUX_BIAS;
   const int l32 = lane & 31;
+  const int lmf = lane & (MF - 1);
+  const int q4 = lane >> 4;
   const int ccol0 = n0 + wn * WTN;  // first output column of the wave
   float* stg = (float*)smem + wave * TR::STG_FLOATS;
   constexpr int SP = TR::SPITCH;
@@ -732,7 +865,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   for (int j = 0; j < NBO; ++j) {
     bias_mf[j] = 0.0f;
     if constexpr (HAS_BIAS) {
-      const int c = ccol0 + 32 * j + l32;
+      const int c = ccol0 + MF * j + lmf;
       if (c < N) bias_mf[j] = E::to_f32(((const uint16_t*)p.bias)[c]);
     }
   }
@@ -740,7 +873,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 
   // DRELU_BGRAD: the slab's mask words (32 rows x WPR words) are fetched before it is staged,
   // NW per lane: word (row, w) sits in register row / RPW of lane (row % RPW) * WPR + w.
-  constexpr int WPR = NBO;
+  constexpr int WPR = TR::WPR;
   constexpr int NW = WPR / 2 > 0 ? WPR / 2 : 1;
   constexpr int RPW = 64 / WPR;
   // DSWIGLU reads gate and up per element in the staged layout, for a whole slab before it
@@ -748,8 +881,9 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr int PF_GU = (EPI == E_DSWIGLU || EPI == E_DGELU_BGRAD) ? TR::ITERS : 1;
   u32x4 pf_g[PF_GU], pf_u[PF_GU];
 
+  // 32-row slabs: 32x32 block row i, or 16x16 block rows 2i and 2i + 1
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
+  for (int i = 0; i < WTM / 32; ++i) {
     const int srow0 = m0 + wm * WTM + i * 32;  // first row of the slab
     uint32_t pf_w[NW];
     if constexpr (EPI == E_DRELU_BGRAD) {
@@ -781,36 +915,71 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     // ---- accumulator space, then the slab is staged
     uint32_t* mk = (uint32_t*)(smem + TR::MASK_OFF) + wm * 32 * TR::WPT;  // [32 rows][WPT words]
     constexpr bool XFORM = HAS_BIAS || DUAL;
+    // one accumulator value of the epilog's column transform (bias, ReLU, SiLU * up)
+    auto xform = [&](const AccT* arow, int j, int r, bool& pr) __attribute__((always_inline)) {
+      float v;
+      // (16x16 accumulators come from asm MFMAs: read one at a time, or the compiler copies
+      // all of them out of the AGPRs at once)
+      if constexpr (XFORM || MF == 16) v = acc_read(arow[j][r]);
+      else v = arow[j][r];
+      if constexpr (HAS_BIAS) v += bias_mf[j];
+      pr = v > 0.0f;
+      if constexpr (RELU) {
+        v = pr ? v : 0.0f;
+      } else if constexpr (DUAL) {
+        // block j holds the gate columns, block j + NB/2 the up columns of the same outputs
+        const float u = acc_read(arow[j + NB / 2][r]);
+        v = v * sigmoid_f(v) * u;
+      }
+      return v;
+    };
+    if constexpr (MF == 32) {
 #pragma unroll
-    for (int j = 0; j < NBO; ++j) {
+      for (int j = 0; j < NBO; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int r0 = 8 * (r >> 2) + (r & 3);  // block row held by lanes 0-31 (lanes 32-63: +4)
-        float v;
-        if constexpr (XFORM) v = acc_read(acc[i][j][r]);
-        else v = acc[i][j][r];
-        if constexpr (HAS_BIAS) v += bias_mf[j];
-        if constexpr (RELU) {
-          const bool pr = v > 0.0f;
-          v = pr ? v : 0.0f;
+        for (int r = 0; r < 16; ++r) {
+          const int r0 = 8 * (r >> 2) + (r & 3);  // block row held by lanes 0-31 (lanes 32-63: +4)
+          bool pr;
+          const float v = xform(acc[i], j, r, pr);
           if constexpr (EPI == E_RELU_AUX_BIAS) {
             // bit l of the ballot is column 32 j + l%32 of row r0 (l < 32) or r0 + 4 (l >= 32)
             // (every lane writes the same wave-uniform word to the same LDS address)
             const uint64_t b = __builtin_amdgcn_ballot_w64(pr);
-            mk[r0 * TR::WPT + wn * NBO + j] = (uint32_t)b;
-            mk[(r0 + 4) * TR::WPT + wn * NBO + j] = (uint32_t)(b >> 32);
+            mk[r0 * TR::WPT + wn * WPR + j] = (uint32_t)b;
+            mk[(r0 + 4) * TR::WPT + wn * WPR + j] = (uint32_t)(b >> 32);
           }
-        } else if constexpr (DUAL) {
-          // block j holds the gate columns, block j + NB/2 the up columns of the same outputs
-          const float u = acc_read(acc[i][j + NB / 2][r]);
-          v = v * sigmoid_f(v) * u;
+          // staged right away (row 8 (r/4) + 4 (l/32) + r%4 of the slab, column 32 j + l%32)
+          stg[(r0 + 4 * hlf) * SP + j * 32 + l32] = v;
+          // one register at a time: otherwise the scheduler hoists every ballot / lane read
+          // of the slab and runs out of scalar registers
+          if constexpr (EPI == E_RELU_AUX_BIAS) __builtin_amdgcn_sched_barrier(0);
         }
-        // staged right away (row 8 (r/4) + 4 (l/32) + r%4 of the slab, column 32 j + l%32)
-        stg[(r0 + 4 * hlf) * SP + j * 32 + l32] = v;
-        // one register at a time: otherwise the scheduler hoists every ballot / lane read
-        // of the slab and runs out of scalar registers
-        if constexpr (EPI == E_RELU_AUX_BIAS) __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+      // blocks j = 2 jw and 2 jw + 1 make up the 32 columns of mask word jw
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int jw = 0; jw < NBO / 2; ++jw)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bool pr0, pr1;
+            const float v0 = xform(acc[2 * i + h], 2 * jw, r, pr0);
+            const float v1 = xform(acc[2 * i + h], 2 * jw + 1, r, pr1);
+            if constexpr (EPI == E_RELU_AUX_BIAS) {
+              // bit l of a ballot is column l%16 of the block and row 4 (l/16) + r
+              const uint64_t b0 = __builtin_amdgcn_ballot_w64(pr0);
+              const uint64_t b1 = __builtin_amdgcn_ballot_w64(pr1);
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+                mk[(16 * h + 4 * g + r) * TR::WPT + wn * WPR + jw] =
+                    ((uint32_t)(b0 >> (16 * g)) & 0xffffu) | ((uint32_t)(b1 >> (16 * g)) << 16);
+            }
+            const int srow = 16 * h + 4 * q4 + r;
+            stg[srow * SP + 2 * jw * 16 + lmf] = v0;
+            stg[srow * SP + (2 * jw + 1) * 16 + lmf] = v1;
+            if constexpr (EPI == E_RELU_AUX_BIAS) __builtin_amdgcn_sched_barrier(0);
+          }
     }
 
     __syncthreads();
@@ -934,13 +1103,24 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       // accumulators, go to d2 columns [0, N) and [N, 2N)
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
+        if constexpr (MF == 32) {
 #pragma unroll
-        for (int j = 0; j < NBO; ++j)
+          for (int j = 0; j < NBO; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int r0 = 8 * (r >> 2) + (r & 3);
-            stg[(r0 + 4 * hlf) * SP + j * 32 + l32] = pass == 0 ? acc[i][j][r] : acc[i][j + NB / 2][r];
-          }
+            for (int r = 0; r < 16; ++r) {
+              const int r0 = 8 * (r >> 2) + (r & 3);
+              stg[(r0 + 4 * hlf) * SP + j * 32 + l32] = pass == 0 ? acc[i][j][r] : acc[i][j + NB / 2][r];
+            }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < NBO; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                stg[(16 * h + 4 * q4 + r) * SP + j * 16 + lmf] =
+                    acc_read(pass == 0 ? acc[2 * i + h][j][r] : acc[2 * i + h][j + NB / 2][r]);
+        }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < TR::ITERS; ++it) {

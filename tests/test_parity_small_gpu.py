@@ -154,9 +154,9 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
     p.free()
 
 
-# tile configurations 0-7 of the library; those with a 128-row B tile cannot hold the gate
-# and up sub-tiles of a K x N dual B operand
-NUM_TILE_CFGS = 9
+# every tile configuration of the library (9 issues 16x16x32 MFMAs); those with a
+# 128-row B tile cannot hold the gate and up sub-tiles of a K x N dual B operand
+NUM_TILE_CFGS = 10
 BNT128_CFGS = (1, 2, 6)
 
 
@@ -182,10 +182,10 @@ def test_small_shapes_fused(epi, dtname, layout, cfg):
 @pytest.mark.parametrize("epi", EPIS)
 def test_split_k(epi, layout, splits):
     """K split over 2-4 workgroups per tile (fp32 partials, then a fixup launch that sums them
-    and runs the epilog): every epilog, both dtypes, three tile configurations, a K that
+    and runs the epilog): every epilog, both dtypes, four tile configurations, a K that
     divides unevenly and a K too short for the requested number of ranges."""
     require_gpu()
-    for cfg in (0, 1, 6):
+    for cfg in (0, 1, 6, 9):
         if epi in ("SWIGLU", "SWIGLU_AUX") and layout == "KN" and cfg in BNT128_CFGS:
             continue
         for dtname in ("f16", "bf16"):
@@ -232,16 +232,17 @@ def test_transposed_a(dtname, layout):
                 p.free()
 
 
-@pytest.mark.parametrize("m,n,layout,ld_extra,want_cfg", [
-    (4096, 4096, "NK", 64, 8),      # one round of 256x256 tiles, N x K B: register-staged, 64 deep
-    (4096, 4096, "KN", 0, 0),       # K x N B: the 32-deep ring
-    (16384, 32768, "NK", 64, 0),    # 32 rounds: the 32-deep ring
-    (16384, 32768, "NK", 0, 8),     # 32 rounds, B rows 32 KiB apart: 64 deep (whole lines)
+@pytest.mark.parametrize("m,n,layout,ld_extra,dual,want_cfg", [
+    (4096, 4096, "NK", 64, False, 9),      # one round of 256x256 tiles: 16x16x32 MFMAs
+    (4096, 4096, "KN", 0, False, 9),
+    (16384, 32768, "NK", 64, False, 9),    # 32 rounds
+    (16384, 32768, "NK", 0, False, 9),     # 32 rounds, B rows 32 KiB apart
+    (2048, 8192, "NK", 0, True, 8),        # dual-B SwiGLU, N x K weights, 2 rounds: register-staged
 ])
-def test_planner_tile_choice(m, n, layout, ld_extra, want_cfg):
+def test_planner_tile_choice(m, n, layout, ld_extra, dual, want_cfg):
     """The planner's default tile configuration at full-chip shapes (256 CUs), B rows 16384
     (+ ld_extra) elements apart when B is N x K; the result is checked against the oracle on
-    sampled rows and columns."""
+    sampled rows and columns (the dual-B case on h = silu(x Wg^T) * (x Wu^T))."""
     require_gpu()
     import dense_gemm_epilogues_amd as ep
     dev = torch.device("cuda")
@@ -251,20 +252,30 @@ def test_planner_tile_choice(m, n, layout, ld_extra, want_cfg):
     g = torch.Generator(device=dev)
     g.manual_seed(m + n + ld_extra)
     a = torch.randn(m, k, device=dev, generator=g).half()
-    if layout == "NK":
-        b = (torch.randn(n, 16384 + ld_extra, device=dev, generator=g) * k ** -0.5).half()[:, :k]
-    else:
-        b = (torch.randn(k, n, device=dev, generator=g) * k ** -0.5).half()
-    say(f"case planner choice layout={layout} ldb={b.stride(0)} {m}x{n}x{k}")
-    p = ep.Plan(a, b, "DEFAULT", b_layout=layout)
-    assert f"tile_cfg={want_cfg} " in p.info(), p.info()
-    out, _ = p.execute()
-    torch.cuda.synchronize()
+
+    def b_of():
+        if layout == "NK":
+            return (torch.randn(n, 16384 + ld_extra, device=dev, generator=g) * k ** -0.5).half()[:, :k]
+        return (torch.randn(k, n, device=dev, generator=g) * k ** -0.5).half()
+    b = b_of()
+    say(f"case planner choice layout={layout} dual={dual} ldb={b.stride(0)} {m}x{n}x{k}")
     rows = torch.tensor(np.r_[0:32, m // 2 - 8:m // 2 + 24, m - 32:m], device=dev)
     cols = torch.tensor(np.r_[0:64, n // 2:n // 2 + 64, n - 64:n], device=dev)
-    bsel = b[cols] if layout == "NK" else b[:, cols]
-    ref = oracle.matmul(f64(a[rows]), f64(bsel), layout)
-    assert_half(f64(out[rows][:, cols]), ref, f"planner {layout}/{m}x{n}/{ld_extra}")
+    if dual:
+        b2 = b_of()
+        p = ep.Plan(a, b, "SWIGLU", {"b2": b2}, b_layout=layout)
+        assert f"tile_cfg={want_cfg} " in p.info(), p.info()
+        out, _ = p.execute()
+        torch.cuda.synchronize()
+        ref = oracle.swiglu(f64(a[rows]), f64(b[cols]), f64(b2[cols]), layout)[0]
+    else:
+        p = ep.Plan(a, b, "DEFAULT", b_layout=layout)
+        assert f"tile_cfg={want_cfg} " in p.info(), p.info()
+        out, _ = p.execute()
+        torch.cuda.synchronize()
+        bsel = b[cols] if layout == "NK" else b[:, cols]
+        ref = oracle.matmul(f64(a[rows]), f64(bsel), layout)
+    assert_half(f64(out[rows][:, cols]), ref, f"planner {layout}/{m}x{n}/{ld_extra}/dual={dual}")
     p.free()
 
 
