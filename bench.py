@@ -41,8 +41,8 @@ METRIC = "fused GEMM+epilogue TFLOP/s, % MFMA peak, speedup vs unfused path"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-large", action="store_true", help="skip the large-workload summary")
     ap.add_argument("--only", default=None,

@@ -217,22 +217,6 @@ __device__ __forceinline__ int swf(int r) {
   return (r ^ (r >> 3)) & (CPR - 1);
 }
 
-// 16x16 blocks, reading window [T0, T1) of a k-slice: the B fragment reads are spread over
-// the first half of the window (RPMB per MFMA), and A fragment i (APF reads) is read at MFMA
-// max(T0, (i + 1) NB - 1), after the B reads of that MFMA.  Returns the number of A reads
-// issued after the last B read.
-constexpr int reads_after_b(int T0, int T1, int MB, int NB, int B_OPS, int APF) {
-  const int bspan = (T1 - T0) / 2 > 0 ? (T1 - T0) / 2 : 1;
-  const int rpmb = (B_OPS + bspan - 1) / bspan;
-  const int tb = T0 + (B_OPS - 1) / rpmb;
-  int n = 0;
-  for (int i = 0; i < MB; ++i) {
-    const int at = (i + 1) * NB - 1 > T0 ? (i + 1) * NB - 1 : T0;
-    if (at >= tb) n += APF;
-  }
-  return n;
-}
-
 template <int DT, int LAY, int EPI, int CFG>
 struct GemmTraits {
   static constexpr int BM = cfg_bm(CFG), BNT = cfg_bnt(CFG), BK = cfg_bk(CFG), NST = cfg_nst(CFG);
@@ -550,11 +534,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   }
 
   // ---------------------------------------------------------------- main loop
-  // 16x16 blocks: one set of A fragments (fragment i of the next k-slice replaces A[i] as
-  // soon as block row i is done; the MFMAs run row by row), two sets of B fragments.
-  // 32x32 blocks: two sets of each.
-  constexpr int NFA = MF == 16 ? 1 : 2;
-  u32x4 fa[NFA][MB], fb[2][NB];
+  u32x4 fa[2][MB], fb[2][NB];
   // One read op = one LDS fragment read: A blocks first, then B blocks (K x N: two
   // transpose reads of 4 k-values each per block).
   constexpr int A_OPS = AKM ? 2 * MB : MB;
@@ -590,37 +570,29 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       tr_read(lds_addr(Bs + b_rd[j]) + ks * KMF * 256 + half * 1024, B[j], half);
     }
   };
-  // (16x16 blocks: B first, so that the A reads are the youngest, as in the K loop)
   auto read_frags = [&](const char* As, int ks, u32x4* A, u32x4* B) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < N_RD; ++q) read_op(As, ks, MF == 16 ? (q + A_OPS) % N_RD : q, A, B);
+    for (int r = 0; r < N_RD; ++r) read_op(As, ks, r, A, B);
   };
   // Wait for every outstanding LDS read and tie the wait to the fragments the transpose
   // reads wrote, so no MFMA that consumes them can be scheduled above it.
-  // (LDS reads complete in issue order: waiting until at most NL are outstanding completes
-  // all but the NL youngest; no scalar memory load is in flight inside the K loop)
-  auto tie4 = [&](u32x4* F, auto n_c, auto nl_c) __attribute__((always_inline)) {
+  auto tie4 = [&](u32x4* F, auto n_c) __attribute__((always_inline)) {
     constexpr int NF = decltype(n_c)::value;
-    constexpr int NL = decltype(nl_c)::value;
     static_assert(NF == 1 || NF == 2 || NF == 4 || NF == 8, "unsupported fragment count");
-    static_assert(NL >= 0 && NL <= 15, "lgkmcnt range");
     if constexpr (NF == 8) {
-      asm volatile("s_waitcnt lgkmcnt(%8)"
-                   : "+v"(F[0]), "+v"(F[1]), "+v"(F[2]), "+v"(F[3]), "+v"(F[4]), "+v"(F[5]), "+v"(F[6]), "+v"(F[7])
-                   : "n"(NL));
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(F[0]), "+v"(F[1]), "+v"(F[2]), "+v"(F[3]), "+v"(F[4]), "+v"(F[5]), "+v"(F[6]), "+v"(F[7]));
     } else if constexpr (NF == 4) {
-      asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(F[0]), "+v"(F[1]), "+v"(F[2]), "+v"(F[3]) : "n"(NL));
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F[0]), "+v"(F[1]), "+v"(F[2]), "+v"(F[3]));
     } else if constexpr (NF == 2) {
-      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(F[0]), "+v"(F[1]) : "n"(NL));
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F[0]), "+v"(F[1]));
     } else {
-      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(F[0]) : "n"(NL));
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(F[0]));
     }
   };
-  // NL: LDS reads issued after the last transpose read of B that may stay in flight (the
-  // A fragments of 16x16 blocks that are read after B, see reads_after_b)
-  auto lgkm_fence = [&](u32x4* A, u32x4* B, auto nl_c) __attribute__((always_inline)) {
-    if constexpr (AKM) tie4(A, std::integral_constant<int, MB>{}, std::integral_constant<int, 0>{});
-    if constexpr (BLAY == L_KN) tie4(B, std::integral_constant<int, NB>{}, nl_c);
+  auto lgkm_fence = [&](u32x4* A, u32x4* B) __attribute__((always_inline)) {
+    if constexpr (AKM) tie4(A, std::integral_constant<int, MB>{});
+    if constexpr (BLAY == L_KN) tie4(B, std::integral_constant<int, NB>{});
   };
   // The instruction order inside a k-step is fixed explicitly: every sched_barrier below
   // stops the scheduler from moving instructions across it.  Each MFMA is followed by its
@@ -649,13 +621,11 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     constexpr int T0 = decltype(t0_c)::value, T1 = decltype(t1_c)::value;
     // fragment reads per MFMA so that they finish (when the slice is long enough) 4 MFMAs
     // before the end of the slice
-    constexpr int RSPAN = (T1 - T0) > 8 ? (T1 - T0) - 4 : (T1 - T0);
+    // (16x16 blocks: 12 MFMAs before the end, as the MFMAs are half as long; the k-step's
+    // first MFMA then finds its fragments landed)
+    constexpr int RTAIL = MF == 16 ? 12 : 4;
+    constexpr int RSPAN = (T1 - T0) > 2 * RTAIL ? (T1 - T0) - RTAIL : ((T1 - T0) > 8 ? (T1 - T0) - 4 : (T1 - T0));
     constexpr int RPM = (N_RD + RSPAN - 1) / RSPAN;
-    // 16x16 blocks: the B reads spread over the first half of the window, and A fragment i
-    // read right after the last MFMA of block row i (at the window's start if that is earlier)
-    constexpr int BSPAN = (T1 - T0) / 2 > 0 ? (T1 - T0) / 2 : 1;
-    constexpr int RPMB = (B_OPS + BSPAN - 1) / BSPAN;
-    constexpr int APF = A_OPS / MB;  // read ops per A fragment
 #pragma unroll
     for (int t = T0; t < T1; ++t) {
       acc[t / NB][t % NB] = E::mfma(A[t / NB], B[t % NB], acc[t / NB][t % NB]);
@@ -672,34 +642,16 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
             }
           }
       }
-      if constexpr (RD && MF == 32) {
+      if constexpr (RD) {
 #pragma unroll
         for (int r = (t - T0) * RPM; r < (t - T0 + 1) * RPM; ++r)
           if (r < N_RD) read_op(rstage, rks, r, RA, RB);
-      } else if constexpr (RD) {
-#pragma unroll
-        for (int r = (t - T0) * RPMB; r < (t - T0 + 1) * RPMB; ++r)
-          if (r < B_OPS) read_op(rstage, rks, A_OPS + r, RA, RB);
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const int at = (i + 1) * NB - 1 > T0 ? (i + 1) * NB - 1 : T0;
-          if (at == t) {
-#pragma unroll
-            for (int h = 0; h < APF; ++h) read_op(rstage, rks, i * APF + h, RA, RB);
-          }
-        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   using Z_ = std::integral_constant<int, 0>;
   using H_ = std::integral_constant<int, HB>;
-  // A reads issued after the last B read of a reading window [T0, NMMA) (16x16 blocks with a
-  // K x N B; 0 otherwise): the fence before the next slice leaves them in flight
-  using NLH_ = std::integral_constant<int, (MF == 16 && !AKM && BLAY == L_KN)
-                                                ? reads_after_b(HB, NMMA, MB, NB, B_OPS, A_OPS / MB) : 0>;
-  using NL0_ = std::integral_constant<int, (MF == 16 && !AKM && BLAY == L_KN)
-                                                ? reads_after_b(0, NMMA, MB, NB, B_OPS, A_OPS / MB) : 0>;
   using W_ = std::integral_constant<int, NMMA>;
   static_assert(!VST || DWIN <= GBAR, "register-staged writes must precede the k-step barrier");
   constexpr int DPRE_RAW = ((GBAR + DSTRIDE - 1) / DSTRIDE) * DPER;
@@ -733,12 +685,11 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     const KnSrc kr = kn_rsrc(kl);
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) {
-      u32x4* A = fa[((B0 + ks) & 1) % NFA];
+      u32x4* A = fa[(B0 + ks) & 1];
       u32x4* B = fb[(B0 + ks) & 1];
-      u32x4* RA = fa[((B0 + ks + 1) & 1) % NFA];
+      u32x4* RA = fa[(B0 + ks + 1) & 1];
       u32x4* RB = fb[(B0 + ks + 1) & 1];
-      if (ks == 0) lgkm_fence(A, B, NLH_{});
-      else lgkm_fence(A, B, NL0_{});
+      lgkm_fence(A, B);
       __builtin_amdgcn_sched_barrier(0);
       if (ks == 0)
         slice(T_{}, std::integral_constant<int, 0>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB);
@@ -750,12 +701,12 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     constexpr int L = (B0 + KS - 1) & 1;  // buffer of the last slice
     constexpr int NX = (B0 + KS) & 1;     // buffer of the next k-step's first slice
     using GL = std::integral_constant<int, (KS - 1) * NMMA>;
-    lgkm_fence(fa[L % NFA], fb[L], std::conditional_t<KS == 1, NLH_, NL0_>{});
+    lgkm_fence(fa[L], fb[L]);
     __builtin_amdgcn_sched_barrier(0);
-    slice(F_{}, GL{}, fa[L % NFA], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[NX % NFA], fb[NX]);
+    slice(F_{}, GL{}, fa[L], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[NX], fb[NX]);
     ring_barrier(std::integral_constant<int, VMC_LOOP>{});
     __builtin_amdgcn_sched_barrier(0);
-    slice(T_{}, GL{}, fa[L % NFA], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[NX % NFA], fb[NX]);
+    slice(T_{}, GL{}, fa[L], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[NX], fb[NX]);
   };
   using P0_ = std::integral_constant<int, 0>;
   using P1_ = std::integral_constant<int, 1>;
@@ -776,6 +727,10 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       for (int s = 0; s < NST - 1; ++s) issue_tile(s, smem + s * TR::STAGE);
     }
     ring_barrier(std::integral_constant<int, VMC_PRO>{});
+    // the same wait, visible to the compiler (the barrier's is inline asm): with no scalar
+    // or LDS load of its own in flight at the K loop's entry, its waits inside the loop
+    // count the fragment reads exactly instead of waiting for all of them
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited for
     __builtin_amdgcn_sched_barrier(0);
     read_frags(smem, 0, fa[0], fb[0]);
     if constexpr (KS % 2 == 0) {
@@ -793,8 +748,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // loads issued past the last k-step (they read as zeros) must land before LDS is reused
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if constexpr (MF == 16) mfma_drain();
-  lgkm_fence(fa[0], fb[0], std::integral_constant<int, 0>{});
-  lgkm_fence(fa[NFA - 1], fb[1], std::integral_constant<int, 0>{});
+  lgkm_fence(fa[0], fb[0]);
+  lgkm_fence(fa[1], fb[1]);
   __syncthreads();
 
   // ---------------------------------------------------------------- split-K
