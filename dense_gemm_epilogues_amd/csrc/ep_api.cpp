@@ -163,7 +163,7 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   // fastest wherever it fills the chip.
   // (the configuration run for a 256x256 tile, 16x16x32 or register-staged, is chosen by
   // pick_cfg's rule, not by this model)
-  static const double kEff[kNumTileCfgs] = {1.0, 0.70, 0.80, 0.80, 0.85, 0.97, 0.80, 0.82, 0.0, 0.0};
+  static const double kEff[kNumTileCfgs] = {1.0, 0.70, 0.80, 0.80, 0.85, 0.97, 0.80, 0.82, 0.0, 0.0, 0.0};
   int best = 0;
   double best_t = 1e300;
   for (int c = 0; c < kNumTileCfgs; ++c) {
@@ -181,23 +181,30 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   return best;
 }
 
-// The 256x256 tile is run with 16x16x32 MFMAs (configuration 9): on MI355X the card runs
-// these at a higher clock for the same power, and the kernel measured 2-7 % faster than the
-// 32x32x16 form for both B layouts, every workload shape from one round of tiles (4096^3) to
-// 64 (65536 x 8192 x 16384), N x K operands whose 32 KiB row stride makes L2 sets conflict,
-// the split-K down GEMM and the dSwiGLU GEMM.  The exception is the dual-B SwiGLU GEMM with
-// N x K weights at up to 16 rounds (M 2048, I 17408: 0.624 vs 0.638 ms): there the 64-deep
-// register-staged 32x32 configuration, whose loads arrive as whole 128-byte lines one
-// k-step ahead, stays ahead.  The unfused path's GEMM takes the tile the fused epilog would.
+// The 256x256 tile is run with 16x16x32 MFMAs: on MI355X the card runs these at a higher
+// clock for the same power, and the kernel measured 2-7 % faster than the 32x32x16 form for
+// both B layouts, every workload shape from one round of tiles (4096^3) to 64 (65536 x 8192
+// x 16384), N x K operands whose 32 KiB row stride makes L2 sets conflict, the split-K down
+// GEMM and the dSwiGLU GEMM.  When A and B together fit well within the 256 MB Infinity
+// Cache it takes the LDS layout free of bank conflicts (configuration 9: 4096^3 backward
+// 1174 -> 1195 TFLOP/s sustained); operands streamed from HBM take the layout that keeps
+// k-contiguous rows whole in each DMA lane quad (configuration 10: 65536 x 16384 x 8192
+// backward 1149 -> 1177 TFLOP/s; the 2048 x 5120 x 17408 down GEMM's split partials, 250 MB
+// of operands over only 160 tiles, 333 -> 302 us).  The exception is the dual-B SwiGLU GEMM
+// with N x K weights at up to 16 rounds (M 2048, I 17408: 0.624 vs 0.638 ms): there the
+// 64-deep register-staged 32x32 configuration, whose loads arrive as whole 128-byte lines
+// one k-step ahead, stays ahead.  The unfused path's GEMM takes the tile the fused epilog
+// would.
 constexpr int kVstCfg = 8;
 constexpr int kM16Cfg = 9;
+constexpr int kM16RowsCfg = 10;
+constexpr double kCacheResidentBytes = 128.0 * 1024 * 1024;
 int pick_cfg(const ep_shape* s, int model_cfg, int cus, bool dual) {
   if (model_cfg != 0) return model_cfg;
-  if (dual && s->a_layout == EP_A_MK && s->b_layout == EP_B_NK) {
-    const int64_t tiles = ((s->m + 255) / 256) * ((s->n + 127) / 128);
-    if (tiles <= 16LL * cus) return kVstCfg;
-  }
-  return kM16Cfg;
+  const int64_t tiles = ((s->m + 255) / 256) * ((s->n + (dual ? 127 : 255)) / (dual ? 128 : 256));
+  if (dual && s->a_layout == EP_A_MK && s->b_layout == EP_B_NK && tiles <= 16LL * cus) return kVstCfg;
+  const double operand_bytes = ((double)s->m + (dual ? 2.0 : 1.0) * (double)s->n) * (double)s->k * 2.0;
+  return operand_bytes <= kCacheResidentBytes ? kM16Cfg : kM16RowsCfg;
 }
 
 // Split-K: how many K ranges per tile.  Only grids that leave CUs idle are split: the time
@@ -526,9 +533,8 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
                       : pick_cfg(s, choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount),
                                  prop.multiProcessorCount, kernel_dual);
 
-  ep_plan_s* h = new (std::nothrow) ep_plan_s;
+  ep_plan_s* h = new (std::nothrow) ep_plan_s{};  // every member zero / null
   if (!h) return fail(EP_ERR_OUT_OF_MEMORY, "host allocation failed");
-  memset(h, 0, sizeof *h);
   h->magic = kMagic;
   h->shape = *s;
   h->dtype = dtype;
@@ -672,6 +678,12 @@ static ep_status check_launch(const char* what) {
   return EP_OK;
 }
 
+// status of a launch whose launcher returned the runtime's error itself
+static ep_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return EP_OK;
+}
+
 ep_status ep_execute(ep_handle h, void* stream) {
   if (!h || h->magic != kMagic) return fail(EP_ERR_INVALID_ARG, "invalid or freed handle");
   hipStream_t s = (hipStream_t)stream;
@@ -695,7 +707,7 @@ ep_status ep_execute(ep_handle h, void* stream) {
   const bool bgrad_epi = h->epilog == EP_EPILOG_DRELU_BGRAD || h->epilog == EP_EPILOG_DGELU_BGRAD;
   if (h->opt.path == EP_PATH_FUSED) {
     if (bgrad_epi && h->opt.bgrad_mode == EP_BGRAD_ATOMIC) {
-      if (launch_fill_zero_f32(h->io.bgrad, N, s) != hipSuccess) return check_launch("fill_zero");
+      if ((st = launched(launch_fill_zero_f32(h->io.bgrad, N, s), "fill_zero")) != EP_OK) return st;
     }
     if (h->splits > 1) {
       h->launch_partial(h->args, s);
@@ -707,64 +719,62 @@ ep_status ep_execute(ep_handle h, void* stream) {
       if ((st = check_launch("fused gemm")) != EP_OK) return st;
     }
     if (bgrad_epi && h->opt.bgrad_mode == EP_BGRAD_TWO_PASS) {
-      launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s);
-      if ((st = check_launch("bgrad_reduce")) != EP_OK) return st;
+      if ((st = launched(launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s), "bgrad_reduce")) != EP_OK)
+        return st;
     }
     return EP_OK;
   }
   // ---- unfused baseline: DEFAULT GEMM(s) then separate kernels through HBM, in place on d
+  // (each launcher returns the launch's error: the status it took from the runtime is not
+  // there for a later check_launch to see)
   h->launch(h->args, s);
   if ((st = check_launch("gemm")) != EP_OK) return st;
   switch (h->epilog) {
     case EP_EPILOG_DEFAULT:
-      break;
+      return EP_OK;
     case EP_EPILOG_BIAS:
-      launch_bias_add(dt, sh.d, sh.ldd, h->io.bias, M, N, s);
-      break;
+      return launched(launch_bias_add(dt, sh.d, sh.ldd, h->io.bias, M, N, s), "bias_add");
     case EP_EPILOG_RELU_BIAS:
     case EP_EPILOG_RELU_AUX_BIAS:
-      launch_bias_add(dt, sh.d, sh.ldd, h->io.bias, M, N, s);
-      if ((st = check_launch("bias_add")) != EP_OK) return st;
-      launch_relu_pack(dt, sh.d, sh.ldd, sh.d, sh.ldd, h->io.relu_aux, h->io.ld_aux, M, N,
-                       h->epilog == EP_EPILOG_RELU_AUX_BIAS, s);
-      break;
+      if ((st = launched(launch_bias_add(dt, sh.d, sh.ldd, h->io.bias, M, N, s), "bias_add")) != EP_OK) return st;
+      return launched(launch_relu_pack(dt, sh.d, sh.ldd, sh.d, sh.ldd, h->io.relu_aux, h->io.ld_aux, M, N,
+                                       h->epilog == EP_EPILOG_RELU_AUX_BIAS, s),
+                      "relu_pack");
     case EP_EPILOG_DRELU_BGRAD:
-      launch_mask_apply(dt, sh.d, sh.ldd, h->io.relu_aux_in, h->io.ld_aux, sh.d, sh.ldd, M, N, s);
-      if ((st = check_launch("mask_apply")) != EP_OK) return st;
-      launch_colsum_partial(dt, sh.d, sh.ldd, h->part, M, N, h->colsum_rows, s);
-      if ((st = check_launch("colsum")) != EP_OK) return st;
-      launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s);
-      break;
+      if ((st = launched(launch_mask_apply(dt, sh.d, sh.ldd, h->io.relu_aux_in, h->io.ld_aux, sh.d, sh.ldd, M, N, s),
+                         "mask_apply")) != EP_OK)
+        return st;
+      if ((st = launched(launch_colsum_partial(dt, sh.d, sh.ldd, h->part, M, N, h->colsum_rows, s), "colsum")) != EP_OK)
+        return st;
+      return launched(launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s), "bgrad_reduce");
     case EP_EPILOG_SWIGLU:
       h->launch(h->args2, s);
       if ((st = check_launch("gemm up")) != EP_OK) return st;
-      launch_silu_mul(dt, h->uf.z, h->uf.z2, h->uf.ldz, sh.d, sh.ldd, M, N, s);
-      break;
+      return launched(launch_silu_mul(dt, h->uf.z, h->uf.z2, h->uf.ldz, sh.d, sh.ldd, M, N, s), "silu_mul");
     case EP_EPILOG_SWIGLU_AUX:
       h->launch(h->args2, s);
       if ((st = check_launch("gemm up")) != EP_OK) return st;
-      launch_silu_mul(dt, h->io.d2, (const char*)h->io.d2 + N * 2, h->io.ldd2, sh.d, sh.ldd, M, N, s);
-      break;
+      return launched(launch_silu_mul(dt, h->io.d2, (const char*)h->io.d2 + N * 2, h->io.ldd2, sh.d, sh.ldd, M, N, s),
+                      "silu_mul");
     case EP_EPILOG_DSWIGLU:
-      launch_dswiglu(dt, sh.d, sh.ldd, h->io.gate, h->io.up, h->io.ld_gu, sh.d, sh.ldd, h->io.d2, h->io.ldd2, M,
-                     N, s);
-      break;
+      return launched(launch_dswiglu(dt, sh.d, sh.ldd, h->io.gate, h->io.up, h->io.ld_gu, sh.d, sh.ldd, h->io.d2,
+                                     h->io.ldd2, M, N, s),
+                      "dswiglu");
     case EP_EPILOG_GELU_BIAS:
     case EP_EPILOG_GELU_AUX_BIAS:
-      launch_bias_add(dt, sh.d, sh.ldd, h->io.bias, M, N, s);
-      if ((st = check_launch("bias_add")) != EP_OK) return st;
-      launch_gelu_apply(dt, sh.d, sh.ldd, h->epilog == EP_EPILOG_GELU_AUX_BIAS ? h->io.gelu_aux : nullptr,
-                        h->io.ld_gelu_aux, M, N, s);
-      break;
+      if ((st = launched(launch_bias_add(dt, sh.d, sh.ldd, h->io.bias, M, N, s), "bias_add")) != EP_OK) return st;
+      return launched(launch_gelu_apply(dt, sh.d, sh.ldd, h->epilog == EP_EPILOG_GELU_AUX_BIAS ? h->io.gelu_aux : nullptr,
+                                        h->io.ld_gelu_aux, M, N, s),
+                      "gelu_apply");
     case EP_EPILOG_DGELU_BGRAD:
-      launch_dgelu_apply(dt, sh.d, sh.ldd, h->io.gelu_aux, h->io.ld_gelu_aux, M, N, s);
-      if ((st = check_launch("dgelu_apply")) != EP_OK) return st;
-      launch_colsum_partial(dt, sh.d, sh.ldd, h->part, M, N, h->colsum_rows, s);
-      if ((st = check_launch("colsum")) != EP_OK) return st;
-      launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s);
-      break;
+      if ((st = launched(launch_dgelu_apply(dt, sh.d, sh.ldd, h->io.gelu_aux, h->io.ld_gelu_aux, M, N, s),
+                         "dgelu_apply")) != EP_OK)
+        return st;
+      if ((st = launched(launch_colsum_partial(dt, sh.d, sh.ldd, h->part, M, N, h->colsum_rows, s), "colsum")) != EP_OK)
+        return st;
+      return launched(launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s), "bgrad_reduce");
   }
-  return check_launch("unfused epilogue");
+  return EP_OK;
 }
 
 ep_status ep_free(ep_handle h) {

@@ -60,18 +60,27 @@ struct GemmArgs {
 //         only); 0: global -> LDS directly;
 //   mf  = edge of the MFMA output block: 32 (v_mfma_f32_32x32x16, 16 k per instruction) or
 //         16 (v_mfma_f32_16x16x32, 32 k per instruction; a quarter of the accumulator
-//         traffic per instruction for half the FLOP).
+//         traffic per instruction for half the FLOP);
+//   cfl = 1 (16x16 only): k-contiguous tiles in the LDS layout whose fragment reads are free
+//         of bank conflicts; each DMA lane quad then fetches 16 bytes of four different rows
+//         instead of 64 contiguous bytes of one.  0: rows kept whole (2-way bank conflicts).
 struct TileCfg {
-  int bm, bnt, bk, nst, occ, vst, mf;
+  int bm, bnt, bk, nst, occ, vst, mf, cfl;
   const char* name;
 };
-constexpr int kNumTileCfgs = 10;
+constexpr int kNumTileCfgs = 11;
 constexpr TileCfg kTileCfgs[kNumTileCfgs] = {
-    {256, 256, 32, 4, 1, 0, 32, "256x256x32x4st"},     {128, 128, 64, 4, 1, 0, 32, "128x128x64x4st"},
-    {256, 128, 32, 4, 1, 0, 32, "256x128x32x4st"},     {128, 256, 32, 4, 1, 0, 32, "128x256x32x4st"},
-    {256, 256, 64, 2, 1, 0, 32, "256x256x64x2st"},     {256, 256, 32, 5, 1, 0, 32, "256x256x32x5st"},
-    {256, 128, 32, 3, 2, 0, 32, "256x128x32x3st_2wg"}, {128, 256, 32, 3, 2, 0, 32, "128x256x32x3st_2wg"},
-    {256, 256, 64, 2, 1, 1, 32, "256x256x64x2st_vst"}, {256, 256, 32, 4, 1, 0, 16, "256x256x32x4st_m16"},
+    {256, 256, 32, 4, 1, 0, 32, 0, "256x256x32x4st"},
+    {128, 128, 64, 4, 1, 0, 32, 0, "128x128x64x4st"},
+    {256, 128, 32, 4, 1, 0, 32, 0, "256x128x32x4st"},
+    {128, 256, 32, 4, 1, 0, 32, 0, "128x256x32x4st"},
+    {256, 256, 64, 2, 1, 0, 32, 0, "256x256x64x2st"},
+    {256, 256, 32, 5, 1, 0, 32, 0, "256x256x32x5st"},
+    {256, 128, 32, 3, 2, 0, 32, 0, "256x128x32x3st_2wg"},
+    {128, 256, 32, 3, 2, 0, 32, 0, "128x256x32x3st_2wg"},
+    {256, 256, 64, 2, 1, 1, 32, 0, "256x256x64x2st_vst"},
+    {256, 256, 32, 4, 1, 0, 16, 1, "256x256x32x4st_m16"},
+    {256, 256, 32, 4, 1, 0, 16, 0, "256x256x32x4st_m16rows"},
 };
 
 typedef void (*GemmLauncher)(const GemmArgs&, hipStream_t);

@@ -54,6 +54,7 @@ constexpr int cfg_nst(int cfg) { return kTileCfgs[cfg].nst; }
 constexpr int cfg_occ(int cfg) { return kTileCfgs[cfg].occ; }
 constexpr bool cfg_vst(int cfg) { return kTileCfgs[cfg].vst != 0; }
 constexpr int cfg_mf(int cfg) { return kTileCfgs[cfg].mf; }
+constexpr bool cfg_cfl(int cfg) { return kTileCfgs[cfg].cfl != 0; }
 
 // The 16x16x32 MFMAs are issued as inline asm whose accumulator operand must sit in AGPRs:
 // with the builtin, the register allocator spreads the 64 four-register accumulators of a
@@ -217,6 +218,31 @@ __device__ __forceinline__ int swf(int r) {
   return (r ^ (r >> 3)) & (CPR - 1);
 }
 
+// LDS layouts of the 16x16x32 configurations (32-deep k-steps).  With the 32x32 layouts every
+// 16x16 fragment read conflicts on two LDS banks (SQ_LDS_BANK_CONFLICT = half of the LDS
+// cycles on MI355X; a probe of the read pattern measured the same for every XOR swizzle of
+// the chunks within a row, and none for the layouts below):
+//   * k-contiguous tiles, 64-byte rows, 1 KiB slots of 16 rows (configurations with cfl):
+//     the 16-byte chunk c (k-values 8c .. 8c+7) of slot row r is stored in slot row r ^ 4c,
+//     at chunk position r / 4.  A fragment read (16 rows at one chunk per 16-lane group) then
+//     covers 16 distinct bank groups; the layout is a permutation of each slot, and slot
+//     byte 16 L holds row 4 (L & 3) + (L >> 2 & 3), chunk (L >> 4 ^ L) & 3.  Each DMA lane
+//     quad then reads 16 bytes of four rows: measured 1-2 % faster at one round of tiles
+//     (operands mostly in the Infinity Cache), 2.5 % slower at 64 rounds streamed from HBM,
+//     where the configuration without cfl keeps rows whole (as for 32x32 blocks).
+//   * [BK k][128 n] sub-tiles: as for 32x32 blocks (64-byte segment g of k-row k at segment
+//     g ^ (k & 3)), and in addition the two 32-byte halves of each segment swap when bit 3 of
+//     k is set, so that the lane groups reading k-rows 8 apart use opposite halves.
+__device__ __forceinline__ int m16_slot_row(int lane) { return 4 * (lane & 3) + ((lane >> 2) & 3); }
+__device__ __forceinline__ int m16_slot_chunk(int lane) { return ((lane >> 4) ^ lane) & 3; }
+__device__ __forceinline__ int m16_frag_addr(int r, int c) {  // byte offset of row r, chunk c
+  return (((r & ~15) | ((r & 15) ^ (c << 2))) << 6) + (((r >> 2) & 3) << 4);
+}
+__device__ __forceinline__ int kn_col(int pch, int k, bool m16) {  // first column of 16-byte chunk pch
+  const int piece = m16 ? ((pch & 3) ^ (((k >> 3) & 1) << 1)) : (pch & 3);
+  return (((pch >> 2) ^ (k & 3)) << 5) + (piece << 3);
+}
+
 template <int DT, int LAY, int EPI, int CFG>
 struct GemmTraits {
   static constexpr int BM = cfg_bm(CFG), BNT = cfg_bnt(CFG), BK = cfg_bk(CFG), NST = cfg_nst(CFG);
@@ -262,6 +288,9 @@ struct GemmTraits {
       (EPI == E_DSWIGLU || EPI == E_DRELU_BGRAD || EPI == E_DGELU_BGRAD) ? 1 : (ITERS < 8 ? ITERS : 8);
   static_assert(KS == 1 || KS == 2 || KS == 4, "k-slices per step: 1, 2 or 4");
   static_assert(MF == 32 || MF == 16, "MFMA block edge");
+  static_assert(MF == 32 || (BK == 32 && !cfg_vst(CFG)), "the 16x16 LDS layouts are for 32-deep k-steps loaded directly");
+  static_assert(MF == 16 || !cfg_cfl(CFG), "the conflict-free k-contiguous layout is for 16x16 blocks");
+  static constexpr bool CFL = cfg_cfl(CFG);
   static_assert(A_SLOTS >= 1 && B_SLOTS >= 1, "tile too small for 1 KiB DMA slots");
   static_assert(LDS_BYTES * cfg_occ(CFG) <= 160 * 1024, "LDS budget");
 };
@@ -334,13 +363,12 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     if constexpr (AKM) {
       const int t = (wave * A_SLOTS + q) % TR::KN_SPS;
       const int k = 4 * t + (lane >> 4);
-      const int pch = lane & 15;
-      const int ml = (((pch >> 2) ^ (k & 3)) << 5) + ((pch & 3) << 3);
+      const int ml = kn_col(lane & 15, k, MF == 16);
       a_voff[q] = (m0 + wa_mbase + ml < M) ? (uint32_t)(k * p.lda * 2) + ml * 2 : kOOB;
       a_klim[q] = 0;
     } else {
-      const int row = (wave * A_SLOTS + q) * RPS + lane / CPR;
-      const int c = (lane % CPR) ^ swf<CPR>(row);
+      const int row = (wave * A_SLOTS + q) * RPS + (TR::CFL ? m16_slot_row(lane) : lane / CPR);
+      const int c = TR::CFL ? m16_slot_chunk(lane) : (lane % CPR) ^ swf<CPR>(row);
       a_voff[q] = (uint32_t)(row * p.lda * 2) + c * 16;
       a_klim[q] = K - c * 8;
     }
@@ -361,18 +389,18 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   for (int q = 0; q < B_SLOTS; ++q) {
     const int s = wave * B_SLOTS + q;
     if constexpr (BLAY == L_NK) {
-      const int row = s * RPS + lane / CPR;
-      const int c = (lane % CPR) ^ swf<CPR>(row);
+      const int row = s * RPS + (TR::CFL ? m16_slot_row(lane) : lane / CPR);
+      const int c = TR::CFL ? m16_slot_chunk(lane) : (lane % CPR) ^ swf<CPR>(row);
       const int srow = DUAL ? (row % (BNT / 2)) : row;
       b_voff[q] = (uint32_t)(srow * p.ldb * 2) + c * 16;
       b_klim[q] = K - c * 8;
     } else {
       // B tile = BNT/128 sub-tiles of [BK k][128 n] (256-byte rows); 64-byte segment g of
-      // k-row k is stored at segment g ^ (k & 3).  DUAL: sub-tile 0 = gate, 1 = up columns.
+      // k-row k is stored at segment g ^ (k & 3) (see kn_col).  DUAL: sub-tile 0 = gate,
+      // 1 = up columns.
       const int t = s % TR::KN_SPS;
       const int k = 4 * t + (lane >> 4);
-      const int pch = lane & 15;
-      const int nl = (((pch >> 2) ^ (k & 3)) << 5) + ((pch & 3) << 3);
+      const int nl = kn_col(lane & 15, k, MF == 16);
       // relative to the sub-tile's column base; columns past N read as zero
       b_voff[q] = (n0 + w_cbase + nl < N) ? (uint32_t)(k * p.ldb * 2) + nl * 2 : kOOB;
       b_klim[q] = 0;
@@ -485,13 +513,16 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     const int g = lane >> 4, i = lane & 15;
     const int u = base >> 7, cb = base & 127;
     const int krow = MF == 32 ? 8 * (g >> 1) + (i >> 2) : 8 * g + (i >> 2);
-    const int cbyte = MF == 32 ? 32 * (g & 1) : 2 * (cb & 31);
+    const int cbyte = MF == 32 ? 32 * (g & 1) : 32 * (((cb & 31) >> 4) ^ ((krow >> 3) & 1));
     return (uint32_t)(u * TR::KN_SUB + krow * 256 + ((((cb >> 5) ^ (i >> 2)) & 3) << 6) + cbyte + 8 * (i & 3));
   };
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     if constexpr (AKM) {
       a_rd[i] = tr_addr(wm * WTM + i * MF);
+      a_f[i] = 0;
+    } else if constexpr (TR::CFL) {
+      a_rd[i] = m16_frag_addr(wm * WTM + i * MF + (lane & 15), kq);
       a_f[i] = 0;
     } else {
       const int row = wm * WTM + i * MF + (lane & (MF - 1));
@@ -507,7 +538,10 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     } else {
       brow = wn * WTB + j * MF;
     }
-    if constexpr (BLAY == L_NK) {
+    if constexpr (BLAY == L_NK && TR::CFL) {
+      b_rd[j] = m16_frag_addr(brow + (lane & 15), kq);
+      b_f[j] = 0;
+    } else if constexpr (BLAY == L_NK) {
       const int row = brow + (lane & (MF - 1));
       b_rd[j] = row * ROWB;
       b_f[j] = swf<CPR>(row);
@@ -556,13 +590,17 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       if constexpr (AKM) {
         const int i = r >> 1, half = r & 1;
         tr_read(lds_addr(As + a_rd[i]) + ks * KMF * 256 + half * 1024, A[i], half);
+      } else if constexpr (TR::CFL) {
+        A[r] = *(const u32x4*)(As + a_rd[r]);  // (one k-slice per k-step)
       } else {
         A[r] = *(const u32x4*)(As + a_rd[r] + ((((ks * CPS + kq) ^ a_f[r]) & (CPR - 1)) << 4));
       }
       return;
     }
     const char* Bs = As + TR::A_BYTES;
-    if constexpr (BLAY == L_NK) {
+    if constexpr (BLAY == L_NK && TR::CFL) {
+      B[r - A_OPS] = *(const u32x4*)(Bs + b_rd[r - A_OPS]);
+    } else if constexpr (BLAY == L_NK) {
       const int j = r - A_OPS;
       B[j] = *(const u32x4*)(Bs + b_rd[j] + ((((ks * CPS + kq) ^ b_f[j]) & (CPR - 1)) << 4));
     } else {

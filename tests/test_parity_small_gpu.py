@@ -154,9 +154,9 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
     p.free()
 
 
-# every tile configuration of the library (9 issues 16x16x32 MFMAs); those with a
+# every tile configuration of the library (9 and 10 issue 16x16x32 MFMAs); those with a
 # 128-row B tile cannot hold the gate and up sub-tiles of a K x N dual B operand
-NUM_TILE_CFGS = 10
+NUM_TILE_CFGS = 11
 BNT128_CFGS = (1, 2, 6)
 
 
@@ -182,10 +182,10 @@ def test_small_shapes_fused(epi, dtname, layout, cfg):
 @pytest.mark.parametrize("epi", EPIS)
 def test_split_k(epi, layout, splits):
     """K split over 2-4 workgroups per tile (fp32 partials, then a fixup launch that sums them
-    and runs the epilog): every epilog, both dtypes, four tile configurations, a K that
+    and runs the epilog): every epilog, both dtypes, five tile configurations, a K that
     divides unevenly and a K too short for the requested number of ranges."""
     require_gpu()
-    for cfg in (0, 1, 6, 9):
+    for cfg in (0, 1, 6, 9, 10):
         if epi in ("SWIGLU", "SWIGLU_AUX") and layout == "KN" and cfg in BNT128_CFGS:
             continue
         for dtname in ("f16", "bf16"):
@@ -233,10 +233,10 @@ def test_transposed_a(dtname, layout):
 
 
 @pytest.mark.parametrize("m,n,layout,ld_extra,dual,want_cfg", [
-    (4096, 4096, "NK", 64, False, 9),      # one round of 256x256 tiles: 16x16x32 MFMAs
+    (4096, 4096, "NK", 64, False, 9),      # one round of 256x256 tiles: 16x16x32, conflict-free LDS layout
     (4096, 4096, "KN", 0, False, 9),
-    (16384, 32768, "NK", 64, False, 9),    # 32 rounds
-    (16384, 32768, "NK", 0, False, 9),     # 32 rounds, B rows 32 KiB apart
+    (16384, 32768, "NK", 64, False, 10),   # 32 rounds: 16x16x32, rows kept whole
+    (16384, 32768, "NK", 0, False, 10),    # 32 rounds, B rows 32 KiB apart
     (2048, 8192, "NK", 0, True, 8),        # dual-B SwiGLU, N x K weights, 2 rounds: register-staged
 ])
 def test_planner_tile_choice(m, n, layout, ld_extra, dual, want_cfg):
