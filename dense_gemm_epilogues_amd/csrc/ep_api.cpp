@@ -185,26 +185,23 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
 // clock for the same power, and the kernel measured 2-7 % faster than the 32x32x16 form for
 // both B layouts, every workload shape from one round of tiles (4096^3) to 64 (65536 x 8192
 // x 16384), N x K operands whose 32 KiB row stride makes L2 sets conflict, the split-K down
-// GEMM and the dSwiGLU GEMM.  When A and B together fit well within the 256 MB Infinity
-// Cache it takes the LDS layout free of bank conflicts (configuration 9: 4096^3 backward
-// 1174 -> 1195 TFLOP/s sustained); operands streamed from HBM take the layout that keeps
-// k-contiguous rows whole in each DMA lane quad (configuration 10: 65536 x 16384 x 8192
-// backward 1149 -> 1177 TFLOP/s; the 2048 x 5120 x 17408 down GEMM's split partials, 250 MB
-// of operands over only 160 tiles, 333 -> 302 us).  The exception is the dual-B SwiGLU GEMM
-// with N x K weights at up to 16 rounds (M 2048, I 17408: 0.624 vs 0.638 ms): there the
-// 64-deep register-staged 32x32 configuration, whose loads arrive as whole 128-byte lines
-// one k-step ahead, stays ahead.  The unfused path's GEMM takes the tile the fused epilog
-// would.
+// GEMM and the dSwiGLU GEMM.  Of its two LDS layouts for k-contiguous tiles (both free of
+// bank conflicts), whole rows (configuration 10) measured faster wherever B is given N x K
+// (65536 x 16384 x 8192 backward 1173 -> 1213 TFLOP/s sustained, 16384 x 32768 x 4096
+// 1235 -> 1272, the 2048 x 5120 x 17408 down GEMM 0.396 -> 0.353 ms; 4096^3 on par), and
+// spread chunks (configuration 9) where only A is k-contiguous (4096^3 forward 1174 -> 1190,
+// 65536 x 8192 x 16384 forward 1205 -> 1231).  The exception is the dual-B SwiGLU GEMM with
+// N x K weights at up to 16 rounds of resident tiles: there the 64-deep register-staged
+// 32x32 configuration, whose loads arrive as whole 128-byte lines one k-step ahead, stays
+// ahead.  The unfused path's GEMM takes the tile the fused epilog would.
 constexpr int kVstCfg = 8;
-constexpr int kM16Cfg = 9;
+constexpr int kM16SpreadCfg = 9;
 constexpr int kM16RowsCfg = 10;
-constexpr double kCacheResidentBytes = 128.0 * 1024 * 1024;
 int pick_cfg(const ep_shape* s, int model_cfg, int cus, bool dual) {
   if (model_cfg != 0) return model_cfg;
   const int64_t tiles = ((s->m + 255) / 256) * ((s->n + (dual ? 127 : 255)) / (dual ? 128 : 256));
   if (dual && s->a_layout == EP_A_MK && s->b_layout == EP_B_NK && tiles <= 16LL * cus) return kVstCfg;
-  const double operand_bytes = ((double)s->m + (dual ? 2.0 : 1.0) * (double)s->n) * (double)s->k * 2.0;
-  return operand_bytes <= kCacheResidentBytes ? kM16Cfg : kM16RowsCfg;
+  return s->b_layout == EP_B_NK ? kM16RowsCfg : kM16SpreadCfg;
 }
 
 // Split-K: how many K ranges per tile.  Only grids that leave CUs idle are split: the time

@@ -61,9 +61,10 @@ struct GemmArgs {
 //   mf  = edge of the MFMA output block: 32 (v_mfma_f32_32x32x16, 16 k per instruction) or
 //         16 (v_mfma_f32_16x16x32, 32 k per instruction; a quarter of the accumulator
 //         traffic per instruction for half the FLOP);
-//   cfl = 1 (16x16 only): k-contiguous tiles in the LDS layout whose fragment reads are free
-//         of bank conflicts; each DMA lane quad then fetches 16 bytes of four different rows
-//         instead of 64 contiguous bytes of one.  0: rows kept whole (2-way bank conflicts).
+//   cfl = 1 (16x16 only): k-contiguous tiles in the LDS layout that spreads each row's
+//         chunks over four slot rows; 0: rows kept whole (16x16: slot rows transposed as
+//         4 x 4).  Both keep the 16x16 fragment reads free of bank conflicts; with spread
+//         chunks each DMA lane quad fetches 16 bytes of four rows instead of one 64-byte piece.
 struct TileCfg {
   int bm, bnt, bk, nst, occ, vst, mf, cfl;
   const char* name;

@@ -219,21 +219,24 @@ __device__ __forceinline__ int swf(int r) {
 }
 
 // LDS layouts of the 16x16x32 configurations (32-deep k-steps).  With the 32x32 layouts every
-// 16x16 fragment read conflicts on two LDS banks (SQ_LDS_BANK_CONFLICT = half of the LDS
-// cycles on MI355X; a probe of the read pattern measured the same for every XOR swizzle of
-// the chunks within a row, and none for the layouts below):
-//   * k-contiguous tiles, 64-byte rows, 1 KiB slots of 16 rows (configurations with cfl):
+// 16x16 fragment read (16 rows at one chunk per 16-lane group) conflicts on two LDS banks
+// (SQ_LDS_BANK_CONFLICT = half of the LDS cycles on MI355X).  A probe of the read pattern
+// measured the same for every XOR swizzle of the chunks within a row, and none for:
+//   * k-contiguous tiles, 64-byte rows, 1 KiB slots of 16 rows, configurations with cfl:
 //     the 16-byte chunk c (k-values 8c .. 8c+7) of slot row r is stored in slot row r ^ 4c,
-//     at chunk position r / 4.  A fragment read (16 rows at one chunk per 16-lane group) then
-//     covers 16 distinct bank groups; the layout is a permutation of each slot, and slot
-//     byte 16 L holds row 4 (L & 3) + (L >> 2 & 3), chunk (L >> 4 ^ L) & 3.  Each DMA lane
-//     quad then reads 16 bytes of four rows: measured 1-2 % faster at one round of tiles
-//     (operands mostly in the Infinity Cache), 2.5 % slower at 64 rounds streamed from HBM,
-//     where the configuration without cfl keeps rows whole (as for 32x32 blocks).
+//     at chunk position r / 4; slot byte 16 L holds row 4 (L & 3) + (L >> 2 & 3), chunk
+//     (L >> 4 ^ L) & 3.  Each DMA lane quad then reads 16 bytes of four rows.
+//   * the same tiles without cfl: rows kept whole (each DMA lane quad reads one 64-byte row
+//     piece) with the 32x32 chunk swizzle, and slot row 4i + j stored in slot row 4j + i.
+//     Measured the faster of the two wherever B is given N x K (65536 x 16384 x 8192
+//     backward 1173 -> 1213 TFLOP/s sustained, the down GEMM 0.396 -> 0.353 ms), 1-2 %
+//     slower than spread chunks where only A is k-contiguous (B given K x N).
 //   * [BK k][128 n] sub-tiles: as for 32x32 blocks (64-byte segment g of k-row k at segment
 //     g ^ (k & 3)), and in addition the two 32-byte halves of each segment swap when bit 3 of
 //     k is set, so that the lane groups reading k-rows 8 apart use opposite halves.
 __device__ __forceinline__ int m16_slot_row(int lane) { return 4 * (lane & 3) + ((lane >> 2) & 3); }
+// whole-row layout: slot row 4i + j stored in slot row 4j + i (its own inverse)
+__device__ __forceinline__ int m16_row_perm(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int m16_slot_chunk(int lane) { return ((lane >> 4) ^ lane) & 3; }
 __device__ __forceinline__ int m16_frag_addr(int r, int c) {  // byte offset of row r, chunk c
   return (((r & ~15) | ((r & 15) ^ (c << 2))) << 6) + (((r >> 2) & 3) << 4);
@@ -367,7 +370,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       a_voff[q] = (m0 + wa_mbase + ml < M) ? (uint32_t)(k * p.lda * 2) + ml * 2 : kOOB;
       a_klim[q] = 0;
     } else {
-      const int row = (wave * A_SLOTS + q) * RPS + (TR::CFL ? m16_slot_row(lane) : lane / CPR);
+      const int row = (wave * A_SLOTS + q) * RPS +
+                      (TR::CFL ? m16_slot_row(lane) : (MF == 16 ? m16_row_perm(lane / CPR) : lane / CPR));
       const int c = TR::CFL ? m16_slot_chunk(lane) : (lane % CPR) ^ swf<CPR>(row);
       a_voff[q] = (uint32_t)(row * p.lda * 2) + c * 16;
       a_klim[q] = K - c * 8;
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   for (int q = 0; q < B_SLOTS; ++q) {
     const int s = wave * B_SLOTS + q;
     if constexpr (BLAY == L_NK) {
-      const int row = s * RPS + (TR::CFL ? m16_slot_row(lane) : lane / CPR);
+      const int row = s * RPS + (TR::CFL ? m16_slot_row(lane) : (MF == 16 ? m16_row_perm(lane / CPR) : lane / CPR));
       const int c = TR::CFL ? m16_slot_chunk(lane) : (lane % CPR) ^ swf<CPR>(row);
       const int srow = DUAL ? (row % (BNT / 2)) : row;
       b_voff[q] = (uint32_t)(srow * p.ldb * 2) + c * 16;
@@ -526,7 +530,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       a_f[i] = 0;
     } else {
       const int row = wm * WTM + i * MF + (lane & (MF - 1));
-      a_rd[i] = row * ROWB;
+      a_rd[i] = (MF == 16 ? m16_row_perm(row) : row) * ROWB;
       a_f[i] = swf<CPR>(row);
     }
   }
@@ -543,7 +547,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       b_f[j] = 0;
     } else if constexpr (BLAY == L_NK) {
       const int row = brow + (lane & (MF - 1));
-      b_rd[j] = row * ROWB;
+      b_rd[j] = (MF == 16 ? m16_row_perm(row) : row) * ROWB;
       b_f[j] = swf<CPR>(row);
     } else {
       b_rd[j] = tr_addr(brow);

@@ -233,10 +233,11 @@ def test_transposed_a(dtname, layout):
 
 
 @pytest.mark.parametrize("m,n,layout,ld_extra,dual,want_cfg", [
-    (4096, 4096, "NK", 64, False, 9),      # one round of 256x256 tiles: 16x16x32, conflict-free LDS layout
-    (4096, 4096, "KN", 0, False, 9),
-    (16384, 32768, "NK", 64, False, 10),   # 32 rounds: 16x16x32, rows kept whole
+    (4096, 4096, "NK", 64, False, 10),     # B N x K: 16x16x32, k-contiguous rows kept whole
+    (4096, 4096, "KN", 0, False, 9),       # B K x N: 16x16x32, A's chunks spread over slot rows
+    (16384, 32768, "NK", 64, False, 10),   # 32 rounds
     (16384, 32768, "NK", 0, False, 10),    # 32 rounds, B rows 32 KiB apart
+    (16384, 32768, "KN", 0, False, 9),
     (2048, 8192, "NK", 0, True, 8),        # dual-B SwiGLU, N x K weights, 2 rounds: register-staged
 ])
 def test_planner_tile_choice(m, n, layout, ld_extra, dual, want_cfg):
