@@ -14,21 +14,31 @@
 
 namespace ep {
 
-__device__ __forceinline__ float norm_cdf_pdf(float t, float* pdf) {
+// Phi(-|t|) = erfc(|t| / sqrt 2) / 2, and the density e^(-t^2/2) / sqrt(2 pi) in *pdf (the
+// polynomial's coefficients are A&S's a1..a5 halved, which folds in the / 2)
+__device__ __forceinline__ float norm_tail_pdf(float t, float* pdf) {
   const float x = __builtin_fabsf(t) * 0.70710678118654752f;
   const float r = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * x);
-  const float poly =
-      r * (0.254829592f + r * (-0.284496736f + r * (1.421413741f + r * (-1.453152027f + r * 1.061405429f))));
+  const float half_poly =
+      r * (0.127414796f + r * (-0.142248368f + r * (0.7107068705f + r * (-0.7265760135f + r * 0.5307027145f))));
   const float e = __builtin_amdgcn_exp2f(-0.72134752044448170f * t * t);  // e^(-t^2/2)
   *pdf = 0.39894228040143268f * e;                                       // 1/sqrt(2 pi) e^(-t^2/2)
-  const float q = 0.5f * poly * e;                                       // erfc(x) / 2 = Phi(-|t|)
+  return half_poly * e;
+}
+
+__device__ __forceinline__ float norm_cdf_pdf(float t, float* pdf) {
+  const float q = norm_tail_pdf(t, pdf);
   return t >= 0.0f ? 1.0f - q : q;
 }
 
-// exact-form GELU t Phi(t) and its derivative Phi(t) + t phi(t)
+// exact-form GELU t Phi(t) = max(t, 0) - |t| Phi(-|t|) (for t >= 0: t - t Phi(-t); for t < 0:
+// t Phi(t)), and its derivative Phi(t) + t phi(t).  |t| enters the product clamped to 40:
+// Phi(-|t|) is exactly 0 in fp32 well before that, and the clamp keeps t = +-inf from
+// multiplying infinity by zero (GELU(+inf) = +inf, GELU(-inf) = 0, NaN stays NaN).
 __device__ __forceinline__ float gelu_f(float t) {
   float pdf;
-  return t * norm_cdf_pdf(t, &pdf);
+  const float q = norm_tail_pdf(t, &pdf);
+  return __builtin_fmaxf(t, 0.0f) - __builtin_fminf(__builtin_fabsf(t), 40.0f) * q;
 }
 __device__ __forceinline__ float gelu_grad_f(float t) {
   float pdf;
