@@ -334,6 +334,25 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   const int m0 = pm * BM;
   const int n0 = pn * TR::BN_OUT;
   const int M = p.M, N = p.N, K = p.K;
+
+  // DRELU_BGRAD: the mask words of the wave's 32-row slabs (32 rows x WPR words each), loaded
+  // here so that their latency passes behind the K loop: word (row, w) of slab i sits in
+  // register [i][row / RPW] of lane (row % RPW) * WPR + w
+  constexpr int NSLAB = TR::WTM / 32;
+  constexpr int WPR = TR::WPR;
+  constexpr int NW = WPR / 2 > 0 ? WPR / 2 : 1;
+  constexpr int RPW = 64 / WPR;
+  uint32_t mw_all[EPI == E_DRELU_BGRAD ? NSLAB : 1][NW];
+  if constexpr (EPI == E_DRELU_BGRAD && MODE != 1) {
+#pragma unroll
+    for (int i = 0; i < NSLAB; ++i)
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        const int grow = m0 + wm * TR::WTM + i * 32 + q * RPW + lane / WPR;
+        const int wc = (n0 + wn * TR::WTN) / 32 + lane % WPR;
+        mw_all[i][q] = (grow < M && wc * 32 < N) ? p.aux_in[(int64_t)grow * p.ld_aux + wc] : 0u;
+      }
+  }
   const int KT_ALL = (K + BK - 1) / BK;
   // this block's K-steps: [KT0, KTE); local k-step kt loads global k-step KT0 + kt, and every
   // k-step past KTE reads as zeros (its global index is replaced by KT_ALL, past K)
@@ -868,15 +887,23 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   }
   f32x4 colsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // bias gradients: the lane's 8 columns
 
-  // DRELU_BGRAD: the slab's mask words (32 rows x WPR words) are fetched before it is staged,
-  // NW per lane: word (row, w) sits in register row / RPW of lane (row % RPW) * WPR + w.
-  constexpr int WPR = TR::WPR;
-  constexpr int NW = WPR / 2 > 0 ? WPR / 2 : 1;
-  constexpr int RPW = 64 / WPR;
   // DSWIGLU reads gate and up per element in the staged layout, for a whole slab before it
-  // is staged, so their latency overlaps the staging.
+  // is staged, so their latency overlaps the staging.  DGELU_BGRAD reads the pre-activation
+  // the same way one slab ahead (two buffers): slab 0 here, slab i + 1 while slab i is staged.
   constexpr int PF_GU = (EPI == E_DSWIGLU || EPI == E_DGELU_BGRAD) ? TR::ITERS : 1;
   u32x4 pf_g[PF_GU], pf_u[PF_GU];
+  u32x4 pf_a[EPI == E_DGELU_BGRAD ? 2 : 1][PF_GU];
+  auto load_gaux = [&](int i, u32x4* dst) __attribute__((always_inline)) {
+    const int srow0 = m0 + wm * WTM + i * 32;
+#pragma unroll
+    for (int it = 0; it < TR::ITERS; ++it) {
+      const int grow = srow0 + it * TR::RPI + lr;
+      const bool ok = colok && grow < M;
+      const int64_t go = ((int64_t)grow * p.ld_gaux + gcol) * 2;
+      dst[it] = ok ? __builtin_nontemporal_load((const u32x4*)((const char*)p.gaux + go)) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  if constexpr (EPI == E_DGELU_BGRAD) load_gaux(0, pf_a[0]);
 
   // 32-row slabs: 32x32 block row i, or 16x16 block rows 2i and 2i + 1
 #pragma unroll
@@ -885,19 +912,9 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     uint32_t pf_w[NW];
     if constexpr (EPI == E_DRELU_BGRAD) {
 #pragma unroll
-      for (int q = 0; q < NW; ++q) {
-        const int grow = srow0 + q * RPW + lane / WPR;
-        const int wc = ccol0 / 32 + lane % WPR;
-        pf_w[q] = (grow < M && wc * 32 < N) ? p.aux_in[(int64_t)grow * p.ld_aux + wc] : 0u;
-      }
+      for (int q = 0; q < NW; ++q) pf_w[q] = mw_all[i][q];
     } else if constexpr (EPI == E_DGELU_BGRAD) {
-#pragma unroll
-      for (int it = 0; it < TR::ITERS; ++it) {
-        const int grow = srow0 + it * TR::RPI + lr;
-        const bool ok = colok && grow < M;
-        const int64_t go = ((int64_t)grow * p.ld_gaux + gcol) * 2;
-        pf_g[it] = ok ? __builtin_nontemporal_load((const u32x4*)((const char*)p.gaux + go)) : u32x4{0u, 0u, 0u, 0u};
-      }
+      if (i + 1 < NSLAB) load_gaux(i + 1, pf_a[(i + 1) & 1]);
     } else if constexpr (EPI == E_DSWIGLU) {
 #pragma unroll
       for (int it = 0; it < TR::ITERS; ++it) {
@@ -1080,7 +1097,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
           if constexpr (EPI == E_DGELU_BGRAD) {  // rows past M: aux read as 0, staged value 0
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              const f32x4 pa = unpack4<DT>(u32x2{pf_g[c0 + c][2 * h], pf_g[c0 + c][2 * h + 1]});
+              const f32x4 pa = unpack4<DT>(u32x2{pf_a[i & 1][c0 + c][2 * h], pf_a[i & 1][c0 + c][2 * h + 1]});
 #pragma unroll
               for (int e = 0; e < 4; ++e) vv[c][h][e] *= gelu_grad_f(pa[e]);
             }
