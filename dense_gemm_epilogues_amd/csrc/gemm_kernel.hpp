@@ -675,8 +675,24 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr int DWIN = VST ? ((TOT * 3) / 4 < GBAR ? (TOT * 3) / 4 : GBAR) : (NST == 2 ? TOT / 2 : TOT);
   constexpr int DSTRIDE = DWIN / N_DMA > 0 ? DWIN / N_DMA : 1;
   constexpr int DPER = (N_DMA + DWIN - 1) / DWIN;      // DMA ops per issue point
+  // K-step pairs (configuration 10 with A given M x K and B given N x K).  Both operands
+  // arrive as k-contiguous row pieces of 64 bytes per k-step: half of a 128-byte cache line,
+  // whose other half the next k-step loads.  Loaded one k-step at a time, every line is
+  // fetched from L2 twice (the L1 has long evicted it by then).  Here k-steps kt+3 and kt+4
+  // (kt odd) are loaded together, slot by slot alternately, so that the second load of a
+  // line meets the first one's fill in the L1: L2 read requests halve (TCP_TCC_READ_REQ).
+  // Stage (kt+4) % NST is the one k-step kt consumes, free once the k-step's barrier has
+  // passed.  The pair's 2 N_DMA loads are spread one every PSTRIDE MFMAs from that barrier
+  // on: PAFTER of them in k-step kt, the other PBEFORE before the barrier of k-step kt+1
+  // (k-step kt+3's loads then land more than a k-step before its barrier in k-step kt+2).
+  constexpr bool PAIR = MF == 16 && !TR::CFL && NST == 4 && !VST && KS == 1 && !TR::DUAL && !AKM && BLAY == L_NK;
+  constexpr int PSTRIDE = NMMA / (2 * N_DMA);
+  constexpr int PBEFORE = HB / (PSTRIDE > 0 ? PSTRIDE : 1), PAFTER = 2 * N_DMA - PBEFORE;
+  static_assert(!PAIR || (PSTRIDE >= 1 && HB % PSTRIDE == 0 && (NMMA - HB) / PSTRIDE == PAFTER), "pair load schedule");
+  // odd k-step kt: stage of k-step kt+4; even kt: of k-step kt+2 (the pair begun in kt-1)
+  char* pair_dst = smem;
   auto slice = [&](auto rd_c, auto g0_c, const u32x4* A, const u32x4* B, auto t0_c, auto t1_c, int kt,
-                   char* dst, const KnSrc& kr, const char* rstage, int rks, u32x4* RA, u32x4* RB) __attribute__((always_inline)) {
+                   char* dst, const KnSrc& kr, const char* rstage, int rks, u32x4* RA, u32x4* RB, auto par_s) __attribute__((always_inline)) {
     constexpr bool RD = decltype(rd_c)::value;
     constexpr int G0 = decltype(g0_c)::value;        // k-step MFMA index of MFMA t = 0
     constexpr int T0 = decltype(t0_c)::value, T1 = decltype(t1_c)::value;
@@ -691,7 +707,23 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     for (int t = T0; t < T1; ++t) {
       acc[t / NB][t % NB] = E::mfma(A[t / NB], B[t % NB], acc[t / NB][t % NB]);
       const int g = G0 + t;
-      if (g % DSTRIDE == 0) {
+      if constexpr (PAIR) {
+        // load d of a pair: slot d / 2 of its first (d even) or second k-step.  The slice
+        // gets kt = k-step + 3 and its stage; K x N sources are unused (B is N x K here).
+        if (decltype(par_s)::value == 1 && g >= HB && (g - HB) % PSTRIDE == 0) {
+          const int d = (g - HB) / PSTRIDE;  // pair (kt, kt + 1), this k-step's loads 0 .. PAFTER-1
+          if (d & 1)
+            dma_op(kt + 1, pair_dst, d >> 1, kr);
+          else
+            dma_op(kt, dst, d >> 1, kr);
+        } else if (decltype(par_s)::value == 0 && g < HB && g % PSTRIDE == 0) {
+          const int d = PAFTER + g / PSTRIDE;  // pair (kt - 1, kt), its loads PAFTER .. 2 N_DMA-1
+          if (d & 1)
+            dma_op(kt, dst, d >> 1, kr);
+          else
+            dma_op(kt - 1, pair_dst, d >> 1, kr);
+        }
+      } else if (g % DSTRIDE == 0) {
 #pragma unroll
         for (int d = (g / DSTRIDE) * DPER; d < (g / DSTRIDE + 1) * DPER; ++d)
           if (d < N_DMA) {
@@ -724,7 +756,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr int VMC_LOOP = NST >= 3 ? N_DMA * (NST - 3) + DPRE : 0;  // younger loads allowed in flight
   constexpr int VMC_PRO = N_DMA * (NST - 2);           // after the prologue
   static_assert(NST >= 2, "the ring needs at least 2 stages");
-  static_assert(VMC_LOOP <= 63 && VMC_PRO <= 63, "vmcnt range");
+  static_assert(VMC_LOOP <= 63 && VMC_PRO <= 63 && (!PAIR || N_DMA + PAFTER <= 63), "vmcnt range");
   auto ring_barrier = [&](auto vmc_c) __attribute__((always_inline)) {
     if constexpr (VST)  // the stage was written from registers: only LDS traffic to wait for
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -744,6 +776,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     // registers holding k-step kt + 1 on their way to dst)
     const int kl = VST ? kt + 2 : kt + NST - 1;
     const KnSrc kr = kn_rsrc(kl);
+    if constexpr (PAIR) pair_dst = smem + ((kt + (decltype(par_c)::value == 1 ? 4 : 2)) % NST) * TR::STAGE;
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks) {
       u32x4* A = fa[(B0 + ks) & 1];
@@ -753,21 +786,25 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       lgkm_fence(A, B);
       __builtin_amdgcn_sched_barrier(0);
       if (ks == 0)
-        slice(T_{}, std::integral_constant<int, 0>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB);
+        slice(T_{}, std::integral_constant<int, 0>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c);
       else if (ks == 1)
-        slice(T_{}, std::integral_constant<int, NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB);
+        slice(T_{}, std::integral_constant<int, NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c);
       else
-        slice(T_{}, std::integral_constant<int, 2 * NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB);
+        slice(T_{}, std::integral_constant<int, 2 * NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c);
     }
     constexpr int L = (B0 + KS - 1) & 1;  // buffer of the last slice
     constexpr int NX = (B0 + KS) & 1;     // buffer of the next k-step's first slice
     using GL = std::integral_constant<int, (KS - 1) * NMMA>;
     lgkm_fence(fa[L], fb[L]);
     __builtin_amdgcn_sched_barrier(0);
-    slice(F_{}, GL{}, fa[L], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[NX], fb[NX]);
-    ring_barrier(std::integral_constant<int, VMC_LOOP>{});
+    slice(F_{}, GL{}, fa[L], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[NX], fb[NX], par_c);
+    // with k-step pairs the stage needed next is the second of the pair begun three k-steps
+    // before (even kt: the pair begun in k-step kt-1 is younger, PAFTER loads there and
+    // PBEFORE here) or the first of the pair begun two k-steps before (odd kt: only that
+    // pair's last load is younger)
+    ring_barrier(std::integral_constant<int, !PAIR ? VMC_LOOP : (decltype(par_c)::value == 0 ? 2 * N_DMA : 1)>{});
     __builtin_amdgcn_sched_barrier(0);
-    slice(T_{}, GL{}, fa[L], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[NX], fb[NX]);
+    slice(T_{}, GL{}, fa[L], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[NX], fb[NX], par_c);
   };
   using P0_ = std::integral_constant<int, 0>;
   using P1_ = std::integral_constant<int, 1>;
@@ -784,10 +821,20 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 #pragma unroll
       for (int t = 0; t < N_DMA; ++t) sreg[t] = gload(1, t, k1);
     } else {
+      if constexpr (PAIR) {
+        // k-steps 0 and 1, then the first PAFTER loads of the pair (2, 3), which k-step 0
+        // completes as if the pair had been begun in k-step -1
+        issue_tile(0, smem);
+        issue_tile(1, smem + TR::STAGE);
+        const KnSrc k2 = kn_rsrc(2);
 #pragma unroll
-      for (int s = 0; s < NST - 1; ++s) issue_tile(s, smem + s * TR::STAGE);
+        for (int d = 0; d < PAFTER; ++d) dma_op(2 + (d & 1), smem + (2 + (d & 1)) * TR::STAGE, d >> 1, k2);
+      } else {
+#pragma unroll
+        for (int s = 0; s < NST - 1; ++s) issue_tile(s, smem + s * TR::STAGE);
+      }
     }
-    ring_barrier(std::integral_constant<int, VMC_PRO>{});
+    ring_barrier(std::integral_constant<int, PAIR ? N_DMA + PAFTER : VMC_PRO>{});
     // the same wait, visible to the compiler (the barrier's is inline asm): with no scalar
     // or LDS load of its own in flight at the K loop's entry, its waits inside the loop
     // count the fragment reads exactly instead of waiting for all of them

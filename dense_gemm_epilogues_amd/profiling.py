@@ -14,7 +14,9 @@
       per (kernel, grid size) averages of every counter in the `--pmc` runs, with the
       sustained shader clock (GRBM_GUI_ACTIVE / XCDs / duration), the MFMA busy fraction
       (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x SIMDs)) and the LDS bank-conflict fraction
-      (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE); durations come from the kernel trace.
+      (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE), the L1 -> L2 read bytes and mean latency
+      (TCP_TCC_READ_REQ_sum x 128, TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum);
+      durations come from the kernel trace.
   python -m dense_gemm_epilogues_amd.profiling traffic FETCH_DIR WRITE_DIR KERNEL_SUBSTR \
       --copy-bytes B [--grid G] [--out FILE]
       HBM bytes per launch of the kernel whose name contains KERNEL_SUBSTR (and, with
@@ -146,6 +148,11 @@ def counters(pmc_dirs, trace_dir):
                 der["mfma_busy"] = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS)
         if mean.get("SQ_LDS_IDX_ACTIVE"):
             der["lds_bank_conflict_frac"] = mean.get("SQ_LDS_BANK_CONFLICT", 0.0) / mean["SQ_LDS_IDX_ACTIVE"]
+        if mean.get("TCP_TCC_READ_REQ_sum"):
+            # L1 -> L2 read requests (128-byte lines) and their mean latency in cycles
+            der["l2_read_MB"] = mean["TCP_TCC_READ_REQ_sum"] * 128 / 1e6
+            if "TCP_TCC_READ_REQ_LATENCY_sum" in mean:
+                der["l2_read_latency_cycles"] = mean["TCP_TCC_READ_REQ_LATENCY_sum"] / mean["TCP_TCC_READ_REQ_sum"]
         out.append((key[0], key[1], max(len(v) for v in cs.values()), mean, der))
     return sorted(out, key=lambda x: -der_time(x))
 
