@@ -191,6 +191,57 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Load schedule of the k-step pairs (in gemm_kernel).  Of a wave's N_DMA load slots per
+// stage, nps are paired: the 2 nps loads of the pair (k-steps kt+3, kt+4; kt odd) run one
+// every ps MFMAs from the odd k-step's barrier (MFMA hb) on, pafter of them in that k-step and
+// the rest before the next k-step's barrier.  The other nu slots are loaded every k-step for
+// k-step kt+3, one every us MFMAs from MFMA uoff (positions never shared with a paired load).
+// vmc_odd / vmc_even: loads younger than the last one of the stage needed next, at the
+// barrier of an odd / even k-step; vmc_pro: younger than stage 0's after the prologue.
+struct PairSched {
+  int ps, pafter, us, uoff, vmc_odd, vmc_even, vmc_pro;
+};
+constexpr PairSched pair_sched(int nmma, int hb, int nps, int nu, int n_dma) {
+  PairSched s{};
+  s.ps = nmma / (2 * nps);
+  s.pafter = (nmma - hb) / s.ps;
+  s.us = nu > 0 ? nmma / nu : nmma;
+  s.uoff = s.ps / 2;
+  // position of paired load d (in its k-step) and whether it is issued in the odd k-step
+  auto ppos = [&](int d) { return d < s.pafter ? hb + s.ps * d : (d - s.pafter) * s.ps; };
+  // loads of a k-step of parity par at MFMA positions > pos (par 0 even, 1 odd)
+  auto after = [&](int par, int pos) {
+    int n = 0;
+    for (int d = 0; d < 2 * nps; ++d)
+      if ((d < s.pafter) == (par == 1) && ppos(d) > pos) ++n;
+    for (int j = 0; j < nu; ++j)
+      if (s.uoff + s.us * j > pos) ++n;
+    return n;
+  };
+  auto before_barrier = [&](int par) {
+    int n = 0;
+    for (int d = 0; d < 2 * nps; ++d)
+      if ((d < s.pafter) == (par == 1) && ppos(d) < hb) ++n;
+    for (int j = 0; j < nu; ++j)
+      if (s.uoff + s.us * j < hb) ++n;
+    return n;
+  };
+  // odd kt needs k-step kt+1: unpaired loads from k-step kt-2, paired loads as the first of
+  // the pair begun in kt-2, the last of which (the last even d) is issued in k-step kt-1
+  int last3 = 0;
+  for (int d = s.pafter; d < 2 * nps; ++d)
+    if (d % 2 == 0) last3 = ppos(d);
+  s.vmc_odd = after(0, last3) + before_barrier(1);
+  // even kt needs k-step kt+1: its unpaired loads and the pair's second half both come last
+  // in k-step kt-2; then all of k-step kt-1 and what kt issues before its barrier
+  int lastl = ppos(2 * nps - 1);
+  if (nu > 0 && s.uoff + s.us * (nu - 1) > lastl) lastl = s.uoff + s.us * (nu - 1);
+  s.vmc_even = after(0, lastl) + after(1, -1) + before_barrier(0);
+  // prologue: k-steps 0 and 1, the unpaired loads of k-step 2, the pair (2, 3)'s first pafter
+  s.vmc_pro = n_dma + nu + s.pafter;
+  return s;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a contiguous range
 // of the tile order so that tiles sharing A rows / B columns share that XCD's L2, and
 // walk tiles in groups of kGroupM tile-rows.
@@ -675,20 +726,22 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr int DWIN = VST ? ((TOT * 3) / 4 < GBAR ? (TOT * 3) / 4 : GBAR) : (NST == 2 ? TOT / 2 : TOT);
   constexpr int DSTRIDE = DWIN / N_DMA > 0 ? DWIN / N_DMA : 1;
   constexpr int DPER = (N_DMA + DWIN - 1) / DWIN;      // DMA ops per issue point
-  // K-step pairs (configuration 10 with A given M x K and B given N x K).  Both operands
-  // arrive as k-contiguous row pieces of 64 bytes per k-step: half of a 128-byte cache line,
-  // whose other half the next k-step loads.  Loaded one k-step at a time, every line is
-  // fetched from L2 twice (the L1 has long evicted it by then).  Here k-steps kt+3 and kt+4
-  // (kt odd) are loaded together, slot by slot alternately, so that the second load of a
-  // line meets the first one's fill in the L1: L2 read requests halve (TCP_TCC_READ_REQ).
-  // Stage (kt+4) % NST is the one k-step kt consumes, free once the k-step's barrier has
-  // passed.  The pair's 2 N_DMA loads are spread one every PSTRIDE MFMAs from that barrier
-  // on: PAFTER of them in k-step kt, the other PBEFORE before the barrier of k-step kt+1
-  // (k-step kt+3's loads then land more than a k-step before its barrier in k-step kt+2).
-  constexpr bool PAIR = MF == 16 && !TR::CFL && NST == 4 && !VST && KS == 1 && !TR::DUAL && !AKM && BLAY == L_NK;
-  constexpr int PSTRIDE = NMMA / (2 * N_DMA);
-  constexpr int PBEFORE = HB / (PSTRIDE > 0 ? PSTRIDE : 1), PAFTER = 2 * N_DMA - PBEFORE;
-  static_assert(!PAIR || (PSTRIDE >= 1 && HB % PSTRIDE == 0 && (NMMA - HB) / PSTRIDE == PAFTER), "pair load schedule");
+  // K-step pairs (16x16 configurations with A given M x K).  A k-contiguous operand arrives
+  // as row pieces of 64 bytes per k-step: half of a 128-byte cache line, whose other half the
+  // next k-step loads.  Loaded one k-step at a time, every line is fetched from L2 twice (the
+  // L1 has long evicted it by then).  Here k-steps kt+3 and kt+4 (kt odd) are loaded
+  // together, slot by slot alternately, so that the second load of a line meets the first
+  // one's fill in the L1: L2 read requests halve (TCP_TCC_READ_REQ).  Paired are all slots
+  // when B is N x K (configuration 10), A's when B is K x N (its rows are whole lines; B is
+  // loaded every k-step as before).  Stage (kt+4) % NST is the one k-step kt consumes, free
+  // once the k-step's barrier has passed, so the pair's loads start there and run into the
+  // next k-step (pair_sched).
+  constexpr bool PAIR = MF == 16 && NST == 4 && !VST && KS == 1 && !TR::DUAL && !AKM && (BLAY == L_KN || !TR::CFL);
+  constexpr int NPS = BLAY == L_NK ? N_DMA : A_SLOTS, NU = N_DMA - NPS;  // paired, unpaired slots
+  constexpr PairSched PS_ = PAIR ? pair_sched(NMMA, HB, NPS, NU, N_DMA) : PairSched{2, 1, 1, 1, 0, 0, 0};
+  static_assert(!PAIR || (PS_.ps >= 2 && HB % PS_.ps == 0 && (NMMA - HB) % PS_.ps == 0 && PS_.pafter < 2 * NPS &&
+                          (NU == 0 || (NMMA % NU == 0 && PS_.us % PS_.ps == 0))), "pair load schedule");
+  static_assert(!PAIR || (PS_.vmc_odd <= 63 && PS_.vmc_even <= 63 && PS_.vmc_pro <= 63), "vmcnt range");
   // odd k-step kt: stage of k-step kt+4; even kt: of k-step kt+2 (the pair begun in kt-1)
   char* pair_dst = smem;
   auto slice = [&](auto rd_c, auto g0_c, const u32x4* A, const u32x4* B, auto t0_c, auto t1_c, int kt,
@@ -708,20 +761,25 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       acc[t / NB][t % NB] = E::mfma(A[t / NB], B[t % NB], acc[t / NB][t % NB]);
       const int g = G0 + t;
       if constexpr (PAIR) {
-        // load d of a pair: slot d / 2 of its first (d even) or second k-step.  The slice
-        // gets kt = k-step + 3 and its stage; K x N sources are unused (B is N x K here).
-        if (decltype(par_s)::value == 1 && g >= HB && (g - HB) % PSTRIDE == 0) {
-          const int d = (g - HB) / PSTRIDE;  // pair (kt, kt + 1), this k-step's loads 0 .. PAFTER-1
+        // load d of a pair: slot d / 2 (paired slots come first: all, or A's) of its first
+        // (d even) or second k-step.  The slice gets kt = k-step + 3, its stage and its K x N
+        // source, which only the unpaired (K x N B) slots use.
+        constexpr int PS = PS_.ps, PAFTER = PS_.pafter;
+        if (decltype(par_s)::value == 1 && g >= HB && (g - HB) % PS == 0) {
+          const int d = (g - HB) / PS;  // pair (kt, kt + 1), this k-step's loads 0 .. PAFTER-1
           if (d & 1)
             dma_op(kt + 1, pair_dst, d >> 1, kr);
           else
             dma_op(kt, dst, d >> 1, kr);
-        } else if (decltype(par_s)::value == 0 && g < HB && g % PSTRIDE == 0) {
-          const int d = PAFTER + g / PSTRIDE;  // pair (kt - 1, kt), its loads PAFTER .. 2 N_DMA-1
+        } else if (decltype(par_s)::value == 0 && g < HB && g % PS == 0) {
+          const int d = PAFTER + g / PS;  // pair (kt - 1, kt), its loads PAFTER .. 2 NPS-1
           if (d & 1)
             dma_op(kt, dst, d >> 1, kr);
           else
             dma_op(kt - 1, pair_dst, d >> 1, kr);
+        }
+        if constexpr (NU > 0) {
+          if (g % PS_.us == PS_.uoff) dma_op(kt, dst, NPS + g / PS_.us, kr);
         }
       } else if (g % DSTRIDE == 0) {
 #pragma unroll
@@ -756,7 +814,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   constexpr int VMC_LOOP = NST >= 3 ? N_DMA * (NST - 3) + DPRE : 0;  // younger loads allowed in flight
   constexpr int VMC_PRO = N_DMA * (NST - 2);           // after the prologue
   static_assert(NST >= 2, "the ring needs at least 2 stages");
-  static_assert(VMC_LOOP <= 63 && VMC_PRO <= 63 && (!PAIR || N_DMA + PAFTER <= 63), "vmcnt range");
+  static_assert(VMC_LOOP <= 63 && VMC_PRO <= 63, "vmcnt range");
   auto ring_barrier = [&](auto vmc_c) __attribute__((always_inline)) {
     if constexpr (VST)  // the stage was written from registers: only LDS traffic to wait for
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -799,10 +857,9 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     __builtin_amdgcn_sched_barrier(0);
     slice(F_{}, GL{}, fa[L], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[NX], fb[NX], par_c);
     // with k-step pairs the stage needed next is the second of the pair begun three k-steps
-    // before (even kt: the pair begun in k-step kt-1 is younger, PAFTER loads there and
-    // PBEFORE here) or the first of the pair begun two k-steps before (odd kt: only that
-    // pair's last load is younger)
-    ring_barrier(std::integral_constant<int, !PAIR ? VMC_LOOP : (decltype(par_c)::value == 0 ? 2 * N_DMA : 1)>{});
+    // before (even kt) or the first of the pair begun two k-steps before (odd kt); the counts
+    // of younger loads are pair_sched's
+    ring_barrier(std::integral_constant<int, !PAIR ? VMC_LOOP : (decltype(par_c)::value == 0 ? PS_.vmc_even : PS_.vmc_odd)>{});
     __builtin_amdgcn_sched_barrier(0);
     slice(T_{}, GL{}, fa[L], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[NX], fb[NX], par_c);
   };
@@ -822,19 +879,21 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       for (int t = 0; t < N_DMA; ++t) sreg[t] = gload(1, t, k1);
     } else {
       if constexpr (PAIR) {
-        // k-steps 0 and 1, then the first PAFTER loads of the pair (2, 3), which k-step 0
-        // completes as if the pair had been begun in k-step -1
+        // k-steps 0 and 1, k-step 2's unpaired slots, then the first pafter loads of the
+        // pair (2, 3), which k-step 0 completes as if the pair had been begun in k-step -1
         issue_tile(0, smem);
         issue_tile(1, smem + TR::STAGE);
         const KnSrc k2 = kn_rsrc(2);
 #pragma unroll
-        for (int d = 0; d < PAFTER; ++d) dma_op(2 + (d & 1), smem + (2 + (d & 1)) * TR::STAGE, d >> 1, k2);
+        for (int j = 0; j < NU; ++j) dma_op(2, smem + 2 * TR::STAGE, NPS + j, k2);
+#pragma unroll
+        for (int d = 0; d < PS_.pafter; ++d) dma_op(2 + (d & 1), smem + (2 + (d & 1)) * TR::STAGE, d >> 1, k2);
       } else {
 #pragma unroll
         for (int s = 0; s < NST - 1; ++s) issue_tile(s, smem + s * TR::STAGE);
       }
     }
-    ring_barrier(std::integral_constant<int, PAIR ? N_DMA + PAFTER : VMC_PRO>{});
+    ring_barrier(std::integral_constant<int, PAIR ? PS_.vmc_pro : VMC_PRO>{});
     // the same wait, visible to the compiler (the barrier's is inline asm): with no scalar
     // or LDS load of its own in flight at the K loop's entry, its waits inside the loop
     // count the fragment reads exactly instead of waiting for all of them
