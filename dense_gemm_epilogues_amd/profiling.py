@@ -44,7 +44,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 # the files whose text defines the fused GEMM kernels' device code (the planner, the C ABI
 # and the elementwise kernels do not change what a counter run of a GEMM launch measures)
-KERNEL_SOURCES = ("ep_internal.hpp", "gemm_inst.hip", "gemm_kernel.hpp", "normal_dist.hpp")
+KERNEL_SOURCES = ("ep_internal.hpp", "gemm_inst.hip", "gemm_kernel.hpp", "normal_dist.hpp", "pair_sched.hpp")
 
 
 def source_hash():
