@@ -193,6 +193,23 @@ def test_split_k(epi, layout, splits):
                 run_and_check(epi, dtname, layout, m, n, k, cfg, split_k=splits)
 
 
+@pytest.mark.parametrize("cfg", [9, 10])
+@pytest.mark.parametrize("layout", ["KN", "NK"])
+def test_kstep_pair_k_lengths(layout, cfg):
+    """The 16x16 configurations load k-steps in pairs (k-steps kt+3 and kt+4 issued from each
+    odd k-step kt on, the prologue starting the pair (2, 3)): K from one 32-deep k-step to 18,
+    even and odd counts, ragged last k-steps, and split-K ranges of either parity."""
+    require_gpu()
+    for k in (32, 64, 96, 128, 160, 192, 224, 256, 288, 320, 544, 576, 40, 104):
+        run_and_check("DEFAULT", "f16", layout, 260, 296, k, cfg)
+    for epi in ("RELU_AUX_BIAS", "DRELU_BGRAD", "DSWIGLU"):
+        for k in (64, 256):
+            run_and_check(epi, "bf16", layout, 260, 296, k, cfg)
+    for splits in (2, 3):
+        for k in (512, 1024, 608):
+            run_and_check("DEFAULT", "f16", layout, 260, 296, k, cfg, split_k=splits)
+
+
 @pytest.mark.parametrize("epi", EPIS)
 def test_autotune(epi):
     """Plan-time tuning picks some (tile, split) pair; the tuned plan must still be exact, and a
