@@ -686,7 +686,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // loaded every k-step as before).  Stage (kt+4) % NST is the one k-step kt consumes, free
   // once the k-step's barrier has passed, so the pair's loads start there and run into the
   // next k-step (pair_sched).
-  constexpr bool PAIR = MF == 16 && NST == 4 && !VST && KS == 1 && !TR::DUAL && !AKM && (BLAY == L_KN || !TR::CFL);
+  constexpr bool PAIR = MF == 16 && NST == 4 && !VST && KS == 1 && !AKM && (BLAY == L_KN || !TR::CFL);
   constexpr int NPS = BLAY == L_NK ? N_DMA : A_SLOTS, NU = N_DMA - NPS;  // paired, unpaired slots
   constexpr PairSched PS_ = PAIR ? pair_sched(NMMA, HB, NPS, NU, N_DMA) : PairSched{2, 1, 1, 1, 0, 0, 0};
   static_assert(!PAIR || (PS_.ps >= 2 && HB % PS_.ps == 0 && (NMMA - HB) % PS_.ps == 0 && PS_.pafter < 2 * NPS &&

@@ -202,7 +202,7 @@ def test_kstep_pair_k_lengths(layout, cfg):
     require_gpu()
     for k in (32, 64, 96, 128, 160, 192, 224, 256, 288, 320, 544, 576, 40, 104):
         run_and_check("DEFAULT", "f16", layout, 260, 296, k, cfg)
-    for epi in ("RELU_AUX_BIAS", "DRELU_BGRAD", "DSWIGLU"):
+    for epi in ("RELU_AUX_BIAS", "DRELU_BGRAD", "DSWIGLU", "SWIGLU", "SWIGLU_AUX"):
         for k in (64, 256):
             run_and_check(epi, "bf16", layout, 260, 296, k, cfg)
     for splits in (2, 3):
