@@ -190,17 +190,16 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
 // (65536 x 16384 x 8192 backward 1173 -> 1213 TFLOP/s sustained, 16384 x 32768 x 4096
 // 1235 -> 1272, the 2048 x 5120 x 17408 down GEMM 0.396 -> 0.353 ms; 4096^3 on par), and
 // spread chunks (configuration 9) where only A is k-contiguous (4096^3 forward 1174 -> 1190,
-// 65536 x 8192 x 16384 forward 1205 -> 1231).  The exception is the dual-B SwiGLU GEMM with
-// N x K weights at up to 16 rounds of resident tiles: there the 64-deep register-staged
-// 32x32 configuration, whose loads arrive as whole 128-byte lines one k-step ahead, stays
-// ahead.  The unfused path's GEMM takes the tile the fused epilog would.
-constexpr int kVstCfg = 8;
+// 65536 x 8192 x 16384 forward 1205 -> 1231).  The dual-B SwiGLU GEMM with N x K weights
+// at few rounds had been faster on the 64-deep register-staged 32x32 configuration, whose
+// loads arrive as whole 128-byte lines; since the 16x16 kernels load k-steps in line-sharing
+// pairs, configuration 10 is ahead there too (M 2048 / 4096, H 5120, I 17408: 0.730 ->
+// 0.706 ms, 1.209 -> 1.161 ms).  The unfused path's GEMM takes the tile the fused epilog
+// would.
 constexpr int kM16SpreadCfg = 9;
 constexpr int kM16RowsCfg = 10;
-int pick_cfg(const ep_shape* s, int model_cfg, int cus, bool dual) {
+int pick_cfg(const ep_shape* s, int model_cfg) {
   if (model_cfg != 0) return model_cfg;
-  const int64_t tiles = ((s->m + 255) / 256) * ((s->n + (dual ? 127 : 255)) / (dual ? 128 : 256));
-  if (dual && s->a_layout == EP_A_MK && s->b_layout == EP_B_NK && tiles <= 16LL * cus) return kVstCfg;
   return s->b_layout == EP_B_NK ? kM16RowsCfg : kM16SpreadCfg;
 }
 
@@ -527,8 +526,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
                 opt.tile_cfg);
   const int cfg = opt.tile_cfg >= 0
                       ? opt.tile_cfg
-                      : pick_cfg(s, choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount),
-                                 prop.multiProcessorCount, kernel_dual);
+                      : pick_cfg(s, choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount));
 
   ep_plan_s* h = new (std::nothrow) ep_plan_s{};  // every member zero / null
   if (!h) return fail(EP_ERR_OUT_OF_MEMORY, "host allocation failed");
