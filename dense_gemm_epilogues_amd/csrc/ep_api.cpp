@@ -194,23 +194,32 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
 // at few rounds had been faster on the 64-deep register-staged 32x32 configuration, whose
 // loads arrive as whole 128-byte lines; since the 16x16 kernels load k-steps in line-sharing
 // pairs, configuration 10 is ahead there too (M 2048 / 4096, H 5120, I 17408: 0.730 ->
-// 0.706 ms, 1.209 -> 1.161 ms).  The unfused path's GEMM takes the tile the fused epilog
-// would.
+// 0.706 ms, 1.209 -> 1.161 ms).  The exception is a single-B GEMM with N x K weights that
+// fills less than one round of CUs (long-K GEMMs such as the SwiGLU down and dx GEMMs, 160
+// tiles): there the 64-deep register-staged 32x32 configuration measured 7-10% faster with
+// cold operands (2048 x 5120 x 17408: 0.386 -> 0.351 ms unsplit; 2048 x 5120 x 34816: 0.746
+// -> 0.676 ms with 3 splits).  The unfused path's GEMM takes the tile the fused epilog would.
+constexpr int kVstCfg = 8;
 constexpr int kM16SpreadCfg = 9;
 constexpr int kM16RowsCfg = 10;
-int pick_cfg(const ep_shape* s, int model_cfg) {
+int pick_cfg(const ep_shape* s, int model_cfg, int cus, bool dual) {
   if (model_cfg != 0) return model_cfg;
+  const int64_t tiles = ((s->m + 255) / 256) * ((s->n + 255) / 256);
+  if (!dual && s->a_layout == EP_A_MK && s->b_layout == EP_B_NK && tiles < cus) return kVstCfg;
   return s->b_layout == EP_B_NK ? kM16RowsCfg : kM16SpreadCfg;
 }
 
 // Split-K: how many K ranges per tile.  Only grids that leave CUs idle are split: the time
 // of one resident round of tiles scales as rounds(tiles * S) / S, and every split adds a
-// write and a read of the fp32 tile partials (BM * BNT * 4 bytes), priced at a CU's share of
-// HBM bandwidth (about 20 GB/s) against the tile's K loop (about 1 us per 32-deep k-step).
+// write and a read of the fp32 tile partials (BM * BNT * 4 bytes) and their share of the
+// fixup launch, priced at about 11 GB/s per CU, against the tile's K loop (about 0.65 us per
+// 32-deep k-step).  Both rates are fitted to the 2048 x 5120 GEMMs at K 17408 and 34816 with
+// cold operands (unsplit 0.351 / 0.707 ms, 3 splits 0.377 / 0.676 ms), where the earlier
+// guesses (1 us, 20 GB/s) split the first one to its loss.
 int choose_splits(int64_t tiles, int slots, int kt, int cfg) {
   if (tiles >= slots) return 1;
-  const double tile_us = kt * (kTileCfgs[cfg].bk / 32.0) * 1.0;
-  const double part_us = 2.0 * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * 4.0 / 20e3;  // bytes / (bytes/us)
+  const double tile_us = kt * (kTileCfgs[cfg].bk / 32.0) * 0.65;
+  const double part_us = 2.0 * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * 4.0 / 11e3;  // bytes / (bytes/us)
   int best = 1;
   double best_t = 1.0;
   for (int sp = 2; sp <= EP_MAX_SPLIT_K; ++sp) {
@@ -526,7 +535,8 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
                 opt.tile_cfg);
   const int cfg = opt.tile_cfg >= 0
                       ? opt.tile_cfg
-                      : pick_cfg(s, choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount));
+                      : pick_cfg(s, choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount),
+                                 prop.multiProcessorCount, kernel_dual);
 
   ep_plan_s* h = new (std::nothrow) ep_plan_s{};  // every member zero / null
   if (!h) return fail(EP_ERR_OUT_OF_MEMORY, "host allocation failed");

@@ -256,6 +256,8 @@ def test_transposed_a(dtname, layout):
     (16384, 32768, "NK", 0, False, 10),    # 32 rounds, B rows 32 KiB apart
     (16384, 32768, "KN", 0, False, 9),
     (2048, 8192, "NK", 0, True, 10),       # dual-B SwiGLU, N x K weights, 2 rounds: whole rows too
+    (2048, 5120, "NK", 0, False, 8),       # single B, N x K, 160 tiles (under one round): register-staged
+    (2048, 5120, "KN", 0, False, 9),
 ])
 def test_planner_tile_choice(m, n, layout, ld_extra, dual, want_cfg):
     """The planner's default tile configuration at full-chip shapes (256 CUs), B rows 16384
