@@ -6,7 +6,7 @@ plan / execute / free sequence of the pages (nvmath-python's Matmul as described
 "Fusing Matmul Epilogs with nvmath-python" and in the hotdry.top cuBLASLt post):
 
     p = Plan(x, w, epilog="RELU_AUX_BIAS", epilog_inputs={"bias": b}, b_layout="KN")
-    y, aux = p.execute()          # aux["relu_aux"]: int32 view of the uint32 mask words
+    y, aux = p.execute()          # aux["relu_aux"]: int32 tensor holding the uint32 mask words
     dp = Plan(dy, w, epilog="DRELU_BGRAD", epilog_inputs={"relu_aux": aux["relu_aux"]},
               b_layout="NK")
     dx, aux = dp.execute()        # aux["drelu_bgrad"]: float32 bias gradient
@@ -20,7 +20,7 @@ import os
 
 import torch
 
-__all__ = ["Plan", "EPError", "EPILOGS", "lib", "library_path", "abi_version", "num_tile_cfgs"]
+__all__ = ["Plan", "EPError", "EPILOGS", "lib", "library_path", "abi_version", "num_tile_cfgs", "validate_operands"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libep.so")
@@ -128,6 +128,96 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _check_tensor(name, t, rows, cols, dtype, device, min_cols=False):
+    """Raise ValueError unless `t` is a tensor of `dtype` on `device` laid out as the C ABI
+    reads it: 2-D (rows x cols, or at least `cols` columns when min_cols) with unit column
+    stride, or 1-D of length cols (rows None) with unit stride.  The library receives only a
+    pointer and leading dimensions, so these checks stand between a wrong tensor and kernels
+    that would read or write past its storage."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if rows is None:
+        if t.dim() != 1 or t.shape[0] != cols or (cols > 1 and t.stride(0) != 1):
+            raise ValueError(f"{name} must be a contiguous ({cols},) vector, got shape {tuple(t.shape)} "
+                             f"stride {t.stride()}")
+    else:
+        ok_cols = t.dim() == 2 and (t.shape[1] >= cols if min_cols else t.shape[1] == cols)
+        if t.dim() != 2 or t.shape[0] != rows or not ok_cols:
+            want = f"({rows}, >= {cols})" if min_cols else f"({rows}, {cols})"
+            raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+        if t.stride(1) != 1 and t.shape[1] > 1:
+            raise ValueError(f"{name} must have unit column stride, got stride {t.stride()}")
+        if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+            raise ValueError(f"{name}: row stride {t.stride(0)} is below the row length {t.shape[1]}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the operands are on {device}")
+
+
+def validate_operands(a, b, epilog, epilog_inputs, b_layout, a_layout, out, aux_out):
+    """Check every tensor a Plan would hand to the C ABI against the problem a and b define
+    (raises ValueError; returns (m, n, k)).  All tensors must be on a.device, which must be a
+    CUDA (HIP) device; b, b2, out, bias, gate, up, gelu_aux, gu and d_up have a's dtype;
+    relu_aux holds int32 words; bias gradients are float32."""
+    if not isinstance(a, torch.Tensor) or not isinstance(b, torch.Tensor):
+        raise ValueError("a and b must be torch tensors")
+    if a.dtype not in _DTYPES:
+        raise ValueError(f"a must be float16 or bfloat16, got {a.dtype}")
+    if b_layout not in _LAYOUTS:
+        raise ValueError(f"unknown b_layout {b_layout!r}")
+    if a_layout not in ("MK", "KM"):
+        raise ValueError(f"unknown a_layout {a_layout!r}")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    dt, dev = a.dtype, a.device
+    m, k = (a.shape[0], a.shape[1]) if a_layout == "MK" else (a.shape[1], a.shape[0])
+    n = b.shape[1] if b_layout == "KN" else b.shape[0]
+    _check_tensor("a", a, a.shape[0], a.shape[1], dt, dev)
+    _check_tensor("b", b, k if b_layout == "KN" else n, k if b_layout == "NK" else n, dt, dev)
+    if out is not None:
+        _check_tensor("out", out, m, n, dt, dev)
+    ins = epilog_inputs
+    nw = (n + 31) // 32
+    need = {
+        "BIAS": ("bias",), "RELU_BIAS": ("bias",), "RELU_AUX_BIAS": ("bias",), "GELU_BIAS": ("bias",),
+        "GELU_AUX_BIAS": ("bias",), "DRELU_BGRAD": ("relu_aux",), "SWIGLU": ("b2",), "SWIGLU_AUX": ("b2",),
+        "DSWIGLU": ("gate", "up"), "DGELU_BGRAD": ("gelu_aux",),
+    }.get(epilog, ())
+    for key in need:
+        if key not in ins:
+            raise ValueError(f"epilog {epilog} needs epilog_inputs[{key!r}]")
+    for key in ins:
+        if key not in need:
+            raise ValueError(f"epilog {epilog} takes no epilog_inputs[{key!r}]")
+    if "bias" in ins:
+        _check_tensor("bias", ins["bias"], None, n, dt, dev)
+    if "relu_aux" in ins:
+        _check_tensor("relu_aux", ins["relu_aux"], m, nw, torch.int32, dev, min_cols=True)
+    if "b2" in ins:
+        _check_tensor("b2", ins["b2"], b.shape[0], b.shape[1], dt, dev)
+        if ins["b2"].stride(0) != b.stride(0):
+            raise ValueError("b2 must have the same row stride as b")
+    if "gate" in ins:
+        _check_tensor("gate", ins["gate"], m, n, dt, dev)
+        _check_tensor("up", ins["up"], m, n, dt, dev)
+        if ins["gate"].stride(0) != ins["up"].stride(0):
+            raise ValueError("gate and up must share a row stride")
+    if "gelu_aux" in ins:
+        _check_tensor("gelu_aux", ins["gelu_aux"], m, n, dt, dev)
+    aux_shapes = {"relu_aux": (m, nw, torch.int32, True), "drelu_bgrad": (None, n, torch.float32, False),
+                  "dgelu_bgrad": (None, n, torch.float32, False), "gelu_aux": (m, n, dt, False),
+                  "d_up": (m, n, dt, False), "gu": (m, 2 * n, dt, False)}
+    for key, t in aux_out.items():
+        if key not in aux_shapes:
+            raise ValueError(f"unknown aux_out {key!r}")
+        rows, cols, adt, mc = aux_shapes[key]
+        _check_tensor(f"aux_out[{key!r}]", t, rows, cols, adt, dev, min_cols=mc)
+    if dev.type != "cuda":
+        raise ValueError(f"operands must be on a CUDA (HIP) device, got {dev}")
+    return m, n, k
+
+
 class Plan:
     """A planned fused GEMM + epilog (the C library's ep_handle).
 
@@ -157,12 +247,7 @@ class Plan:
         aux_out = dict(aux_out or {})
         if epilog not in EPILOGS:
             raise ValueError(f"unknown epilog {epilog!r}")
-        if a.dtype not in _DTYPES or b.dtype != a.dtype:
-            raise ValueError("a and b must both be float16 or both bfloat16")
-        if a_layout not in ("MK", "KM"):
-            raise ValueError(f"unknown a_layout {a_layout!r}")
-        m, k = a.shape if a_layout == "MK" else (a.shape[1], a.shape[0])
-        n = b.shape[1] if b_layout == "KN" else b.shape[0]
+        m, n, k = validate_operands(a, b, epilog, epilog_inputs, b_layout, a_layout, out, aux_out)
         if out is None:
             out = torch.empty((m, n), dtype=a.dtype, device=a.device)
         self.epilog = epilog
@@ -211,8 +296,6 @@ class Plan:
             self.aux["gu"] = gu
         if epilog == "DSWIGLU":
             g, u = epilog_inputs["gate"], epilog_inputs["up"]
-            if g.stride(0) != u.stride(0):
-                raise ValueError("gate and up must share a row stride")
             io.gate, io.up, io.ld_gu = _ptr(g), _ptr(u), g.stride(0)
             d2 = aux_out.get("d_up")
             if d2 is None:
