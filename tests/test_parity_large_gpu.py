@@ -248,7 +248,8 @@ def test_swiglu_mlp_training_step_all_gradients():
                dx = [d_gate | d_up] . W_gu  (one GEMM over the concatenated K = 2I),
                [dWg; dWu] = [d_gate | d_up]^T . x and dWd = dout^T . h (transposed-A GEMMs).
     Every step is compared with the oracle applied to the same inputs the GPU step consumed
-    (the previous GPU step's output), so each kernel is checked on its own."""
+    (the previous GPU step's output), so each kernel is checked on its own, on sampled tiles
+    that cover every region of its output."""
     require_gpu()
     ep = _ep()
     dev = torch.device("cuda")
@@ -282,27 +283,39 @@ def test_swiglu_mlp_training_step_all_gradients():
     dwd = run(dout, h, "DEFAULT", b_layout="KN", a_layout="KM")          # H x I
     torch.cuda.synchronize()
 
-    x64, wg64, wu64, wd64, dout64 = f64(x), f64(wg), f64(wu), f64(wd), f64(dout)
-    # forward pieces
-    rows = slice(0, 512)  # the oracle's full-width products on a row block (the kernels tile rows identically)
-    assert_half(f64(gu[rows, :idim]), oracle.matmul(x64[rows], wg64, "NK"), "saved g")
-    assert_half(f64(gu[rows, idim:]), oracle.matmul(x64[rows], wu64, "NK"), "saved u")
-    assert_half(f64(gu_re[rows]), f64(gu[rows]), "recomputed [g | u] against the saved one")
-    href, _, _ = oracle.swiglu(x64[rows], wg64, wu64)
-    assert_half(f64(h[rows]), href, "h")
-    h64 = f64(h)
-    assert_half(f64(out[rows]), oracle.matmul(h64[rows], wd64, "NK"), "out")
-    # backward pieces, each on the GPU's own inputs
-    gu64 = f64(gu)
-    dg_ref, du_ref, _ = oracle.dswiglu(dout64[rows], wd64, gu64[rows, :idim], gu64[rows, idim:])
-    assert_half(f64(dgu[rows, :idim]), dg_ref, "d_gate")
-    assert_half(f64(dgu[rows, idim:]), du_ref, "d_up")
-    dgu64 = f64(dgu)
-    w_gu64 = f64(w_gu)
-    assert_half(f64(dx[rows]), oracle.matmul(dgu64[rows], w_gu64, "KN"), "dx = d_gate Wg + d_up Wu")
-    # weight gradients: full contraction over the batch, checked on column blocks
-    cols = slice(0, 640)
-    assert_half(f64(dw_gu[:, cols]), dgu64.T @ x64[:, cols], "[dWg; dWu] = [d_gate | d_up]^T x")
-    assert_half(f64(dwd[:, :640]), dout64.T @ h64[:, :640], "dWd = dout^T h")
+    # Every output is checked on seeded 128 x 128 tiles spread over all of it, the four corner
+    # tiles included (so the last tile-row and tile-column of every kernel are covered), each
+    # against the oracle evaluated on exactly the rows and columns the tile needs.
+    def tiles(rows, cols, seed):
+        return oracle.sample_tiles(rows, cols, count=12, seed=seed)
+
+    for (r0, r1, c0, c1) in tiles(m, idim, 61):
+        xr = f64(x[r0:r1])
+        g_ref = oracle.matmul(xr, f64(wg[c0:c1]), "NK")
+        u_ref = oracle.matmul(xr, f64(wu[c0:c1]), "NK")
+        at = f"tile {(r0, c0)}"
+        assert_half(f64(gu[r0:r1, c0:c1]), g_ref, "saved g " + at)
+        assert_half(f64(gu[r0:r1, idim + c0:idim + c1]), u_ref, "saved u " + at)
+        assert_half(f64(gu_re[r0:r1, c0:c1]), g_ref, "recomputed g " + at)
+        assert_half(f64(gu_re[r0:r1, idim + c0:idim + c1]), u_ref, "recomputed u " + at)
+        assert_half(f64(h[r0:r1, c0:c1]), oracle.swiglu(xr, f64(wg[c0:c1]), f64(wu[c0:c1]))[0], "h " + at)
+        # backward on the GPU's own saved g and u
+        dg_ref, du_ref, _ = oracle.dswiglu(f64(dout[r0:r1]), f64(wd[:, c0:c1]), f64(gu[r0:r1, c0:c1]),
+                                           f64(gu[r0:r1, idim + c0:idim + c1]))
+        assert_half(f64(dgu[r0:r1, c0:c1]), dg_ref, "d_gate " + at)
+        assert_half(f64(dgu[r0:r1, idim + c0:idim + c1]), du_ref, "d_up " + at)
+    for (r0, r1, c0, c1) in tiles(m, hd, 62):
+        at = f"tile {(r0, c0)}"
+        assert_half(f64(out[r0:r1, c0:c1]), oracle.matmul(f64(h[r0:r1]), f64(wd[c0:c1]), "NK"), "out " + at)
+        assert_half(f64(dx[r0:r1, c0:c1]), oracle.matmul(f64(dgu[r0:r1]), f64(w_gu[:, c0:c1]), "KN"),
+                    "dx = d_gate Wg + d_up Wu " + at)
+    # weight gradients contract over the whole batch: tile (r, c) of [dWg; dWu] is
+    # [d_gate | d_up][:, r]^T x[:, c], of dWd dout[:, r]^T h[:, c]
+    for (r0, r1, c0, c1) in tiles(2 * idim, hd, 63):
+        assert_half(f64(dw_gu[r0:r1, c0:c1]), oracle.matmul(f64(dgu[:, r0:r1]).T, f64(x[:, c0:c1]), "KN"),
+                    f"[dWg; dWu] tile {(r0, c0)}")
+    for (r0, r1, c0, c1) in tiles(hd, idim, 64):
+        assert_half(f64(dwd[r0:r1, c0:c1]), oracle.matmul(f64(dout[:, r0:r1]).T, f64(h[:, c0:c1]), "KN"),
+                    f"dWd tile {(r0, c0)}")
     for p in plans:
         p.free()

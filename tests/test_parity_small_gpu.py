@@ -93,7 +93,7 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
                 aux_out=aux_out, path=path, tile_cfg=cfg, split_k=split_k, bgrad_mode=bgrad_mode,
                 autotune=autotune)
     if split_k > 1:
-        kt = -(-k // (64 if cfg in (1, 4) else 32))
+        kt = -(-k // (64 if cfg in (1, 4, 8) else 32))
         per = -(-kt // min(split_k, kt))
         want = -(-kt // per)
         assert f"splits={want} " in p.info(), p.info()
@@ -183,9 +183,11 @@ def test_small_shapes_fused(epi, dtname, layout, cfg):
 def test_split_k(epi, layout, splits):
     """K split over 2-4 workgroups per tile (fp32 partials, then a fixup launch that sums them
     and runs the epilog): every epilog, both dtypes, five tile configurations, a K that
-    divides unevenly and a K too short for the requested number of ranges."""
+    divides unevenly and a K too short for the requested number of ranges.  Configuration 8
+    (register-staged, 64-deep k-steps) is the planner's choice for N x K GEMMs under one round
+    of tiles, where the split model splits long K ranges."""
     require_gpu()
-    for cfg in (0, 1, 6, 9, 10):
+    for cfg in (0, 1, 6, 8, 9, 10):
         if epi in ("SWIGLU", "SWIGLU_AUX") and layout == "KN" and cfg in BNT128_CFGS:
             continue
         for dtname in ("f16", "bf16"):
@@ -296,6 +298,38 @@ def test_planner_tile_choice(m, n, layout, ld_extra, dual, want_cfg):
         bsel = b[cols] if layout == "NK" else b[:, cols]
         ref = oracle.matmul(f64(a[rows]), f64(bsel), layout)
     assert_half(f64(out[rows][:, cols]), ref, f"planner {layout}/{m}x{n}/{ld_extra}/dual={dual}")
+    p.free()
+
+
+@pytest.mark.parametrize("a_layout", ["MK", "KM"])
+def test_planner_split_choice(a_layout):
+    """A long-K GEMM under one round of tiles, B given N x K (the SwiGLU dx GEMM's shape,
+    2048 x 5120 x 34816): the planner picks register-staged configuration 8 with 3 split-K
+    ranges; sampled rows and columns against the oracle."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev = torch.device("cuda")
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the expected choice assumes 256 CUs")
+    m, n, k = 2048, 5120, 34816
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    a = torch.randn(m, k, device=dev, generator=g).half()
+    if a_layout == "KM":
+        a = a.t().contiguous()
+    b = (torch.randn(n, k, device=dev, generator=g) * k ** -0.5).half()
+    say(f"case planner split choice A {a_layout} {m}x{n}x{k}")
+    p = ep.Plan(a, b, "DEFAULT", b_layout="NK", a_layout=a_layout)
+    info = p.info()
+    if a_layout == "MK":
+        assert "tile_cfg=8 " in info and "splits=3 " in info, info
+    out, _ = p.execute()
+    torch.cuda.synchronize()
+    rows = torch.tensor(np.r_[0:32, m // 2 - 8:m // 2 + 24, m - 32:m], device=dev)
+    cols = torch.tensor(np.r_[0:64, n // 2:n // 2 + 64, n - 64:n], device=dev)
+    am = a if a_layout == "MK" else a.t()
+    ref = oracle.matmul(f64(am[rows]), f64(b[cols]), "NK")
+    assert_half(f64(out[rows][:, cols]), ref, f"planner split {a_layout} {info}")
     p.free()
 
 
