@@ -4,8 +4,17 @@ Usage: python -m dense_gemm_epilogues_amd.build   (or __graft_entry__.build()).
 Objects go to dense_gemm_epilogues_amd/_build/, the library to
 dense_gemm_epilogues_amd/libep.so.  The fused-GEMM template is compiled once per
 (dtype, B layout, epilog) in parallel.
+
+Resource guard: every object is compiled with the compiler's kernel-resource-usage remarks,
+and the build fails if any kernel uses scratch memory or spills registers.  For the
+configurations that issue their MFMAs as inline asm (16x16x32, whose hazards the compiler
+does not track), a spill or register move around the MFMAs can make them read accumulators
+before their results land, so such a build must never reach a GPU; for the others a spill
+is a performance bug.  The per-kernel figures go to _build/resource_usage.json.
 """
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -27,16 +36,66 @@ FLAGS = [
     "-I", CSRC, "-I", INCLUDE,
 ]
 N_EPI = 11
+REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+REPORT = os.path.join(BUILD, "resource_usage.json")
+
+_FIELDS = {"TotalSGPRs": "sgprs", "VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch",
+           "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill", "LDS Size [bytes/block]": "lds"}
+
+
+def parse_resource_usage(text):
+    """{mangled kernel name: {field: int}} from the compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in text.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][^:]*?): (-?\d+)\s", line + " ")
+        if m and cur is not None and m.group(1) in _FIELDS:
+            cur[_FIELDS[m.group(1)]] = int(m.group(2))
+    return out
+
+
+def asm_mfma_cfgs():
+    """Tile configurations whose MFMAs are inline asm: the kTileCfgs rows of ep_internal.hpp with
+    a 16-wide MFMA block (the field after vst)."""
+    text = open(os.path.join(CSRC, "ep_internal.hpp")).read()
+    table = text[text.index("kTileCfgs[kNumTileCfgs] = {"):]
+    table = table[:table.index("};")]
+    rows = re.findall(r"\{\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*\"", table)
+    return {i for i, r in enumerate(rows) if int(r[6]) == 16}
+
+
+def check_resource_usage(usage, asm_cfgs=None):
+    """Raise RuntimeError naming every kernel that uses scratch or spills registers (see the
+    module docstring); returns the number of kernels checked."""
+    asm_cfgs = asm_mfma_cfgs() if asm_cfgs is None else asm_cfgs
+    bad = []
+    for name, u in usage.items():
+        missing = [f for f in ("scratch", "vgpr_spill", "sgpr_spill") if f not in u]
+        if missing:
+            bad.append(f"{name}: no {', '.join(missing)} figure in the compiler's remarks")
+            continue
+        if u["scratch"] or u["vgpr_spill"] or u["sgpr_spill"]:
+            m = re.search(r"gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", name)
+            why = ("inline-asm MFMA configuration: spills or moves around the MFMAs break their hazard "
+                   "handling" if m and int(m.group(4)) in asm_cfgs else "spilling kernel")
+            bad.append(f"{name}: scratch {u['scratch']} B/lane, VGPR spill {u['vgpr_spill']}, "
+                       f"SGPR spill {u['sgpr_spill']} ({why})")
+    if bad:
+        raise RuntimeError("resource guard failed:\n  " + "\n  ".join(bad))
+    return len(usage)
 
 
 def _compile(args):
     src, obj, defines = args
-    cmd = [HIPCC] + FLAGS + defines + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + defines + REMARKS + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{out}")
-    return obj
+    return obj, parse_resource_usage(r.stdout)
 
 
 def build(verbose=False, jobs=None):
@@ -53,7 +112,16 @@ def build(verbose=False, jobs=None):
     tasks.append((os.path.join(CSRC, "ep_api.cpp"), os.path.join(BUILD, "ep_api.o"), []))
     jobs = jobs or min(16, os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, tasks))
+        done = list(ex.map(_compile, tasks))
+    objs = [o for o, _ in done]
+    usage = {}
+    for _, u in done:
+        usage.update(u)
+    with open(REPORT, "w") as f:
+        json.dump(usage, f, indent=0, sort_keys=True)
+    n = check_resource_usage(usage)
+    if verbose:
+        print(f"resource guard: {n} kernels, none uses scratch or spills")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -1162,6 +1162,9 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
           if constexpr (BGRAD) {  // rows past M are staged as 0
             colsum[0] += vv[c][0];
             colsum[1] += vv[c][1];
+            // the running sums are taken here: left free, the compiler sank every addition to
+            // the end of the epilogue and kept each row's values live until then (spills)
+            asm volatile("" : "+v"(colsum[0]), "+v"(colsum[1]));
           }
         }
       }
