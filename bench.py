@@ -1,27 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the fused GEMM + epilogue library on one MI355X.
 
-Prints ONE JSON line.  The headline workload is the square fp16 ReLU linear layer
-(M = N = K = 4096): one step is the fused forward RELU_AUX_BIAS followed by the fused
-backward DRELU_BGRAD that consumes the forward's relu_aux.  `value` is that step's
-GEMM throughput in TFLOP/s (2*M*N*K per GEMM; epilog flops not counted).  The same line
-carries the unfused-path step time (same GEMM core, DEFAULT epilog, separate kernels
-through HBM) and, under "configs", the fused/unfused timings of the large workloads:
-the H200-shape fp16 layer (65536 x 16384 x 8192), the bf16 SwiGLU forward
-(M 2048, H 5120, I 17408), the GEMM + dSwiGLU backward (M 16384), a whole SwiGLU-MLP
-training step, an M sweep, the GELU layer, launch overhead and plan-time tuning.  Where
-stated, torch (hipBLASLt GEMMs plus elementwise ops) runs the same step as a vendor-library
-reference.
+Prints ONE JSON line.  The headline workload is the fp16 ReLU linear layer at the H200 shape
+of "Fusing Matmul Epilogs with nvmath-python" ("Suitable evaluation scenarios"): X 65536 x 16384,
+W 16384 x 8192.  One step is the fused forward RELU_AUX_BIAS (Y and its relu_aux) followed by
+the fused backward DRELU_BGRAD (dY W^T masked by a separate 65536 x 16384 relu_aux, plus the
+bias gradient).  `value` is that step's GEMM throughput in TFLOP/s (2*M*N*K per GEMM; epilog
+flops not counted).  The same line carries the unfused-path step time (same GEMM core,
+DEFAULT epilog, separate kernels through HBM) and, under "configs", the square 4096^3 layer,
+the bf16 SwiGLU forward (M 2048, H 5120, I 17408), the GEMM + dSwiGLU backward (M 16384), a
+whole SwiGLU-MLP training step, an M sweep, the GELU layer, launch overhead and plan-time
+tuning.  Where stated, torch (hipBLASLt GEMMs plus elementwise ops) runs the same step as a
+vendor-library reference.
 
-Timing: HIP events on the stream the kernels run on.  The headline layer runs its steps back
-to back over several copies of its inputs that together exceed the 256 MB Infinity Cache, so
-no step finds its operands cached, with one event pair around each block of steps; fused,
-unfused and torch blocks alternate, so clock and power drift over the run reach each alike.
-The other workloads time one event pair per step, with a 512 MiB buffer overwritten between
-steps (outside the events), the variants alternating step by step.  An event record costs
-about 6 us of GPU time before the next launch, so per-kernel durations (the roofline's
-average launch) come from launches run back to back between a single event pair.  Inputs are
-seeded synthetic tensors generated on the device.  The CPU oracle (float64 numpy) is timed on this host as a baseline only.
+Timing: HIP events on the stream the kernels run on.  The layers run their steps back to
+back over enough copies of their inputs that together exceed the 256 MB Infinity Cache (one
+copy at the H200 shape), so no step finds its operands cached, with one event pair around
+each block of steps; fused, unfused and torch blocks alternate, so clock and power drift over
+the run reach each alike.  The other workloads time one event pair per step, with a 512 MiB
+buffer overwritten between steps (outside the events), the variants alternating step by
+step.  An event record costs about 6 us of GPU time before the next launch, so per-kernel
+durations (the roofline's average launch) come from launches run back to back between a
+single event pair.  Inputs are seeded synthetic tensors generated on the device.  The CPU
+oracle (float64 numpy) is timed on this host on a sample of each large workload (seeded
+output tiles and bias-gradient columns), as a baseline only.
 """
 import argparse
 import json
@@ -33,8 +35,12 @@ import numpy as np
 import torch
 
 PEAK_F16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense fp16/bf16 FLOP/clk/CU
-# read X, W, bias once; write Y and the relu_aux words once (4096^3 fp16 forward)
-ALGO_BYTES_SQ4096_FWD = 3 * 4096 * 4096 * 2 + 4096 * 2 + 4096 * 128 * 4
+
+
+def algo_bytes_fwd(m, n, k):
+    """Algorithmic HBM bytes of one RELU_AUX_BIAS forward launch: read X (m x k), W (k x n)
+    and the bias once; write Y (m x n) and the relu_aux words (m x ceil(n/32)) once."""
+    return 2 * (m * k + k * n + n + m * n) + 4 * m * ((n + 31) // 32)
 METRIC = "fused GEMM+epilogue TFLOP/s, % MFMA peak, speedup vs unfused path"
 
 
@@ -55,16 +61,16 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "traffic_gemm_relu_aux_bias_f16_KN_4096.txt")
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_gemm_relu_aux_bias_f16_KN_65536x8192x16384.txt")
 
 
-def measured_traffic():
+def measured_traffic(path=TRAFFIC_FILE):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
     summary, or None when it is missing or was measured on different kernel sources."""
     try:
         from dense_gemm_epilogues_amd.profiling import read_record, source_hash
-        rec = read_record(TRAFFIC_FILE)
+        rec = read_record(path)
         if rec.get("source_hash") != source_hash():
             return None
         return rec
@@ -248,7 +254,8 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True, with_clock=Fal
             plans[path].append((pf, pb))
     variants = {path: [[pf.execute, pb.execute] for pf, pb in plans[path]] for path in paths}
     if with_unfused:
-        # vendor-library reference: hipBLASLt GEMMs + torch elementwise, byte mask instead of bits
+        # vendor-library reference: hipBLASLt GEMMs + torch elementwise, byte mask instead of
+        # bits; the bias gradient sums the masked product, as DRELU_BGRAD does
         def torch_step_of(ins):
             x, w, bias, dy = ins["x"], ins["w"], ins["bias"], ins["dy"]
             if separate:  # the separate backward mask (M x K bits) as bytes, unpacked untimed
@@ -258,8 +265,8 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True, with_clock=Fal
             def torch_step():
                 yy = torch.addmm(bias, x, w).relu_()
                 keep = yy > 0
-                (dy @ w.t()) * (keep_b if separate else keep)
-                dy.float().sum(0)
+                g = (dy @ w.t()) * (keep_b if separate else keep)
+                g.float().sum(0)  # the bias gradient: column sums of the masked product
             return torch_step
         variants["torch"] = [[torch_step_of(ins)] for ins in sets]
     timed = run_rotating(variants, steps, warmup)
@@ -336,9 +343,11 @@ def swiglu_fwd(c, steps, warmup, flush, dev):
     x, wg, wu, wd = inp["x"], inp["wg"], inp["wu"], inp["wd"]
     m, h, i = c.m, c.h, c.i
     plans = {}
+    hs = {}
     for path in ("fused", "unfused"):
         ps = ep.Plan(x, wg, "SWIGLU", {"b2": wu}, b_layout="NK", path=path)
         hh, _ = ps.execute()
+        hs[path] = hh
         pd = ep.Plan(hh, wd, "DEFAULT", b_layout="NK")
         plans[path] = (ps, pd)
     timed = run_interleaved({p_: [ps.execute, pd.execute] for p_, (ps, pd) in plans.items()}, steps, warmup, flush)
@@ -354,7 +363,7 @@ def swiglu_fwd(c, steps, warmup, flush, dev):
     f["tflops_down"] = flop_d / (f["down_ms"] * 1e-3) / 1e12
     f["tflops_step"] = (flop_s + flop_d) / (f["step_ms"] * 1e-3) / 1e12
     return {"fused": f, "unfused": u, "speedup_swiglu": u["swiglu_ms"] / f["swiglu_ms"],
-            "speedup_step": u["step_ms"] / f["step_ms"]}
+            "speedup_step": u["step_ms"] / f["step_ms"], "inputs": inp, "h": hs["fused"]}
 
 
 def dswiglu_bwd(c, steps, warmup, flush, dev):
@@ -371,7 +380,7 @@ def dswiglu_bwd(c, steps, warmup, flush, dev):
     flop = 2.0 * c.m * c.h * c.i
     f, u = res["fused"], res["unfused"]
     f["tflops"] = flop / (f["ms"] * 1e-3) / 1e12
-    return {"fused": f, "unfused": u, "speedup": u["ms"] / f["ms"]}
+    return {"fused": f, "unfused": u, "speedup": u["ms"] / f["ms"], "inputs": inp}
 
 
 def mlp_training_step(c, steps, warmup, flush, dev):
@@ -572,31 +581,150 @@ def execute_overhead(dev):
             "swiglu_fwd_M2048_graph_ms": round(times["graph"], 4)}
 
 
-def cpu_baseline(inputs, c):
-    """The float64 oracle on the same inputs: one full forward + backward step of the square
-    layer, repeated until about 10 s of CPU work (at least once)."""
-    import oracle
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    x = oracle.decode_f16(inputs["x"].cpu().numpy())
-    w = oracle.decode_f16(inputs["w"].cpu().numpy())
-    b = oracle.decode_f16(inputs["bias"].cpu().numpy())
-    dy = oracle.decode_f16(inputs["dy"].cpu().numpy())
-    reps, t_total = 0, 0.0
-    while reps == 0 or (t_total < 10.0 and reps < 5):
+        return len(os.sched_getaffinity(0))
+
+
+def timed_reps(fn, min_s, max_reps):
+    """Mean wall time of fn() over repetitions until min_s seconds have passed (at least one,
+    at most max_reps)."""
+    reps, tot = 0, 0.0
+    while reps == 0 or (tot < min_s and reps < max_reps):
         t0 = time.perf_counter()
-        _, words, _ = oracle.relu_aux_bias(x, w, b, "KN")
-        oracle.drelu_bgrad(dy, w, "NK", words)
-        t_total += time.perf_counter() - t0
+        fn()
+        tot += time.perf_counter() - t0
         reps += 1
-    flop = 2 * 2.0 * c.m * c.n * c.k
-    sec = t_total / reps
-    return {"value": flop / sec / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"full fp64 forward RELU_AUX_BIAS + backward DRELU_BGRAD at M=N=K={c.m} on the "
-                      f"same inputs, {reps} rep(s), {sec:.2f} s each; host has {os.cpu_count()} logical CPUs"}
+    return tot / reps, reps
+
+
+def host(t):
+    """numpy copy of a device tensor (bf16 as its uint16 bits, int32 mask words as uint32)."""
+    import workloads as W
+    return W.to_numpy(t)
+
+
+def oracle_rate(sample_flop, step_flop, sec, reps, what, copy_s):
+    rate = sample_flop / sec
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{what}; {sample_flop / 1e9:.1f} GFLOP per pass, {reps} pass(es) of {sec:.2f} s; "
+                      f"device-to-host copies ({copy_s:.2f} s) not timed; host has {os.cpu_count()} logical CPUs",
+            "sample_gflop": round(sample_flop / 1e9, 2),
+            "extrapolated_full_step_s": round(step_flop / rate, 1),
+            "extrapolated_note": "extrapolated: the whole step's GEMM FLOP at the sampled rate, not measured"}
+
+
+def cpu_baseline_linear(inp, c, min_s=10.0):
+    """The float64 oracle on a sample of the ReLU layer's step, on the same inputs: 32 seeded
+    128 x 128 tiles plus the 4 corners of the forward (RELU_AUX_BIAS: Y and mask words) and of
+    the backward (DRELU_BGRAD: masked dY W^T), and 64 seeded bias-gradient columns plus the
+    first and last (each a full column sum of the masked product over all rows)."""
+    import oracle
+    m, n, k = c.m, c.n, c.k
+    t0 = time.perf_counter()
+    ftiles = oracle.sample_tiles(m, n, count=32, seed=31)
+    btiles = oracle.sample_tiles(m, k, count=32, seed=37)
+    cols = oracle.sample_columns(k, count=64, seed=41)
+    bias = host(inp["bias"])
+    fwd = [(host(inp["x"][r0:r1]), host(inp["w"][:, c0:c1]), bias[c0:c1]) for (r0, r1, c0, c1) in ftiles]
+    words_all = inp["mask_in"]
+    bwd = [(host(inp["dy"][r0:r1]), host(inp["w"][c0:c1]), host(words_all[r0:r1, c0 // 32:(c1 + 31) // 32]))
+           for (r0, r1, c0, c1) in btiles]
+    cwords = sorted(set(int(cc) // 32 for cc in cols))
+    widx = np.array([cwords.index(int(cc) // 32) * 32 + int(cc) % 32 for cc in cols])
+    dy_h = host(inp["dy"])
+    w_cols = host(inp["w"][torch.as_tensor(cols, device=inp["w"].device)])
+    words_cols = host(words_all[:, torch.as_tensor(cwords, device=words_all.device)])
+    copy_s = time.perf_counter() - t0
+    d = oracle.decode_f16
+
+    def run():
+        for xt, wt, bt in fwd:
+            oracle.relu_aux_bias(d(xt), d(wt), d(bt), "KN")
+        for dyt, wr, wd in bwd:
+            oracle.drelu_bgrad(d(dyt), d(wr), "NK", wd)
+        acc = np.zeros(len(cols))
+        w64 = d(w_cols)
+        for r0 in range(0, m, 8192):
+            g = oracle.matmul(d(dy_h[r0:r0 + 8192]), w64, "NK")
+            bits = oracle.unpack_relu_mask(words_cols[r0:r0 + 8192], 32 * len(cwords))[:, widx]
+            acc += np.where(bits, g, 0.0).sum(axis=0)
+        return acc
+
+    sec, reps = timed_reps(run, min_s, 5)
+    flop = sum(2.0 * (r1 - r0) * (c1 - c0) * k for (r0, r1, c0, c1) in ftiles)
+    flop += sum(2.0 * (r1 - r0) * (c1 - c0) * n for (r0, r1, c0, c1) in btiles)
+    flop += 2.0 * m * n * len(cols)
+    what = (f"{len(ftiles)} forward and {len(btiles)} backward 128x128 output tiles and {len(cols)} full "
+            f"bias-gradient columns of the {m}x{k}x{n} fp16 layer step (fp64 oracle)")
+    return oracle_rate(flop, 2 * 2.0 * m * n * k, sec, reps, what, copy_s)
+
+
+def cpu_baseline_swiglu(inp, h_gpu, c, min_s=3.0):
+    """The oracle on 32 seeded + 4 corner 128 x 128 tiles of the SwiGLU output h (two GEMMs and
+    silu*mul each) and as many tiles of the down projection (on the GPU's h)."""
+    import oracle
+    m, hd, i = c.m, c.h, c.i
+    t0 = time.perf_counter()
+    ht = oracle.sample_tiles(m, i, count=32, seed=51)
+    ot = oracle.sample_tiles(m, hd, count=32, seed=52)
+    hs = [(host(inp["x"][r0:r1]), host(inp["wg"][c0:c1]), host(inp["wu"][c0:c1])) for (r0, r1, c0, c1) in ht]
+    ds = [(host(h_gpu[r0:r1]), host(inp["wd"][c0:c1])) for (r0, r1, c0, c1) in ot]
+    copy_s = time.perf_counter() - t0
+    d = oracle.decode_bf16_bits
+
+    def run():
+        for xt, g, u in hs:
+            oracle.swiglu(d(xt), d(g), d(u))
+        for ht_, wd in ds:
+            oracle.matmul(d(ht_), d(wd), "NK")
+
+    sec, reps = timed_reps(run, min_s, 5)
+    flop = sum(4.0 * (r1 - r0) * (c1 - c0) * hd for (r0, r1, c0, c1) in ht)
+    flop += sum(2.0 * (r1 - r0) * (c1 - c0) * i for (r0, r1, c0, c1) in ot)
+    what = f"{len(ht)} tiles of h and {len(ot)} tiles of the down projection (bf16 SwiGLU forward, fp64 oracle)"
+    return oracle_rate(flop, 6.0 * m * hd * i, sec, reps, what, copy_s)
+
+
+def cpu_baseline_dswiglu(inp, c, min_s=3.0):
+    """The oracle on 32 seeded + 4 corner 128 x 128 tiles of d_gate and d_up."""
+    import oracle
+    m, hd, i = c.m, c.h, c.i
+    t0 = time.perf_counter()
+    tl = oracle.sample_tiles(m, i, count=32, seed=53)
+    ts = [(host(inp["dout"][r0:r1]), host(inp["wd"][:, c0:c1]), host(inp["gate"][r0:r1, c0:c1]),
+           host(inp["up"][r0:r1, c0:c1])) for (r0, r1, c0, c1) in tl]
+    copy_s = time.perf_counter() - t0
+    d = oracle.decode_bf16_bits
+
+    def run():
+        for dt, wd, g, u in ts:
+            oracle.dswiglu(d(dt), d(wd), d(g), d(u))
+
+    sec, reps = timed_reps(run, min_s, 5)
+    flop = sum(2.0 * (r1 - r0) * (c1 - c0) * hd for (r0, r1, c0, c1) in tl)
+    what = f"{len(tl)} tiles of d_gate and d_up (bf16 GEMM + dSwiGLU, fp64 oracle)"
+    return oracle_rate(flop, 2.0 * m * hd * i, sec, reps, what, copy_s)
+
+
+def linear_summary(r, c):
+    f = r["fused"]
+    flop = r["flop_per_gemm"]
+    return {"fused_step_tflops": round(f["tflops_step"], 1),
+            "step_pct_peak": round(100 * f["tflops_step"] / PEAK_F16_TFLOPS, 2),
+            "fused_step_ms": round(f["step_ms"], 4), "unfused_step_ms": round(r["unfused"]["step_ms"], 4),
+            "speedup_step": round(r["speedup_step"], 4),
+            "fused_fwd_tflops": round(f["tflops_fwd"], 1), "fused_bwd_tflops": round(f["tflops_bwd"], 1),
+            "fwd_pct_peak": round(100 * f["tflops_fwd"] / PEAK_F16_TFLOPS, 2),
+            "bwd_pct_peak": round(100 * f["tflops_bwd"] / PEAK_F16_TFLOPS, 2),
+            "fused_fwd_ms": round(f["fwd_ms"], 5), "fused_bwd_ms": round(f["bwd_ms"], 5),
+            "unfused_fwd_ms": round(r["unfused"]["fwd_ms"], 5), "unfused_bwd_ms": round(r["unfused"]["bwd_ms"], 5),
+            "speedup_fwd": round(r["speedup_fwd"], 4), "speedup_bwd": round(r["speedup_bwd"], 4),
+            "torch_step_ms": round(r["torch"]["step_ms"], 4), "speedup_vs_torch": round(r["speedup_vs_torch"], 4),
+            "gemm_flop": flop, "input_sets": f["input_sets"]}
 
 
 def main():
@@ -631,80 +759,86 @@ def main():
             r.pop("inputs")
         elif args.only == "swiglu":
             r = swiglu_fwd(W.SWIGLU[4], st, wu, flush, dev)
+            r.pop("h")
+            r.pop("inputs")
         elif args.only == "gelu":
             r = gelu_layer(W.LINEAR[2], st, wu, flush, dev)
         elif args.only == "mlp_step":
             r = mlp_training_step(W.SWIGLU[4], st, wu, flush, dev)
         elif args.only == "dswiglu":
             r = dswiglu_bwd(W.SWIGLU[5], st, wu, flush, dev)
+            r.pop("inputs")
         else:
             raise SystemExit(f"unknown --only {args.only}")
-        print(json.dumps({"only": args.only, "result": r}))
+        print(json.dumps({"only": args.only, "result": r}, default=str))
         return
 
-    c2 = W.LINEAR[2]
+    c3 = W.LINEAR[3]
     t_start = time.time()
-    r2 = linear_layer(c2, args.steps, args.warmup, flush, dev, with_clock=True)
-    f2 = r2["fused"]
-    fwd_tflops = f2["tflops_fwd"]
+    r3 = linear_layer(c3, args.steps, args.warmup, flush, dev, with_clock=True)
+    f3 = r3["fused"]
+    fwd_tflops = f3["tflops_fwd"]
     line = {
         "metric": METRIC,
-        "value": round(f2["tflops_step"], 2),
+        "value": round(f3["tflops_step"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(f2["step_ms"], 5),
+        "ms_per_step": round(f3["step_ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "square ReLU linear layer, fp16 in / fp32 acc: fused RELU_AUX_BIAS forward "
-                               "(X 4096x4096 . W 4096x4096 + bias) then fused DRELU_BGRAD backward "
-                               "(dY . W^T masked by the forward relu_aux, + bgrad)",
-                   "m": c2.m, "n": c2.n, "k": c2.k,
-                   "cache": f"cold: steps rotate over {f2['input_sets']} copies of the inputs (more than the "
-                            "256 MB Infinity Cache together)"},
+        "config": {"workload": "H200-shape ReLU linear layer, fp16 in / fp32 acc: fused RELU_AUX_BIAS forward "
+                               "(X 65536x16384 . W 16384x8192 + bias, Y 65536x8192 and its relu_aux) then fused "
+                               "DRELU_BGRAD backward (dY 65536x8192 . W^T masked by a separate 65536x16384 "
+                               "relu_aux, + bgrad of length 16384)",
+                   "m": c3.m, "n": c3.n, "k": c3.k,
+                   "cache": "cold: the step's operands (6.5 GB) exceed the 256 MB Infinity Cache"},
         "timing": "4 blocks of steps/4 back-to-back steps per variant, one HIP event pair per block, "
                   "fused / unfused / torch blocks alternating; median/min/max are over the blocks",
-        "ms_per_step_median": round(f2["step_ms_median"], 5),
-        "ms_per_step_min": round(f2["step_ms_min"], 5), "ms_per_step_max": round(f2["step_ms_max"], 5),
-        "pct_peak": round(100.0 * f2["tflops_step"] / PEAK_F16_TFLOPS, 2),
-        "speedup_vs_unfused": round(r2["speedup_step"], 4),
-        "unfused_ms_per_step": round(r2["unfused"]["step_ms"], 5),
-        "torch_ms_per_step": round(r2["torch"]["step_ms"], 5),
-        "speedup_vs_torch": round(r2["speedup_vs_torch"], 4),
-        "fwd_ms": round(f2["fwd_ms"], 5), "bwd_ms": round(f2["bwd_ms"], 5),
-        "roofline": {"bound": "mfma", "kernel": f2["fwd_info"].split("kernels=")[1],
+        "ms_per_step_median": round(f3["step_ms_median"], 4),
+        "ms_per_step_min": round(f3["step_ms_min"], 4), "ms_per_step_max": round(f3["step_ms_max"], 4),
+        "pct_peak": round(100.0 * f3["tflops_step"] / PEAK_F16_TFLOPS, 2),
+        "speedup_vs_unfused": round(r3["speedup_step"], 4),
+        "unfused_ms_per_step": round(r3["unfused"]["step_ms"], 4),
+        "torch_ms_per_step": round(r3["torch"]["step_ms"], 4),
+        "speedup_vs_torch": round(r3["speedup_vs_torch"], 4),
+        "fwd_ms": round(f3["fwd_ms"], 4), "bwd_ms": round(f3["bwd_ms"], 4),
+        "fwd_tflops": round(f3["tflops_fwd"], 1), "bwd_tflops": round(f3["tflops_bwd"], 1),
+        "speedup_fwd_vs_unfused": round(r3["speedup_fwd"], 4), "speedup_bwd_vs_unfused": round(r3["speedup_bwd"], 4),
+        "roofline": {"bound": "mfma", "kernel": f3["fwd_info"].split("kernels=")[1],
                      "achieved": round(fwd_tflops, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fwd_tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
-                     "algorithmic_per_launch": f"{r2['flop_per_gemm']:.6g} FLOP (2*4096^3)",
-                     "algorithmic_bytes_per_launch": ALGO_BYTES_SQ4096_FWD,
-                     "avg_launch_ms": round(f2["fwd_ms"], 5),
+                     "algorithmic_per_launch": f"{r3['flop_per_gemm']:.6g} FLOP (2*65536*8192*16384)",
+                     "algorithmic_bytes_per_launch": algo_bytes_fwd(c3.m, c3.n, c3.k),
+                     "avg_launch_ms": round(f3["fwd_ms"], 4),
                      "avg_launch_how": "20 back-to-back launches of the forward between one HIP event pair "
                                        "on the launch stream"},
+        "bwd_kernel": f3["bwd_info"].split("kernels=")[1],
     }
-    line["clock_under_load"] = r2["clock"]
+    line["clock_under_load"] = r3["clock"]
     tr = measured_traffic()
     if tr is not None:
         line["roofline"]["traffic"] = round(tr["traffic_bytes_per_launch"])
         line["roofline"]["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    cpu = {}
+    if not args.no_cpu:
+        cpu["h200"] = cpu_baseline_linear(r3["inputs"], c3)
+    r3.pop("inputs")
+    torch.cuda.empty_cache()
     if not args.no_large:
         large = {}
-        s_l, w_l = max(3, args.steps // 4), max(1, args.warmup // 2)
-        r3 = linear_layer(W.LINEAR[3], s_l, w_l, flush, dev)
-        r3.pop("inputs")
-        large["h200_fp16_65536x16384x8192"] = {
-            "fused_fwd_tflops": round(r3["fused"]["tflops_fwd"], 1),
-            "fused_bwd_tflops": round(r3["fused"]["tflops_bwd"], 1),
-            "fwd_pct_peak": round(100 * r3["fused"]["tflops_fwd"] / PEAK_F16_TFLOPS, 2),
-            "bwd_pct_peak": round(100 * r3["fused"]["tflops_bwd"] / PEAK_F16_TFLOPS, 2),
-            "fused_fwd_ms": round(r3["fused"]["fwd_ms"], 4), "fused_bwd_ms": round(r3["fused"]["bwd_ms"], 4),
-            "unfused_fwd_ms": round(r3["unfused"]["fwd_ms"], 4), "unfused_bwd_ms": round(r3["unfused"]["bwd_ms"], 4),
-            "speedup_fwd": round(r3["speedup_fwd"], 4), "speedup_bwd": round(r3["speedup_bwd"], 4),
-            "torch_step_ms": round(r3["torch"]["step_ms"], 4), "speedup_step_vs_torch": round(r3["speedup_vs_torch"], 4)}
+        r2 = linear_layer(W.LINEAR[2], args.steps, args.warmup, flush, dev)
+        r2.pop("inputs")
+        large["square_fp16_4096x4096x4096"] = linear_summary(r2, W.LINEAR[2])
+        tr2 = measured_traffic(os.path.join(PROFILES, "traffic_gemm_relu_aux_bias_f16_KN_4096.txt"))
+        large["square_fp16_4096x4096x4096"]["fwd_traffic_bytes"] = (round(tr2["traffic_bytes_per_launch"])
+                                                                    if tr2 is not None else None)
         torch.cuda.empty_cache()
+        s_l, w_l = max(3, args.steps // 4), max(1, args.warmup // 2)
         r4 = swiglu_fwd(W.SWIGLU[4], args.steps, args.warmup, flush, dev)
         large["swiglu_fwd_bf16_M2048_H5120_I17408"] = {
             "fused_swiglu_tflops": round(r4["fused"]["tflops_swiglu"], 1),
@@ -713,6 +847,10 @@ def main():
             "fused_swiglu_ms": round(r4["fused"]["swiglu_ms"], 4),
             "unfused_swiglu_ms": round(r4["unfused"]["swiglu_ms"], 4),
             "speedup_swiglu": round(r4["speedup_swiglu"], 4), "speedup_fwd_step": round(r4["speedup_step"], 4)}
+        if not args.no_cpu:
+            large["swiglu_fwd_bf16_M2048_H5120_I17408"]["cpu_oracle_sampled"] = cpu_baseline_swiglu(
+                r4["inputs"], r4["h"], W.SWIGLU[4])
+        del r4
         torch.cuda.empty_cache()
         r5 = dswiglu_bwd(W.SWIGLU[5], args.steps, args.warmup, flush, dev)
         large["dswiglu_bwd_bf16_M16384_H5120_I17408"] = {
@@ -720,6 +858,10 @@ def main():
             "pct_peak": round(100 * r5["fused"]["tflops"] / PEAK_F16_TFLOPS, 2),
             "fused_ms": round(r5["fused"]["ms"], 4), "unfused_ms": round(r5["unfused"]["ms"], 4),
             "speedup": round(r5["speedup"], 4)}
+        if not args.no_cpu:
+            large["dswiglu_bwd_bf16_M16384_H5120_I17408"]["cpu_oracle_sampled"] = cpu_baseline_dswiglu(
+                r5["inputs"], W.SWIGLU[5])
+        del r5
         torch.cuda.empty_cache()
         large["swiglu_fwd_bf16_M_sweep_H5120_I17408"] = swiglu_m_sweep(s_l, w_l, flush, dev)
         large["swiglu_mlp_training_step_bf16_M2048_H5120_I17408"] = mlp_training_step(W.SWIGLU[4], args.steps, args.warmup, flush, dev)
@@ -729,7 +871,7 @@ def main():
         large["autotune_vs_model"] = autotune_vs_model(s_l, w_l, flush, dev)
         line["configs"] = large
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(r2["inputs"], c2)
+        line["cpu_baseline"] = cpu["h200"]
     line["wall_s"] = round(time.time() - t_start, 1)
     print(json.dumps(line), flush=True)
 
