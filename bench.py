@@ -301,7 +301,7 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True, with_clock=Fal
         out["speedup_bwd"] = u["bwd_ms"] / f["bwd_ms"]
         out["torch"] = res["torch"]
         out["speedup_vs_torch"] = res["torch"]["step_ms"] / f["step_ms"]
-    out["inputs"] = {"x": x, "w": w, "bias": bias, "dy": dy}
+    out["inputs"] = {"x": x, "w": w, "bias": bias, "dy": dy, "mask_in": inp["mask_in"]}
     out["clock"] = clock
     return out
 
