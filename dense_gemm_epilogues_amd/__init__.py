@@ -23,7 +23,8 @@ import torch
 __all__ = ["Plan", "EPError", "EPILOGS", "lib", "library_path", "abi_version", "num_tile_cfgs", "validate_operands"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libep.so")
+# EP_LIBRARY names another build of the same library (the host-sanitizer build the CPU tests use)
+library_path = os.environ.get("EP_LIBRARY") or os.path.join(_HERE, "libep.so")
 
 EPILOGS = {
     "DEFAULT": 0, "BIAS": 1, "RELU_BIAS": 2, "RELU_AUX_BIAS": 3,

@@ -133,6 +133,35 @@ def build(verbose=False, jobs=None):
     return LIB
 
 
+HOSTSAN_LIB = os.path.join(BUILD, "libep_hostsan.so")
+
+
+def build_host_sanitized(verbose=False):
+    """Host-sanitizer build of the C ABI for the CPU tests: ep_api.cpp (validation, planning,
+    dispatch; host code only) compiled by g++ with AddressSanitizer and UndefinedBehavior-
+    Sanitizer, linked with the kernel objects of the last build() (not instrumented).  Load it
+    with EP_LIBRARY pointing here and the sanitizer runtimes in LD_PRELOAD."""
+    src = os.path.join(CSRC, "ep_api.cpp")
+    obj = os.path.join(BUILD, "ep_api_hostsan.o")
+    objs = sorted(os.path.join(BUILD, f) for f in os.listdir(BUILD) if f.startswith("gemm_") and f.endswith(".o"))
+    objs.append(os.path.join(BUILD, "elementwise.o"))
+    if not all(os.path.exists(o) for o in objs) or len(objs) < 2:
+        raise RuntimeError("run build() first: the sanitized library links its kernel objects")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
+    gxx_compile = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"), "-I", CSRC, "-I", INCLUDE, "-c", src, "-o", obj] + san
+    r = subprocess.run(gxx_compile, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host-sanitizer compile failed:\n{r.stdout}")
+    gxx_link = ["g++", "-shared", "-o", HOSTSAN_LIB, obj] + objs + ["-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")] + san
+    r = subprocess.run(gxx_link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host-sanitizer link failed:\n{r.stdout}")
+    if verbose:
+        print(f"built {HOSTSAN_LIB}")
+    return HOSTSAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

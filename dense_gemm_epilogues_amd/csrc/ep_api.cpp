@@ -234,16 +234,27 @@ int choose_splits(int64_t tiles, int slots, int kt, int cfg) {
   return best;
 }
 
+// The integer a caller stored in an enum-typed field.  A C caller may store any int there;
+// loading a value outside the enumerators as the enum type is undefined in C++, so the
+// checks read the raw int.
+template <class E>
+int raw_enum(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "ABI enums are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io,
                    const ep_options* opt) {
   if (!s) return fail(EP_ERR_INVALID_ARG, "shape is NULL");
   if (!io) return fail(EP_ERR_INVALID_ARG, "epilog_io is NULL");
   if (dtype != EP_F16 && dtype != EP_BF16) return fail(EP_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   if ((int)epi < 0 || (int)epi >= E_NUM) return fail(EP_ERR_UNSUPPORTED, "unknown epilog %d", (int)epi);
-  if (s->b_layout != EP_B_KN && s->b_layout != EP_B_NK)
-    return fail(EP_ERR_UNSUPPORTED, "unknown B layout %d", (int)s->b_layout);
-  if (s->a_layout != EP_A_MK && s->a_layout != EP_A_KM)
-    return fail(EP_ERR_UNSUPPORTED, "unknown A layout %d", (int)s->a_layout);
+  if (raw_enum(s->b_layout) != EP_B_KN && raw_enum(s->b_layout) != EP_B_NK)
+    return fail(EP_ERR_UNSUPPORTED, "unknown B layout %d", raw_enum(s->b_layout));
+  if (raw_enum(s->a_layout) != EP_A_MK && raw_enum(s->a_layout) != EP_A_KM)
+    return fail(EP_ERR_UNSUPPORTED, "unknown A layout %d", raw_enum(s->a_layout));
   if (s->a_layout == EP_A_KM && epi != EP_EPILOG_DEFAULT)
     return fail(EP_ERR_UNSUPPORTED, "a K x M A operand is supported with the DEFAULT epilog only");
   if (s->m < 1 || s->n < 1 || s->k < 1) return fail(EP_ERR_INVALID_ARG, "m, n, k must be >= 1");
@@ -252,10 +263,10 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   if (s->n % 8 || s->k % 8) return fail(EP_ERR_UNSUPPORTED, "n and k must be multiples of 8");
   if (s->a_layout == EP_A_KM && s->m % 8) return fail(EP_ERR_UNSUPPORTED, "a K x M A needs m % 8 == 0");
   if (opt) {
-    if (opt->path != EP_PATH_FUSED && opt->path != EP_PATH_UNFUSED)
-      return fail(EP_ERR_INVALID_ARG, "unknown path %d", (int)opt->path);
-    if (opt->bgrad_mode != EP_BGRAD_TWO_PASS && opt->bgrad_mode != EP_BGRAD_ATOMIC)
-      return fail(EP_ERR_INVALID_ARG, "unknown bgrad mode %d", (int)opt->bgrad_mode);
+    if (raw_enum(opt->path) != EP_PATH_FUSED && raw_enum(opt->path) != EP_PATH_UNFUSED)
+      return fail(EP_ERR_INVALID_ARG, "unknown path %d", raw_enum(opt->path));
+    if (raw_enum(opt->bgrad_mode) != EP_BGRAD_TWO_PASS && raw_enum(opt->bgrad_mode) != EP_BGRAD_ATOMIC)
+      return fail(EP_ERR_INVALID_ARG, "unknown bgrad mode %d", raw_enum(opt->bgrad_mode));
     if (opt->tile_cfg < -1 || opt->tile_cfg >= kNumTileCfgs)
       return fail(EP_ERR_INVALID_ARG, "tile_cfg %d out of range", opt->tile_cfg);
     if (opt->split_k < 0 || opt->split_k > EP_MAX_SPLIT_K)
