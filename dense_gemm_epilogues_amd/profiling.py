@@ -22,9 +22,9 @@
       HBM bytes per launch of the kernel whose name contains KERNEL_SUBSTR (and, with
       --grid, whose grid size is G), from a `--pmc FETCH_SIZE` run and a `--pmc WRITE_SIZE`
       run (KiB per dispatch).  Each counter is scaled by what it reads for a plain device
-      copy of B bytes recorded in the same run (the largest dispatch of a kernel whose name
-      contains "copy"), and the result is tagged with the hash of the kernel sources it was
-      measured on.
+      copy of B bytes recorded in the same run (the largest dispatch of the runtime's
+      device-to-device copy kernel, __amd_rocclr_copyBuffer), and the result is tagged with the
+      hash of the kernel sources it was measured on.
 
 A traffic file is '#' comment lines (how it was made) followed by one JSON object;
 read_record() parses it.  source_hash() is the hash of the HIP/C++ sources of libep.so; a stored traffic figure is
@@ -168,13 +168,18 @@ def _mean(rows, substr, grid=None):
     return sum(vals) / len(vals), len(vals), next(k for (k, g, v) in rows if substr in k)
 
 
+CALIB_KERNEL = "__amd_rocclr_copyBuffer"
+
+
 def traffic(fetch_dir, write_dir, kernel, copy_bytes, grid=None):
     f = pmc_dispatches(fetch_dir, "FETCH_SIZE")
     w = pmc_dispatches(write_dir, "WRITE_SIZE")
     fk, fn, kname = _mean(f, kernel, grid)
     wk, wn, _ = _mean(w, kernel, grid)
-    cf = max(v for (k, g, v) in f if "copy" in k)
-    cw = max(v for (k, g, v) in w if "copy" in k)
+    # the calibration copy is the runtime's device-to-device copy kernel (torch's dtype casts
+    # also carry "copy" in their names and count differently)
+    cf = max(v for (k, g, v) in f if CALIB_KERNEL in k)
+    cw = max(v for (k, g, v) in w if CALIB_KERNEL in k)
     fetch_scale = copy_bytes / (cf * 1024.0)
     write_scale = copy_bytes / (cw * 1024.0)
     return {
