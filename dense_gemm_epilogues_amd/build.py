@@ -109,6 +109,7 @@ def build(verbose=False, jobs=None):
                 obj = os.path.join(BUILD, f"gemm_{dt}_{lay}_{epi}.o")
                 tasks.append((inst, obj, [f"-DEP_DT={dt}", f"-DEP_LAY={lay}", f"-DEP_EPI={epi}"]))
     tasks.append((os.path.join(CSRC, "elementwise.hip"), os.path.join(BUILD, "elementwise.o"), []))
+    tasks.append((os.path.join(CSRC, "static_scratch.hip"), os.path.join(BUILD, "static_scratch.o"), []))
     tasks.append((os.path.join(CSRC, "ep_api.cpp"), os.path.join(BUILD, "ep_api.o"), []))
     jobs = jobs or min(16, os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
@@ -144,8 +145,8 @@ def build_host_sanitized(verbose=False):
     src = os.path.join(CSRC, "ep_api.cpp")
     obj = os.path.join(BUILD, "ep_api_hostsan.o")
     objs = sorted(os.path.join(BUILD, f) for f in os.listdir(BUILD) if f.startswith("gemm_") and f.endswith(".o"))
-    objs.append(os.path.join(BUILD, "elementwise.o"))
-    if not all(os.path.exists(o) for o in objs) or len(objs) < 2:
+    objs += [os.path.join(BUILD, "elementwise.o"), os.path.join(BUILD, "static_scratch.o")]
+    if not all(os.path.exists(o) for o in objs) or len(objs) < 3:
         raise RuntimeError("run build() first: the sanitized library links its kernel objects")
     rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
     san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer"]

@@ -19,6 +19,7 @@
 
 #include "ep.h"
 #include "ep_internal.hpp"
+#include "static_scratch.hpp"
 
 namespace ep {
 
@@ -97,6 +98,8 @@ static const char* kEpiNames[E_NUM] = {"DEFAULT", "BIAS",     "RELU_BIAS",     "
 
 using namespace ep;
 
+static_assert(EP_NOALLOC_SCRATCH_BYTES == kStaticScratchBytes, "the header states the scratch size");
+
 namespace {
 
 constexpr uint64_t kMagic = 0x6570706c616e3031ULL;  // "epplan01"
@@ -138,8 +141,10 @@ struct ep_plan_s {
   GemmLauncher launch;
   GemmLauncher launch_partial, launch_fixup;  // split-K (splits > 1)
   int splits;
-  void* workspace;     // single allocation owned by the plan
+  void* workspace;     // single allocation owned by the plan (NULL for a plan on the stack)
   size_t workspace_bytes;
+  size_t part_bytes, z_bytes, kpart_bytes;  // its pieces: bgrad partials, unfused intermediates
+                                            // (two of z_bytes), split-K partials
   float* part;         // bgrad partials (two-pass)
   int nparts;
   UnfusedBufs uf;
@@ -489,54 +494,58 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int ep_abi_version(void) { return EP_ABI_VERSION; }
+// What planning needs to know about a device, queried once per device (so that the
+// allocation-free entry point makes no property query per call).
+struct DevInfo {
+  int cus;
+  char arch[64];
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+DevInfo g_dev[kMaxDevices];
+bool g_dev_known[kMaxDevices];
 
-int ep_num_tile_cfgs(void) { return kNumTileCfgs; }
-
-const char* ep_status_string(ep_status s) {
-  switch (s) {
-    case EP_OK: return "EP_OK";
-    case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
-    case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED";
-    case EP_ERR_OUT_OF_MEMORY: return "EP_ERR_OUT_OF_MEMORY";
-    case EP_ERR_HIP: return "EP_ERR_HIP";
-    case EP_ERR_INTERNAL: return "EP_ERR_INTERNAL";
+ep_status device_info(int dev, DevInfo* out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(EP_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (!g_dev_known[dev]) {
+      hipDeviceProp_t prop;
+      hipError_t he = hipGetDeviceProperties(&prop, dev);
+      if (he != hipSuccess) return fail(EP_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(he));
+      g_dev[dev].cus = prop.multiProcessorCount;
+      snprintf(g_dev[dev].arch, sizeof g_dev[dev].arch, "%s", prop.gcnArchName);
+      g_dev_known[dev] = true;
+    }
+    *out = g_dev[dev];
   }
-  return "EP_ERR_UNKNOWN";
+  if (strncmp(out->arch, "gfx950", 6) != 0)
+    return fail(EP_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev, out->arch);
+  return EP_OK;
 }
 
-const char* ep_last_error(void) { return t_last_error.c_str(); }
-
-ep_status ep_plan(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog, const ep_epilog_io* io, ep_handle* out) {
-  return ep_plan_ex(shape, dtype, epilog, io, nullptr, out);
+// The device a stream launches on (the calling thread's current device for the null stream).
+ep_status stream_device(hipStream_t s, int* dev) {
+  if (s == nullptr) {
+    if (hipGetDevice(dev) != hipSuccess) return fail(EP_ERR_HIP, "hipGetDevice failed");
+    return EP_OK;
+  }
+  hipDevice_t sd = -1;
+  if (hipStreamGetDevice(s, &sd) != hipSuccess) return fail(EP_ERR_INVALID_ARG, "the stream is not valid");
+  *dev = (int)sd;
+  return EP_OK;
 }
 
-ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io,
-                     const ep_options* opt_in, ep_handle* out) {
-  t_last_error.clear();
-  if (!out) return fail(EP_ERR_INVALID_ARG, "out handle pointer is NULL");
-  *out = nullptr;
-  ep_status st = validate(s, dtype, epi, io, opt_in);
-  if (st != EP_OK) return st;
-  ep_options opt = opt_in ? *opt_in : ep_options{EP_PATH_FUSED, EP_BGRAD_TWO_PASS, -1, 0, 0};
+size_t round_up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-  // ---- first HIP call: the device must exist and be usable
-  int dev = -1;
-  hipError_t he = hipGetDevice(&dev);
-  if (he != hipSuccess) return fail(EP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(he));
-  hipDeviceProp_t prop;
-  he = hipGetDeviceProperties(&prop, dev);
-  if (he != hipSuccess) return fail(EP_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(he));
-  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-    return fail(EP_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
-
-  if (opt.autotune) {
-    st = autotune(s, dtype, epi, io, opt, dev);
-    if (st != EP_OK) return st;
-  }
-
+// Plans into *h (value-initialised by the caller): tile configuration, split, kernels, kernel
+// arguments and the workspace layout.  ws_limit is the most workspace the caller can provide: a
+// split chosen by shape is reduced until its partials fit, and a plan that still needs more is
+// EP_ERR_UNSUPPORTED.  Pointers into the workspace are set by bind_workspace.
+ep_status plan_into(ep_plan_s* h, const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io,
+                    const ep_options& opt, int dev, int cus, size_t ws_limit) {
   const bool dual = epi == EP_EPILOG_SWIGLU || epi == EP_EPILOG_SWIGLU_AUX;
   const bool unfused = opt.path == EP_PATH_UNFUSED;
   // the unfused path runs plain DEFAULT GEMMs (single-B) into intermediates
@@ -544,13 +553,8 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   if (opt.tile_cfg >= 0 && !cfg_allowed(opt.tile_cfg, kernel_dual, s->b_layout))
     return fail(EP_ERR_UNSUPPORTED, "tile_cfg %d cannot run SWIGLU with a K x N weight (needs a 256-row B tile)",
                 opt.tile_cfg);
-  const int cfg = opt.tile_cfg >= 0
-                      ? opt.tile_cfg
-                      : pick_cfg(s, choose_cfg(s->m, s->n, kernel_dual, s->b_layout, prop.multiProcessorCount),
-                                 prop.multiProcessorCount, kernel_dual);
-
-  ep_plan_s* h = new (std::nothrow) ep_plan_s{};  // every member zero / null
-  if (!h) return fail(EP_ERR_OUT_OF_MEMORY, "host allocation failed");
+  const int cfg = opt.tile_cfg >= 0 ? opt.tile_cfg
+                                    : pick_cfg(s, choose_cfg(s->m, s->n, kernel_dual, s->b_layout, cus), cus, kernel_dual);
   h->magic = kMagic;
   h->shape = *s;
   h->dtype = dtype;
@@ -568,40 +572,12 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
   const int fused_epi = unfused ? (int)E_DEFAULT : (int)epi;
   const int klay = (int)s->b_layout + (s->a_layout == EP_A_KM ? 2 : 0);  // kernel layout index
   h->launch = gemm_launcher((int)dtype, klay, fused_epi, cfg);
-  if (!h->launch) {
-    delete h;
-    return fail(EP_ERR_INTERNAL, "no kernel instantiated for this combination");
-  }
-  // split-K (fused path only)
-  const int kt_all = (int)((s->k + kTileCfgs[cfg].bk - 1) / kTileCfgs[cfg].bk);
-  int splits = 1;
-  if (!unfused) {
-    splits = opt.split_k > 0 ? opt.split_k
-                             : choose_splits((int64_t)a.tiles_m * a.tiles_n,
-                                             prop.multiProcessorCount * kTileCfgs[cfg].occ, kt_all, cfg);
-    if (splits > kt_all) splits = kt_all;
-  }
-  if (splits > 1) {
-    a.kt_per_split = (kt_all + splits - 1) / splits;
-    splits = (kt_all + a.kt_per_split - 1) / a.kt_per_split;  // no empty K range
-  }
-  h->splits = splits;
-  a.splits = splits;
-  if (splits > 1) {
-    h->launch_partial = gemm_partial_launcher((int)dtype, klay, kernel_dual, cfg);
-    h->launch_fixup = gemm_fixup_launcher((int)dtype, (int)epi, cfg);
-    if (!h->launch_partial || !h->launch_fixup) {
-      delete h;
-      return fail(EP_ERR_INTERNAL, "no split-K kernel instantiated for this combination");
-    }
-  }
+  if (!h->launch) return fail(EP_ERR_INTERNAL, "no kernel instantiated for this combination");
 
-  // ---- workspace sizing
+  // ---- workspace pieces other than the split-K partials
   const int64_t M = s->m, N = s->n;
-  size_t part_bytes = 0, z_bytes = 0, z2_bytes = 0, kpart_bytes = 0;
-  if (splits > 1)
-    kpart_bytes = (size_t)splits * a.tiles_m * a.tiles_n * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * sizeof(float);
   const bool bgrad_epi = epi == EP_EPILOG_DRELU_BGRAD || epi == EP_EPILOG_DGELU_BGRAD;
+  size_t part_bytes = 0, z_bytes = 0;
   if (bgrad_epi) {
     if (unfused) {
       // rows per column-sum block: about 1024 blocks of 2048 columns over the matrix, so
@@ -617,29 +593,43 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
       part_bytes = (size_t)h->nparts * N * sizeof(float);
     }
   }
-  if (unfused && epi == EP_EPILOG_SWIGLU) {
-    // the two branch GEMMs of the unfused SwiGLU need intermediates; every other unfused
-    // sequence runs its elementwise passes in place on the output
-    z_bytes = (size_t)M * N * 2;
-    z2_bytes = z_bytes;
+  // the two branch GEMMs of the unfused SwiGLU need intermediates; every other unfused
+  // sequence runs its elementwise passes in place on the output
+  if (unfused && epi == EP_EPILOG_SWIGLU) z_bytes = (size_t)M * N * 2;
+
+  // ---- split-K (fused path only)
+  const int kt_all = (int)((s->k + kTileCfgs[cfg].bk - 1) / kTileCfgs[cfg].bk);
+  auto kpart_of = [&](int sp) {
+    return sp > 1 ? (size_t)sp * a.tiles_m * a.tiles_n * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * sizeof(float) : 0;
+  };
+  auto total_of = [&](int sp) { return round_up256(part_bytes) + 2 * round_up256(z_bytes) + round_up256(kpart_of(sp)); };
+  int splits = 1;
+  if (!unfused) {
+    splits = opt.split_k > 0 ? opt.split_k
+                             : choose_splits((int64_t)a.tiles_m * a.tiles_n, cus * kTileCfgs[cfg].occ, kt_all, cfg);
+    if (splits > kt_all) splits = kt_all;
+    if (opt.split_k == 0)
+      while (splits > 1 && total_of(splits) > ws_limit) --splits;
   }
-  auto round_up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  h->workspace_bytes = round_up(part_bytes) + round_up(z_bytes) + round_up(z2_bytes) + round_up(kpart_bytes);
-  if (h->workspace_bytes) {
-    he = hipMalloc(&h->workspace, h->workspace_bytes);
-    if (he != hipSuccess) {
-      const size_t bytes = h->workspace_bytes;
-      delete h;
-      (void)hipGetLastError();
-      return fail(EP_ERR_OUT_OF_MEMORY, "hipMalloc(%zu): %s", bytes, hipGetErrorString(he));
-    }
-    char* w = (char*)h->workspace;
-    if (part_bytes) { h->part = (float*)w; w += round_up(part_bytes); }
-    if (z_bytes) { h->uf.z = w; w += round_up(z_bytes); }
-    if (z2_bytes) { h->uf.z2 = w; w += round_up(z2_bytes); }
-    if (kpart_bytes) a.part = (float*)w;
-    h->uf.ldz = N;
+  if (splits > 1) {
+    a.kt_per_split = (kt_all + splits - 1) / splits;
+    splits = (kt_all + a.kt_per_split - 1) / a.kt_per_split;  // no empty K range
   }
+  h->splits = splits;
+  a.splits = splits;
+  if (splits > 1) {
+    h->launch_partial = gemm_partial_launcher((int)dtype, klay, kernel_dual, cfg);
+    h->launch_fixup = gemm_fixup_launcher((int)dtype, (int)epi, cfg);
+    if (!h->launch_partial || !h->launch_fixup)
+      return fail(EP_ERR_INTERNAL, "no split-K kernel instantiated for this combination");
+  }
+  h->part_bytes = part_bytes;
+  h->z_bytes = z_bytes;
+  h->kpart_bytes = kpart_of(splits);
+  h->workspace_bytes = total_of(splits);
+  if (h->workspace_bytes > ws_limit)
+    return fail(EP_ERR_UNSUPPORTED, "this plan needs %zu bytes of workspace; at most %zu are available",
+                h->workspace_bytes, ws_limit);
 
   // ---- kernel arguments
   if (!unfused) {
@@ -657,16 +647,15 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
     a.ld_gaux = h->io.ld_gelu_aux;
     if (bgrad_epi) {
       a.bgrad_atomic = opt.bgrad_mode == EP_BGRAD_ATOMIC;
-      a.bgrad_part = a.bgrad_atomic ? io->bgrad : h->part;
+      a.bgrad_part = a.bgrad_atomic ? io->bgrad : nullptr;  // two-pass: the partials (bind_workspace)
     }
     h->args = a;
   } else {
-    // unfused: the GEMM writes its DEFAULT result straight to d (or, for SwiGLU, to the
-    // two branch intermediates)
-    // (SWIGLU_AUX: the two branch results go straight to their halves of d2)
+    // unfused: the GEMM writes its DEFAULT result straight to d (SWIGLU: to the two branch
+    // intermediates; SWIGLU_AUX: to their halves of d2)
     if (epi == EP_EPILOG_SWIGLU) {
-      a.d = h->uf.z;
-      a.ldd = h->uf.ldz;
+      a.d = nullptr;
+      a.ldd = N;
     } else if (epi == EP_EPILOG_SWIGLU_AUX) {
       a.d = io->d2;
       a.ldd = h->io.ldd2;
@@ -675,7 +664,7 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
     if (dual) {
       GemmArgs a2 = a;
       a2.b = io->b2;
-      a2.d = epi == EP_EPILOG_SWIGLU ? h->uf.z2 : (void*)((char*)io->d2 + N * 2);
+      a2.d = epi == EP_EPILOG_SWIGLU ? nullptr : (void*)((char*)io->d2 + N * 2);
       h->args2 = a2;
     }
   }
@@ -684,38 +673,49 @@ ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_
             (long long)N, (long long)s->k, dtype == EP_F16 ? "f16" : "bf16", s->b_layout == EP_B_KN ? "KN" : "NK",
             kEpiNames[epi], kTileCfgs[cfg].name, a.tiles_m, a.tiles_n, splits, h->workspace_bytes);
   }
-  *out = h;
   return EP_OK;
 }
 
-static ep_status check_launch(const char* what) {
+// Points every user of the workspace at its piece of ws (laid out as plan_into sized it).
+void bind_workspace(ep_plan_s* h, void* ws) {
+  char* w = (char*)ws;
+  h->part = nullptr;
+  h->uf.z = h->uf.z2 = nullptr;
+  if (h->part_bytes) {
+    h->part = (float*)w;
+    w += round_up256(h->part_bytes);
+  }
+  if (h->z_bytes) {
+    h->uf.z = w;
+    w += round_up256(h->z_bytes);
+    h->uf.z2 = w;
+    w += round_up256(h->z_bytes);
+  }
+  h->args.part = h->kpart_bytes ? (float*)w : nullptr;
+  h->uf.ldz = h->shape.n;
+  const bool bgrad_epi = h->epilog == EP_EPILOG_DRELU_BGRAD || h->epilog == EP_EPILOG_DGELU_BGRAD;
+  if (h->opt.path == EP_PATH_FUSED) {
+    if (bgrad_epi && h->opt.bgrad_mode == EP_BGRAD_TWO_PASS) h->args.bgrad_part = h->part;
+  } else if (h->epilog == EP_EPILOG_SWIGLU) {
+    h->args.d = h->uf.z;
+    h->args2.d = h->uf.z2;
+  }
+}
+
+ep_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(EP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return EP_OK;
 }
 
 // status of a launch whose launcher returned the runtime's error itself
-static ep_status launched(hipError_t e, const char* what) {
+ep_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(EP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return EP_OK;
 }
 
-ep_status ep_execute(ep_handle h, void* stream) {
-  if (!h || h->magic != kMagic) return fail(EP_ERR_INVALID_ARG, "invalid or freed handle");
-  hipStream_t s = (hipStream_t)stream;
-  // The launches go to the stream's device (the calling thread's current device for the null
-  // stream); the plan's pointers and workspace live on the device it was planned on.
-  int dev = -1;
-  if (s == nullptr) {
-    if (hipGetDevice(&dev) != hipSuccess) return fail(EP_ERR_HIP, "hipGetDevice failed");
-  } else {
-    hipDevice_t sd = -1;
-    if (hipStreamGetDevice(s, &sd) != hipSuccess) return fail(EP_ERR_INVALID_ARG, "the stream is not valid");
-    dev = (int)sd;
-  }
-  if (dev != h->device)
-    return fail(EP_ERR_INVALID_ARG, "the stream's device (%d) is not the device the plan was made on (%d)", dev,
-                h->device);
+// Enqueues a bound plan's kernels on s.
+ep_status launch_plan(const ep_plan_s* h, hipStream_t s) {
   const ep_shape& sh = h->shape;
   const int dt = (int)h->dtype;
   const int M = (int)sh.m, N = (int)sh.n;
@@ -791,6 +791,117 @@ ep_status ep_execute(ep_handle h, void* stream) {
       return launched(launch_bgrad_reduce(h->part, h->nparts, h->io.bgrad, N, s), "bgrad_reduce");
   }
   return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_abi_version(void) { return EP_ABI_VERSION; }
+
+int ep_num_tile_cfgs(void) { return kNumTileCfgs; }
+
+const char* ep_status_string(ep_status s) {
+  switch (s) {
+    case EP_OK: return "EP_OK";
+    case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
+    case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED";
+    case EP_ERR_OUT_OF_MEMORY: return "EP_ERR_OUT_OF_MEMORY";
+    case EP_ERR_HIP: return "EP_ERR_HIP";
+    case EP_ERR_INTERNAL: return "EP_ERR_INTERNAL";
+  }
+  return "EP_ERR_UNKNOWN";
+}
+
+const char* ep_last_error(void) { return t_last_error.c_str(); }
+
+ep_status ep_plan(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog, const ep_epilog_io* io, ep_handle* out) {
+  return ep_plan_ex(shape, dtype, epilog, io, nullptr, out);
+}
+
+ep_status ep_plan_ex(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io,
+                     const ep_options* opt_in, ep_handle* out) {
+  t_last_error.clear();
+  if (!out) return fail(EP_ERR_INVALID_ARG, "out handle pointer is NULL");
+  *out = nullptr;
+  ep_status st = validate(s, dtype, epi, io, opt_in);
+  if (st != EP_OK) return st;
+  ep_options opt = opt_in ? *opt_in : ep_options{EP_PATH_FUSED, EP_BGRAD_TWO_PASS, -1, 0, 0};
+
+  // ---- first HIP call: the device must exist and be usable
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return fail(EP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(he));
+  DevInfo di;
+  if ((st = device_info(dev, &di)) != EP_OK) return st;
+
+  if (opt.autotune) {
+    st = autotune(s, dtype, epi, io, opt, dev);
+    if (st != EP_OK) return st;
+  }
+
+  ep_plan_s* h = new (std::nothrow) ep_plan_s{};  // every member zero / null
+  if (!h) return fail(EP_ERR_OUT_OF_MEMORY, "host allocation failed");
+  st = plan_into(h, s, dtype, epi, io, opt, dev, di.cus, SIZE_MAX);
+  if (st != EP_OK) {
+    delete h;
+    return st;
+  }
+  if (h->workspace_bytes) {
+    he = hipMalloc(&h->workspace, h->workspace_bytes);
+    if (he != hipSuccess) {
+      const size_t bytes = h->workspace_bytes;
+      delete h;
+      (void)hipGetLastError();
+      return fail(EP_ERR_OUT_OF_MEMORY, "hipMalloc(%zu): %s", bytes, hipGetErrorString(he));
+    }
+  }
+  bind_workspace(h, h->workspace);
+  *out = h;
+  return EP_OK;
+}
+
+ep_status ep_execute(ep_handle h, void* stream) {
+  if (!h || h->magic != kMagic) return fail(EP_ERR_INVALID_ARG, "invalid or freed handle");
+  hipStream_t s = (hipStream_t)stream;
+  // The launches go to the stream's device (the calling thread's current device for the null
+  // stream); the plan's pointers and workspace live on the device it was planned on.
+  int dev = -1;
+  ep_status st = stream_device(s, &dev);
+  if (st != EP_OK) return st;
+  if (dev != h->device)
+    return fail(EP_ERR_INVALID_ARG, "the stream's device (%d) is not the device the plan was made on (%d)", dev,
+                h->device);
+  return launch_plan(h, s);
+}
+
+ep_status ep_execute_noalloc(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io,
+                             const ep_options* opt_in, void* stream) {
+  t_last_error.clear();
+  ep_status st = validate(s, dtype, epi, io, opt_in);
+  if (st != EP_OK) return st;
+  const ep_options opt = opt_in ? *opt_in : ep_options{EP_PATH_FUSED, EP_BGRAD_TWO_PASS, -1, 0, 0};
+  if (opt.autotune) return fail(EP_ERR_INVALID_ARG, "autotune allocates its timing buffers; not available here");
+  if (opt.path != EP_PATH_FUSED)
+    return fail(EP_ERR_UNSUPPORTED, "the unfused path needs HBM intermediates; only the fused path runs here");
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return fail(EP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(he));
+  hipStream_t hs = (hipStream_t)stream;
+  int sdev = -1;
+  if ((st = stream_device(hs, &sdev)) != EP_OK) return st;
+  if (sdev != dev)
+    return fail(EP_ERR_INVALID_ARG, "the stream's device (%d) is not the current device (%d)", sdev, dev);
+  DevInfo di;
+  if ((st = device_info(dev, &di)) != EP_OK) return st;
+  void* scratch = nullptr;
+  size_t cap = 0;
+  he = static_scratch(dev, &scratch, &cap);
+  if (he != hipSuccess) return fail(EP_ERR_HIP, "static scratch of device %d: %s", dev, hipGetErrorString(he));
+  ep_plan_s h{};  // on the stack: nothing is allocated
+  if ((st = plan_into(&h, s, dtype, epi, io, opt, dev, di.cus, cap)) != EP_OK) return st;
+  bind_workspace(&h, scratch);
+  return launch_plan(&h, hs);
 }
 
 ep_status ep_free(ep_handle h) {

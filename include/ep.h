@@ -212,6 +212,31 @@ ep_status ep_plan_ex(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog,
  */
 ep_status ep_execute(ep_handle h, void* stream);
 
+/*
+ * ep_execute_noalloc: for callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Plans the request exactly as
+ * ep_plan_ex does (same checks, statuses and tile choice) and enqueues it on `stream` as
+ * ep_execute does, in one call, without any allocation: no plan handle is created, and the
+ * workspace (the two-pass bias-gradient partials, the split-K partial tiles) is a static device
+ * array of EP_NOALLOC_SCRATCH_BYTES that each GPU holds for the life of the process.
+ *   - fused path only (EP_ERR_UNSUPPORTED for EP_PATH_UNFUSED); autotune is EP_ERR_INVALID_ARG;
+ *   - a split-K count chosen by shape is reduced until its partials fit the scratch; a request
+ *     whose workspace still exceeds it (an explicit split_k, or two-pass bias-gradient
+ *     partials -- n floats per row of output tiles, ceil(m/256) rows for the 256-row tiles --
+ *     beyond it) is EP_ERR_UNSUPPORTED, with the sizes in ep_last_error;
+ *   - `stream` (NULL = null stream) must belong to the calling thread's current device
+ *     (EP_ERR_INVALID_ARG otherwise);
+ *   - every call on one GPU shares that GPU's scratch: calls that overlap on one GPU (two
+ *     streams, or two threads) race and may produce wrong bias gradients or split results;
+ *     calls on one stream are ordered and safe.  The scratch keeps the last call's contents;
+ *     each call writes every partial it reads.
+ * The caller owns every tensor, as with ep_plan.  The first call on a device looks up the
+ * scratch's device address (hipGetSymbolAddress) and the device's properties once.
+ */
+#define EP_NOALLOC_SCRATCH_BYTES (64u << 20)
+ep_status ep_execute_noalloc(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog,
+                             const ep_epilog_io* io, const ep_options* opt, void* stream);
+
 /* ep_free: release the handle and its workspace.  ep_free(NULL) is EP_OK. The caller must
  * make sure no execution of the handle is still running. */
 ep_status ep_free(ep_handle h);
