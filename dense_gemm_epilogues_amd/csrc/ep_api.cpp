@@ -160,6 +160,11 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 bool cfg_allowed(int cfg, bool dual, ep_b_layout lay) {
   return !(dual && lay == EP_B_KN && kTileCfgs[cfg].bnt < 256);
 }
+// The 64-deep 16x16 configuration loads whole k-steps with no per-lane bounds on k, so it runs
+// only where K is a multiple of 64.
+bool cfg_fits_k(int cfg, int64_t k) {
+  return !(kTileCfgs[cfg].mf == 16 && kTileCfgs[cfg].bk == 64 && k % 64 != 0);
+}
 
 int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   // Estimated time ~ rounds of resident tiles x work per tile / relative efficiency.
@@ -168,7 +173,7 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
   // fastest wherever it fills the chip.
   // (the configuration run for a 256x256 tile, 16x16x32 or register-staged, is chosen by
   // pick_cfg's rule, not by this model)
-  static const double kEff[kNumTileCfgs] = {1.0, 0.70, 0.80, 0.80, 0.85, 0.97, 0.80, 0.82, 0.0, 0.0, 0.0};
+  static const double kEff[kNumTileCfgs] = {1.0, 0.70, 0.80, 0.80, 0.85, 0.97, 0.80, 0.82, 0.0, 0.0, 0.0, 0.0};
   int best = 0;
   double best_t = 1e300;
   for (int c = 0; c < kNumTileCfgs; ++c) {
@@ -204,13 +209,23 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
 // tiles): there the 64-deep register-staged 32x32 configuration measured 7-10% faster with
 // cold operands (2048 x 5120 x 17408: 0.386 -> 0.351 ms unsplit; 2048 x 5120 x 34816: 0.746
 // -> 0.676 ms with 3 splits).  The unfused path's GEMM takes the tile the fused epilog would.
+//
+// 64-deep k-steps with 128-byte row pieces (configuration 11) replace both 32-deep 16x16
+// configurations wherever K is a multiple of 64: each row piece is then a whole cache line
+// fetched by 8 consecutive lanes (the 32-deep ones fetch half lines, which stalled the texture
+// addresser on the L1 4-12 times as often as a library GEMM of the same shape), the loop needs
+// 5 VALU instructions per 64 k instead of 38-51 and one barrier instead of two.  Measured at
+// 65536 x 8192 x 16384 (B K x N) 14.50 -> 13.85 ms, 65536 x 16384 x 8192 (B N x K)
+// 14.54 -> 13.72 ms, 4096^3 120.9 -> 116.1 us (K x N) and 114.6 -> 108.3 us (N x K).
 constexpr int kVstCfg = 8;
 constexpr int kM16SpreadCfg = 9;
 constexpr int kM16RowsCfg = 10;
+constexpr int kM16DeepCfg = 11;
 int pick_cfg(const ep_shape* s, int model_cfg, int cus, bool dual) {
   if (model_cfg != 0) return model_cfg;
   const int64_t tiles = ((s->m + 255) / 256) * ((s->n + 255) / 256);
   if (!dual && s->a_layout == EP_A_MK && s->b_layout == EP_B_NK && tiles < cus) return kVstCfg;
+  if (cfg_fits_k(kM16DeepCfg, s->k)) return kM16DeepCfg;
   return s->b_layout == EP_B_NK ? kM16RowsCfg : kM16SpreadCfg;
 }
 
@@ -553,6 +568,9 @@ ep_status plan_into(ep_plan_s* h, const ep_shape* s, ep_dtype dtype, ep_epilog e
   if (opt.tile_cfg >= 0 && !cfg_allowed(opt.tile_cfg, kernel_dual, s->b_layout))
     return fail(EP_ERR_UNSUPPORTED, "tile_cfg %d cannot run SWIGLU with a K x N weight (needs a 256-row B tile)",
                 opt.tile_cfg);
+  if (opt.tile_cfg >= 0 && !cfg_fits_k(opt.tile_cfg, s->k))
+    return fail(EP_ERR_UNSUPPORTED, "tile_cfg %d needs k to be a multiple of 64 (k = %lld)", opt.tile_cfg,
+                (long long)s->k);
   const int cfg = opt.tile_cfg >= 0 ? opt.tile_cfg
                                     : pick_cfg(s, choose_cfg(s->m, s->n, kernel_dual, s->b_layout, cus), cus, kernel_dual);
   h->magic = kMagic;

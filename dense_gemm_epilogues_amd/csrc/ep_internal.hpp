@@ -65,11 +65,13 @@ struct GemmArgs {
 //         chunks over four slot rows; 0: rows kept whole (16x16: slot rows transposed as
 //         4 x 4).  Both keep the 16x16 fragment reads free of bank conflicts; with spread
 //         chunks each DMA lane quad fetches 16 bytes of four rows instead of one 64-byte piece.
+//   The 64-deep 16x16 configuration keeps 128-byte k-contiguous rows, each a whole cache line
+//   fetched by 8 consecutive lanes, in a 2-stage ring loaded right after each k-step's barrier.
 struct TileCfg {
   int bm, bnt, bk, nst, occ, vst, mf, cfl;
   const char* name;
 };
-constexpr int kNumTileCfgs = 11;
+constexpr int kNumTileCfgs = 12;
 constexpr TileCfg kTileCfgs[kNumTileCfgs] = {
     {256, 256, 32, 4, 1, 0, 32, 0, "256x256x32x4st"},
     {128, 128, 64, 4, 1, 0, 32, 0, "128x128x64x4st"},
@@ -82,6 +84,7 @@ constexpr TileCfg kTileCfgs[kNumTileCfgs] = {
     {256, 256, 64, 2, 1, 1, 32, 0, "256x256x64x2st_vst"},
     {256, 256, 32, 4, 1, 0, 16, 1, "256x256x32x4st_m16"},
     {256, 256, 32, 4, 1, 0, 16, 0, "256x256x32x4st_m16rows"},
+    {256, 256, 64, 2, 1, 0, 16, 0, "256x256x64x2st_m16"},
 };
 
 typedef void (*GemmLauncher)(const GemmArgs&, hipStream_t);

@@ -192,21 +192,35 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a contiguous range
-// of the tile order so that tiles sharing A rows / B columns share that XCD's L2, and
-// walk tiles in groups of kGroupM tile-rows.
+// Workgroups are dispatched round-robin over the 8 XCDs, so workgroup bid runs on XCD bid % 8
+// and the chip runs 256 of them at a time (one per CU).  When both tile counts are multiples of
+// 16, each such round of 256 tiles is a 16 x 16 block of the output, and XCD x takes a 4 x 8
+// sub-block of it: an XCD's L2 then fills 4 A and 8 B panels per round, and the whole chip
+// touches 16 + 16 panels, which the 8 XCDs share through the Infinity Cache; successive rounds
+// walk along the columns of a 16-row band, so the band's A panels stay cached.  (Each XCD working
+// down its own rows, the chip touched 64 + 4 panels per round, too many to stay cached.)
+// Otherwise each XCD gets a contiguous range of the tile order, walked in groups of kGroupM
+// tile-rows, so that tiles sharing A rows / B columns share that XCD's L2.
 __device__ __forceinline__ void map_tile(int bid, int nblocks, int tiles_m, int tiles_n, int& pm,
                                          int& pn) {
-  const int q = nblocks >> 3, r = nblocks & 7;
+  // both orders are computed and one is selected (a branch here made the register allocator
+  // spill the 64-deep 16x16 kernels)
   const int x = bid & 7, l = bid >> 3;
+  const int rnd = l >> 5, j = l & 31;
+  const int nbc = max(tiles_n >> 4, 1);
+  const int br = rnd / nbc, bc = rnd - br * nbc;
+  const int bm = br * 16 + 4 * (x >> 1) + (j & 3);
+  const int bn = bc * 16 + 8 * (x & 1) + (j >> 2);
+  const int q = nblocks >> 3, r = nblocks & 7;
   const int t = (x < r) ? x * (q + 1) + l : r * (q + 1) + (x - r) * q + l;
   const int group = kGroupM * tiles_n;
   const int g = t / group;
   const int first_m = g * kGroupM;
   const int gm = min(tiles_m - first_m, kGroupM);
   const int w = t - g * group;
-  pm = first_m + w % gm;
-  pn = w / gm;
+  const bool blk = ((tiles_m | tiles_n) & 15) == 0;
+  pm = blk ? bm : first_m + w % gm;
+  pn = blk ? bn : w / gm;
 }
 
 // XOR swizzle of the 16-byte chunks of an LDS tile row (CPR chunks per row): chunk c of row r
@@ -246,6 +260,41 @@ __device__ __forceinline__ int kn_col(int pch, int k, bool m16) {  // first colu
   const int piece = m16 ? ((pch & 3) ^ (((k >> 3) & 1) << 1)) : (pch & 3);
   return (((pch >> 2) ^ (k & 3)) << 5) + (piece << 3);
 }
+
+// k-contiguous tiles kept as whole rows (every configuration but the spread-chunk one): the LDS
+// row holding tile row r, the tile row held in LDS row s, and the XOR applied to the 16-byte
+// chunk index of row r.  32x32 blocks: rows in order, chunk swizzle swf.  16x16 blocks with
+// 64-byte rows: slot rows transposed 4 x 4 (m16_row_perm, its own inverse), swizzle swf.
+// 16x16 blocks with 128-byte rows (64-deep k-steps): see r128_*.
+__device__ __forceinline__ int r128_row(int r);
+__device__ __forceinline__ int r128_inv(int s);
+__device__ __forceinline__ int r128_sig(int r);
+template <int MF, int BK>
+__device__ __forceinline__ int kc_row(int r) {
+  if constexpr (MF == 32) return r;
+  else if constexpr (BK == 32) return m16_row_perm(r);
+  else return r128_row(r);
+}
+template <int MF, int BK>
+__device__ __forceinline__ int kc_row_inv(int s) {
+  if constexpr (MF == 32) return s;
+  else if constexpr (BK == 32) return m16_row_perm(s);
+  else return r128_inv(s);
+}
+template <int MF, int BK>
+__device__ __forceinline__ int kc_sig(int r) {
+  if constexpr (MF == 16 && BK == 64) return r128_sig(r);
+  else return swf<BK / 8>(r);
+}
+// 128-byte rows read as 16x16 fragments (16 rows at one 16-byte chunk per 16-lane group): rows
+// in order, chunk c of row r stored at chunk c ^ (r & 7).  A probe of exactly this read pattern
+// over 24 layouts (row permutations within 8 and 16 rows x eight chunk swizzles) measured no
+// bank conflict for it (SQ_LDS_BANK_CONFLICT 0, 4 LDS cycles per ds_read_b128, i.e. 256 bytes
+// per clock), against conflicts on half or three quarters of the cycles for most others,
+// swf's (r ^ r >> 3) & 7 included.  The DMA side is a whole row per 8 consecutive lanes.
+__device__ __forceinline__ int r128_row(int r) { return r; }
+__device__ __forceinline__ int r128_inv(int s) { return s; }
+__device__ __forceinline__ int r128_sig(int r) { return r & 7; }
 
 template <int DT, int LAY, int EPI, int CFG>
 struct GemmTraits {
@@ -292,7 +341,8 @@ struct GemmTraits {
       (EPI == E_DSWIGLU || EPI == E_DRELU_BGRAD || EPI == E_DGELU_BGRAD) ? 1 : (ITERS < 8 ? ITERS : 8);
   static_assert(KS == 1 || KS == 2 || KS == 4, "k-slices per step: 1, 2 or 4");
   static_assert(MF == 32 || MF == 16, "MFMA block edge");
-  static_assert(MF == 32 || (BK == 32 && !cfg_vst(CFG)), "the 16x16 LDS layouts are for 32-deep k-steps loaded directly");
+  static_assert(MF == 32 || ((BK == 32 || (BK == 64 && NST == 2 && !cfg_cfl(CFG))) && !cfg_vst(CFG)),
+                "16x16 LDS layouts: 32-deep k-steps, or 64-deep ones in a 2-stage ring, loaded directly");
   static_assert(MF == 16 || !cfg_cfl(CFG), "the conflict-free k-contiguous layout is for 16x16 blocks");
   static constexpr bool CFL = cfg_cfl(CFG);
   static_assert(A_SLOTS >= 1 && B_SLOTS >= 1, "tile too small for 1 KiB DMA slots");
@@ -390,9 +440,9 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       a_voff[q] = (m0 + wa_mbase + ml < M) ? (uint32_t)(k * p.lda * 2) + ml * 2 : kOOB;
       a_klim[q] = 0;
     } else {
-      const int row = (wave * A_SLOTS + q) * RPS +
-                      (TR::CFL ? m16_slot_row(lane) : (MF == 16 ? m16_row_perm(lane / CPR) : lane / CPR));
-      const int c = TR::CFL ? m16_slot_chunk(lane) : (lane % CPR) ^ swf<CPR>(row);
+      const int row = TR::CFL ? (wave * A_SLOTS + q) * RPS + m16_slot_row(lane)
+                              : kc_row_inv<MF, BK>((wave * A_SLOTS + q) * RPS + lane / CPR);
+      const int c = TR::CFL ? m16_slot_chunk(lane) : (lane % CPR) ^ kc_sig<MF, BK>(row);
       a_voff[q] = (uint32_t)(row * p.lda * 2) + c * 16;
       a_klim[q] = K - c * 8;
     }
@@ -413,8 +463,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   for (int q = 0; q < B_SLOTS; ++q) {
     const int s = wave * B_SLOTS + q;
     if constexpr (BLAY == L_NK) {
-      const int row = s * RPS + (TR::CFL ? m16_slot_row(lane) : (MF == 16 ? m16_row_perm(lane / CPR) : lane / CPR));
-      const int c = TR::CFL ? m16_slot_chunk(lane) : (lane % CPR) ^ swf<CPR>(row);
+      const int row = TR::CFL ? s * RPS + m16_slot_row(lane) : kc_row_inv<MF, BK>(s * RPS + lane / CPR);
+      const int c = TR::CFL ? m16_slot_chunk(lane) : (lane % CPR) ^ kc_sig<MF, BK>(row);
       const int srow = DUAL ? (row % (BNT / 2)) : row;
       b_voff[q] = (uint32_t)(srow * p.ldb * 2) + c * 16;
       b_klim[q] = K - c * 8;
@@ -456,14 +506,27 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 
   // One DMA op = one 1 KiB slot of a stage (A slots first, then B slots).
   constexpr int N_DMA = A_SLOTS + B_SLOTS;
-  auto dma_op = [&](int kt, char* As, int t, const KnSrc& kr) __attribute__((always_inline)) {
+  // The 64-deep 16x16 configuration runs only with K a multiple of 64 (the planner's rule), so
+  // each k-contiguous load lies wholly inside K: its k offset goes in the instruction's scalar
+  // offset and the per-lane offset is fixed for the tile (it still range-checks the rows: rows
+  // past the matrix read zeros).  A k-step past the block's range reloads the last k-step of the
+  // matrix instead of reading zeros: its stage is never read.  The other configurations compare
+  // each lane's chunk with K per load (chunks past K and k-steps past the end read zeros).
+  constexpr bool SOFF = MF == 16 && BK == 64 && NST == 2;
+  auto dma_op = [&](int kt, char* As, int t, const KnSrc& kr, auto full_c) __attribute__((always_inline)) {
     const int k0 = gkt(kt) * BK;
+    constexpr bool kfull = SOFF;
+    (void)full_c;
+    const int ksoff = (gkt(kt) < KT_ALL ? gkt(kt) : KT_ALL - 1) * BK * 2;  // kfull: scalar k offset in bytes
     if (t < A_SLOTS) {
       const int q = t;
       if constexpr (AKM) {
         const __amdgpu_buffer_rsrc_t rka = make_rsrc_raw(kr.abase, kr.anum);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rka, (__attribute__((address_space(3))) void*)(As + (wave * A_SLOTS + q) * 1024), 16, (int)a_voff[q], 0, 0, 0);
+      } else if constexpr (kfull) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rA, (__attribute__((address_space(3))) void*)(As + (wave * A_SLOTS + q) * 1024), 16, (int)a_voff[q], ksoff, 0, 0);
       } else {
         const uint32_t off = (k0 < a_klim[q]) ? a_voff[q] + k0 * 2 : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -473,9 +536,14 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       const int q = t - A_SLOTS;
       char* Bs = As + TR::A_BYTES;
       if constexpr (BLAY == L_NK) {
-        const uint32_t off = (k0 < b_klim[q]) ? b_voff[q] + k0 * 2 : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rB_nk, (__attribute__((address_space(3))) void*)(Bs + (wave * B_SLOTS + q) * 1024), 16, (int)off, 0, 0, 0);
+        if constexpr (kfull) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rB_nk, (__attribute__((address_space(3))) void*)(Bs + (wave * B_SLOTS + q) * 1024), 16, (int)b_voff[q], ksoff, 0, 0);
+        } else {
+          const uint32_t off = (k0 < b_klim[q]) ? b_voff[q] + k0 * 2 : kOOB;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rB_nk, (__attribute__((address_space(3))) void*)(Bs + (wave * B_SLOTS + q) * 1024), 16, (int)off, 0, 0, 0);
+        }
       } else {
         const __amdgpu_buffer_rsrc_t rk = make_rsrc_raw(kr.base, kr.num);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -486,7 +554,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   auto issue_tile = [&](int kt, char* As) __attribute__((always_inline)) {
     const KnSrc kr = kn_rsrc(kt);
 #pragma unroll
-    for (int t = 0; t < N_DMA; ++t) dma_op(kt, As, t, kr);
+    for (int t = 0; t < N_DMA; ++t) dma_op(kt, As, t, kr, std::false_type{});
   };
 
   // Register staging (vst configurations): the same 16 bytes per lane as dma_op, loaded into
@@ -550,8 +618,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       a_f[i] = 0;
     } else {
       const int row = wm * WTM + i * MF + (lane & (MF - 1));
-      a_rd[i] = (MF == 16 ? m16_row_perm(row) : row) * ROWB;
-      a_f[i] = swf<CPR>(row);
+      a_rd[i] = kc_row<MF, BK>(row) * ROWB;
+      a_f[i] = kc_sig<MF, BK>(row);
     }
   }
 #pragma unroll
@@ -567,8 +635,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       b_f[j] = 0;
     } else if constexpr (BLAY == L_NK) {
       const int row = brow + (lane & (MF - 1));
-      b_rd[j] = (MF == 16 ? m16_row_perm(row) : row) * ROWB;
-      b_f[j] = swf<CPR>(row);
+      b_rd[j] = kc_row<MF, BK>(row) * ROWB;
+      b_f[j] = kc_sig<MF, BK>(row);
     } else {
       b_rd[j] = tr_addr(brow);
       b_f[j] = 0;
@@ -670,12 +738,29 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // Register staging writes the next stage from registers, which must happen before the
   // barrier (GBAR below): spread over the first three quarters (measured 1-2.5 % faster than
   // the first half, whose LDS writes crowd the fragment reads).
-  constexpr int HB = NMMA >= 8 ? NMMA / 4 : NMMA / 2;  // MFMAs of the last slice before the barrier
+  // Two barriers per k-step (16x16 blocks, 64-deep k-steps in a 2-stage ring).  The first, at
+  // MFMA POST_BA, follows the reads of the k-step's second-slice fragments: every wave is then
+  // done with stage kt % 2, and the loads of k-step kt + 2 go into it, spread evenly up to the
+  // second barrier, HB MFMAs into the second slice.  The second barrier waits for the loads of
+  // k-step kt + 1 (issued a k-step earlier; this k-step's own loads may stay in flight) before
+  // the next k-step's first-slice fragments are read from its stage.  A load thus has from its
+  // issue to the next k-step's second barrier -- a k-step or more -- to land.  Each 128-byte row
+  // piece is a whole cache line fetched by 8 consecutive lanes.  (POST_BA 0: one barrier, between
+  // the slices, with the loads after it.)
+  constexpr bool POSTW = MF == 16 && NST == 2 && !VST;
+  // (two barriers measured 2.7 % faster where both operands are k-contiguous -- B given N x K --
+  // and 0.5 % slower where B is given K x N, whose row pieces were whole lines already)
+  constexpr int POST_BA = (POSTW && BLAY == L_NK && !AKM) ? 20 : 0;
+  constexpr int HB = POSTW ? (POST_BA > 0 ? NMMA / 2 : 0) : (NMMA >= 8 ? NMMA / 4 : NMMA / 2);  // MFMAs of the last slice before the barrier
   // DMA ops of the current k-step issued before its barrier
   constexpr int GBAR = (KS - 1) * NMMA + HB;
   constexpr int DWIN = VST ? ((TOT * 3) / 4 < GBAR ? (TOT * 3) / 4 : GBAR) : (NST == 2 ? TOT / 2 : TOT);
   constexpr int DSTRIDE = DWIN / N_DMA > 0 ? DWIN / N_DMA : 1;
   constexpr int DPER = (N_DMA + DWIN - 1) / DWIN;      // DMA ops per issue point
+  // two-barrier k-steps: the MFMA window the loads are spread over
+  constexpr int POST_LW0 = POST_BA > 0 ? POST_BA : GBAR;
+  constexpr int POST_LW1 = POST_BA > 0 ? GBAR : TOT;
+  static_assert(!POSTW || (KS == 2 && POST_LW1 - POST_LW0 >= N_DMA && POST_BA < NMMA), "post-barrier load window");
   // K-step pairs (16x16 configurations with A given M x K).  A k-contiguous operand arrives
   // as row pieces of 64 bytes per k-step: half of a 128-byte cache line, whose other half the
   // next k-step loads.  Loaded one k-step at a time, every line is fetched from L2 twice (the
@@ -695,7 +780,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // odd k-step kt: stage of k-step kt+4; even kt: of k-step kt+2 (the pair begun in kt-1)
   char* pair_dst = smem;
   auto slice = [&](auto rd_c, auto g0_c, const u32x4* A, const u32x4* B, auto t0_c, auto t1_c, int kt,
-                   char* dst, const KnSrc& kr, const char* rstage, int rks, u32x4* RA, u32x4* RB, auto par_s) __attribute__((always_inline)) {
+                   char* dst, const KnSrc& kr, const char* rstage, int rks, u32x4* RA, u32x4* RB, auto par_s,
+                   auto full_c) __attribute__((always_inline)) {
     constexpr bool RD = decltype(rd_c)::value;
     constexpr int G0 = decltype(g0_c)::value;        // k-step MFMA index of MFMA t = 0
     constexpr int T0 = decltype(t0_c)::value, T1 = decltype(t1_c)::value;
@@ -705,7 +791,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     // first MFMA then finds its fragments landed)
     constexpr int RTAIL = MF == 16 ? 12 : 4;
     constexpr int RSPAN = (T1 - T0) > 2 * RTAIL ? (T1 - T0) - RTAIL : ((T1 - T0) > 8 ? (T1 - T0) - 4 : (T1 - T0));
-    constexpr int RPM = (N_RD + RSPAN - 1) / RSPAN;
+    constexpr int RPM = RSPAN > 0 ? (N_RD + RSPAN - 1) / RSPAN : 1;
 #pragma unroll
     for (int t = T0; t < T1; ++t) {
       acc[t / NB][t % NB] = E::mfma(A[t / NB], B[t % NB], acc[t / NB][t % NB]);
@@ -718,19 +804,25 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
         if (decltype(par_s)::value == 1 && g >= HB && (g - HB) % PS == 0) {
           const int d = (g - HB) / PS;  // pair (kt, kt + 1), this k-step's loads 0 .. PAFTER-1
           if (d & 1)
-            dma_op(kt + 1, pair_dst, d >> 1, kr);
+            dma_op(kt + 1, pair_dst, d >> 1, kr, std::false_type{});
           else
-            dma_op(kt, dst, d >> 1, kr);
+            dma_op(kt, dst, d >> 1, kr, std::false_type{});
         } else if (decltype(par_s)::value == 0 && g < HB && g % PS == 0) {
           const int d = PAFTER + g / PS;  // pair (kt - 1, kt), its loads PAFTER .. 2 NPS-1
           if (d & 1)
-            dma_op(kt, dst, d >> 1, kr);
+            dma_op(kt, dst, d >> 1, kr, std::false_type{});
           else
-            dma_op(kt - 1, pair_dst, d >> 1, kr);
+            dma_op(kt - 1, pair_dst, d >> 1, kr, std::false_type{});
         }
         if constexpr (NU > 0) {
-          if (g % PS_.us == PS_.uoff) dma_op(kt, dst, NPS + g / PS_.us, kr);
+          if (g % PS_.us == PS_.uoff) dma_op(kt, dst, NPS + g / PS_.us, kr, std::false_type{});
         }
+      } else if constexpr (POSTW) {
+        // load d at MFMA POST_LW0 + floor(d * window / N_DMA): g issues load ceil((g - LW0) N_DMA / window)
+        // when that load's position is g
+        constexpr int WIN = POST_LW1 - POST_LW0;
+        const int d = ((g - POST_LW0) * N_DMA + WIN - 1) / WIN;
+        if (g >= POST_LW0 && d < N_DMA && POST_LW0 + (d * WIN) / N_DMA == g) dma_op(kt, dst, d, kr, full_c);
       } else if (g % DSTRIDE == 0) {
 #pragma unroll
         for (int d = (g / DSTRIDE) * DPER; d < (g / DSTRIDE + 1) * DPER; ++d)
@@ -739,7 +831,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
               lput(dst, d);              // k-step kt - 1 (loaded one k-step ago) into its stage
               sreg[d] = gload(kt, d, kr);  // k-step kt into the freed register
             } else {
-              dma_op(kt, dst, d, kr);
+              dma_op(kt, dst, d, kr, std::false_type{});
             }
           }
       }
@@ -761,8 +853,11 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // stage needed next (k-step kt+1) have landed -- everything younger may stay in flight --
   // and for its LDS reads, then s_barrier.  The memory clobber keeps the compiler from
   // moving LDS accesses across it (__syncthreads would also wait for every younger stage).
-  constexpr int VMC_LOOP = NST >= 3 ? N_DMA * (NST - 3) + DPRE : 0;  // younger loads allowed in flight
-  constexpr int VMC_PRO = N_DMA * (NST - 2);           // after the prologue
+  // younger loads allowed in flight at a k-step's barrier / after the prologue (post-barrier
+  // loads: none are issued between those the barrier waits for and the barrier; the prologue
+  // issues both stages and waits for the first)
+  constexpr int VMC_LOOP = POSTW ? (POST_BA > 0 ? N_DMA : 0) : (NST >= 3 ? N_DMA * (NST - 3) + DPRE : 0);
+  constexpr int VMC_PRO = POSTW ? N_DMA : N_DMA * (NST - 2);
   static_assert(NST >= 2, "the ring needs at least 2 stages");
   static_assert(VMC_LOOP <= 63 && VMC_PRO <= 63, "vmcnt range");
   auto ring_barrier = [&](auto vmc_c) __attribute__((always_inline)) {
@@ -775,14 +870,15 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // fragment buffer (B0 + ks) & 1 and reads the next slice into the other one; with an odd
   // number of slices per k-step (one) the buffers alternate between k-steps, so k-steps come
   // in pairs of parity 0 and 1 (B0 = parity * KS).
-  auto kstep = [&](int kt, auto par_c) __attribute__((always_inline)) {
+  auto kstep = [&](int kt, auto par_c, auto full_c) __attribute__((always_inline)) {
     constexpr int B0 = (decltype(par_c)::value * KS) & 1;
     const char* cur = smem + (kt % NST) * TR::STAGE;
     const char* nxt = smem + ((kt + 1) % NST) * TR::STAGE;
-    char* dst = smem + ((kt + NST - 1) % NST) * TR::STAGE;
-    // the k-step whose loads are issued: NST - 1 ahead (register staging: one more, the
-    // registers holding k-step kt + 1 on their way to dst)
-    const int kl = VST ? kt + 2 : kt + NST - 1;
+    // the stage written by this k-step's loads and the k-step they load: NST - 1 ahead into the
+    // stage k-step kt - 1 used (register staging: one more, the registers holding k-step kt + 1
+    // on their way to dst; post-barrier loads: two ahead, into this k-step's own stage)
+    char* dst = smem + ((POSTW ? kt : kt + NST - 1) % NST) * TR::STAGE;
+    const int kl = (VST || POSTW) ? kt + 2 : kt + NST - 1;
     const KnSrc kr = kn_rsrc(kl);
     if constexpr (PAIR) pair_dst = smem + ((kt + (decltype(par_c)::value == 1 ? 4 : 2)) % NST) * TR::STAGE;
 #pragma unroll
@@ -793,25 +889,33 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       u32x4* RB = fb[(B0 + ks + 1) & 1];
       lgkm_fence(A, B);
       __builtin_amdgcn_sched_barrier(0);
-      if (ks == 0)
-        slice(T_{}, std::integral_constant<int, 0>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c);
+      if constexpr (POSTW && POST_BA > 0) {
+        // (KS == 2: ks is 0) the second slice's fragments are read first; then the first barrier
+        // frees the stage
+        using BA_ = std::integral_constant<int, POST_BA>;
+        slice(T_{}, std::integral_constant<int, 0>{}, A, B, Z_{}, BA_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c, full_c);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        slice(F_{}, std::integral_constant<int, 0>{}, A, B, BA_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c, full_c);
+      } else if (ks == 0)
+        slice(T_{}, std::integral_constant<int, 0>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c, full_c);
       else if (ks == 1)
-        slice(T_{}, std::integral_constant<int, NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c);
+        slice(T_{}, std::integral_constant<int, NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c, full_c);
       else
-        slice(T_{}, std::integral_constant<int, 2 * NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c);
+        slice(T_{}, std::integral_constant<int, 2 * NMMA>{}, A, B, Z_{}, W_{}, kl, dst, kr, cur, ks + 1, RA, RB, par_c, full_c);
     }
     constexpr int L = (B0 + KS - 1) & 1;  // buffer of the last slice
     constexpr int NX = (B0 + KS) & 1;     // buffer of the next k-step's first slice
     using GL = std::integral_constant<int, (KS - 1) * NMMA>;
     lgkm_fence(fa[L], fb[L]);
     __builtin_amdgcn_sched_barrier(0);
-    slice(F_{}, GL{}, fa[L], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[NX], fb[NX], par_c);
+    slice(F_{}, GL{}, fa[L], fb[L], Z_{}, H_{}, kl, dst, kr, cur, 0, fa[NX], fb[NX], par_c, full_c);
     // with k-step pairs the stage needed next is the second of the pair begun three k-steps
     // before (even kt) or the first of the pair begun two k-steps before (odd kt); the counts
     // of younger loads are pair_sched's
     ring_barrier(std::integral_constant<int, !PAIR ? VMC_LOOP : (decltype(par_c)::value == 0 ? PS_.vmc_even : PS_.vmc_odd)>{});
     __builtin_amdgcn_sched_barrier(0);
-    slice(T_{}, GL{}, fa[L], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[NX], fb[NX], par_c);
+    slice(T_{}, GL{}, fa[L], fb[L], H_{}, W_{}, kl, dst, kr, nxt, 0, fa[NX], fb[NX], par_c, full_c);
   };
   using P0_ = std::integral_constant<int, 0>;
   using P1_ = std::integral_constant<int, 1>;
@@ -835,12 +939,12 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
         issue_tile(1, smem + TR::STAGE);
         const KnSrc k2 = kn_rsrc(2);
 #pragma unroll
-        for (int j = 0; j < NU; ++j) dma_op(2, smem + 2 * TR::STAGE, NPS + j, k2);
+        for (int j = 0; j < NU; ++j) dma_op(2, smem + 2 * TR::STAGE, NPS + j, k2, std::false_type{});
 #pragma unroll
-        for (int d = 0; d < PS_.pafter; ++d) dma_op(2 + (d & 1), smem + (2 + (d & 1)) * TR::STAGE, d >> 1, k2);
+        for (int d = 0; d < PS_.pafter; ++d) dma_op(2 + (d & 1), smem + (2 + (d & 1)) * TR::STAGE, d >> 1, k2, std::false_type{});
       } else {
 #pragma unroll
-        for (int s = 0; s < NST - 1; ++s) issue_tile(s, smem + s * TR::STAGE);
+        for (int s = 0; s < (POSTW ? NST : NST - 1); ++s) issue_tile(s, smem + s * TR::STAGE);
       }
     }
     ring_barrier(std::integral_constant<int, PAIR ? PS_.vmc_pro : VMC_PRO>{});
@@ -851,14 +955,14 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     __builtin_amdgcn_sched_barrier(0);
     read_frags(smem, 0, fa[0], fb[0]);
     if constexpr (KS % 2 == 0) {
-      for (int kt = 0; kt < KT; ++kt) kstep(kt, P0_{});
+      for (int kt = 0; kt < KT; ++kt) kstep(kt, P0_{}, F_{});
     } else {
       // k-steps in pairs; an odd count gets one more k-step, whose loads lie past the block's
       // K range and read as zeros, so that the loop has a single body (a separate last k-step
       // makes the register allocator move the accumulators between register files)
       for (int kt = 0; kt < KT; kt += 2) {
-        kstep(kt, P0_{});
-        kstep(kt + 1, P1_{});
+        kstep(kt, P0_{}, F_{});
+        kstep(kt + 1, P1_{}, F_{});
       }
     }
   }

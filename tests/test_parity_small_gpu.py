@@ -54,11 +54,21 @@ def make_inputs(epi, dt, layout, m, n, k, seed, dev):
     return {kk: v.to(dev) for kk, v in ins.items()}
 
 
+K64_ONLY_CFGS = (11,)  # configurations that need K to be a multiple of 64
+
+
 def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split_k=0, bgrad_mode="two_pass",
                   autotune=False):
     import dense_gemm_epilogues_amd as ep
     dev = torch.device("cuda")
     dt = DTYPES[dtname]
+    if cfg in K64_ONLY_CFGS and k % 64:
+        # refused with a ragged K; the case then runs with K rounded up to a multiple of 64
+        a = torch.zeros((m, k), dtype=dt, device=dev)
+        b = torch.zeros((k, n) if layout == "KN" else (n, k), dtype=dt, device=dev)
+        with pytest.raises(ep.EPError, match="EP_ERR_UNSUPPORTED.*multiple of 64"):
+            ep.Plan(a, b, "DEFAULT", b_layout=layout, tile_cfg=cfg)
+        k = -(-k // 64) * 64
     ins = make_inputs(epi, dt, layout, m, n, k, seed, dev)
     obuf, out = padded(m, n, dt, dev)
     aux_out, epi_in = {}, {}
@@ -93,7 +103,7 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
                 aux_out=aux_out, path=path, tile_cfg=cfg, split_k=split_k, bgrad_mode=bgrad_mode,
                 autotune=autotune)
     if split_k > 1:
-        kt = -(-k // (64 if cfg in (1, 4, 8) else 32))
+        kt = -(-k // (64 if cfg in BK64_CFGS else 32))
         per = -(-kt // min(split_k, kt))
         want = -(-kt // per)
         assert f"splits={want} " in p.info(), p.info()
@@ -156,8 +166,9 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
 
 # every tile configuration of the library (9 and 10 issue 16x16x32 MFMAs); those with a
 # 128-row B tile cannot hold the gate and up sub-tiles of a K x N dual B operand
-NUM_TILE_CFGS = 11
+NUM_TILE_CFGS = 12
 BNT128_CFGS = (1, 2, 6)
+BK64_CFGS = (1, 4, 8, 11)  # 64-deep k-steps
 
 
 @pytest.mark.parametrize("cfg", list(range(NUM_TILE_CFGS)))
@@ -187,7 +198,7 @@ def test_split_k(epi, layout, splits):
     (register-staged, 64-deep k-steps) is the planner's choice for N x K GEMMs under one round
     of tiles, where the split model splits long K ranges."""
     require_gpu()
-    for cfg in (0, 1, 6, 8, 9, 10):
+    for cfg in (0, 1, 6, 8, 9, 10, 11):
         if epi in ("SWIGLU", "SWIGLU_AUX") and layout == "KN" and cfg in BNT128_CFGS:
             continue
         for dtname in ("f16", "bf16"):
@@ -195,12 +206,14 @@ def test_split_k(epi, layout, splits):
                 run_and_check(epi, dtname, layout, m, n, k, cfg, split_k=splits)
 
 
-@pytest.mark.parametrize("cfg", [9, 10])
+@pytest.mark.parametrize("cfg", [9, 10, 11])
 @pytest.mark.parametrize("layout", ["KN", "NK"])
 def test_kstep_pair_k_lengths(layout, cfg):
-    """The 16x16 configurations load k-steps in pairs (k-steps kt+3 and kt+4 issued from each
-    odd k-step kt on, the prologue starting the pair (2, 3)): K from one 32-deep k-step to 18,
-    even and odd counts, ragged last k-steps, and split-K ranges of either parity."""
+    """The 16x16 configurations' load schedules over many K lengths.  Configurations 9 and 10
+    load k-steps in pairs (k-steps kt+3 and kt+4 issued from each odd k-step kt on, the prologue
+    starting the pair (2, 3)); configuration 11 loads k-step kt+2 right after k-step kt's
+    barrier into a 2-stage ring.  K from one 32-deep k-step to 18, even and odd counts, ragged
+    last k-steps, and split-K ranges of either parity."""
     require_gpu()
     for k in (32, 64, 96, 128, 160, 192, 224, 256, 288, 320, 544, 576, 40, 104):
         run_and_check("DEFAULT", "f16", layout, 260, 296, k, cfg)
@@ -231,7 +244,7 @@ def test_transposed_a(dtname, layout):
     import dense_gemm_epilogues_amd as ep
     dev = torch.device("cuda")
     dt = DTYPES[dtname]
-    for (m, n, k) in [(296, 200, 136), (40, 8, 8), (136, 264, 520), (8, 64, 72)]:
+    for (m, n, k) in [(296, 200, 136), (40, 8, 8), (136, 264, 520), (8, 64, 72), (136, 200, 192), (8, 72, 640)]:
         g = torch.Generator().manual_seed(m + n + k)
         at = (torch.randn(k, m, generator=g)).to(dt).to(dev)          # K x M
         b = (torch.randn(k, n, generator=g) * k ** -0.5).to(dt) if layout == "KN" else \
@@ -239,6 +252,10 @@ def test_transposed_a(dtname, layout):
         b = b.to(dev)
         ref = oracle.matmul(f64(at).T, f64(b), layout)
         for cfg in range(NUM_TILE_CFGS):
+            if cfg in K64_ONLY_CFGS and k % 64:
+                with pytest.raises(ep.EPError, match="EP_ERR_UNSUPPORTED"):
+                    ep.Plan(at, b, "DEFAULT", b_layout=layout, tile_cfg=cfg, a_layout="KM")
+                continue
             for split in (1, 2):
                 obuf, out = padded(m, n, dt, dev)
                 say(f"case A^T dt={dtname} layout={layout} m={m} n={n} k={k} cfg={cfg} split={split}")
@@ -251,17 +268,19 @@ def test_transposed_a(dtname, layout):
                 p.free()
 
 
-@pytest.mark.parametrize("m,n,layout,ld_extra,dual,want_cfg", [
-    (4096, 4096, "NK", 64, False, 10),     # B N x K: 16x16x32, k-contiguous rows kept whole
-    (4096, 4096, "KN", 0, False, 9),       # B K x N: 16x16x32, A's chunks spread over slot rows
-    (16384, 32768, "NK", 64, False, 10),   # 32 rounds
-    (16384, 32768, "NK", 0, False, 10),    # 32 rounds, B rows 32 KiB apart
-    (16384, 32768, "KN", 0, False, 9),
-    (2048, 8192, "NK", 0, True, 10),       # dual-B SwiGLU, N x K weights, 2 rounds: whole rows too
-    (2048, 5120, "NK", 0, False, 8),       # single B, N x K, 160 tiles (under one round): register-staged
-    (2048, 5120, "KN", 0, False, 9),
+@pytest.mark.parametrize("m,n,layout,ld_extra,dual,want_cfg,k", [
+    (4096, 4096, "NK", 64, False, 11, 4096),    # K % 64 == 0: 64-deep 16x16x32 k-steps, both layouts
+    (4096, 4096, "KN", 0, False, 11, 4096),
+    (16384, 32768, "NK", 64, False, 11, 4096),  # 32 rounds
+    (16384, 32768, "NK", 0, False, 11, 4096),   # 32 rounds, B rows 32 KiB apart
+    (16384, 32768, "KN", 0, False, 11, 4096),
+    (2048, 8192, "NK", 0, True, 11, 4096),      # dual-B SwiGLU, N x K weights, 2 rounds
+    (2048, 5120, "NK", 0, False, 8, 4096),      # single B, N x K, 160 tiles (under one round): register-staged
+    (2048, 5120, "KN", 0, False, 11, 4096),
+    (4096, 4096, "NK", 64, False, 10, 4064),    # K % 64 != 0: 32-deep, rows kept whole for N x K B
+    (4096, 4096, "KN", 0, False, 9, 4064),      # ... chunks spread for K x N B
 ])
-def test_planner_tile_choice(m, n, layout, ld_extra, dual, want_cfg):
+def test_planner_tile_choice(m, n, layout, ld_extra, dual, want_cfg, k):
     """The planner's default tile configuration at full-chip shapes (256 CUs), B rows 16384
     (+ ld_extra) elements apart when B is N x K; the result is checked against the oracle on
     sampled rows and columns (the dual-B case on h = silu(x Wg^T) * (x Wu^T))."""
@@ -270,7 +289,6 @@ def test_planner_tile_choice(m, n, layout, ld_extra, dual, want_cfg):
     dev = torch.device("cuda")
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the expected choices assume 256 CUs")
-    k = 4096
     g = torch.Generator(device=dev)
     g.manual_seed(m + n + ld_extra)
     a = torch.randn(m, k, device=dev, generator=g).half()
