@@ -56,7 +56,7 @@ class ep_epilog_io(ctypes.Structure):
 
 class ep_options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("bgrad_mode", ctypes.c_int), ("tile_cfg", ctypes.c_int),
-                ("split_k", ctypes.c_int), ("autotune", ctypes.c_int)]
+                ("split_k", ctypes.c_int), ("split_tail", ctypes.c_int), ("autotune", ctypes.c_int)]
 
 
 class EPError(RuntimeError):
@@ -235,14 +235,16 @@ class Plan:
     Outputs are allocated here with torch.empty unless `out` / `aux_out` are given and are
     reused by every execute().  Tensors are kept alive for the plan's lifetime.
     path "fused" | "unfused"; bgrad_mode "two_pass" | "atomic"; tile_cfg -1 (by shape) or an
-    index < num_tile_cfgs(); split_k 0 (by shape), 1 (never) or 2..4 K ranges per tile;
+    index < num_tile_cfgs(); split_k 0 (by shape), 1 (never) or 2..8 K ranges per tile;
+    split_tail=True (with split_k >= 2) splits only the tiles of the last, partly filled round
+    of workgroups and runs the others whole;
     autotune=True times every (tile configuration, split) on these buffers at plan time
     (overwriting the outputs) and keeps the fastest, cached per problem for the process.
     """
 
     def __init__(self, a, b, epilog="DEFAULT", epilog_inputs=None, b_layout="KN", out=None,
                  aux_out=None, path="fused", bgrad_mode="two_pass", tile_cfg=-1, split_k=0, autotune=False,
-                 a_layout="MK"):
+                 a_layout="MK", split_tail=False):
         L = lib()
         epilog_inputs = dict(epilog_inputs or {})
         aux_out = dict(aux_out or {})
@@ -306,7 +308,7 @@ class Plan:
         shape = ep_shape(m=m, n=n, k=k, b_layout=_LAYOUTS[b_layout], a=_ptr(a), lda=_ld(a),
                          b=_ptr(b), ldb=_ld(b), d=_ptr(out), ldd=_ld(out), a_layout=0 if a_layout == "MK" else 1)
         opt = ep_options(path=_PATHS[path], bgrad_mode=_BGRAD[bgrad_mode], tile_cfg=tile_cfg, split_k=split_k,
-                         autotune=int(bool(autotune)))
+                         split_tail=int(bool(split_tail)), autotune=int(bool(autotune)))
         handle = ctypes.c_void_p()
         self._keep = (a, b, out, epilog_inputs, dict(self.aux))
         _check(L.ep_plan_ex(ctypes.byref(shape), _DTYPES[a.dtype], EPILOGS[epilog], ctypes.byref(io),

@@ -216,7 +216,12 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
 // addresser on the L1 4-12 times as often as a library GEMM of the same shape), the loop needs
 // 5 VALU instructions per 64 k instead of 38-51 and one barrier instead of two.  Measured at
 // 65536 x 8192 x 16384 (B K x N) 14.50 -> 13.85 ms, 65536 x 16384 x 8192 (B N x K)
-// 14.54 -> 13.72 ms, 4096^3 120.9 -> 116.1 us (K x N) and 114.6 -> 108.3 us (N x K).
+// 14.54 -> 13.72 ms, 4096^3 120.9 -> 116.1 us (K x N) and 114.6 -> 108.3 us (N x K).  It
+// also takes over the single-B N x K GEMMs under one round once they are split: with the
+// split-K fixup reading its partials in batches, the 2048 x 5120 x 17408 down GEMM runs in
+// 0.316 ms on it with 3 splits against 0.339 ms for the register-staged configuration's best
+// (3 splits) and 0.357 ms unsplit; the register-staged one remains the choice there when K is
+// not a multiple of 64.
 constexpr int kVstCfg = 8;
 constexpr int kM16SpreadCfg = 9;
 constexpr int kM16RowsCfg = 10;
@@ -224,31 +229,53 @@ constexpr int kM16DeepCfg = 11;
 int pick_cfg(const ep_shape* s, int model_cfg, int cus, bool dual) {
   if (model_cfg != 0) return model_cfg;
   const int64_t tiles = ((s->m + 255) / 256) * ((s->n + 255) / 256);
-  if (!dual && s->a_layout == EP_A_MK && s->b_layout == EP_B_NK && tiles < cus) return kVstCfg;
   if (cfg_fits_k(kM16DeepCfg, s->k)) return kM16DeepCfg;
+  if (!dual && s->a_layout == EP_A_MK && s->b_layout == EP_B_NK && tiles < cus) return kVstCfg;
   return s->b_layout == EP_B_NK ? kM16RowsCfg : kM16SpreadCfg;
 }
 
-// Split-K: how many K ranges per tile.  Only grids that leave CUs idle are split: the time
-// of one resident round of tiles scales as rounds(tiles * S) / S, and every split adds a
-// write and a read of the fp32 tile partials (BM * BNT * 4 bytes) and their share of the
-// fixup launch, priced at about 11 GB/s per CU, against the tile's K loop (about 0.65 us per
-// 32-deep k-step).  Both rates are fitted to the 2048 x 5120 GEMMs at K 17408 and 34816 with
-// cold operands (unsplit 0.351 / 0.707 ms, 3 splits 0.377 / 0.676 ms), where the earlier
-// guesses (1 us, 20 GB/s) split the first one to its loss.
-int choose_splits(int64_t tiles, int slots, int kt, int cfg) {
-  if (tiles >= slots) return 1;
-  const double tile_us = kt * (kTileCfgs[cfg].bk / 32.0) * 0.65;
-  const double part_us = 2.0 * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * 4.0 / 11e3;  // bytes / (bytes/us)
-  int best = 1;
-  double best_t = 1.0;
+// Split-K: how many K ranges per tile, and over which tiles.  Times are modelled in
+// microseconds: a tile's K loop takes about 0.8 us per 32 k-values with every CU busy (the
+// 64-deep 16x16 kernels at MI355X's clock under load: 65536 x 8192 x 16384 and the SwiGLU-MLP
+// GEMMs), a round of resident tiles takes one tile time, and each split tile adds the write
+// and the read of its fp32 partial (BM * BNT * 4 bytes each way) at about 3.6 TB/s, plus the
+// fixup launch.  Two forms:
+//   * grids under one round: every tile is split (2048 x 5120 at K 17408 / 34816, 160 tiles:
+//     3 splits measured 0.364 -> 0.316 ms and 0.857 -> 0.639 ms; each further split costs
+//     about 23 us there, as the model says);
+//   * grids with a partly filled last round: the tiles of the whole rounds run unsplit and
+//     only the last round's tiles are split, which costs a fixed ~35 us more (two more
+//     launches and the fixup's epilog): 2048 x 17408 x 5120 dSwiGLU (2 rounds + 32 tiles)
+//     0.428 -> 0.409 ms with 4 splits, the dual-B SwiGLU forward at M 2048 (4 rounds + 64)
+//     0.601 -> 0.583 ms with 3; the short-K (2048) weight-gradient GEMMs lose with any split.
+// A split is taken when the model expects it at least 3 % faster (one more range than the
+// best so far only when 1 % faster still), and only with at least 16 k-steps per range.
+struct SplitChoice {
+  int splits, tail0;  // K ranges per split tile; tiles [0, tail0) run unsplit
+};
+SplitChoice choose_splits(int64_t tiles, int slots, int kt, int cfg) {
+  const double tile_us = kt * (kTileCfgs[cfg].bk / 32.0) * 0.8;
+  const double part_us = 2.0 * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * 4.0 / 3.6e6;  // per split tile
+  auto rounds = [&](int64_t n) { return (double)((n + slots - 1) / slots); };
+  const int64_t whole = tiles / slots * slots, rem = tiles - whole;
+  SplitChoice best{1, 0};
+  double best_t = rounds(tiles) * tile_us * 0.97;
   for (int sp = 2; sp <= EP_MAX_SPLIT_K; ++sp) {
     if (kt / sp < 16) break;
-    const double rounds = (double)((tiles * sp + slots - 1) / slots);
-    const double t = rounds / sp + sp * part_us / tile_us;
-    if (t < best_t * 0.97) {
+    double t;
+    SplitChoice c;
+    if (whole == 0) {
+      t = rounds(tiles * sp) / sp * tile_us + sp * tiles * part_us + 10.0;
+      c = {sp, 0};
+    } else if (rem > 0) {
+      t = (whole / slots) * tile_us + rounds(rem * sp) / sp * tile_us + sp * rem * part_us + 35.0;
+      c = {sp, (int)whole};
+    } else {
+      break;  // whole rounds: nothing to gain
+    }
+    if (t < (best.splits > 1 ? best_t * 0.99 : best_t)) {  // more ranges only for a clear gain
       best_t = t;
-      best = sp;
+      best = c;
     }
   }
   return best;
@@ -293,6 +320,8 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
       return fail(EP_ERR_INVALID_ARG, "split_k %d out of range [0, %d]", opt->split_k, EP_MAX_SPLIT_K);
     if (opt->path == EP_PATH_UNFUSED && opt->split_k > 1)
       return fail(EP_ERR_UNSUPPORTED, "split_k applies to the fused path only");
+    if (opt->split_tail != 0 && opt->split_tail != 1)
+      return fail(EP_ERR_INVALID_ARG, "split_tail must be 0 or 1");
     if (opt->autotune != 0 && opt->autotune != 1)
       return fail(EP_ERR_INVALID_ARG, "autotune must be 0 or 1");
     if (opt->autotune && (opt->path != EP_PATH_FUSED || opt->tile_cfg >= 0 || opt->split_k != 0))
@@ -412,7 +441,10 @@ namespace {
 // The choice is cached for the process under the problem's key.
 using TuneKey = std::tuple<int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int, int, int, int, int>;
 std::mutex g_tune_mu;
-std::map<TuneKey, std::pair<int, int>> g_tune_cache;
+struct TuneChoice {
+  int cfg, split, tail;
+};
+std::map<TuneKey, TuneChoice> g_tune_cache;
 
 ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io, ep_options& opt,
                    int dev) {
@@ -422,8 +454,9 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
     std::lock_guard<std::mutex> lk(g_tune_mu);
     auto it = g_tune_cache.find(key);
     if (it != g_tune_cache.end()) {
-      opt.tile_cfg = it->second.first;
-      opt.split_k = it->second.second;
+      opt.tile_cfg = it->second.cfg;
+      opt.split_k = it->second.split;
+      opt.split_tail = it->second.tail;
       opt.autotune = 0;
       return EP_OK;
     }
@@ -433,7 +466,7 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   // them alike; the median of each candidate's rounds decides.
   struct Cand {
     ep_handle h;
-    int cfg, split;
+    int cfg, split, tail;
     std::vector<float> ms;
   };
   std::vector<Cand> cands;
@@ -449,7 +482,7 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
         ep_free(t);
         continue;
       }
-      cands.push_back({t, c, t->splits, {}});
+      cands.push_back({t, c, t->splits, t->args.tail0 > 0 ? 1 : 0, {}});
     }
   }
   constexpr int kRounds = 5;
@@ -478,7 +511,7 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
     }
   }
   float best_ms = 1e30f;
-  int best_cfg = -1, best_split = 1;
+  int best_cfg = -1, best_split = 1, best_tail = 0;
   for (auto& cd : cands) {
     if (ok && (int)cd.ms.size() == kRounds) {
       std::sort(cd.ms.begin(), cd.ms.end());
@@ -487,6 +520,7 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
         best_ms = med;
         best_cfg = cd.cfg;
         best_split = cd.split;
+        best_tail = cd.tail;
       }
     }
     ep_free(cd.h);
@@ -498,11 +532,12 @@ ep_status autotune(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   if (best_cfg < 0) return fail(EP_ERR_INTERNAL, "autotune: no candidate configuration ran");
   {
     std::lock_guard<std::mutex> lk(g_tune_mu);
-    g_tune_cache[key] = {best_cfg, best_split};
+    g_tune_cache[key] = {best_cfg, best_split, best_tail};
   }
   t_last_error.clear();
   opt.tile_cfg = best_cfg;
   opt.split_k = best_split;
+  opt.split_tail = best_tail;
   opt.autotune = 0;
   return EP_OK;
 }
@@ -617,14 +652,28 @@ ep_status plan_into(ep_plan_s* h, const ep_shape* s, ep_dtype dtype, ep_epilog e
 
   // ---- split-K (fused path only)
   const int kt_all = (int)((s->k + kTileCfgs[cfg].bk - 1) / kTileCfgs[cfg].bk);
+  const int64_t ntiles = (int64_t)a.tiles_m * a.tiles_n;
+  const int slots = cus * kTileCfgs[cfg].occ;
+  int tail0 = 0;  // tiles [0, tail0) run whole when a split plan splits only the last round's
   auto kpart_of = [&](int sp) {
-    return sp > 1 ? (size_t)sp * a.tiles_m * a.tiles_n * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * sizeof(float) : 0;
+    return sp > 1 ? (size_t)sp * (ntiles - tail0) * kTileCfgs[cfg].bm * kTileCfgs[cfg].bnt * sizeof(float) : 0;
   };
   auto total_of = [&](int sp) { return round_up256(part_bytes) + 2 * round_up256(z_bytes) + round_up256(kpart_of(sp)); };
   int splits = 1;
   if (!unfused) {
-    splits = opt.split_k > 0 ? opt.split_k
-                             : choose_splits((int64_t)a.tiles_m * a.tiles_n, cus * kTileCfgs[cfg].occ, kt_all, cfg);
+    if (opt.split_k > 0) {
+      splits = opt.split_k;
+      if (splits > 1 && opt.split_tail) {
+        if (ntiles <= slots || ntiles % slots == 0)
+          return fail(EP_ERR_UNSUPPORTED, "split_tail needs a partly filled last round (%lld tiles, %d slots)",
+                      (long long)ntiles, slots);
+        tail0 = (int)(ntiles / slots * slots);
+      }
+    } else {
+      const SplitChoice c = choose_splits(ntiles, slots, kt_all, cfg);
+      splits = c.splits;
+      tail0 = c.tail0;
+    }
     if (splits > kt_all) splits = kt_all;
     if (opt.split_k == 0)
       while (splits > 1 && total_of(splits) > ws_limit) --splits;
@@ -633,8 +682,10 @@ ep_status plan_into(ep_plan_s* h, const ep_shape* s, ep_dtype dtype, ep_epilog e
     a.kt_per_split = (kt_all + splits - 1) / splits;
     splits = (kt_all + a.kt_per_split - 1) / a.kt_per_split;  // no empty K range
   }
+  if (splits == 1) tail0 = 0;
   h->splits = splits;
   a.splits = splits;
+  a.tail0 = tail0;
   if (splits > 1) {
     h->launch_partial = gemm_partial_launcher((int)dtype, klay, kernel_dual, cfg);
     h->launch_fixup = gemm_fixup_launcher((int)dtype, (int)epi, cfg);
@@ -690,6 +741,7 @@ ep_status plan_into(ep_plan_s* h, const ep_shape* s, ep_dtype dtype, ep_epilog e
     fprintf(stderr, "[ep] plan m=%lld n=%lld k=%lld %s %s %s cfg=%s tiles=%dx%d splits=%d ws=%zu\n", (long long)M,
             (long long)N, (long long)s->k, dtype == EP_F16 ? "f16" : "bf16", s->b_layout == EP_B_KN ? "KN" : "NK",
             kEpiNames[epi], kTileCfgs[cfg].name, a.tiles_m, a.tiles_n, splits, h->workspace_bytes);
+    if (tail0 > 0) fprintf(stderr, "[ep]   split tail: tiles [0, %d) whole\n", tail0);
   }
   return EP_OK;
 }
@@ -744,6 +796,10 @@ ep_status launch_plan(const ep_plan_s* h, hipStream_t s) {
       if ((st = launched(launch_fill_zero_f32(h->io.bgrad, N, s), "fill_zero")) != EP_OK) return st;
     }
     if (h->splits > 1) {
+      if (h->args.tail0 > 0) {  // the tiles of the whole rounds, then the split tail
+        h->launch(h->args, s);
+        if ((st = check_launch("fused gemm (whole rounds)")) != EP_OK) return st;
+      }
       h->launch_partial(h->args, s);
       if ((st = check_launch("split-K partial gemm")) != EP_OK) return st;
       h->launch_fixup(h->args, s);
@@ -948,7 +1004,14 @@ ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
                      (h->opt.path == EP_PATH_FUSED ? kEpiNames[h->epilog] : "DEFAULT") + "," +
                      kTileCfgs[h->cfg].name + ">";
   std::string extra;
-  if (h->splits > 1) kern += " split-K x" + std::to_string(h->splits) + " (partial + fixup)";
+  if (h->splits > 1) {
+    if (h->args.tail0 > 0)
+      kern += " on tiles [0, " + std::to_string(h->args.tail0) + "), split-K x" + std::to_string(h->splits) +
+              " (partial + fixup) on the other " +
+              std::to_string((int64_t)h->args.tiles_m * h->args.tiles_n - h->args.tail0);
+    else
+      kern += " split-K x" + std::to_string(h->splits) + " (partial + fixup)";
+  }
   if (h->opt.path == EP_PATH_FUSED) {
     if (h->epilog == EP_EPILOG_DRELU_BGRAD || h->epilog == EP_EPILOG_DGELU_BGRAD)
       extra = h->opt.bgrad_mode == EP_BGRAD_TWO_PASS ? " + bgrad_reduce" : " (after fill_zero; atomic bgrad)";
@@ -969,10 +1032,10 @@ ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
   }
   snprintf(buf, n,
            "epilog=%s path=%s dtype=%s layout=%s m=%lld n=%lld k=%lld tile=%s tile_cfg=%d grid=%dx%d "
-           "splits=%d workspace_bytes=%zu kernels=%s%s",
+           "splits=%d split_tail0=%d workspace_bytes=%zu kernels=%s%s",
            kEpiNames[h->epilog], h->opt.path == EP_PATH_FUSED ? "fused" : "unfused", dt, lay, (long long)s.m,
            (long long)s.n, (long long)s.k, kTileCfgs[h->cfg].name, h->cfg, h->args.tiles_m, h->args.tiles_n,
-           h->splits, h->workspace_bytes, kern.c_str(), extra.c_str());
+           h->splits, h->args.tail0, h->workspace_bytes, kern.c_str(), extra.c_str());
   return EP_OK;
 }
 

@@ -44,8 +44,9 @@ struct GemmArgs {
   void* d2;
   int64_t ldd2;
   // split-K (see the MODE parameter of gemm_kernel): K-ranges per tile, K-steps per range,
-  // and the fp32 partial accumulators [splits][tiles][BM * BNT]
-  int splits, kt_per_split;
+  // the first split tile (tiles before it run whole) and the fp32 partial accumulators
+  // [splits][tiles - tail0][BM * BNT]
+  int splits, kt_per_split, tail0;
   float* part;
   void* gaux;           // GELU_AUX_BIAS output / DGELU_BGRAD input: pre-activation, element type
   int64_t ld_gaux;

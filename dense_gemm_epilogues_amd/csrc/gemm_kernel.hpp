@@ -44,7 +44,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kMaxSplits = 4;  // split-K ranges per tile
+constexpr int kMaxSplits = 8;  // split-K ranges per tile
 constexpr int kGroupM = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every num_records we build
 
@@ -349,10 +349,12 @@ struct GemmTraits {
   static_assert(LDS_BYTES * cfg_occ(CFG) <= 160 * 1024, "LDS budget");
 };
 
-// MODE 0: whole K range, then the epilog.  MODE 1 (split-K partial): block b computes the
-// K-steps [s * kt_per_split, (s + 1) * kt_per_split) of tile b % tiles, s = b / tiles, and stores
-// its fp32 accumulators to p.part.  MODE 2 (split-K fixup): block b sums the p.splits partials
-// of tile b in split order and runs the epilog (no K loop).
+// MODE 0: whole K range, then the epilog.  MODE 1 (split-K partial): of the nt = tiles -
+// p.tail0 split tiles (tile indices before the XCD remap, from p.tail0 on), block b computes
+// the K-steps [s * kt_per_split, (s + 1) * kt_per_split) of tile p.tail0 + b % nt, s = b / nt,
+// and stores its fp32 accumulators to p.part.  MODE 2 (split-K fixup): block b sums the
+// p.splits partials of tile p.tail0 + b in split order and runs the epilog (no K loop).  A
+// split plan with p.tail0 > 0 runs tiles [0, p.tail0) whole in a MODE 0 launch of its own.
 template <int DT, int LAY, int EPI, int CFG, int MODE>
 __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p) {
   using E = Elem<DT>;
@@ -378,8 +380,10 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   const int wm = wave >> 1, wn = wave & 1;
 
   const int ntiles = p.tiles_m * p.tiles_n;
-  const int split = MODE == 1 ? (int)blockIdx.x / ntiles : 0;
-  const int tbid = (int)blockIdx.x - split * ntiles;  // tile index before the XCD remap
+  const int nsplit = ntiles - p.tail0;  // tiles of the split range (MODE 1, 2)
+  const int split = MODE == 1 ? (int)blockIdx.x / nsplit : 0;
+  // tile index before the XCD remap
+  const int tbid = MODE == 0 ? (int)blockIdx.x : p.tail0 + (int)blockIdx.x - split * nsplit;
   int pm, pn;
   map_tile(tbid, ntiles, p.tiles_m, p.tiles_n, pm, pn);
   const int m0 = pm * BM;
@@ -978,7 +982,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // float offset (q * 256 + t) * 4, so each store / load instruction covers 1 KiB contiguously.
   constexpr int ACC4 = MB * NB * (ACC_R / 4);  // f32x4 accumulator groups per thread
   if constexpr (MODE == 1) {
-    float* dst = p.part + ((int64_t)split * ntiles + tbid) * (int64_t)(ACC4 * kThreads * 4);
+    float* dst = p.part + ((int64_t)split * nsplit + (tbid - p.tail0)) * (int64_t)(ACC4 * kThreads * 4);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -992,25 +996,35 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     return;
   } else {
   if constexpr (MODE == 2) {
-    // each f32x4 group is summed over the splits in split order (so the result does not
-    // depend on which split finished first) and written to the accumulators once
-    const float* src = p.part + (int64_t)tbid * (ACC4 * kThreads * 4);
-    const int64_t sstride = (int64_t)ntiles * (ACC4 * kThreads * 4);
+    // the partials are summed in split order (so the result does not depend on which split
+    // finished first), QB f32x4 groups at a time: the group's loads of one split are all
+    // issued before they are added, so that a batch costs one memory latency per split
+    // rather than one per load, and only the accumulators already summed are live
+    constexpr int QB = ACC4 < 16 ? ACC4 : 16;
+    static_assert(ACC4 % QB == 0, "accumulator groups per batch");
+    constexpr int GPB = ACC_R / 4;  // f32x4 groups per MFMA block
+    const float* src = p.part + (int64_t)(tbid - p.tail0) * (ACC4 * kThreads * 4) + tid * 4;
+    const int64_t sstride = (int64_t)nsplit * (ACC4 * kThreads * 4);
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int q0 = 0; q0 < ACC4; q0 += QB) {
+      f32x4 sum[QB];
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
+      for (int u = 0; u < QB; ++u) sum[u] = __builtin_nontemporal_load((const f32x4*)(src + (int64_t)(q0 + u) * kThreads * 4));
+      for (int sp = 1; sp < p.splits; ++sp) {
+        f32x4 t[QB];
 #pragma unroll
-        for (int g = 0; g < ACC_R / 4; ++g) {
-          const int q = (i * NB + j) * (ACC_R / 4) + g;
-          const float* sq = src + ((int64_t)q * kThreads + tid) * 4;
-          f32x4 v = __builtin_nontemporal_load((const f32x4*)sq);
+        for (int u = 0; u < QB; ++u)
+          t[u] = __builtin_nontemporal_load((const f32x4*)(src + sp * sstride + (int64_t)(q0 + u) * kThreads * 4));
 #pragma unroll
-          for (int sp = 1; sp < kMaxSplits; ++sp)
-            if (sp < p.splits) v += __builtin_nontemporal_load((const f32x4*)(sq + sp * sstride));
+        for (int u = 0; u < QB; ++u) sum[u] += t[u];
+      }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] = v[e];
-        }
+      for (int u = 0; u < QB; ++u) {
+        const int q = q0 + u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[q / GPB / NB][q / GPB % NB][4 * (q % GPB) + e] = sum[u][e];
+      }
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -1047,23 +1061,58 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   }
   f32x4 colsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // bias gradients: the lane's 8 columns
 
-  // DSWIGLU reads gate and up per element in the staged layout, for a whole slab before it
-  // is staged, so their latency overlaps the staging.  DGELU_BGRAD reads the pre-activation
-  // the same way one slab ahead (two buffers): slab 0 here, slab i + 1 while slab i is staged.
+  // DSWIGLU reads gate and up, and DGELU_BGRAD the pre-activation, per element in the staged
+  // layout one slab ahead (two buffers): slab 0 right after the K loop, slab i + 1 while slab
+  // i is staged and stored, so that their latency passes behind the work of a whole slab.
+  // (DSWIGLU with two workgroups per CU has the registers for one buffer only: it reads a
+  // slab's gate and up when the slab begins, so that they arrive during its staging.)
   constexpr int PF_GU = (EPI == E_DSWIGLU || EPI == E_DGELU_BGRAD) ? TR::ITERS : 1;
-  u32x4 pf_g[PF_GU], pf_u[PF_GU];
+  constexpr int GUB = (EPI == E_DSWIGLU && cfg_occ(CFG) == 1) ? 2 : 1;  // gate / up buffers
+  u32x4 pf_g[GUB][PF_GU], pf_u[GUB][PF_GU];
   u32x4 pf_a[EPI == E_DGELU_BGRAD ? 2 : 1][PF_GU];
+  // The epilog's row-wise inputs and outputs (the output d; DSWIGLU's gate, up and d_up; the
+  // GELU pre-activation) go through buffer descriptors, one per 32-row slab, whose extent
+  // ends with the slab's last row inside M: rows past M then read as zeros and their stores
+  // are dropped by the hardware's range check (which covers the per-lane offset),
+  // and lanes whose 8 columns lie past N (N is a multiple of 8) use an offset beyond every
+  // extent.  The descriptors are wave-uniform (scalar), so a row costs one offset addition.
+  // (Leading dimensions are below 2^22 elements, so every offset fits in 32 bits; with no row
+  // inside M the extent (rc - 1) * ld2 + 2 N is at most 0, as ld >= N.)
+  auto slab_rsrc = [&](const void* base, int64_t ld, int i) __attribute__((always_inline)) {
+    const int srow0 = __builtin_amdgcn_readfirstlane(m0 + wm * WTM + i * 32);
+    const int ld2 = (int)ld * 2;
+    const int rc = min(max(M - srow0, 0), 32);  // rows of the slab inside M
+    const uint32_t num = (uint32_t)max((rc - 1) * ld2 + N * 2, 0);
+    // the base and extent read from lane 0: the compiler then keeps the descriptor in scalar
+    // registers (it otherwise wraps some buffer instructions in a per-lane loop)
+    const uint64_t a = (uint64_t)((const char*)base + (int64_t)srow0 * ld2);
+    const uint64_t au = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    return make_rsrc_raw((const void*)au, (uint32_t)__builtin_amdgcn_readfirstlane((int)num));
+  };
+  constexpr uint32_t kOffNone = 0x80000000u;  // beyond every extent above (each is under 2^29)
+  const uint32_t vo_gu = colok ? (uint32_t)(lr * p.ld_gu + gcol) * 2u : kOffNone;
+  const uint32_t vo_d = colok ? (uint32_t)(lr * p.ldd + gcol) * 2u : kOffNone;
+  const uint32_t vo_d2 = colok ? (uint32_t)(lr * p.ldd2 + gcol) * 2u : kOffNone;
+  const uint32_t vo_ga = colok ? (uint32_t)(lr * p.ld_gaux + gcol) * 2u : kOffNone;
   auto load_gaux = [&](int i, u32x4* dst) __attribute__((always_inline)) {
-    const int srow0 = m0 + wm * WTM + i * 32;
+    const __amdgpu_buffer_rsrc_t ra = slab_rsrc(p.gaux, p.ld_gaux, i);
+#pragma unroll
+    for (int it = 0; it < TR::ITERS; ++it)
+      dst[it] = __builtin_amdgcn_raw_buffer_load_b128(ra, vo_ga + (uint32_t)(it * TR::RPI * (int)p.ld_gaux * 2), 0, 2);
+  };
+  auto load_gu = [&](int i, u32x4* g, u32x4* u) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rg = slab_rsrc(p.gate, p.ld_gu, i), ru = slab_rsrc(p.up, p.ld_gu, i);
 #pragma unroll
     for (int it = 0; it < TR::ITERS; ++it) {
-      const int grow = srow0 + it * TR::RPI + lr;
-      const bool ok = colok && grow < M;
-      const int64_t go = ((int64_t)grow * p.ld_gaux + gcol) * 2;
-      dst[it] = ok ? __builtin_nontemporal_load((const u32x4*)((const char*)p.gaux + go)) : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t vo = vo_gu + (uint32_t)(it * TR::RPI * (int)p.ld_gu * 2);
+      // cache policy 2: non-temporal (each element is read once)
+      g[it] = __builtin_amdgcn_raw_buffer_load_b128(rg, vo, 0, 2);
+      u[it] = __builtin_amdgcn_raw_buffer_load_b128(ru, vo, 0, 2);
     }
   };
   if constexpr (EPI == E_DGELU_BGRAD) load_gaux(0, pf_a[0]);
+  if constexpr (EPI == E_DSWIGLU && GUB == 2) load_gu(0, pf_g[0], pf_u[0]);
 
   // 32-row slabs: 32x32 block row i, or 16x16 block rows 2i and 2i + 1
 #pragma unroll
@@ -1076,13 +1125,10 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     } else if constexpr (EPI == E_DGELU_BGRAD) {
       if (i + 1 < NSLAB) load_gaux(i + 1, pf_a[(i + 1) & 1]);
     } else if constexpr (EPI == E_DSWIGLU) {
-#pragma unroll
-      for (int it = 0; it < TR::ITERS; ++it) {
-        const int grow = srow0 + it * TR::RPI + lr;
-        const bool ok = colok && grow < M;
-        const int64_t go = ((int64_t)grow * p.ld_gu + gcol) * 2;
-        pf_g[it] = ok ? __builtin_nontemporal_load((const u32x4*)((const char*)p.gate + go)) : u32x4{0u, 0u, 0u, 0u};
-        pf_u[it] = ok ? __builtin_nontemporal_load((const u32x4*)((const char*)p.up + go)) : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (GUB == 2) {
+        if (i + 1 < NSLAB) load_gu(i + 1, pf_g[(i + 1) & 1], pf_u[(i + 1) & 1]);
+      } else {
+        load_gu(i, pf_g[0], pf_u[0]);
       }
     }
 
@@ -1189,6 +1235,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     // ---- stores: CH staged rows per chunk, their LDS reads issued together
     // (the lane's output address of staged row 0; staged row t is t * ldd elements further)
     char* const dslab = (char*)p.d + ((int64_t)(srow0 + lr) * p.ldd + gcol) * 2;
+    // DSWIGLU: the slab's d_gate and d_up rows (unused by the other epilogs)
+    const __amdgpu_buffer_rsrc_t rs_d = slab_rsrc(p.d, p.ldd, i), rs_d2 = slab_rsrc(p.d2, p.ldd2, i);
     constexpr int OUTER_UNROLL = EPI == E_DRELU_BGRAD ? 2 : TR::ITERS;
 #pragma unroll OUTER_UNROLL
     for (int c0 = 0; c0 < TR::ITERS; c0 += TR::CH) {
@@ -1225,12 +1273,12 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
         const bool ok = colok && grow < M;
         char* const dptr = dslab + (int64_t)((c0 + c) * TR::RPI) * p.ldd * 2;
         if constexpr (EPI == E_DSWIGLU) {
-          if (ok) {
+          {
             f32x4 dg[2], du[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              const f32x4 g = unpack4<DT>(u32x2{pf_g[c0 + c][2 * h], pf_g[c0 + c][2 * h + 1]});
-              const f32x4 u = unpack4<DT>(u32x2{pf_u[c0 + c][2 * h], pf_u[c0 + c][2 * h + 1]});
+              const f32x4 g = unpack4<DT>(u32x2{pf_g[i % GUB][c0 + c][2 * h], pf_g[i % GUB][c0 + c][2 * h + 1]});
+              const f32x4 u = unpack4<DT>(u32x2{pf_u[i % GUB][c0 + c][2 * h], pf_u[i % GUB][c0 + c][2 * h + 1]});
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const float sg = sigmoid_f(g[e]);
@@ -1239,19 +1287,23 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
                 dg[h][e] = t * u[e] * (1.0f + g[e] * (1.0f - sg));
               }
             }
-            *(u32x4*)dptr = pack8<DT>(dg[0], dg[1]);
-            *(u32x4*)((char*)p.d2 + ((int64_t)grow * p.ldd2 + gcol) * 2) = pack8<DT>(du[0], du[1]);
+            // (rows past M and columns past N are dropped by the range check)
+            const int rr = (c0 + c) * TR::RPI;
+            __builtin_amdgcn_raw_buffer_store_b128(pack8<DT>(dg[0], dg[1]), rs_d, vo_d + (uint32_t)(rr * (int)p.ldd * 2), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(pack8<DT>(du[0], du[1]), rs_d2, vo_d2 + (uint32_t)(rr * (int)p.ldd2 * 2), 0, 0);
           }
         } else if constexpr (EPI == E_GELU_BIAS || EPI == E_GELU_AUX_BIAS) {
-          if (ok) {
+          {
+            const int rr = (c0 + c) * TR::RPI;
             if constexpr (EPI == E_GELU_AUX_BIAS)
-              *(u32x4*)((char*)p.gaux + ((int64_t)grow * p.ld_gaux + gcol) * 2) = pack8<DT>(vv[c][0], vv[c][1]);
+              __builtin_amdgcn_raw_buffer_store_b128(pack8<DT>(vv[c][0], vv[c][1]), slab_rsrc(p.gaux, p.ld_gaux, i),
+                                                     vo_ga + (uint32_t)(rr * (int)p.ld_gaux * 2), 0, 0);
             f32x4 y[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
               for (int e = 0; e < 4; ++e) y[h][e] = gelu_f(vv[c][h][e]);
-            *(u32x4*)dptr = pack8<DT>(y[0], y[1]);
+            __builtin_amdgcn_raw_buffer_store_b128(pack8<DT>(y[0], y[1]), rs_d, vo_d + (uint32_t)(rr * (int)p.ldd * 2), 0, 0);
           }
         } else {
           if constexpr (EPI == E_DGELU_BGRAD) {  // rows past M: aux read as 0, staged value 0
@@ -1262,7 +1314,8 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
               for (int e = 0; e < 4; ++e) vv[c][h][e] *= gelu_grad_f(pa[e]);
             }
           }
-          if (ok) *(u32x4*)dptr = pack8<DT>(vv[c][0], vv[c][1]);
+          __builtin_amdgcn_raw_buffer_store_b128(pack8<DT>(vv[c][0], vv[c][1]), rs_d,
+                                                 vo_d + (uint32_t)((c0 + c) * TR::RPI * (int)p.ldd * 2), 0, 0);
           if constexpr (BGRAD) {  // rows past M are staged as 0
             colsum[0] += vv[c][0];
             colsum[1] += vv[c][1];
@@ -1345,7 +1398,9 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
 
 template <int DT, int LAY, int EPI, int CFG, int MODE = 0>
 void launch_gemm(const GemmArgs& a, hipStream_t s) {
-  const int nblocks = a.tiles_m * a.tiles_n * (MODE == 1 ? a.splits : 1);
+  const int ntiles = a.tiles_m * a.tiles_n;
+  // MODE 0 runs every tile, or the whole-K tiles [0, tail0) of a split plan
+  const int nblocks = MODE == 0 ? (a.splits > 1 ? a.tail0 : ntiles) : (ntiles - a.tail0) * (MODE == 1 ? a.splits : 1);
   hipLaunchKernelGGL((gemm_kernel<DT, LAY, EPI, CFG, MODE>), dim3(nblocks), dim3(kThreads), 0, s, a);
 }
 

@@ -172,6 +172,13 @@ typedef struct {
                               workgroup into fp32 partials that a second launch sums (in a fixed
                               order) before running the epilog.  Must be 0 or 1 for the unfused
                               path. */
+  int split_tail;          /* with split_k >= 2: 0 = split every tile; 1 = split only the tiles
+                              of the last, partly filled round of workgroups (tiles beyond the
+                              largest multiple of the resident workgroup slots, fewer than one
+                              round), while the others run their whole K range in a launch of
+                              their own before them.  Ignored with split_k 0 (the shape model
+                              picks both) and 1.  EP_ERR_UNSUPPORTED when the tiles fill whole
+                              rounds or less than one. */
   int autotune;            /* fused path, tile_cfg -1 and split_k 0 only: 1 = ep_plan times every
                               allowed (tile configuration, split) pair on the bound buffers and
                               keeps the one with the lowest median of 5 executes (candidates
@@ -185,7 +192,7 @@ typedef struct {
                               0 = choose by the shape model (default). */
 } ep_options;
 
-#define EP_MAX_SPLIT_K 4
+#define EP_MAX_SPLIT_K 8
 
 /*
  * ep_plan: validate the request, pick a tile configuration, allocate the workspace and

@@ -124,7 +124,9 @@ CASES = [
                                                  ep_epilog_io(relu_aux_in=X_PTR, bgrad=X_PTR + 4096),
                                                  opt=ep_options(path=1, bgrad_mode=1, tile_cfg=-1))[0], UNSUPPORTED),
     ("split_k negative", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=-1))[0], INVALID),
-    ("split_k above 4", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=5))[0], INVALID),
+    ("split_k above 8", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=9))[0], INVALID),
+    ("split_tail not 0/1", lambda L: plan(L, shape(), opt=ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=2,
+                                                                       split_tail=2))[0], INVALID),
     ("unfused with split_k", lambda L: plan(L, shape(), opt=ep_options(path=1, bgrad_mode=0, tile_cfg=-1, split_k=2))[0],
      UNSUPPORTED),
     ("unknown A layout", lambda L: plan(L, shape(alay=2))[0], UNSUPPORTED),

@@ -58,7 +58,7 @@ K64_ONLY_CFGS = (11,)  # configurations that need K to be a multiple of 64
 
 
 def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split_k=0, bgrad_mode="two_pass",
-                  autotune=False):
+                  autotune=False, split_tail=False):
     import dense_gemm_epilogues_amd as ep
     dev = torch.device("cuda")
     dt = DTYPES[dtname]
@@ -98,15 +98,20 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
         epi_in["gate"], epi_in["up"] = ins["gate"], ins["up"]
         ubuf, uview = padded(m, n, dt, dev)
         aux_out["d_up"] = uview
-    say(f"case epi={epi} dt={dtname} layout={layout} m={m} n={n} k={k} cfg={cfg} path={path} split_k={split_k}")
+    say(f"case epi={epi} dt={dtname} layout={layout} m={m} n={n} k={k} cfg={cfg} path={path} split_k={split_k}"
+        f" split_tail={split_tail} bgrad_mode={bgrad_mode}")
     p = ep.Plan(ins["a"], ins["b"], epilog=epi, epilog_inputs=epi_in, b_layout=layout, out=out,
                 aux_out=aux_out, path=path, tile_cfg=cfg, split_k=split_k, bgrad_mode=bgrad_mode,
-                autotune=autotune)
+                autotune=autotune, split_tail=split_tail)
     if split_k > 1:
         kt = -(-k // (64 if cfg in BK64_CFGS else 32))
         per = -(-kt // min(split_k, kt))
         want = -(-kt // per)
         assert f"splits={want} " in p.info(), p.info()
+        if split_tail and want > 1:
+            bn = 128 if epi in ("SWIGLU", "SWIGLU_AUX") else 256
+            tiles = -(-m // 256) * -(-n // bn)
+            assert f"split_tail0={tiles // 256 * 256} " in p.info(), p.info()
     p.execute()
     torch.cuda.synchronize()
 
@@ -206,6 +211,34 @@ def test_split_k(epi, layout, splits):
                 run_and_check(epi, dtname, layout, m, n, k, cfg, split_k=splits)
 
 
+@pytest.mark.parametrize("layout", ["KN", "NK"])
+@pytest.mark.parametrize("epi", EPIS)
+def test_split_tail(epi, layout):
+    """Split-K on the last, partly filled round only: 17 x 16 = 272 output tiles on 256 CUs,
+    so tiles [0, 256) run whole-K in one launch and the other 16 are split into K ranges whose
+    partials a fixup launch sums before the epilog.  Every epilog, both dtypes, the 64-deep
+    16x16 configuration (3 and 8 ranges) and a 32x32 one (8 ranges); the two-pass bias
+    gradient sums column partials written by both launches' epilogs."""
+    require_gpu()
+    n = 2048 if epi in ("SWIGLU", "SWIGLU_AUX") else 4096
+    for dtname, cfg, splits in (("f16", 11, 3), ("bf16", 11, 8), ("bf16", 0, 8)):
+        run_and_check(epi, dtname, layout, 4352 - 40, n - 24, 512, cfg, split_k=splits, split_tail=True)
+
+
+def test_split_tail_refusals_and_atomic_bgrad():
+    """split_tail needs a partly filled last round: a grid under one round and one of whole
+    rounds are refused; the atomic bias gradient also works with a split tail."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev = torch.device("cuda")
+    for (m, n) in [(300, 200), (4096, 4096)]:
+        a = torch.zeros((m, 64), dtype=torch.float16, device=dev)
+        b = torch.zeros((64, n), dtype=torch.float16, device=dev)
+        with pytest.raises(ep.EPError, match="EP_ERR_UNSUPPORTED.*split_tail"):
+            ep.Plan(a, b, "DEFAULT", b_layout="KN", tile_cfg=11, split_k=2, split_tail=True)
+    run_and_check("DRELU_BGRAD", "f16", "NK", 4352, 4096, 512, 11, split_k=4, split_tail=True, bgrad_mode="atomic")
+
+
 @pytest.mark.parametrize("cfg", [9, 10, 11])
 @pytest.mark.parametrize("layout", ["KN", "NK"])
 def test_kstep_pair_k_lengths(layout, cfg):
@@ -275,8 +308,9 @@ def test_transposed_a(dtname, layout):
     (16384, 32768, "NK", 0, False, 11, 4096),   # 32 rounds, B rows 32 KiB apart
     (16384, 32768, "KN", 0, False, 11, 4096),
     (2048, 8192, "NK", 0, True, 11, 4096),      # dual-B SwiGLU, N x K weights, 2 rounds
-    (2048, 5120, "NK", 0, False, 8, 4096),      # single B, N x K, 160 tiles (under one round): register-staged
+    (2048, 5120, "NK", 0, False, 11, 4096),     # single B, N x K, 160 tiles (under one round)
     (2048, 5120, "KN", 0, False, 11, 4096),
+    (2048, 5120, "NK", 0, False, 8, 4072),      # ... with K % 64 != 0: register-staged
     (4096, 4096, "NK", 64, False, 10, 4064),    # K % 64 != 0: 32-deep, rows kept whole for N x K B
     (4096, 4096, "KN", 0, False, 9, 4064),      # ... chunks spread for K x N B
 ])
@@ -319,11 +353,52 @@ def test_planner_tile_choice(m, n, layout, ld_extra, dual, want_cfg, k):
     p.free()
 
 
+@pytest.mark.parametrize("m,n,k,dual,layout,want", [
+    (2048, 17408, 5120, False, "KN", "splits=4 split_tail0=512 "),   # dSwiGLU GEMM at M 2048: 2 rounds + 32 tiles
+    (2048, 17408, 5120, True, "NK", "splits=3 split_tail0=1024 "),   # dual-B SwiGLU at M 2048: 4 rounds + 64 tiles
+    (34816, 5120, 2048, False, "KN", "splits=1 split_tail0=0 "),     # short K: never split
+    (16384, 17408, 5120, False, "KN", "splits=1 split_tail0=0 "),    # whole rounds (17)
+])
+def test_planner_split_tail_choice(m, n, k, dual, layout, want):
+    """Grids with a partly filled last round: the planner splits only the last round's tiles
+    where its model expects a gain (the SwiGLU-MLP GEMMs at M 2048, K 5120), and nowhere for a
+    short K or whole rounds.  Sampled rows and columns against the oracle."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev = torch.device("cuda")
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the expected choice assumes 256 CUs")
+    g = torch.Generator(device=dev)
+    g.manual_seed(m + n + k)
+    a = torch.randn(m, k, device=dev, generator=g).to(torch.bfloat16)
+    shape_b = (n, k) if layout == "NK" else (k, n)
+    b = (torch.randn(*shape_b, device=dev, generator=g) * k ** -0.5).to(torch.bfloat16)
+    say(f"case planner split tail {m}x{n}x{k} dual={dual} {layout}")
+    if dual:
+        b2 = (torch.randn(*shape_b, device=dev, generator=g) * k ** -0.5).to(torch.bfloat16)
+        p = ep.Plan(a, b, "SWIGLU", {"b2": b2}, b_layout=layout)
+    else:
+        p = ep.Plan(a, b, "DEFAULT", b_layout=layout)
+    info = p.info()
+    assert want in info, info
+    out, _ = p.execute()
+    torch.cuda.synchronize()
+    rows = torch.tensor(np.r_[0:32, m // 2 - 8:m // 2 + 24, m - 32:m], device=dev)
+    cols = torch.tensor(np.r_[0:64, n // 2:n // 2 + 64, n - 64:n], device=dev)
+    bsel = (lambda t: t[cols]) if layout == "NK" else (lambda t: t[:, cols])
+    if dual:
+        ref = oracle.swiglu(f64(a[rows]), f64(bsel(b)), f64(bsel(b2)), layout)[0]
+    else:
+        ref = oracle.matmul(f64(a[rows]), f64(bsel(b)), layout)
+    assert_half(f64(out[rows][:, cols]), ref, f"planner split tail {info}")
+    p.free()
+
+
 @pytest.mark.parametrize("a_layout", ["MK", "KM"])
 def test_planner_split_choice(a_layout):
     """A long-K GEMM under one round of tiles, B given N x K (the SwiGLU dx GEMM's shape,
-    2048 x 5120 x 34816): the planner picks register-staged configuration 8 with 3 split-K
-    ranges; sampled rows and columns against the oracle."""
+    2048 x 5120 x 34816): the planner picks the 64-deep 16x16 configuration 11 with 3 split-K
+    ranges over every tile; sampled rows and columns against the oracle."""
     require_gpu()
     import dense_gemm_epilogues_amd as ep
     dev = torch.device("cuda")
@@ -339,8 +414,7 @@ def test_planner_split_choice(a_layout):
     say(f"case planner split choice A {a_layout} {m}x{n}x{k}")
     p = ep.Plan(a, b, "DEFAULT", b_layout="NK", a_layout=a_layout)
     info = p.info()
-    if a_layout == "MK":
-        assert "tile_cfg=8 " in info and "splits=3 " in info, info
+    assert "tile_cfg=11 " in info and "splits=3 " in info and "split_tail0=0 " in info, info
     out, _ = p.execute()
     torch.cuda.synchronize()
     rows = torch.tensor(np.r_[0:32, m // 2 - 8:m // 2 + 24, m - 32:m], device=dev)
