@@ -63,8 +63,8 @@ def asm_mfma_cfgs():
     text = open(os.path.join(CSRC, "ep_internal.hpp")).read()
     table = text[text.index("kTileCfgs[kNumTileCfgs] = {"):]
     table = table[:table.index("};")]
-    rows = re.findall(r"\{\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*\"", table)
-    return {i for i, r in enumerate(rows) if int(r[6]) == 16}
+    rows = [[int(v) for v in re.findall(r"\d+", r)] for r in re.findall(r"\{((?:\s*\d+,)+)\s*\"", table)]
+    return {i for i, r in enumerate(rows) if r[6] == 16}
 
 
 def check_resource_usage(usage, asm_cfgs=None):

@@ -66,26 +66,29 @@ struct GemmArgs {
 //         chunks over four slot rows; 0: rows kept whole (16x16: slot rows transposed as
 //         4 x 4).  Both keep the 16x16 fragment reads free of bank conflicts; with spread
 //         chunks each DMA lane quad fetches 16 bytes of four rows instead of one 64-byte piece.
-//   The 64-deep 16x16 configuration keeps 128-byte k-contiguous rows, each a whole cache line
-//   fetched by 8 consecutive lanes, in a 2-stage ring loaded right after each k-step's barrier.
+//   The 64-deep 16x16 configurations keep 128-byte k-contiguous rows, each a whole cache line
+//   fetched by 8 consecutive lanes, in a 2-stage ring loaded right after a k-step's barrier;
+//   bar2 = 1: two barriers per k-step for every operand layout (0: only where B is N x K;
+//   see the POST_BA schedule of gemm_kernel).
 struct TileCfg {
-  int bm, bnt, bk, nst, occ, vst, mf, cfl;
+  int bm, bnt, bk, nst, occ, vst, mf, cfl, bar2;
   const char* name;
 };
-constexpr int kNumTileCfgs = 12;
+constexpr int kNumTileCfgs = 13;
 constexpr TileCfg kTileCfgs[kNumTileCfgs] = {
-    {256, 256, 32, 4, 1, 0, 32, 0, "256x256x32x4st"},
-    {128, 128, 64, 4, 1, 0, 32, 0, "128x128x64x4st"},
-    {256, 128, 32, 4, 1, 0, 32, 0, "256x128x32x4st"},
-    {128, 256, 32, 4, 1, 0, 32, 0, "128x256x32x4st"},
-    {256, 256, 64, 2, 1, 0, 32, 0, "256x256x64x2st"},
-    {256, 256, 32, 5, 1, 0, 32, 0, "256x256x32x5st"},
-    {256, 128, 32, 3, 2, 0, 32, 0, "256x128x32x3st_2wg"},
-    {128, 256, 32, 3, 2, 0, 32, 0, "128x256x32x3st_2wg"},
-    {256, 256, 64, 2, 1, 1, 32, 0, "256x256x64x2st_vst"},
-    {256, 256, 32, 4, 1, 0, 16, 1, "256x256x32x4st_m16"},
-    {256, 256, 32, 4, 1, 0, 16, 0, "256x256x32x4st_m16rows"},
-    {256, 256, 64, 2, 1, 0, 16, 0, "256x256x64x2st_m16"},
+    {256, 256, 32, 4, 1, 0, 32, 0, 0, "256x256x32x4st"},
+    {128, 128, 64, 4, 1, 0, 32, 0, 0, "128x128x64x4st"},
+    {256, 128, 32, 4, 1, 0, 32, 0, 0, "256x128x32x4st"},
+    {128, 256, 32, 4, 1, 0, 32, 0, 0, "128x256x32x4st"},
+    {256, 256, 64, 2, 1, 0, 32, 0, 0, "256x256x64x2st"},
+    {256, 256, 32, 5, 1, 0, 32, 0, 0, "256x256x32x5st"},
+    {256, 128, 32, 3, 2, 0, 32, 0, 0, "256x128x32x3st_2wg"},
+    {128, 256, 32, 3, 2, 0, 32, 0, 0, "128x256x32x3st_2wg"},
+    {256, 256, 64, 2, 1, 1, 32, 0, 0, "256x256x64x2st_vst"},
+    {256, 256, 32, 4, 1, 0, 16, 1, 0, "256x256x32x4st_m16"},
+    {256, 256, 32, 4, 1, 0, 16, 0, 0, "256x256x32x4st_m16rows"},
+    {256, 256, 64, 2, 1, 0, 16, 0, 0, "256x256x64x2st_m16"},
+    {256, 256, 64, 2, 1, 0, 16, 0, 1, "256x256x64x2st_m16_2bar"},
 };
 
 typedef void (*GemmLauncher)(const GemmArgs&, hipStream_t);

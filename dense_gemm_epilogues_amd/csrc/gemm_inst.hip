@@ -14,8 +14,8 @@
 
 namespace ep {
 // every tile configuration, in table order
-#define EP_FOR_CFGS(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11)
-static_assert(kNumTileCfgs == 12, "EP_FOR_CFGS must list every tile configuration");
+#define EP_FOR_CFGS(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12)
+static_assert(kNumTileCfgs == 13, "EP_FOR_CFGS must list every tile configuration");
 // Explicit kernel instantiations (emitted in the device pass).
 #define EP_INST(c) template __global__ void gemm_kernel<EP_DT, EP_LAY, EP_EPI, c, 0>(GemmArgs);
 EP_FOR_CFGS(EP_INST)

@@ -56,6 +56,7 @@ constexpr int cfg_occ(int cfg) { return kTileCfgs[cfg].occ; }
 constexpr bool cfg_vst(int cfg) { return kTileCfgs[cfg].vst != 0; }
 constexpr int cfg_mf(int cfg) { return kTileCfgs[cfg].mf; }
 constexpr bool cfg_cfl(int cfg) { return kTileCfgs[cfg].cfl != 0; }
+constexpr bool cfg_bar2(int cfg) { return kTileCfgs[cfg].bar2 != 0; }
 
 // The 16x16x32 MFMAs are issued as inline asm whose accumulator operand must sit in AGPRs:
 // with the builtin, the register allocator spreads the 64 four-register accumulators of a
@@ -752,9 +753,13 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
   // piece is a whole cache line fetched by 8 consecutive lanes.  (POST_BA 0: one barrier, between
   // the slices, with the loads after it.)
   constexpr bool POSTW = MF == 16 && NST == 2 && !VST;
-  // (two barriers measured 2.7 % faster where both operands are k-contiguous -- B given N x K --
-  // and 0.5 % slower where B is given K x N, whose row pieces were whole lines already)
-  constexpr int POST_BA = (POSTW && BLAY == L_NK && !AKM) ? 20 : 0;
+  // (two barriers measured 2.7 % faster where both operands are k-contiguous -- B given N x K.
+  // Where B is given K x N they are 2-7 % faster on the shorter K loops -- the K-concatenated
+  // 2048 x 5120 x 34816 dx GEMM split 3 ways 0.627 -> 0.590 ms, 2048 x 17408 x 5120 0.314 ->
+  // 0.305 ms, its dSwiGLU form 0.378 -> 0.352 ms, 16384 x 17408 x 5120 2.048 -> 2.005 ms -- but
+  // 0.5-1 % slower on the 65536 x 8192 x 16384 forward: configuration 12 has them for K x N B
+  // too, configuration 11 only for N x K.)
+  constexpr int POST_BA = (POSTW && !AKM && (BLAY == L_NK || cfg_bar2(CFG))) ? 20 : 0;
   constexpr int HB = POSTW ? (POST_BA > 0 ? NMMA / 2 : 0) : (NMMA >= 8 ? NMMA / 4 : NMMA / 2);  // MFMAs of the last slice before the barrier
   // DMA ops of the current k-step issued before its barrier
   constexpr int GBAR = (KS - 1) * NMMA + HB;

@@ -10,13 +10,15 @@
       every run of at least N consecutive dispatches (in start-time order, no other kernel
       in between) of the kernel whose name contains KERNEL_SUBSTR, with its mean duration:
       picks out the back-to-back launches a benchmark times between one event pair.
-  python -m dense_gemm_epilogues_amd.profiling counters PMC_DIR [PMC_DIR ...] --trace TRACE_DIR
+  python -m dense_gemm_epilogues_amd.profiling counters PMC_DIR [PMC_DIR ...] --trace TRACE_DIR [--copy-bytes B]
       per (kernel, grid size) averages of every counter in the `--pmc` runs, with the
       sustained shader clock (GRBM_GUI_ACTIVE / XCDs / duration), the MFMA busy fraction
       (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x SIMDs)) and the LDS bank-conflict fraction
       (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE), the L1 -> L2 read bytes and mean latency
-      (TCP_TCC_READ_REQ_sum x 128, TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum);
-      durations come from the kernel trace.
+      (TCP_TCC_READ_REQ_sum x 128, TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum), and
+      with --copy-bytes B the HBM read and write rates from FETCH_SIZE / WRITE_SIZE runs that
+      also recorded one device copy of B bytes (the counters' scale); durations come from
+      the kernel trace.
   python -m dense_gemm_epilogues_amd.profiling traffic FETCH_DIR WRITE_DIR KERNEL_SUBSTR \
       --copy-bytes B [--grid G] [--out FILE]
       HBM bytes per launch of the kernel whose name contains KERNEL_SUBSTR (and, with
@@ -123,17 +125,29 @@ def pmc_dispatches(d, counter):
 XCDS, SIMDS = 8, 256 * 4
 
 
-def counters(pmc_dirs, trace_dir):
-    """[(name, grid, n, {counter: mean}, derived)] for every kernel in the counter runs."""
+def counters(pmc_dirs, trace_dir, copy_bytes=0):
+    """[(name, grid, n, {counter: mean}, derived)] for every kernel in the counter runs.
+
+    With copy_bytes, FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled in each run by
+    what they read for that run's largest device-to-device copy of copy_bytes bytes, and
+    the HBM read / write rates are derived from them."""
     per = defaultdict(lambda: defaultdict(list))
     for d in pmc_dirs:
         disp = defaultdict(dict)
         for r in csv.DictReader(open(_find(d, "*counter_collection.csv"))):
             key = (r["Kernel_Name"], int(r["Grid_Size"]))
             disp[(key, r["Dispatch_Id"])][r["Counter_Name"]] = float(r["Counter_Value"])
+        scale = {}
+        if copy_bytes:
+            for c in ("FETCH_SIZE", "WRITE_SIZE"):
+                cal = [cs[c] for ((name, _), _), cs in disp.items() if CALIB_KERNEL in name and c in cs]
+                if cal:
+                    scale[c] = copy_bytes / (max(cal) * 1024.0)
         for (key, _), cs in disp.items():
             for c, v in cs.items():
                 per[key][c].append(v)
+                if c in scale:
+                    per[key][c + "_bytes"].append(v * 1024.0 * scale[c])
     dur = {(n, g): avg for (n, g, _, avg) in kernel_trace(trace_dir)}
     out = []
     for key, cs in per.items():
@@ -148,6 +162,11 @@ def counters(pmc_dirs, trace_dir):
                 der["mfma_busy"] = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS)
         if mean.get("SQ_LDS_IDX_ACTIVE"):
             der["lds_bank_conflict_frac"] = mean.get("SQ_LDS_BANK_CONFLICT", 0.0) / mean["SQ_LDS_IDX_ACTIVE"]
+        if t:
+            if "FETCH_SIZE_bytes" in mean:
+                der["hbm_read_GBps"] = mean["FETCH_SIZE_bytes"] / t
+            if "WRITE_SIZE_bytes" in mean:
+                der["hbm_write_GBps"] = mean["WRITE_SIZE_bytes"] / t
         if mean.get("TCP_TCC_READ_REQ_sum"):
             # L1 -> L2 read requests (128-byte lines) and their mean latency in cycles
             der["l2_read_MB"] = mean["TCP_TCC_READ_REQ_sum"] * 128 / 1e6
@@ -216,6 +235,7 @@ def main(argv=None):
     c.add_argument("pmc_dirs", nargs="+")
     c.add_argument("--trace", required=True)
     c.add_argument("--only", default="gemm_kernel")
+    c.add_argument("--copy-bytes", type=int, default=0)
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
@@ -230,7 +250,7 @@ def main(argv=None):
         for name, calls, avg, tot in kernel_stats(a.dir):
             print(f"{calls:6d} calls  avg {avg / 1e3:11.2f} us  total {tot / 1e6:10.3f} ms  {name[:110]}")
     elif a.cmd == "counters":
-        for name, grid, n, mean, der in counters(a.pmc_dirs, a.trace):
+        for name, grid, n, mean, der in counters(a.pmc_dirs, a.trace, a.copy_bytes):
             if a.only not in name:
                 continue
             print(f"{name[:60]}  grid {grid}  dispatches {n}")

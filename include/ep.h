@@ -163,9 +163,10 @@ typedef struct {
   ep_bgrad_mode bgrad_mode;/* DRELU_BGRAD: deterministic two-pass reduction (default) or
                               float32 atomics into bgrad (order-dependent rounding) */
   int tile_cfg;            /* -1 = choose by shape; otherwise an index < ep_num_tile_cfgs().
-                              Configuration 11 (256x256 tiles, 64-deep k-steps, 16x16 MFMAs)
-                              needs k % 64 == 0 (EP_ERR_UNSUPPORTED otherwise); it is the choice
-                              by shape for 256x256 tiles whenever k allows it */
+                              Configurations 11 and 12 (256x256 tiles, 64-deep k-steps, 16x16
+                              MFMAs; 12 with a second barrier per k-step where B is K x N too)
+                              need k % 64 == 0 (EP_ERR_UNSUPPORTED otherwise); one of them is
+                              the choice by shape for 256x256 tiles whenever k allows it */
   int split_k;             /* fused path: 0 = chosen by shape (split only when the output tiles
                               leave CUs idle); 1 = never; 2..EP_MAX_SPLIT_K = split the K range of
                               every tile into that many parts, each computed by its own

@@ -33,7 +33,7 @@ M32 = "_ZN2ep11gemm_kernelILi0ELi0ELi3ELi0ELi0EEEvNS_8GemmArgsE"
 
 
 def test_asm_mfma_configurations_from_the_tile_table():
-    assert B.asm_mfma_cfgs() == {9, 10, 11}
+    assert B.asm_mfma_cfgs() == {9, 10, 11, 12}
 
 
 def test_parser_reads_every_field():

@@ -77,7 +77,7 @@ def run_plan(a, b, epi, ins, layout, cfg, path="fused", **kw):
     return p, out, aux
 
 
-CFGS = [0, 8, 9, 10, 11]
+CFGS = [0, 8, 9, 10, 11, 12]
 
 
 @pytest.mark.parametrize("layout", ["KN", "NK"])
@@ -200,7 +200,7 @@ def test_drelu_nonfinite_rows(dtname, bgrad_mode):
     maskd = torch.from_numpy(mask.view(np.int32).copy()).to(dev)
     runs = [("fused", c) for c in CFGS] + ([("unfused", -1)] if bgrad_mode == "two_pass" else [])
     for path, cfg in runs:
-        for split in ((0, 3) if path == "fused" and cfg in (9, 10) else (0,)):
+        for split in ((0, 3) if path == "fused" and cfg in (9, 10, 11, 12) else (0,)):
             what = f"{dtname}/{bgrad_mode}/cfg{cfg}/{path}/split{split}"
             say(f"case DRELU_BGRAD non-finite dY rows {what}")
             p, dx, aux = run_plan(dyd, wd, "DRELU_BGRAD", {"relu_aux": maskd}, "NK", cfg, path,
@@ -236,7 +236,7 @@ def test_square_relu_family_bitwise():
     for epi in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS"):
         say(f"case square {epi} bitwise family")
         p = ep.Plan(x, w, epi, {"bias": bias}, b_layout="KN")
-        assert "tile_cfg=11 " in p.info(), p.info()
+        assert "tile_cfg=12 " in p.info(), p.info()
         outs[epi] = p.execute()
         plans.append(p)
     torch.cuda.synchronize()

@@ -54,7 +54,7 @@ def make_inputs(epi, dt, layout, m, n, k, seed, dev):
     return {kk: v.to(dev) for kk, v in ins.items()}
 
 
-K64_ONLY_CFGS = (11,)  # configurations that need K to be a multiple of 64
+K64_ONLY_CFGS = (11, 12)  # configurations that need K to be a multiple of 64
 
 
 def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split_k=0, bgrad_mode="two_pass",
@@ -171,9 +171,9 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
 
 # every tile configuration of the library (9 and 10 issue 16x16x32 MFMAs); those with a
 # 128-row B tile cannot hold the gate and up sub-tiles of a K x N dual B operand
-NUM_TILE_CFGS = 12
+NUM_TILE_CFGS = 13
 BNT128_CFGS = (1, 2, 6)
-BK64_CFGS = (1, 4, 8, 11)  # 64-deep k-steps
+BK64_CFGS = (1, 4, 8, 11, 12)  # 64-deep k-steps
 
 
 @pytest.mark.parametrize("cfg", list(range(NUM_TILE_CFGS)))
@@ -203,7 +203,7 @@ def test_split_k(epi, layout, splits):
     (register-staged, 64-deep k-steps) is the planner's choice for N x K GEMMs under one round
     of tiles, where the split model splits long K ranges."""
     require_gpu()
-    for cfg in (0, 1, 6, 8, 9, 10, 11):
+    for cfg in (0, 1, 6, 8, 9, 10, 11, 12):
         if epi in ("SWIGLU", "SWIGLU_AUX") and layout == "KN" and cfg in BNT128_CFGS:
             continue
         for dtname in ("f16", "bf16"):
@@ -239,7 +239,7 @@ def test_split_tail_refusals_and_atomic_bgrad():
     run_and_check("DRELU_BGRAD", "f16", "NK", 4352, 4096, 512, 11, split_k=4, split_tail=True, bgrad_mode="atomic")
 
 
-@pytest.mark.parametrize("cfg", [9, 10, 11])
+@pytest.mark.parametrize("cfg", [9, 10, 11, 12])
 @pytest.mark.parametrize("layout", ["KN", "NK"])
 def test_kstep_pair_k_lengths(layout, cfg):
     """The 16x16 configurations' load schedules over many K lengths.  Configurations 9 and 10
@@ -303,13 +303,14 @@ def test_transposed_a(dtname, layout):
 
 @pytest.mark.parametrize("m,n,layout,ld_extra,dual,want_cfg,k", [
     (4096, 4096, "NK", 64, False, 11, 4096),    # K % 64 == 0: 64-deep 16x16x32 k-steps, both layouts
-    (4096, 4096, "KN", 0, False, 11, 4096),
+    (4096, 4096, "KN", 0, False, 12, 4096),     # K x N B: with two barriers per k-step
     (16384, 32768, "NK", 64, False, 11, 4096),  # 32 rounds
     (16384, 32768, "NK", 0, False, 11, 4096),   # 32 rounds, B rows 32 KiB apart
-    (16384, 32768, "KN", 0, False, 11, 4096),
+    (16384, 32768, "KN", 0, False, 12, 4096),
+    (16384, 16384, "KN", 0, False, 11, 8192),   # K x N B, long K over 16 rounds: one barrier
     (2048, 8192, "NK", 0, True, 11, 4096),      # dual-B SwiGLU, N x K weights, 2 rounds
     (2048, 5120, "NK", 0, False, 11, 4096),     # single B, N x K, 160 tiles (under one round)
-    (2048, 5120, "KN", 0, False, 11, 4096),
+    (2048, 5120, "KN", 0, False, 12, 4096),
     (2048, 5120, "NK", 0, False, 8, 4072),      # ... with K % 64 != 0: register-staged
     (4096, 4096, "NK", 64, False, 10, 4064),    # K % 64 != 0: 32-deep, rows kept whole for N x K B
     (4096, 4096, "KN", 0, False, 9, 4064),      # ... chunks spread for K x N B
