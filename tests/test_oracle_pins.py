@@ -386,6 +386,14 @@ def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
     exact = _brute.exact_matmul(a2.tolist(), b2.tolist(), "KN")
     assert any(abs(Fraction(wrong[i, j]) - exact[i][j]) > Fraction(1, 2 ** 20) for i in range(3) for j in range(4))
 
+    # (5) the tanh approximation of GELU in place of the exact form fails the GELU fixture
+    gg = load(golden_dir, "gelu_aux_bias_dgelu_2x2x2.json")
+    tanh_gelu = lambda t: 0.5 * t * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (t + 0.044715 * t ** 3)))
+    monkeypatch.setattr(core, "gelu", tanh_gelu)
+    y, _ = core.gelu_aux_bias(np.array(gg["x"], float), np.array(gg["w"], float), np.array(gg["bias"], float), "KN")
+    assert not np.allclose(y, gg["y"], rtol=0, atol=1e-15)
+    monkeypatch.undo()
+
 
 # ---------------------------------------------------------------------------- GELU
 def test_gelu_golden(golden_dir):
