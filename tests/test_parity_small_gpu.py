@@ -395,17 +395,18 @@ def test_planner_split_tail_choice(m, n, k, dual, layout, want):
     p.free()
 
 
-@pytest.mark.parametrize("a_layout", ["MK", "KM"])
-def test_planner_split_choice(a_layout):
+@pytest.mark.parametrize("a_layout,k,want_cfg", [("MK", 34816, 11), ("KM", 34816, 11), ("MK", 34808, 8)])
+def test_planner_split_choice(a_layout, k, want_cfg):
     """A long-K GEMM under one round of tiles, B given N x K (the SwiGLU dx GEMM's shape,
     2048 x 5120 x 34816): the planner picks the 64-deep 16x16 configuration 11 with 3 split-K
-    ranges over every tile; sampled rows and columns against the oracle."""
+    ranges over every tile; with K not a multiple of 64 (34808) the register-staged
+    configuration 8, also split 3 ways.  Sampled rows and columns against the oracle."""
     require_gpu()
     import dense_gemm_epilogues_amd as ep
     dev = torch.device("cuda")
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the expected choice assumes 256 CUs")
-    m, n, k = 2048, 5120, 34816
+    m, n = 2048, 5120
     g = torch.Generator(device=dev)
     g.manual_seed(77)
     a = torch.randn(m, k, device=dev, generator=g).half()
@@ -415,7 +416,7 @@ def test_planner_split_choice(a_layout):
     say(f"case planner split choice A {a_layout} {m}x{n}x{k}")
     p = ep.Plan(a, b, "DEFAULT", b_layout="NK", a_layout=a_layout)
     info = p.info()
-    assert "tile_cfg=11 " in info and "splits=3 " in info and "split_tail0=0 " in info, info
+    assert f"tile_cfg={want_cfg} " in info and "splits=3 " in info and "split_tail0=0 " in info, info
     out, _ = p.execute()
     torch.cuda.synchronize()
     rows = torch.tensor(np.r_[0:32, m // 2 - 8:m // 2 + 24, m - 32:m], device=dev)
