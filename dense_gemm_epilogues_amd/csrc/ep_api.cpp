@@ -214,7 +214,8 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
 // configurations wherever K is a multiple of 64: each row piece is then a whole cache line
 // fetched by 8 consecutive lanes (the 32-deep ones fetch half lines, which stalled the texture
 // addresser on the L1 4-12 times as often as a library GEMM of the same shape), the loop needs
-// 5 VALU instructions per 64 k instead of 38-51 and one barrier instead of two.  Measured at
+// 5 VALU instructions per 64 k instead of 38-51 and one or two barriers per 64 k instead of two
+// (B K x N / N x K; see configuration 12 below).  Measured at
 // 65536 x 8192 x 16384 (B K x N) 14.50 -> 13.85 ms, 65536 x 16384 x 8192 (B N x K)
 // 14.54 -> 13.72 ms, 4096^3 120.9 -> 116.1 us (K x N) and 114.6 -> 108.3 us (N x K).  It
 // also takes over the single-B N x K GEMMs under one round once they are split: with the

@@ -338,8 +338,10 @@ struct GemmTraits {
   static_assert(!DUAL || NBO >= 1, "dual B needs a block per output column range");
   // staged rows per chunk of the store loop: 8 rows read together where the epilog is a plain
   // store; one row at a time where it has per-row inputs (measured faster on MI355X)
-  static constexpr int CH =
-      (EPI == E_DSWIGLU || EPI == E_DRELU_BGRAD || EPI == E_DGELU_BGRAD) ? 1 : (ITERS < 8 ? ITERS : 8);
+  // (RELU_AUX_BIAS with two workgroups per CU: 4 rows, whose mask bytes then fit the registers)
+  static constexpr int CH = (EPI == E_DSWIGLU || EPI == E_DRELU_BGRAD || EPI == E_DGELU_BGRAD) ? 1
+                            : (EPI == E_RELU_AUX_BIAS && cfg_occ(CFG) > 1)                     ? (ITERS < 4 ? ITERS : 4)
+                                                                                                : (ITERS < 8 ? ITERS : 8);
   static_assert(KS == 1 || KS == 2 || KS == 4, "k-slices per step: 1, 2 or 4");
   static_assert(MF == 32 || MF == 16, "MFMA block edge");
   static_assert(MF == 32 || ((BK == 32 || (BK == 64 && NST == 2 && !cfg_cfl(CFG))) && !cfg_vst(CFG)),
@@ -1005,7 +1007,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
     // finished first), QB f32x4 groups at a time: the group's loads of one split are all
     // issued before they are added, so that a batch costs one memory latency per split
     // rather than one per load, and only the accumulators already summed are live
-    constexpr int QB = ACC4 < 16 ? ACC4 : 16;
+    constexpr int QB = cfg_occ(CFG) > 1 ? (ACC4 < 8 ? ACC4 : 8) : (ACC4 < 16 ? ACC4 : 16);  // (2 workgroups per CU: half the registers)
     static_assert(ACC4 % QB == 0, "accumulator groups per batch");
     constexpr int GPB = ACC_R / 4;  // f32x4 groups per MFMA block
     const float* src = p.part + (int64_t)(tbid - p.tail0) * (ACC4 * kThreads * 4) + tid * 4;
@@ -1166,22 +1168,11 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
           const int r0 = 8 * (r >> 2) + (r & 3);  // block row held by lanes 0-31 (lanes 32-63: +4)
           bool pr;
           const float v = xform(acc[i], j, r, pr);
-          if constexpr (EPI == E_RELU_AUX_BIAS) {
-            // bit l of the ballot is column 32 j + l%32 of row r0 (l < 32) or r0 + 4 (l >= 32)
-            // (every lane writes the same wave-uniform word to the same LDS address)
-            const uint64_t b = __builtin_amdgcn_ballot_w64(pr);
-            mk[r0 * TR::WPT + wn * WPR + j] = (uint32_t)b;
-            mk[(r0 + 4) * TR::WPT + wn * WPR + j] = (uint32_t)(b >> 32);
-          }
           // staged right away (row 8 (r/4) + 4 (l/32) + r%4 of the slab, column 32 j + l%32)
           stg[(r0 + 4 * hlf) * SP + j * 32 + l32] = v;
-          // one register at a time: otherwise the scheduler hoists every ballot / lane read
-          // of the slab and runs out of scalar registers
-          if constexpr (EPI == E_RELU_AUX_BIAS) __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
-      // blocks j = 2 jw and 2 jw + 1 make up the 32 columns of mask word jw
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1191,25 +1182,17 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
             bool pr0, pr1;
             const float v0 = xform(acc[2 * i + h], 2 * jw, r, pr0);
             const float v1 = xform(acc[2 * i + h], 2 * jw + 1, r, pr1);
-            if constexpr (EPI == E_RELU_AUX_BIAS) {
-              // bit l of a ballot is column l%16 of the block and row 4 (l/16) + r
-              const uint64_t b0 = __builtin_amdgcn_ballot_w64(pr0);
-              const uint64_t b1 = __builtin_amdgcn_ballot_w64(pr1);
-#pragma unroll
-              for (int g = 0; g < 4; ++g)
-                mk[(16 * h + 4 * g + r) * TR::WPT + wn * WPR + jw] =
-                    ((uint32_t)(b0 >> (16 * g)) & 0xffffu) | ((uint32_t)(b1 >> (16 * g)) << 16);
-            }
             const int srow = 16 * h + 4 * q4 + r;
             stg[srow * SP + 2 * jw * 16 + lmf] = v0;
             stg[srow * SP + (2 * jw + 1) * 16 + lmf] = v1;
-            if constexpr (EPI == E_RELU_AUX_BIAS) __builtin_amdgcn_sched_barrier(0);
           }
     }
 
     __syncthreads();
 
-    if constexpr (EPI == E_RELU_AUX_BIAS) {
+    // RELU_AUX_BIAS: the slab's mask words, gathered in LDS by the store loop below, go to
+    // relu_aux after it (store_mask)
+    auto store_mask = [&]() __attribute__((always_inline)) {
       // the tile's words of the slab's 32 rows: one contiguous piece of WPT words per row,
       // written by the wn = 0 wave (words past ceil(N / 32) are not part of the row)
       if (wn == 0) {
@@ -1235,7 +1218,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
           }
         }
       }
-    }
+    };
 
     // ---- stores: CH staged rows per chunk, their LDS reads issued together
     // (the lane's output address of staged row 0; staged row t is t * ldd elements further)
@@ -1321,6 +1304,16 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
           }
           __builtin_amdgcn_raw_buffer_store_b128(pack8<DT>(vv[c][0], vv[c][1]), rs_d,
                                                  vo_d + (uint32_t)((c0 + c) * TR::RPI * (int)p.ldd * 2), 0, 0);
+          if constexpr (EPI == E_RELU_AUX_BIAS) {
+            // the mask bits of the lane's 8 columns: the staged values are ReLU's output, which
+            // is +0 exactly where the pre-activation is not > 0 (NaN included) and positive
+            // elsewhere, so bit e is (bits of value e != 0).  They make byte (lane % LPR) of the
+            // wave's piece of the row (LSB = lowest column; columns past N were staged as +0).
+            uint32_t byte = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) byte |= min(__float_as_uint(vv[c][e >> 2][e & 3]), 1u) << e;
+            ((unsigned char*)(mk + ((c0 + c) * TR::RPI + lr) * TR::WPT + wn * WPR))[lane % TR::LPR] = (unsigned char)byte;
+          }
           if constexpr (BGRAD) {  // rows past M are staged as 0
             colsum[0] += vv[c][0];
             colsum[1] += vv[c][1];
@@ -1332,6 +1325,7 @@ __global__ __launch_bounds__(kThreads, cfg_occ(CFG)) void gemm_kernel(GemmArgs p
       }
     }
     __syncthreads();
+    if constexpr (EPI == E_RELU_AUX_BIAS) store_mask();
 
     if constexpr (EPI == E_SWIGLU_AUX) {
       // the gate (pass 0) and up (pass 1) pre-activations of the slab, still in the
