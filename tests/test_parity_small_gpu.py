@@ -218,11 +218,14 @@ def test_split_tail(epi, layout):
     so tiles [0, 256) run whole-K in one launch and the other 16 are split into K ranges whose
     partials a fixup launch sums before the epilog.  Every epilog, both dtypes, the 64-deep
     16x16 configuration (3 and 8 ranges) and a 32x32 one (8 ranges); the two-pass bias
-    gradient sums column partials written by both launches' epilogs."""
+    gradient sums column partials written by both launches' epilogs.  Also 8 ranges over
+    every tile of a small grid (the fixup's largest sum)."""
     require_gpu()
     n = 2048 if epi in ("SWIGLU", "SWIGLU_AUX") else 4096
     for dtname, cfg, splits in (("f16", 11, 3), ("bf16", 11, 8), ("bf16", 0, 8)):
         run_and_check(epi, dtname, layout, 4352 - 40, n - 24, 512, cfg, split_k=splits, split_tail=True)
+    # the most ranges a plan takes, over every tile of a small grid (one k-step per range)
+    run_and_check(epi, "f16", layout, 300, 200, 512, 11, split_k=8)
 
 
 def test_split_tail_refusals_and_atomic_bgrad():

@@ -70,7 +70,7 @@ def drelu_case(m, n, k, seed, split_k=0, expect_split=False):
     ref_plan.free()
 
 
-def relu_aux_case(m, n, k, seed, split_k):
+def relu_aux_case(m, n, k, seed, split_k, split_tail=False, tile_cfg=-1):
     ep = _ep()
     L = ep.lib()
     dev = torch.device("cuda")
@@ -78,14 +78,17 @@ def relu_aux_case(m, n, k, seed, split_k):
     x = torch.randn(m, k, generator=g).to(torch.bfloat16).to(dev)
     w = (torch.randn(k, n, generator=g) * k ** -0.5).to(torch.bfloat16).to(dev)
     bias = (torch.randn(n, generator=g) * 0.1).to(torch.bfloat16).to(dev)
-    ref_plan = ep.Plan(x, w, "RELU_AUX_BIAS", {"bias": bias}, b_layout="KN", split_k=split_k)
+    ref_plan = ep.Plan(x, w, "RELU_AUX_BIAS", {"bias": bias}, b_layout="KN", split_k=split_k, split_tail=split_tail,
+                       tile_cfg=tile_cfg)
+    if split_tail:
+        assert "split_tail0=256 " in ref_plan.info(), ref_plan.info()
     y_ref, aux = ref_plan.execute()
     nw = (n + 31) // 32
     y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=dev)
     words_out = torch.full((m, nw), -1, dtype=torch.int32, device=dev)
     shape = ep.ep_shape(m=m, n=n, k=k, b_layout=0, a=ptr(x), lda=k, b=ptr(w), ldb=n, d=ptr(y), ldd=n, a_layout=0)
     io = ep.ep_epilog_io(bias=ptr(bias), relu_aux=ptr(words_out), ld_aux=nw)
-    opt = ep.ep_options(path=0, bgrad_mode=0, tile_cfg=-1, split_k=split_k, autotune=0)
+    opt = ep.ep_options(path=0, bgrad_mode=0, tile_cfg=tile_cfg, split_k=split_k, split_tail=int(split_tail), autotune=0)
     st = noalloc(L, shape, BF16, ep.EPILOGS["RELU_AUX_BIAS"], io, opt)
     assert st == 0, L.ep_last_error().decode()
     torch.cuda.synchronize()
@@ -115,6 +118,18 @@ def test_noalloc_split_k_two_calls():
     relu_aux_case(260, 296, 520, seed=4, split_k=2)
     drelu_case(1024, 768, 34816, seed=5, split_k=0, expect_split=True)  # few long-K tiles: split by shape
     drelu_case(130, 264, 520, seed=6, split_k=2)
+
+
+def test_noalloc_split_tail_two_calls():
+    """A split of the last round's tiles only (272 256x256 tiles of configuration 11: 256 whole,
+    16 split 3 ways), its partials in the static scratch, then a smaller uniformly split
+    problem."""
+    require_gpu()
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the tail's position assumes 256 CUs")
+    say("case noalloc split tail RELU_AUX_BIAS 4312x4072x512, then 260x296x520")
+    relu_aux_case(4312, 4072, 512, seed=7, split_k=3, split_tail=True, tile_cfg=11)
+    relu_aux_case(260, 296, 520, seed=8, split_k=2)
 
 
 def test_noalloc_rejects_oversized_workspace_and_unsupported_options():
