@@ -7,7 +7,8 @@ W 16384 x 8192.  One step is the fused forward RELU_AUX_BIAS (Y and its relu_aux
 the fused backward DRELU_BGRAD (dY W^T masked by a separate 65536 x 16384 relu_aux, plus the
 bias gradient).  `value` is that step's GEMM throughput in TFLOP/s (2*M*N*K per GEMM; epilog
 flops not counted).  The same line carries the unfused-path step time (same GEMM core,
-DEFAULT epilog, separate kernels through HBM) and, under "configs", the square 4096^3 layer,
+DEFAULT epilog, separate kernels through HBM) and, under "configs", the execute latency of the
+launch-bound 32 x 64 x 128 layer, the square 4096^3 layer,
 the bf16 SwiGLU forward (M 2048, H 5120, I 17408), the GEMM + dSwiGLU backward (M 16384), a
 whole SwiGLU-MLP training step, an M sweep, the GELU layer, launch overhead and plan-time
 tuning.  Where stated, torch (hipBLASLt GEMMs plus elementwise ops) runs the same step as a
@@ -23,7 +24,8 @@ step.  An event record costs about 6 us of GPU time before the next launch, so p
 durations (the roofline's average launch) come from launches run back to back between a
 single event pair.  Inputs are seeded synthetic tensors generated on the device.  The CPU
 oracle (float64 numpy) is timed on this host on a sample of each large workload (seeded
-output tiles and bias-gradient columns), as a baseline only.
+output tiles and bias-gradient columns), and whole for the 32 x 64 x 128 and 4096^3 layers, as a
+baseline only.
 """
 import argparse
 import json
@@ -710,6 +712,66 @@ def cpu_baseline_dswiglu(inp, c, min_s=3.0):
     return oracle_rate(flop, 2.0 * m * hd * i, sec, reps, what, copy_s)
 
 
+def cpu_oracle_full_linear(inp, c, min_s=3.0):
+    """The whole float64 oracle of a ReLU layer step, timed: RELU_AUX_BIAS forward, then
+    DRELU_BGRAD backward on the oracle's own forward mask (square layer) or on the separate
+    mask (the 32 x 64 x 128 layer)."""
+    import oracle
+    t0 = time.perf_counter()
+    d = oracle.decode_f16
+    x, w, bias, dy = (d(host(inp[nm])) for nm in ("x", "w", "bias", "dy"))
+    sep = c.mask_from == "separate"
+    words_in = host(inp["mask_in"]) if sep else None
+    copy_s = time.perf_counter() - t0
+
+    def run():
+        _, words, _ = oracle.relu_aux_bias(x, w, bias, "KN")
+        oracle.drelu_bgrad(dy, w, "NK", words_in if sep else words)
+
+    sec, reps = timed_reps(run, min_s, 50)
+    flop = 2 * 2.0 * c.m * c.n * c.k
+    return {"value": flop / sec / 1e12, "unit": "TFLOP/s", "seconds_per_step": sec, "cores": int(blas_threads()),
+            "kind": "oracle",
+            "sample": f"the whole {c.m}x{c.n}x{c.k} fp16 layer step (forward + backward, fp64 oracle), "
+                      f"{reps} pass(es); device-to-host copies ({copy_s:.2f} s) not timed; host has "
+                      f"{os.cpu_count()} logical CPUs"}
+
+
+def tiny_layer(dev, reps=20, warmup=5):
+    """The 32 x 64 x 128 fp16 layer (launch-bound; TFLOP/s means nothing there): the latency of
+    one execute of the fused RELU_BIAS and RELU_AUX_BIAS forwards and of the DRELU_BGRAD
+    backward (its GEMM launch plus the bias-gradient pass), one HIP event pair per execute on
+    the launch stream, after warm-up executes; median, min and max over the timed ones."""
+    import dense_gemm_epilogues_amd as ep
+    import workloads as W
+    c = W.LINEAR[1]
+    inp = W.linear_inputs(c, device=dev)
+    plans = {"fwd_relu_bias": ep.Plan(inp["x"], inp["w"], "RELU_BIAS", {"bias": inp["bias"]}, b_layout="KN"),
+             "fwd_relu_aux_bias": ep.Plan(inp["x"], inp["w"], "RELU_AUX_BIAS", {"bias": inp["bias"]},
+                                          b_layout="KN"),
+             "bwd_drelu_bgrad": ep.Plan(inp["dy"], inp["w"], "DRELU_BGRAD", {"relu_aux": inp["mask_in"]},
+                                        b_layout="NK")}
+    out = {"m": c.m, "n": c.n, "k": c.k, "timing": f"{warmup} warm-up, {reps} timed executes, one event pair each"}
+    for name, p in plans.items():
+        for _ in range(warmup):
+            p.execute()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            p.execute()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        out[f"{name}_us"] = {"median": round(float(np.median(ts)), 2), "min": round(float(np.min(ts)), 2),
+                             "max": round(float(np.max(ts)), 2)}
+        out[f"{name}_kernels"] = p.info().split("kernels=")[1]
+        p.free()
+    out["inputs"] = inp
+    return out
+
+
 def linear_summary(r, c):
     f = r["fused"]
     flop = r["flop_per_gemm"]
@@ -831,9 +893,16 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_large:
         large = {}
+        r1 = tiny_layer(dev)
+        if not args.no_cpu:
+            r1["cpu_oracle_full"] = cpu_oracle_full_linear(r1["inputs"], W.LINEAR[1], min_s=0.5)
+        r1.pop("inputs")
+        large["tiny_fp16_32x64x128"] = r1
         r2 = linear_layer(W.LINEAR[2], args.steps, args.warmup, flush, dev)
-        r2.pop("inputs")
         large["square_fp16_4096x4096x4096"] = linear_summary(r2, W.LINEAR[2])
+        if not args.no_cpu:
+            large["square_fp16_4096x4096x4096"]["cpu_oracle_full"] = cpu_oracle_full_linear(r2["inputs"], W.LINEAR[2])
+        r2.pop("inputs")
         tr2 = measured_traffic(os.path.join(PROFILES, "traffic_gemm_relu_aux_bias_f16_KN_4096.txt"))
         large["square_fp16_4096x4096x4096"]["fwd_traffic_bytes"] = (round(tr2["traffic_bytes_per_launch"])
                                                                     if tr2 is not None else None)
