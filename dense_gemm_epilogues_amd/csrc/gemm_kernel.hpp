@@ -321,7 +321,13 @@ struct GemmTraits {
   static constexpr int RPS = 1024 / ROWB;        // rows per DMA slot (k-contiguous tiles)
   static constexpr int KN_SUB = BK * 256;        // bytes of one [BK k][128 n] sub-tile
   static constexpr int KN_SPS = BK / 4;          // DMA slots per sub-tile
-  static constexpr int SPITCH = WTN + 8;         // staging pitch in floats
+  // staging pitch in floats.  A staging write stores one float per lane: 32x32 blocks in 2
+  // groups of 32 lanes 4 rows apart, 16x16 blocks in 4 groups of 16 lanes 4 rows apart.  With
+  // 4 * pitch = 32 (mod 64) banks the 2 groups, with 4 * pitch = 16 (mod 64) the 4 groups,
+  // fall on disjoint banks; the reads (16 bytes per lane, 8 lanes per row piece) are
+  // conflict-free with either.  (Probed on MI355X with SQ_LDS_BANK_CONFLICT: the 16x16 writes
+  // at pitch WTN + 8 conflicted on half of their LDS cycles, at WTN + 4 on none.)
+  static constexpr int SPITCH = WTN + (MF == 16 ? 4 : 8);
   static constexpr int STG_FLOATS = 32 * SPITCH;  // per wave: one 32-row slab of the output
   static constexpr int BG_OFF = 4 * STG_FLOATS * 4;      // bytes; cross-wave bgrad exchange
   static constexpr int MASK_OFF = BG_OFF + 2 * WTN * 4;  // bytes; one slab's mask words per M-wave
