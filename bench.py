@@ -326,11 +326,29 @@ def gelu_layer(c, steps, warmup, flush, dev):
     for path, (pf, pb) in plans.items():
         res[path] = {"step_ms": float(np.mean(timed[path][0])), "fwd_ms": launch_avg_ms(pf.execute),
                      "bwd_ms": launch_avg_ms(pb.execute)}
+    # the forward epilogs side by side, same method, alternating (3 rounds, medians): what the
+    # exact GELU costs over ReLU, with (GELU_AUX_BIAS also writes the M x N pre-activation) and
+    # without a saved output
+    fwd = {"RELU_AUX_BIAS": ep.Plan(x, w, "RELU_AUX_BIAS", {"bias": bias}, b_layout="KN"),
+           "GELU_AUX_BIAS": plans["fused"][0],
+           "RELU_BIAS": ep.Plan(x, w, "RELU_BIAS", {"bias": bias}, b_layout="KN"),
+           "GELU_BIAS": ep.Plan(x, w, "GELU_BIAS", {"bias": bias}, b_layout="KN")}
+    side = {k: [] for k in fwd}
+    for _ in range(3):
+        for k, p_ in fwd.items():
+            side[k].append(launch_avg_ms(p_.execute))
+    side = {k: float(np.median(v)) for k, v in side.items()}
+    for k in ("RELU_AUX_BIAS", "RELU_BIAS", "GELU_BIAS"):
+        fwd[k].free()
+    for pf, pb in plans.values():
         pf.free()
         pb.free()
     flop = 2.0 * c.m * c.n * c.k
     f, u = res["fused"], res["unfused"]
-    return {"fused_step_tflops": round(2 * flop / (f["step_ms"] * 1e-3) / 1e12, 1),
+    return {"forward_epilogs_ms": {k: round(v, 5) for k, v in side.items()},
+            "gelu_aux_over_relu_aux": round(side["GELU_AUX_BIAS"] / side["RELU_AUX_BIAS"], 4),
+            "gelu_over_relu": round(side["GELU_BIAS"] / side["RELU_BIAS"], 4),
+            "fused_step_tflops": round(2 * flop / (f["step_ms"] * 1e-3) / 1e12, 1),
             "fwd_pct_peak": round(100 * flop / (f["fwd_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
             "bwd_pct_peak": round(100 * flop / (f["bwd_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
             "fused_fwd_ms": round(f["fwd_ms"], 5), "fused_bwd_ms": round(f["bwd_ms"], 5),

@@ -15,14 +15,16 @@
 namespace ep {
 
 // Phi(-|t|) = erfc(|t| / sqrt 2) / 2, and the density e^(-t^2/2) / sqrt(2 pi) in *pdf (the
-// polynomial's coefficients are A&S's a1..a5 halved, which folds in the / 2)
+// polynomial's coefficients are A&S's a1..a5 halved, which folds in the / 2).  The argument is
+// carried as y = |t| sqrt(log2(e) / 2), so that e^(-t^2/2) = 2^(-y^2) and A&S's p x = p' y with
+// p' = p / sqrt(log2 e): one multiplication fewer than with x = |t| / sqrt 2.
 __device__ __forceinline__ float norm_tail_pdf(float t, float* pdf) {
-  const float x = __builtin_fabsf(t) * 0.70710678118654752f;
-  const float r = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * x);
+  const float y = __builtin_fabsf(t) * 0.84932180028801904f;
+  const float r = __builtin_amdgcn_rcpf(1.0f + 0.27273748087922250f * y);
   const float half_poly =
       r * (0.127414796f + r * (-0.142248368f + r * (0.7107068705f + r * (-0.7265760135f + r * 0.5307027145f))));
-  const float e = __builtin_amdgcn_exp2f(-0.72134752044448170f * t * t);  // e^(-t^2/2)
-  *pdf = 0.39894228040143268f * e;                                       // 1/sqrt(2 pi) e^(-t^2/2)
+  const float e = __builtin_amdgcn_exp2f(-(y * y));  // e^(-t^2/2)
+  *pdf = 0.39894228040143268f * e;                   // 1/sqrt(2 pi) e^(-t^2/2)
   return half_poly * e;
 }
 
@@ -34,11 +36,17 @@ __device__ __forceinline__ float norm_cdf_pdf(float t, float* pdf) {
 // exact-form GELU t Phi(t) = max(t, 0) - |t| Phi(-|t|) (for t >= 0: t - t Phi(-t); for t < 0:
 // t Phi(t)), and its derivative Phi(t) + t phi(t).  |t| enters the product clamped to 40:
 // Phi(-|t|) is exactly 0 in fp32 well before that, and the clamp keeps t = +-inf from
-// multiplying infinity by zero (GELU(+inf) = +inf, GELU(-inf) = 0, NaN stays NaN).
+// multiplying infinity by zero (GELU(-inf) = 0).  The max and the clamp are medians of three
+// (one v_med3_f32 each, where fmaxf / fminf also quiet their inputs; the upper bound of the max
+// is the largest finite float, which the compiler does not turn back into a max, and which
+// rounds to +inf in fp16 and bf16, so GELU(+inf) is still +inf); a NaN t makes the Phi term
+// NaN, so GELU(NaN) is NaN whatever the median returns for it.
 __device__ __forceinline__ float gelu_f(float t) {
   float pdf;
   const float q = norm_tail_pdf(t, &pdf);
-  return __builtin_fmaxf(t, 0.0f) - __builtin_fminf(__builtin_fabsf(t), 40.0f) * q;
+  const float pos = __builtin_amdgcn_fmed3f(t, 0.0f, 3.40282347e38f);
+  const float mag = __builtin_amdgcn_fmed3f(__builtin_fabsf(t), 0.0f, 40.0f);
+  return pos - mag * q;
 }
 __device__ __forceinline__ float gelu_grad_f(float t) {
   float pdf;

@@ -17,6 +17,8 @@ boundary on the GPU:
     in the oracle, and each bias-gradient column non-finite exactly where the oracle's is.
   * bitwise self-consistency at the square layer's size with one tile configuration:
     relu(Y_BIAS) == Y_RELU_BIAS == Y_RELU_AUX_BIAS.
+  * the GELU forward epilogs on the same special pre-activations (A = 0): finite ones follow
+    the oracle to one rounding, the non-finite ones the function's limits.
 """
 import numpy as np
 import pytest
@@ -255,3 +257,59 @@ def test_square_relu_family_bitwise():
     assert torch.equal(bits & ~(ya > 0), bits & (yb.view(torch.int16) == 0)), "mask bits against Y_BIAS"
     for p in plans:
         p.free()
+
+
+@pytest.mark.parametrize("dtname", ["f16", "bf16"])
+def test_gelu_special_preactivations(dtname):
+    """GELU_BIAS and GELU_AUX_BIAS with A = 0, so that the pre-activation P is the bias exactly
+    (the hotdry.top post names GELU_BIAS; the exact form t Phi(t) is this library's reading).
+    Finite special values (signed zeros, subnormals, +-1e4, +-largest finite, +-1.5) follow
+    the oracle's gelu to one rounding of the element type; the non-finite ones follow the
+    function's limits, which the oracle's product form t (1 + erf(t / sqrt 2)) / 2 leaves
+    undefined at -inf: GELU(+inf) = +inf, GELU(-inf) = 0, GELU(NaN) = NaN.  GELU_AUX_BIAS's
+    saved pre-activation is P bit for bit."""
+    require_gpu()
+    dt = DTYPES[dtname]
+    dev = torch.device("cuda")
+    fi = torch.finfo(dt)
+    sub = torch.tensor(1, dtype=torch.int16).view(dt).item()
+    bias_h = edge_bias(dt, seed=13)
+    bias = bias_h.to(dev)
+    a = torch.zeros((M, K), dtype=dt, device=dev)
+    g = torch.Generator().manual_seed(14)
+    b = (torch.randn((K, N), generator=g) * K ** -0.5).to(dt).to(dev)
+    p64 = f64(bias_h)
+    fin = np.isfinite(p64)
+    want = np.zeros(N)
+    want[fin] = oracle.gelu(p64[fin])
+    want[p64 == np.inf] = np.inf
+    want[p64 == -np.inf] = 0.0
+    nan = np.isnan(p64)
+    # one rounding to the element type, plus the device Phi's error (far below it)
+    rel = 2.0 ** -7 if dt == torch.bfloat16 else 2.0 ** -10
+    for path, cfgs in (("fused", [0, 11, 12]), ("unfused", [-1])):
+        for cfg in cfgs:
+            for epi in ("GELU_BIAS", "GELU_AUX_BIAS"):
+                what = f"{epi} {dtname}/cfg{cfg}/{path}"
+                say(f"case GELU special pre-activations {what}")
+                p, y, aux = run_plan(a, b, epi, {"bias": bias}, "KN", cfg, path)
+                got = f64(y)
+                assert np.all(np.isnan(got[:, nan])), f"{what}: GELU(NaN) is not NaN"
+                ok = ~nan
+                err = np.abs(got[:, ok] - want[None, ok])
+                lim = rel * np.abs(want[None, ok]) + 2 * sub
+                inf_ok = np.isinf(want[None, ok]) & (got[:, ok] == want[None, ok])
+                bad = np.argwhere(~((err <= lim) | inf_ok))
+                assert bad.size == 0, (f"{what}: {len(bad)} outputs off, first column "
+                                       f"{np.flatnonzero(ok)[bad[0][1]]}: P = {p64[ok][bad[0][1]]!r}, "
+                                       f"got {got[:, ok][tuple(bad[0])]!r}, want {want[ok][bad[0][1]]!r}")
+                if epi == "GELU_AUX_BIAS":
+                    pa = aux["gelu_aux"]
+                    # (0 + -0 is +0: the sign of a zero sum is not part of the definition)
+                    pb = half_bits(bias_h.unsqueeze(0).expand(M, N).contiguous())
+                    pg = half_bits(pa)
+                    pb[pb == 0x8000] = 0
+                    pg[pg == 0x8000] = 0
+                    same = (pg == pb) | (np.isnan(f64(pa)) & nan[None, :])
+                    assert same.all(), f"{what}: saved pre-activation differs from P"
+                p.free()
