@@ -287,7 +287,7 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True, with_clock=Fal
             pf.free()
             pb.free()
     if with_unfused:
-        res["torch"] = {"step_ms": float(np.mean(timed["torch"]))}
+        res["torch"] = {"step_ms": float(np.mean(timed["torch"])), "step_ms_median": float(np.median(timed["torch"]))}
     x, w, bias, dy = inp["x"], inp["w"], inp["bias"], inp["dy"]
     flop = 2.0 * m * n * k
     out = {"flop_per_gemm": flop, "fused": res["fused"]}
@@ -298,11 +298,12 @@ def linear_layer(c, steps, warmup, flush, dev, with_unfused=True, with_clock=Fal
     if with_unfused:
         u = res["unfused"]
         out["unfused"] = u
-        out["speedup_step"] = u["step_ms"] / f["step_ms"]
+        # speedups are ratios of medians (the step's mean gives `value`)
+        out["speedup_step"] = u["step_ms_median"] / f["step_ms_median"]
         out["speedup_fwd"] = u["fwd_ms"] / f["fwd_ms"]
         out["speedup_bwd"] = u["bwd_ms"] / f["bwd_ms"]
         out["torch"] = res["torch"]
-        out["speedup_vs_torch"] = res["torch"]["step_ms"] / f["step_ms"]
+        out["speedup_vs_torch"] = res["torch"]["step_ms_median"] / f["step_ms_median"]
     out["inputs"] = {"x": x, "w": w, "bias": bias, "dy": dy, "mask_in": inp["mask_in"]}
     out["clock"] = clock
     return out
@@ -324,7 +325,7 @@ def gelu_layer(c, steps, warmup, flush, dev):
     timed = run_interleaved({p_: [pf.execute, pb.execute] for p_, (pf, pb) in plans.items()}, steps, warmup, flush)
     res = {}
     for path, (pf, pb) in plans.items():
-        res[path] = {"step_ms": float(np.mean(timed[path][0])), "fwd_ms": launch_avg_ms(pf.execute),
+        res[path] = {"step_ms": float(np.median(timed[path][0])), "fwd_ms": launch_avg_ms(pf.execute),
                      "bwd_ms": launch_avg_ms(pb.execute)}
     # the forward epilogs side by side, same method, alternating (3 rounds, medians): what the
     # exact GELU costs over ReLU, with (GELU_AUX_BIAS also writes the M x N pre-activation) and
@@ -373,7 +374,7 @@ def swiglu_fwd(c, steps, warmup, flush, dev):
     timed = run_interleaved({p_: [ps.execute, pd.execute] for p_, (ps, pd) in plans.items()}, steps, warmup, flush)
     res = {}
     for path, (ps, pd) in plans.items():
-        res[path] = {"step_ms": float(np.mean(timed[path][0])), "swiglu_ms": launch_avg_ms(ps.execute),
+        res[path] = {"step_ms": float(np.median(timed[path][0])), "swiglu_ms": launch_avg_ms(ps.execute),
                      "down_ms": launch_avg_ms(pd.execute), "swiglu_info": ps.info(), "down_info": pd.info()}
         ps.free()
         pd.free()
@@ -395,7 +396,7 @@ def dswiglu_bwd(c, steps, warmup, flush, dev):
     timed = run_interleaved({p_: [p.execute] for p_, p in plans.items()}, steps, warmup, flush)
     res = {}
     for path, p in plans.items():
-        res[path] = {"ms": float(np.mean(timed[path][0])), "info": p.info()}
+        res[path] = {"ms": float(np.median(timed[path][0])), "info": p.info()}
         p.free()
     flop = 2.0 * c.m * c.h * c.i
     f, u = res["fused"], res["unfused"]
@@ -456,11 +457,11 @@ def mlp_training_step(c, steps, warmup, flush, dev):
     timed = run_interleaved(variants, steps, warmup, flush, per_fn=True)
     res = {}
     for path, pl in plans.items():
-        res[path] = {"step_ms": float(np.mean(timed[path][0])),
-                     "per_ms": [float(np.mean(v)) for v in timed[path][1]]}
+        res[path] = {"step_ms": float(np.median(timed[path][0])),
+                     "per_ms": [float(np.median(v)) for v in timed[path][1]]}
         for p_ in pl:
             p_.free()
-    res["torch"] = {"step_ms": float(np.mean(timed["torch"][0]))}
+    res["torch"] = {"step_ms": float(np.median(timed["torch"][0]))}
     flop = 18.0 * m * hd * idim
     names = ["swiglu_aux_fwd", "down_gemm", "dswiglu", "dx_gemm_K2I", "dw_gate_up_gemm_AKM", "dw_down_gemm_AKM"]
     f, u = res["fused"], res["unfused"]
@@ -487,7 +488,7 @@ def swiglu_m_sweep(steps, warmup, flush, dev, ms=(2048, 4096, 8192, 16384)):
         plans = {path: ep.Plan(inp["x"], inp["wg"], "SWIGLU", {"b2": inp["wu"]}, b_layout="NK", path=path)
                  for path in ("fused", "unfused")}
         timed = run_interleaved({p_: [p.execute] for p_, p in plans.items()}, steps, warmup, flush)
-        res = {path: float(np.mean(timed[path][0])) for path in plans}
+        res = {path: float(np.median(timed[path][0])) for path in plans}
         for p in plans.values():
             p.free()
         tf = 4.0 * m * c.h * c.i / (res["fused"] * 1e-3) / 1e12
@@ -519,7 +520,7 @@ def autotune_vs_model(steps, warmup, flush, dev):
         r = {}
         for k, p in plans.items():
             info = p.info()
-            r[k] = {"ms": round(float(np.mean(timed[k][0])), 4),
+            r[k] = {"ms": round(float(np.median(timed[k][0])), 4),
                     "tile": info.split("tile=")[1].split()[0], "splits": int(info.split("splits=")[1].split()[0])}
             p.free()
         out[name] = r
@@ -878,7 +879,8 @@ def main():
                    "m": c3.m, "n": c3.n, "k": c3.k,
                    "cache": "cold: the step's operands (6.5 GB) exceed the 256 MB Infinity Cache"},
         "timing": "4 blocks of steps/4 back-to-back steps per variant, one HIP event pair per block, "
-                  "fused / unfused / torch blocks alternating; median/min/max are over the blocks",
+                  "fused / unfused / torch blocks alternating; ms_per_step and value are the mean over the "
+                  "blocks, median/min/max are over the blocks, speedups are ratios of the medians",
         "ms_per_step_median": round(f3["step_ms_median"], 4),
         "ms_per_step_min": round(f3["step_ms_min"], 4), "ms_per_step_max": round(f3["step_ms_max"], 4),
         "pct_peak": round(100.0 * f3["tflops_step"] / PEAK_F16_TFLOPS, 2),
