@@ -313,3 +313,60 @@ def test_gelu_special_preactivations(dtname):
                     same = (pg == pb) | (np.isnan(f64(pa)) & nan[None, :])
                     assert same.all(), f"{what}: saved pre-activation differs from P"
                 p.free()
+
+
+@pytest.mark.parametrize("path", ["fused", "unfused"])
+def test_dswiglu_special_gate_up(path):
+    """GEMM + dSwiGLU (gemm_swiglu_mlp_fusion.py docstring; the derivative is this library's
+    reading of h = silu(g) u) with special saved pre-activations: gate columns holding +-0, a
+    subnormal, +-1.5, -100 (where the logistic function underflows to 0 in fp32), +-1e4, the
+    largest finite values, +-inf and NaN; up columns holding 0, +-inf and NaN.  Where the
+    oracle's float64 value, rounded to bf16, is NaN or infinite the GPU's must be the same
+    (NaN, or the same infinity); elsewhere the output tolerance holds."""
+    require_gpu()
+    dt = torch.bfloat16
+    dev = torch.device("cuda")
+    fi = torch.finfo(dt)
+    sub = torch.tensor(1, dtype=torch.int16).view(dt).item()
+    g = torch.Generator().manual_seed(15)
+    m, n, k = M, N, K
+    dout = torch.randn((m, k), generator=g).to(dt)
+    wd = (torch.randn((k, n), generator=g) * k ** -0.5).to(dt)
+    gate = (torch.randn((m, n), generator=g) * 2).to(dt)
+    up = torch.randn((m, n), generator=g).to(dt)
+    gvals = [0.0, -0.0, sub, 1.5, -1.5, -100.0, 1e4, -1e4, fi.max, -fi.max, float("inf"), float("-inf"), float("nan")]
+    for i, v in enumerate(gvals):  # a column each, in the first tile and in the ragged last one
+        gate[:, 3 + i] = v
+        gate[:, n - 1 - i] = v
+    for i, v in enumerate([0.0, float("inf"), float("-inf"), float("nan")]):
+        up[:, 40 + i] = v
+        up[:, 60 + i] = v
+        gate[:, 60 + i] = gvals[6 + i]  # next to gates of 1e4, -1e4, +max, -max
+    d_gate_ref, d_up_ref, _ = oracle.dswiglu(f64(dout), f64(wd), f64(gate), f64(up))
+    plans = []
+    cfgs = [-1, 0, 11, 12] if path == "fused" else [-1]
+    for cfg in cfgs:
+        what = f"DSWIGLU special gate/up cfg{cfg}/{path}"
+        say(f"case {what}")
+        p, dg, aux = run_plan(dout.to(dev), wd.to(dev), "DSWIGLU", {"gate": gate.to(dev), "up": up.to(dev)}, "KN",
+                              cfg, path)
+        plans.append(p)
+        for name, got_t, ref in (("d_gate", dg, d_gate_ref), ("d_up", aux["d_up"], d_up_ref)):
+            got = f64(got_t)
+            with np.errstate(invalid="ignore", over="ignore"):
+                rounded = torch.from_numpy(ref).to(dt).double().numpy()  # ref as bf16: beyond its range -> inf
+            nonfin = ~np.isfinite(rounded)
+            both_nan = np.isnan(rounded) & np.isnan(got)
+            same_inf = np.isinf(rounded) & (got == rounded)
+            bad = np.argwhere(nonfin & ~(both_nan | same_inf))
+            assert bad.size == 0, (f"{what} {name}: {len(bad)} non-finite outputs differ, first {bad[0].tolist()}: "
+                                   f"got {got[tuple(bad[0])]!r}, want {rounded[tuple(bad[0])]!r}, "
+                                   f"gate {float(gate[tuple(bad[0])])!r}, up {float(up[tuple(bad[0])])!r}")
+            bad = np.argwhere(~nonfin & ~np.isfinite(got))
+            assert bad.size == 0, f"{what} {name}: non-finite where the oracle is finite, first {bad[0].tolist()}"
+            fin = ~nonfin
+            rms = float(np.sqrt(np.mean(ref[fin] ** 2)))
+            err = np.abs(got[fin] - ref[fin])
+            assert np.all(err <= 2e-2 * (np.abs(ref[fin]) + rms)), f"{what} {name}: finite outputs off, max err {err.max()}"
+    for p in plans:
+        p.free()
