@@ -104,7 +104,10 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
                 aux_out=aux_out, path=path, tile_cfg=cfg, split_k=split_k, bgrad_mode=bgrad_mode,
                 autotune=autotune, split_tail=split_tail)
     if split_k > 1:
-        kt = -(-k // (64 if cfg in BK64_CFGS else 32))
+        # k-step depth of the tile the plan runs (tile=BMxBNxBK...; the planner's choice when cfg is -1)
+        bk = int(p.info().split(" tile=")[1].split("x")[2].rstrip("abcdefghijklmnopqrstuvwxyz_"))
+        assert cfg < 0 or bk == (64 if cfg in BK64_CFGS else 32), p.info()
+        kt = -(-k // bk)
         per = -(-kt // min(split_k, kt))
         want = -(-kt // per)
         assert f"splits={want} " in p.info(), p.info()
