@@ -112,9 +112,11 @@ def run_and_check(epi, dtname, layout, m, n, k, cfg, path="fused", seed=0, split
         want = -(-kt // per)
         assert f"splits={want} " in p.info(), p.info()
         if split_tail and want > 1:
-            bn = 128 if epi in ("SWIGLU", "SWIGLU_AUX") else 256
-            tiles = -(-m // 256) * -(-n // bn)
-            assert f"split_tail0={tiles // 256 * 256} " in p.info(), p.info()
+            # whole rounds of the plan's own grid run unsplit (256 CUs, x2 for two-workgroup tiles)
+            info = p.info()
+            gm, gn = (int(v) for v in info.split(" grid=")[1].split()[0].split("x"))
+            slots = 256 * (2 if "_2wg" in info.split(" tile=")[1].split()[0] else 1)
+            assert f"split_tail0={gm * gn // slots * slots} " in info, info
     p.execute()
     torch.cuda.synchronize()
 
