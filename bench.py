@@ -371,7 +371,13 @@ def swiglu_fwd(c, steps, warmup, flush, dev):
         hs[path] = hh
         pd = ep.Plan(hh, wd, "DEFAULT", b_layout="NK")
         plans[path] = (ps, pd)
-    timed = run_interleaved({p_: [ps.execute, pd.execute] for p_, (ps, pd) in plans.items()}, steps, warmup, flush)
+    # vendor-library reference: hipBLASLt GEMMs and torch's elementwise ops, bf16 as given
+    def torch_step():
+        hh = torch.nn.functional.silu(x @ wg.t()) * (x @ wu.t())
+        hh @ wd.t()
+    variants = {p_: [ps.execute, pd.execute] for p_, (ps, pd) in plans.items()}
+    variants["torch"] = [torch_step]
+    timed = run_interleaved(variants, steps, warmup, flush)
     res = {}
     for path, (ps, pd) in plans.items():
         res[path] = {"step_ms": float(np.median(timed[path][0])), "swiglu_ms": launch_avg_ms(ps.execute),
@@ -383,8 +389,10 @@ def swiglu_fwd(c, steps, warmup, flush, dev):
     f["tflops_swiglu"] = flop_s / (f["swiglu_ms"] * 1e-3) / 1e12
     f["tflops_down"] = flop_d / (f["down_ms"] * 1e-3) / 1e12
     f["tflops_step"] = (flop_s + flop_d) / (f["step_ms"] * 1e-3) / 1e12
+    torch_ms = float(np.median(timed["torch"][0]))
     return {"fused": f, "unfused": u, "speedup_swiglu": u["swiglu_ms"] / f["swiglu_ms"],
-            "speedup_step": u["step_ms"] / f["step_ms"], "inputs": inp, "h": hs["fused"]}
+            "speedup_step": u["step_ms"] / f["step_ms"], "torch_step_ms": torch_ms,
+            "speedup_vs_torch": torch_ms / f["step_ms"], "inputs": inp, "h": hs["fused"]}
 
 
 def dswiglu_bwd(c, steps, warmup, flush, dev):
@@ -393,7 +401,17 @@ def dswiglu_bwd(c, steps, warmup, flush, dev):
     inp = W.dswiglu_inputs(c, device=dev)
     plans = {path: ep.Plan(inp["dout"], inp["wd"], "DSWIGLU", {"gate": inp["gate"], "up": inp["up"]},
                            b_layout="KN", path=path) for path in ("fused", "unfused")}
-    timed = run_interleaved({p_: [p.execute] for p_, p in plans.items()}, steps, warmup, flush)
+    # vendor-library reference, as autograd would run it: dh = dout Wd with hipBLASLt, then
+    # torch's own SiLU backward kernel and elementwise products, bf16 tensors throughout
+    dout, wd, gate, up = inp["dout"], inp["wd"], inp["gate"], inp["up"]
+
+    def torch_step():
+        dh = dout @ wd
+        torch.ops.aten.silu_backward(dh * up, gate)  # d_gate
+        dh * torch.nn.functional.silu(gate)           # d_up
+    variants = {p_: [p.execute] for p_, p in plans.items()}
+    variants["torch"] = [torch_step]
+    timed = run_interleaved(variants, steps, warmup, flush)
     res = {}
     for path, p in plans.items():
         res[path] = {"ms": float(np.median(timed[path][0])), "info": p.info()}
@@ -401,7 +419,9 @@ def dswiglu_bwd(c, steps, warmup, flush, dev):
     flop = 2.0 * c.m * c.h * c.i
     f, u = res["fused"], res["unfused"]
     f["tflops"] = flop / (f["ms"] * 1e-3) / 1e12
-    return {"fused": f, "unfused": u, "speedup": u["ms"] / f["ms"], "inputs": inp}
+    torch_ms = float(np.median(timed["torch"][0]))
+    return {"fused": f, "unfused": u, "speedup": u["ms"] / f["ms"], "torch_ms": torch_ms,
+            "speedup_vs_torch": torch_ms / f["ms"], "inputs": inp}
 
 
 def mlp_training_step(c, steps, warmup, flush, dev):
@@ -935,7 +955,8 @@ def main():
             "down_gemm_tflops": round(r4["fused"]["tflops_down"], 1),
             "fused_swiglu_ms": round(r4["fused"]["swiglu_ms"], 4),
             "unfused_swiglu_ms": round(r4["unfused"]["swiglu_ms"], 4),
-            "speedup_swiglu": round(r4["speedup_swiglu"], 4), "speedup_fwd_step": round(r4["speedup_step"], 4)}
+            "speedup_swiglu": round(r4["speedup_swiglu"], 4), "speedup_fwd_step": round(r4["speedup_step"], 4),
+            "torch_fwd_step_ms": round(r4["torch_step_ms"], 4), "speedup_fwd_step_vs_torch": round(r4["speedup_vs_torch"], 4)}
         if not args.no_cpu:
             large["swiglu_fwd_bf16_M2048_H5120_I17408"]["cpu_oracle_sampled"] = cpu_baseline_swiglu(
                 r4["inputs"], r4["h"], W.SWIGLU[4])
@@ -946,7 +967,8 @@ def main():
             "fused_tflops": round(r5["fused"]["tflops"], 1),
             "pct_peak": round(100 * r5["fused"]["tflops"] / PEAK_F16_TFLOPS, 2),
             "fused_ms": round(r5["fused"]["ms"], 4), "unfused_ms": round(r5["unfused"]["ms"], 4),
-            "speedup": round(r5["speedup"], 4)}
+            "speedup": round(r5["speedup"], 4), "torch_ms": round(r5["torch_ms"], 4),
+            "speedup_vs_torch": round(r5["speedup_vs_torch"], 4)}
         if not args.no_cpu:
             large["dswiglu_bwd_bf16_M16384_H5120_I17408"]["cpu_oracle_sampled"] = cpu_baseline_dswiglu(
                 r5["inputs"], W.SWIGLU[5])
