@@ -25,15 +25,16 @@ def test_algo_bytes_fwd_counts_each_operand_once():
     assert bench.algo_bytes_fwd(3, 33, 5) == 2 * (15 + 165 + 33 + 99) + 4 * 3 * 2
 
 
-@pytest.mark.parametrize("name", ["traffic_gemm_relu_aux_bias_f16_KN_65536x8192x16384.txt"])
-def test_traffic_record_matches_the_current_sources(name):
-    """The committed headline traffic record was taken on the kernel sources in the tree (else
-    bench.py reports traffic null), and its writes are the algorithmic ones."""
+@pytest.mark.parametrize("name,m,n,k", [("traffic_gemm_relu_aux_bias_f16_KN_65536x8192x16384.txt", 65536, 8192, 16384),
+                                        ("traffic_gemm_relu_aux_bias_f16_KN_4096.txt", 4096, 4096, 4096)])
+def test_traffic_record_matches_the_current_sources(name, m, n, k):
+    """The committed traffic records were taken on the kernel sources in the tree (else bench.py
+    reports their traffic null), and their writes are the algorithmic ones."""
     rec = profiling.read_record(os.path.join(ROOT, "profiles", name))
     assert rec["source_hash"] == profiling.source_hash()
     assert bench.measured_traffic(os.path.join(ROOT, "profiles", name)) is not None
-    algo = bench.algo_bytes_fwd(65536, 8192, 16384)
-    written = 2 * 65536 * 8192 + 4 * 65536 * 256
+    algo = bench.algo_bytes_fwd(m, n, k)
+    written = 2 * m * n + 4 * m * ((n + 31) // 32)
     assert abs(rec["write_bytes_per_launch"] - written) / written < 0.01
     # every operand byte is fetched at least once
     assert rec["fetch_bytes_per_launch"] >= algo - written
