@@ -20,7 +20,8 @@ import os
 
 import torch
 
-__all__ = ["Plan", "EPError", "EPILOGS", "lib", "library_path", "abi_version", "num_tile_cfgs", "validate_operands"]
+__all__ = ["Plan", "EPError", "EPILOGS", "lib", "library_path", "abi_version", "num_tile_cfgs", "validate_operands",
+           "describe_plan"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # EP_LIBRARY names another build of the same library (the host-sanitizer build the CPU tests use)
@@ -96,6 +97,10 @@ def lib():
         L.ep_abi_version.restype = ctypes.c_int
         L.ep_num_tile_cfgs.argtypes = []
         L.ep_num_tile_cfgs.restype = ctypes.c_int
+        L.ep_plan_describe.argtypes = [ctypes.POINTER(ep_shape), ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(ep_epilog_io), ctypes.POINTER(ep_options), ctypes.c_int,
+                                       ctypes.c_char_p, ctypes.c_size_t]
+        L.ep_plan_describe.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -106,6 +111,42 @@ def abi_version():
 
 def num_tile_cfgs():
     return lib().ep_num_tile_cfgs()
+
+
+def describe_plan(m, n, k, epilog="DEFAULT", dtype=torch.float16, b_layout="KN", a_layout="MK", cus=256,
+                  path="fused", bgrad_mode="two_pass", tile_cfg=-1, split_k=0, split_tail=False):
+    """The plan ep_plan_ex would make for an m x n x k GEMM with this epilog on a device with
+    `cus` compute units, as the string Plan.info() returns (ep_plan_describe: no device is
+    touched, nothing is allocated).  The operands are described by their sizes only, with
+    dense leading dimensions; the library checks the pointers it is given for alignment but
+    never reads them, so placeholder addresses stand in for them."""
+    fake = ctypes.c_void_p(1 << 20)  # non-null, 16-byte aligned, never dereferenced
+    dual = epilog in ("SWIGLU", "SWIGLU_AUX")
+    shape = ep_shape(m=m, n=n, k=k, b_layout=_LAYOUTS[b_layout], a=fake, lda=k if a_layout == "MK" else m,
+                     b=fake, ldb=n if b_layout == "KN" else k, d=fake, ldd=n, a_layout=0 if a_layout == "MK" else 1)
+    io = ep_epilog_io()
+    if epilog in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS", "GELU_AUX_BIAS"):
+        io.bias = fake
+    if epilog == "RELU_AUX_BIAS":
+        io.relu_aux = fake
+    if epilog in ("DRELU_BGRAD", "DGELU_BGRAD"):
+        io.bgrad = fake
+    if epilog == "DRELU_BGRAD":
+        io.relu_aux_in = fake
+    if epilog in ("GELU_AUX_BIAS", "DGELU_BGRAD"):
+        io.gelu_aux = fake
+    if dual:
+        io.b2 = fake
+    if epilog in ("DSWIGLU", "SWIGLU_AUX"):
+        io.d2 = fake
+    if epilog == "DSWIGLU":
+        io.gate, io.up = fake, fake
+    opt = ep_options(path=_PATHS[path], bgrad_mode=_BGRAD[bgrad_mode], tile_cfg=tile_cfg, split_k=split_k,
+                     split_tail=int(bool(split_tail)), autotune=0)
+    buf = ctypes.create_string_buffer(1024)
+    _check(lib().ep_plan_describe(ctypes.byref(shape), _DTYPES[dtype], EPILOGS[epilog], ctypes.byref(io),
+                                  ctypes.byref(opt), cus, buf, len(buf)))
+    return buf.value.decode()
 
 
 def _check(status):

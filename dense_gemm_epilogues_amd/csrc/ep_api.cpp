@@ -877,6 +877,9 @@ ep_status launch_plan(const ep_plan_s* h, hipStream_t s) {
   return EP_OK;
 }
 
+// the plan's description, as ep_plan_info and ep_plan_describe write it
+void describe(const ep_plan_s* h, char* buf, size_t n);
+
 }  // namespace
 
 extern "C" {
@@ -1006,6 +1009,29 @@ ep_status ep_free(ep_handle h) {
 ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
   if (!h || h->magic != kMagic) return fail(EP_ERR_INVALID_ARG, "invalid or freed handle");
   if (!buf || n == 0) return fail(EP_ERR_INVALID_ARG, "buffer is NULL or empty");
+  describe(h, buf, n);
+  return EP_OK;
+}
+
+ep_status ep_plan_describe(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_epilog_io* io,
+                           const ep_options* opt_in, int cus, char* buf, size_t n) {
+  t_last_error.clear();
+  if (!buf || n == 0) return fail(EP_ERR_INVALID_ARG, "buffer is NULL or empty");
+  if (cus < 1 || cus > 65536) return fail(EP_ERR_INVALID_ARG, "cus %d is not in 1..65536", cus);
+  ep_status st = validate(s, dtype, epi, io, opt_in);
+  if (st != EP_OK) return st;
+  const ep_options opt = opt_in ? *opt_in : ep_options{EP_PATH_FUSED, EP_BGRAD_TWO_PASS, -1, 0, 0};
+  if (opt.autotune) return fail(EP_ERR_INVALID_ARG, "autotune times kernels on the device; not available here");
+  ep_plan_s h{};  // planned on the stack, never bound to a workspace or launched
+  if ((st = plan_into(&h, s, dtype, epi, io, opt, -1, cus, SIZE_MAX)) != EP_OK) return st;
+  describe(&h, buf, n);
+  return EP_OK;
+}
+
+}  // extern "C"
+
+namespace {
+void describe(const ep_plan_s* h, char* buf, size_t n) {
   const ep_shape& s = h->shape;
   const char* dt = h->dtype == EP_F16 ? "f16" : "bf16";
   const char* lay = s.a_layout == EP_A_KM ? (s.b_layout == EP_B_KN ? "A^T,KN" : "A^T,NK")
@@ -1046,7 +1072,5 @@ ep_status ep_plan_info(ep_handle h, char* buf, size_t n) {
            kEpiNames[h->epilog], h->opt.path == EP_PATH_FUSED ? "fused" : "unfused", dt, lay, (long long)s.m,
            (long long)s.n, (long long)s.k, kTileCfgs[h->cfg].name, h->cfg, h->args.tiles_m, h->args.tiles_n,
            h->splits, h->args.tail0, h->workspace_bytes, kern.c_str(), extra.c_str());
-  return EP_OK;
 }
-
-}  // extern "C"
+}  // namespace

@@ -36,7 +36,8 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 2
+/* 3: ep_options.split_tail, ep_execute_noalloc and ep_plan_describe; 2: ep_options.split_k */
+#define EP_ABI_VERSION 3
 
 typedef struct ep_plan_s* ep_handle;
 
@@ -261,6 +262,19 @@ const char* ep_last_error(void);
 /* Writes a NUL-terminated description (tile configuration, grid, workspace bytes, kernel
  * names) into buf[0..n-1]; truncates to fit. */
 ep_status ep_plan_info(ep_handle h, char* buf, size_t n);
+
+/* ep_plan_describe: the plan ep_plan_ex would make for these arguments on a device with `cus`
+ * compute units, written into buf[0..n-1] as ep_plan_info writes a plan's description
+ * (tile configuration, grid, splits, workspace bytes, kernels).  It makes no HIP call and
+ * allocates nothing: the arguments are validated as ep_plan_ex validates them (so operand
+ * pointers must be non-null and 16-byte aligned where ep_plan_ex requires it), but no pointer
+ * is dereferenced.  For capacity planning, and for checking the planner's choices on a host
+ * without a GPU (the plan/execute split of "Fusing Matmul Epilogs with nvmath-python", "The
+ * problem addressed by fused epilogs": the planning step alone).  Errors: those of
+ * ep_plan_ex's validation; EP_ERR_INVALID_ARG if buf is NULL, n is 0, cus is not in
+ * 1..65536 or opt->autotune is set (autotuning times kernels on the device). */
+ep_status ep_plan_describe(const ep_shape* shape, ep_dtype dtype, ep_epilog epilog, const ep_epilog_io* io,
+                           const ep_options* opt, int cus, char* buf, size_t n);
 
 /* Number of selectable tile configurations (valid ep_options.tile_cfg values). */
 int ep_num_tile_cfgs(void);

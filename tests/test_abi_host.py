@@ -42,7 +42,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.ep_abi_version() == 2
+    assert L.ep_abi_version() == 3
     from tests.test_parity_small_gpu import NUM_TILE_CFGS
     assert L.ep_num_tile_cfgs() == NUM_TILE_CFGS
     for code, name in ep.STATUS.items():

@@ -1,9 +1,10 @@
 """The C ABI's host tests under AddressSanitizer and UndefinedBehaviorSanitizer (CPU only).
 
-The validation path of ep_plan / ep_execute / ep_free / ep_plan_info is host code: it is built
-a second time with both sanitizers (build.build_host_sanitized, g++), loaded through the
-binding's EP_LIBRARY override, and tests/test_abi_host.py runs against it in a child process
-with the sanitizer runtimes preloaded.  Any sanitizer report aborts the child.  (Reading an
+The validation path of ep_plan / ep_execute / ep_free / ep_plan_info and the planner behind
+ep_plan_describe are host code: they are built a second time with both sanitizers
+(build.build_host_sanitized, g++), loaded through the binding's EP_LIBRARY override, and
+tests/test_abi_host.py and tests/test_planner_host.py run against it in a child process with
+the sanitizer runtimes preloaded.  Any sanitizer report aborts the child.  (Reading an
 out-of-range value from an enum-typed field was one such report, now fixed by reading the
 raw int.)
 """
@@ -37,7 +38,7 @@ def test_abi_host_tests_under_asan_and_ubsan():
                            cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=120)
     assert probe.returncode == 0 and probe.stdout.strip().endswith(os.path.basename(lib)), probe.stdout[-2000:]
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", "-m", "not gpu",
-                        os.path.join(ROOT, "tests", "test_abi_host.py")],
+                        os.path.join(ROOT, "tests", "test_abi_host.py"), os.path.join(ROOT, "tests", "test_planner_host.py")],
                        cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=600)
     out = r.stdout
     assert "runtime error" not in out and "ERROR: AddressSanitizer" not in out, out[-4000:]
