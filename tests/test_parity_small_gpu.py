@@ -487,3 +487,41 @@ def test_tiny_linear_layer_config():
     assert_bgrad(aux3["drelu_bgrad"].cpu().numpy(), bgref, "cfg1 bgrad")
     for p in (p1, p2, p3):
         p.free()
+
+
+@pytest.mark.parametrize("m,n,k,epi,dtname,layout,a_layout", [
+    (65536, 8192, 16384, "RELU_AUX_BIAS", "f16", "KN", "MK"),
+    (65536, 16384, 8192, "DRELU_BGRAD", "f16", "NK", "MK"),
+    (2048, 17408, 5120, "SWIGLU", "bf16", "NK", "MK"),
+    (2048, 17408, 5120, "DSWIGLU", "bf16", "KN", "MK"),
+    (2048, 5120, 17408, "DEFAULT", "bf16", "NK", "MK"),
+    (34816, 5120, 2048, "DEFAULT", "bf16", "KN", "KM"),
+    (4096, 4096, 4096, "GELU_AUX_BIAS", "f16", "KN", "MK"),
+    (300, 200, 136, "DGELU_BGRAD", "f16", "NK", "MK"),
+])
+def test_describe_matches_plan(m, n, k, epi, dtname, layout, a_layout):
+    """ep_plan_describe at this device's CU count states exactly the plan ep_plan_ex makes
+    (tile configuration, grid, splits, tail split, workspace, kernels)."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev = torch.device("cuda")
+    dt = DTYPES[dtname]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    a = torch.empty((m, k) if a_layout == "MK" else (k, m), dtype=dt, device=dev)
+    b = torch.empty((k, n) if layout == "KN" else (n, k), dtype=dt, device=dev)
+    ins = {}
+    if epi in ("RELU_AUX_BIAS", "GELU_AUX_BIAS"):
+        ins["bias"] = torch.empty(n, dtype=dt, device=dev)
+    if epi == "DRELU_BGRAD":
+        ins["relu_aux"] = torch.empty((m, (n + 31) // 32), dtype=torch.int32, device=dev)
+    if epi == "DGELU_BGRAD":
+        ins["gelu_aux"] = torch.empty((m, n), dtype=dt, device=dev)
+    if epi == "SWIGLU":
+        ins["b2"] = torch.empty_like(b)
+    if epi == "DSWIGLU":
+        ins["gate"], ins["up"] = torch.empty((m, n), dtype=dt, device=dev), torch.empty((m, n), dtype=dt, device=dev)
+    p = ep.Plan(a, b, epi, ins or None, b_layout=layout, a_layout=a_layout)
+    want = ep.describe_plan(m, n, k, epi, dt, b_layout=layout, a_layout=a_layout, cus=cus)
+    say(f"case describe {epi} {m}x{n}x{k}: {want}")
+    assert p.info() == want, (p.info(), want)
+    p.free()
