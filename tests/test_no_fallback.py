@@ -54,3 +54,21 @@ def test_bench_uses_the_oracle_only_for_the_cpu_baseline():
         if uses:
             assert fn.name.startswith(("cpu_baseline", "cpu_oracle")), fn.name
     assert not any(isinstance(n, ast.Import) and any(a.name == "oracle" for a in n.names) for n in tree.body)
+
+
+def test_oracle_is_independent_of_the_product():
+    """The oracle imports numpy and scipy only: neither the library, its binding, torch nor the
+    input generators (which both sides share)."""
+    for name in sorted(os.listdir(os.path.join(ROOT, "oracle"))):
+        if not name.endswith(".py"):
+            continue
+        tree = ast.parse(open(os.path.join(ROOT, "oracle", name)).read())
+        for node in ast.walk(tree):
+            if isinstance(node, ast.Import):
+                mods = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                mods = [node.module or ""] if node.level == 0 else []
+            else:
+                continue
+            for m in mods:
+                assert m.split(".")[0] in ("numpy", "scipy", "math", "fractions", "json", "os"), f"oracle/{name} imports {m}"
