@@ -224,10 +224,12 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
 // (3 splits) and 0.357 ms unsplit; the register-staged one remains the choice there when K is
 // not a multiple of 64.
 //
-// Where B is given K x N (and A M x K), the 64-deep form with two barriers per k-step
-// (configuration 12) is taken except for long K loops over many rounds: 2-7 % faster on the
-// SwiGLU-MLP GEMMs (K 5120 at M 2048 and 16384, the split dx GEMM at K 34816) and the square
-// layer, 0.5-1 % slower on the 65536 x 8192 x 16384 forward (K 16384, 32 rounds).
+// Where B is given K x N, the 64-deep form with two barriers per k-step (configuration 12)
+// is taken except for long K loops over many rounds: 2-7 % faster on the SwiGLU-MLP GEMMs (K
+// 5120 at M 2048 and 16384, the split dx GEMM at K 34816) and the square layer, 0.5-1 %
+// slower on the 65536 x 8192 x 16384 forward (K 16384, 32 rounds).  With A given K x M as
+// well (the weight gradients, K 2048) it measured 2-2.5 % faster at 5120 x 17408 and
+// 34816 x 5120 and on par at 17408 x 5120; with A K x M and B N x K, 0.2-0.6 % slower.
 constexpr int kVstCfg = 8;
 constexpr int kM16SpreadCfg = 9;
 constexpr int kM16RowsCfg = 10;
@@ -236,8 +238,7 @@ constexpr int kM16Deep2BarCfg = 12;
 int pick_cfg(const ep_shape* s, int model_cfg, int cus, bool dual) {
   if (model_cfg != 0) return model_cfg;
   const int64_t tiles = ((s->m + 255) / 256) * ((s->n + 255) / 256);
-  if (cfg_fits_k(kM16DeepCfg, s->k) && s->b_layout == EP_B_KN && s->a_layout == EP_A_MK &&
-      !(s->k >= 8192 && tiles >= 8 * (int64_t)cus))
+  if (cfg_fits_k(kM16DeepCfg, s->k) && s->b_layout == EP_B_KN && !(s->k >= 8192 && tiles >= 8 * (int64_t)cus))
     return kM16Deep2BarCfg;
   if (cfg_fits_k(kM16DeepCfg, s->k)) return kM16DeepCfg;
   if (!dual && s->a_layout == EP_A_MK && s->b_layout == EP_B_NK && tiles < cus) return kVstCfg;

@@ -57,6 +57,19 @@ def test_split_choice_transposed_a_and_ragged_k():
         assert (f["tile_cfg"], f["splits"]) == (str(cfg), "3"), f
 
 
+@pytest.mark.parametrize("m,n,k,layout,want_cfg", [
+    (5120, 17408, 2048, "KN", 12),   # dW_down = dout^T h: two barriers per k-step for K x N B
+    (34816, 5120, 2048, "KN", 12),   # [dW_gate; dW_up] = [d_gate | d_up]^T x
+    (34816, 5120, 2048, "NK", 11),   # ... with B given N x K: one barrier
+    (65536, 8192, 16384, "KN", 11),  # long K over many rounds: one barrier
+])
+def test_tile_choice_transposed_a(m, n, k, layout, want_cfg):
+    """A given K x M (weight gradients) takes the 64-deep configurations by the B layout's
+    rule, as A given M x K does."""
+    f = fields(ep.describe_plan(m, n, k, "DEFAULT", BF16, b_layout=layout, a_layout="KM"))
+    assert (f["tile_cfg"], f["splits"]) == (str(want_cfg), "1"), f
+
+
 def test_headline_plans():
     """The H200-shape layer step: forward RELU_AUX_BIAS on configuration 11 over 256 x 32
     tiles, unsplit, no workspace; backward DRELU_BGRAD on configuration 11 over 256 x 64 tiles
