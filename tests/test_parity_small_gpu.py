@@ -458,6 +458,17 @@ def test_unfused_rows_past_grid_limit(epi):
                   path="unfused")
 
 
+@pytest.mark.parametrize("epi", ["DRELU_BGRAD", "DGELU_BGRAD"])
+def test_bgrad_over_many_partial_rows(epi):
+    """The two-pass bias gradient's second pass splits the partial rows (one per 256-row tile)
+    over 16 groups of 8 loads, 64 columns per workgroup: 131 partial rows (more than one pass
+    of 128, a ragged last group) and N = 200 (a workgroup with 8 of its 64 columns), against
+    the oracle in full."""
+    require_gpu()
+    run_and_check(epi, "f16", "NK", 131 * 256 - 216, 200, 64, -1)
+    run_and_check(epi, "bf16", "KN", 131 * 256 - 216, 200, 72, 8)
+
+
 def test_tiny_linear_layer_config():
     """The tiny fp16 linear layer: X 32x128, W 128x64, bias 64; backward dY 32x64 masked by a
     separate 32x128 pre-activation's relu_aux."""
