@@ -1,0 +1,161 @@
+"""GPU parity at the largest leading dimensions the C ABI accepts (every ld < 2^22 elements,
+ld_aux < 2^22 words).
+
+The kernels address a tile's rows with 32-bit offsets from a per-tile or per-slab base and
+clamp each buffer extent below 2^31 bytes; a 256-row tile at ld = 2^22 - 8 spans 256 * ld * 2
+= 2,147,479,552 bytes, just inside that extent.  Each case keeps every operand at the maximum
+row stride (a few GiB per buffer), fills every byte outside the logical matrices with NaN or
+a sentinel, and checks the results against the oracle and the padding for stray writes.
+(Epilogs as in "Fusing Matmul Epilogs with nvmath-python"; dSwiGLU as in the
+gemm_swiglu_mlp_fusion.py docstring.)"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests._gpu import assert_bgrad, assert_half, f64, require_gpu, say, words
+
+pytestmark = pytest.mark.gpu
+
+LD = (1 << 22) - 8        # largest element leading dimension (a multiple of 8 below 2^22)
+LD_AUX = (1 << 22) - 1    # largest mask leading dimension, in 32-bit words
+M, N, K = 300, 200, 72    # two tile rows (the first a full 256 rows), ragged N and K
+SENT16 = 0x7A5A           # a finite fp16 / bf16 bit pattern no kernel writes here by chance
+SENT32 = 0x5A5A5A5A
+
+
+def strided(rows, cols, ld, dt, dev, fill):
+    """a rows x cols view with row stride ld into a buffer filled with `fill`, and the buffer"""
+    buf = torch.full((rows, ld), fill, dtype=dt, device=dev)
+    return buf[:, :cols], buf
+
+
+def put(view, src):
+    view.copy_(src.to(view.device))
+    return view
+
+
+def randn(shape, seed, scale, dt):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(dt)
+
+
+def untouched16(buf, cols):
+    return bool((buf[:, cols:].view(torch.int16) == SENT16).all().item())
+
+
+def free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("path", ["fused", "unfused"])
+def test_relu_aux_bias_at_max_ld(path):
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev, dt = torch.device("cuda"), torch.float16
+    say(f"case max-ld RELU_AUX_BIAS f16 KN path={path} m={M} n={N} k={K} ld={LD} ld_aux={LD_AUX}")
+    x_h, w_h = randn((M, K), 1, 1.0, dt), randn((K, N), 2, K ** -0.5, dt)
+    bias_h = randn((N,), 3, 0.1, dt)
+    x, _ = strided(M, K, LD, dt, dev, float("nan"))
+    w, _ = strided(K, N, LD, dt, dev, float("nan"))
+    put(x, x_h), put(w, w_h)
+    bias = bias_h.to(dev)
+    out, obuf = strided(M, N, LD, torch.int16, dev, SENT16)
+    out, obuf = out.view(dt), obuf.view(dt)
+    aux, abuf = strided(M, (N + 31) // 32, LD_AUX, torch.int32, dev, SENT32)
+    p = ep.Plan(x, w, "RELU_AUX_BIAS", {"bias": bias}, b_layout="KN", out=out, aux_out={"relu_aux": aux}, path=path)
+    p.execute()
+    torch.cuda.synchronize()
+    yref, _, pre = oracle.relu_aux_bias(f64(x_h), f64(w_h), f64(bias_h), "KN")
+    assert_half(f64(out.contiguous()), yref, f"max-ld RELU_AUX_BIAS {path} Y")
+    got = words(aux.contiguous())
+    ok, info = oracle.check_mask(got, pre)
+    assert ok, f"max-ld RELU_AUX_BIAS {path} mask: {info}"
+    assert untouched16(obuf, N), "a write outside Y"
+    assert bool((abuf[:, (N + 31) // 32:] == SENT32).all().item()), "a write outside relu_aux"
+    p.free()
+    del x, w, out, obuf, aux, abuf
+    free()
+
+
+def test_drelu_bgrad_at_max_ld():
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev, dt = torch.device("cuda"), torch.bfloat16
+    say(f"case max-ld DRELU_BGRAD bf16 NK m={M} n={N} k={K} ld={LD} ld_aux={LD_AUX}")
+    dy_h, w_h = randn((M, K), 4, 1.0, dt), randn((N, K), 5, K ** -0.5, dt)
+    mask_h = torch.from_numpy(oracle.pack_relu_mask(randn((M, N), 6, 1.0, torch.float32).numpy() > 0)
+                              .view(np.int32).copy())
+    dy, _ = strided(M, K, LD, dt, dev, float("nan"))
+    w, _ = strided(N, K, LD, dt, dev, float("nan"))
+    put(dy, dy_h), put(w, w_h)
+    mask, _ = strided(M, mask_h.shape[1], LD_AUX, torch.int32, dev, -1)
+    put(mask, mask_h)
+    out, obuf = strided(M, N, LD, torch.int16, dev, SENT16)
+    out, obuf = out.view(dt), obuf.view(dt)
+    for bgrad_mode in ("two_pass", "atomic"):
+        p = ep.Plan(dy, w, "DRELU_BGRAD", {"relu_aux": mask}, b_layout="NK", out=out, bgrad_mode=bgrad_mode)
+        _, auxo = p.execute()
+        torch.cuda.synchronize()
+        dref, bref = oracle.drelu_bgrad(f64(dy_h), f64(w_h), "NK", words(mask_h))
+        assert_half(f64(out.contiguous()), dref, f"max-ld DRELU_BGRAD {bgrad_mode} dX")
+        assert_bgrad(auxo["drelu_bgrad"].cpu().numpy().astype(np.float64), bref, f"max-ld DRELU_BGRAD {bgrad_mode} bgrad")
+        assert untouched16(obuf, N), "a write outside dX"
+        p.free()
+    del dy, w, mask, out, obuf
+    free()
+
+
+@pytest.mark.parametrize("split_k", [1, 2])
+def test_transposed_a_at_max_ld(split_k):
+    """A given K x M (a weight gradient's activation; M a multiple of 8) at the maximum
+    stride, B K x N too."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev, dt = torch.device("cuda"), torch.float16
+    m, k = M - 4, K * 4
+    say(f"case max-ld DEFAULT A^T f16 KN m={m} n={N} k={k} ld={LD} split={split_k}")
+    at_h, b_h = randn((k, m), 7, 1.0, dt), randn((k, N), 8, k ** -0.5, dt)
+    at, _ = strided(k, m, LD, dt, dev, float("nan"))
+    b, _ = strided(k, N, LD, dt, dev, float("nan"))
+    put(at, at_h), put(b, b_h)
+    out, obuf = strided(m, N, LD, torch.int16, dev, SENT16)
+    out, obuf = out.view(dt), obuf.view(dt)
+    p = ep.Plan(at, b, "DEFAULT", b_layout="KN", out=out, a_layout="KM", split_k=split_k)
+    p.execute()
+    torch.cuda.synchronize()
+    assert_half(f64(out.contiguous()), oracle.matmul(f64(at_h).T, f64(b_h), "KN"), f"max-ld A^T split {split_k}")
+    assert untouched16(obuf, N), "a write outside D"
+    p.free()
+    del at, b, out, obuf
+    free()
+
+
+def test_dswiglu_at_max_ld():
+    """dout · Wd with gate, up, d_gate and d_up all at the maximum row stride."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev, dt = torch.device("cuda"), torch.bfloat16
+    say(f"case max-ld DSWIGLU bf16 KN m={M} n={N} k={K} ld={LD}")
+    dout_h, wd_h = randn((M, K), 9, 1.0, dt), randn((K, N), 10, K ** -0.5, dt)
+    gate_h, up_h = randn((M, N), 11, 1.0, dt), randn((M, N), 12, 1.0, dt)
+    dout, _ = strided(M, K, LD, dt, dev, float("nan"))
+    wd, _ = strided(K, N, LD, dt, dev, float("nan"))
+    gate, _ = strided(M, N, LD, dt, dev, float("nan"))
+    up, _ = strided(M, N, LD, dt, dev, float("nan"))
+    for v, h in ((dout, dout_h), (wd, wd_h), (gate, gate_h), (up, up_h)):
+        put(v, h)
+    dg, dgbuf = strided(M, N, LD, torch.int16, dev, SENT16)
+    du, dubuf = strided(M, N, LD, torch.int16, dev, SENT16)
+    dg, dgbuf, du, dubuf = dg.view(dt), dgbuf.view(dt), du.view(dt), dubuf.view(dt)
+    p = ep.Plan(dout, wd, "DSWIGLU", {"gate": gate, "up": up}, b_layout="KN", out=dg, aux_out={"d_up": du})
+    p.execute()
+    torch.cuda.synchronize()
+    dg_ref, du_ref, _ = oracle.dswiglu(f64(dout_h), f64(wd_h), f64(gate_h), f64(up_h), "KN")
+    assert_half(f64(dg.contiguous()), dg_ref, "max-ld DSWIGLU d_gate")
+    assert_half(f64(du.contiguous()), du_ref, "max-ld DSWIGLU d_up")
+    assert untouched16(dgbuf, N) and untouched16(dubuf, N), "a write outside d_gate / d_up"
+    p.free()
+    del dout, wd, gate, up, dg, dgbuf, du, dubuf
+    free()
