@@ -47,8 +47,9 @@ __device__ __forceinline__ float sigmoid_f(float t) {
 }
 
 // Row-tiled launch shape shared by the elementwise kernels: blockIdx.y walks rows (grid-stride
-// past 65535), blockIdx.x covers a row's 8-column groups, kGroups groups per thread, kEwThreads
-// apart (each thread loads all of its groups before using any).  No integer division.
+// past 65535; the row index is 64-bit, since a row count up to 2^31 - 1 plus the stride would
+// overflow an int), blockIdx.x covers a row's 8-column groups, kGroups groups per thread,
+// kEwThreads apart (each thread loads all of its groups before using any).  No integer division.
 constexpr int kEwThreads = 256;
 constexpr int kGroups = 2;
 
@@ -59,7 +60,7 @@ __device__ __forceinline__ int group_of(int u) {
 template <int DT>
 __global__ void bias_add_kernel(char* z, int64_t ldz, const char* bias, int M, int N) {
   const int gpr = N / 8;
-  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
     char* zr = z + (int64_t)row * ldz * 2;
     u32x4 w[kGroups], bw[kGroups];
 #pragma unroll
@@ -93,7 +94,7 @@ __global__ void relu_pack_kernel(const char* z, int64_t ldz, char* y, int64_t ld
                                  int64_t ld_aux, int M, int N, int with_mask) {
   const int nw = (N + 31) / 32;
   const int gpr = nw * 4;
-  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
     const char* zr = z + (int64_t)row * ldz * 2;
     char* yr = y + (int64_t)row * ldy * 2;
     u32x4 w[kGroups];
@@ -131,7 +132,7 @@ template <int DT>
 __global__ void mask_apply_kernel(const char* gsrc, int64_t ldg, const uint32_t* aux, int64_t ld_aux,
                                   char* dx, int64_t lddx, int M, int N) {
   const int gpr = N / 8;
-  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
     const char* gr = gsrc + (int64_t)row * ldg * 2;
     const uint32_t* ar = aux + (int64_t)row * ld_aux;
     u32x4 w[kGroups];
@@ -167,14 +168,14 @@ template <int DT>
 __global__ void colsum_partial_kernel(const char* x, int64_t ldx, float* part, int M, int N, int rpb) {
   const int col = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (col >= N) return;
-  const int r0 = blockIdx.y * rpb;
-  const int r1 = min(M, r0 + rpb);
+  const int64_t r0 = (int64_t)blockIdx.y * rpb;
+  const int64_t r1 = r0 + rpb < M ? r0 + rpb : M;
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int rb = r0; rb < r1; rb += 8) {
+  for (int64_t rb = r0; rb < r1; rb += 8) {
     u32x4 w[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (rb + u < r1) w[u] = *(const u32x4*)(x + ((int64_t)(rb + u) * ldx + col) * 2);
+      if (rb + u < r1) w[u] = *(const u32x4*)(x + ((rb + u) * ldx + col) * 2);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (rb + u < r1) {
@@ -197,13 +198,23 @@ __global__ void colsum_partial_kernel(const char* x, int64_t ldx, float* part, i
 // and N / 64 workgroups spread the 4 * nparts * N bytes over the chip (one thread per column
 // quad over all partials left most CUs idle and paid one round trip per 8 partials: 47 us for
 // 256 x 16384 partials).
+// Both sums are compensated (Kahan's summation: each addition's rounding error is carried
+// into the next addend), so the result stays within a few float32 roundings of the partials'
+// exact sum however many partials there are; plain float32 sums of the 8.4 million partials of
+// a 2^31-row matrix, 524288 per row group, drift by about 1e-3 relative.
 constexpr int kBgColsPerBlock = 64;
 constexpr int kBgGroups = kEwThreads / (kBgColsPerBlock / 4);
+__device__ __forceinline__ void kahan_add(f32x4& s, f32x4& c, f32x4 v) {
+  const f32x4 y = v - c;
+  const f32x4 t = s + y;
+  c = (t - s) - y;
+  s = t;
+}
 __global__ __launch_bounds__(kEwThreads) void bgrad_reduce_kernel(const float* part, int nparts, float* bgrad, int N) {
   __shared__ f32x4 red[kBgGroups][kBgColsPerBlock / 4];
   const int q = threadIdx.x % (kBgColsPerBlock / 4), g = threadIdx.x / (kBgColsPerBlock / 4);
   const int col = blockIdx.x * kBgColsPerBlock + q * 4;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  f32x4 s = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
   if (col < N) {
     for (int t0 = g; t0 < nparts; t0 += kBgGroups * 8) {
       f32x4 v[8];
@@ -212,16 +223,16 @@ __global__ __launch_bounds__(kEwThreads) void bgrad_reduce_kernel(const float* p
         if (t0 + kBgGroups * u < nparts) v[u] = *(const f32x4*)(part + (int64_t)(t0 + kBgGroups * u) * N + col);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (t0 + kBgGroups * u < nparts) s += v[u];
+        if (t0 + kBgGroups * u < nparts) kahan_add(s, c, v[u]);
     }
   }
-  red[g][q] = s;
+  red[g][q] = s - c;
   __syncthreads();
   if (g == 0 && col < N) {
-    f32x4 r = red[0][q];
+    f32x4 r = red[0][q], rc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 1; i < kBgGroups; ++i) r += red[i][q];
-    *(f32x4*)(bgrad + col) = r;
+    for (int i = 1; i < kBgGroups; ++i) kahan_add(r, rc, red[i][q]);
+    *(f32x4*)(bgrad + col) = r - rc;
   }
 }
 
@@ -233,7 +244,7 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
 template <int DT>
 __global__ void silu_mul_kernel(const char* g, const char* u, int64_t ldgu, char* h, int64_t ldh, int M, int N) {
   const int gpr = N / 8;
-  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
     const int64_t ro = (int64_t)row * ldgu * 2;
     u32x4 wg[kGroups], wu[kGroups];
 #pragma unroll
@@ -263,7 +274,7 @@ template <int DT>
 __global__ void dswiglu_kernel(const char* dh, int64_t lddh, const char* gate, const char* up, int64_t ld_gu,
                                char* dg, int64_t lddg, char* du, int64_t lddu, int M, int N) {
   const int gpr = N / 8;
-  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
     u32x4 wd[kGroups], wg[kGroups], wu[kGroups];
 #pragma unroll
     for (int q = 0; q < kGroups; ++q) {
@@ -300,7 +311,7 @@ __global__ void dswiglu_kernel(const char* dh, int64_t lddh, const char* gate, c
 template <int DT>
 __global__ void gelu_apply_kernel(char* z, int64_t ldz, char* aux, int64_t ld_aux, int M, int N) {
   const int gpr = N / 8;
-  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
     char* zr = z + (int64_t)row * ldz * 2;
     u32x4 w[kGroups];
 #pragma unroll
@@ -327,7 +338,7 @@ __global__ void gelu_apply_kernel(char* z, int64_t ldz, char* aux, int64_t ld_au
 template <int DT>
 __global__ void dgelu_apply_kernel(char* g, int64_t ldg, const char* aux, int64_t ld_aux, int M, int N) {
   const int gpr = N / 8;
-  for (int row = blockIdx.y; row < M; row += gridDim.y) {
+  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
     char* gr = g + (int64_t)row * ldg * 2;
     u32x4 wg[kGroups], wa[kGroups];
 #pragma unroll
@@ -400,7 +411,7 @@ hipError_t launch_mask_apply(int dtype, const void* g, int64_t ldg, const uint32
 
 hipError_t launch_colsum_partial(int dtype, const void* x, int64_t ldx, float* part, int M, int N, int rpb,
                                  hipStream_t s) {
-  const dim3 grid((N / 8 + kEwThreads - 1) / kEwThreads, (M + rpb - 1) / rpb);
+  const dim3 grid((N / 8 + kEwThreads - 1) / kEwThreads, (unsigned)(((int64_t)M + rpb - 1) / rpb));
   EP_DT_DISPATCH(dtype, hipLaunchKernelGGL(colsum_partial_kernel<DTV>, grid, dim3(kEwThreads), 0, s,
                                            (const char*)x, ldx, part, M, N, rpb));
   return hipGetLastError();

@@ -105,6 +105,8 @@ namespace {
 constexpr uint64_t kMagic = 0x6570706c616e3031ULL;  // "epplan01"
 constexpr uint64_t kDead = 0xdeadbeefdeadbeefULL;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+// threads per workgroup of the GEMM kernels (kThreads of gemm_kernel.hpp)
+constexpr int64_t kGemmWgThreads = 256;
 constexpr int64_t kMaxLd = (int64_t)1 << 22;
 
 thread_local std::string t_last_error;
@@ -703,6 +705,12 @@ ep_status plan_into(ep_plan_s* h, const ep_shape* s, ep_dtype dtype, ep_epilog e
     if (!h->launch_partial || !h->launch_fixup)
       return fail(EP_ERR_INTERNAL, "no split-K kernel instantiated for this combination");
   }
+  // one launch counts its work-items in 32 bits: the largest of the plan's GEMM grids (the
+  // whole-K tiles, or every split range of the split tiles) must stay below 2^32 threads
+  const int64_t blocks = splits > 1 ? std::max<int64_t>(tail0, (ntiles - tail0) * splits) : ntiles;
+  if (blocks * kGemmWgThreads > (int64_t)UINT32_MAX)
+    return fail(EP_ERR_UNSUPPORTED, "a grid of %lld workgroups of %lld threads exceeds one launch's 2^32 work-items",
+                (long long)blocks, (long long)kGemmWgThreads);
   h->part_bytes = part_bytes;
   h->z_bytes = z_bytes;
   h->kpart_bytes = kpart_of(splits);

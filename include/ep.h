@@ -203,6 +203,8 @@ typedef struct {
  * are non-null and the ones it does not use are null; a, b, b2, d, d2, bias, gate, up are
  * 16-byte aligned and relu_aux/relu_aux_in/bgrad 4-byte aligned; every leading dimension is
  * a multiple of 8 elements, at least the row length and below 2^22; ld_aux >= ceil(n/32).
+ * A plan whose GEMM grid would need 2^32 or more threads in one launch (for instance m near
+ * 2^31 with a 128-row tile configuration) is EP_ERR_UNSUPPORTED.
  * Returns EP_ERR_INVALID_ARG or EP_ERR_UNSUPPORTED on a failed check and EP_ERR_HIP when no
  * HIP device is usable.  On success *out is a new handle, otherwise *out is set to NULL.
  */

@@ -1,12 +1,16 @@
-"""GPU parity at the largest leading dimensions the C ABI accepts (every ld < 2^22 elements,
-ld_aux < 2^22 words).
+"""GPU parity at the largest sizes the C ABI accepts: every leading dimension at its maximum
+(ld < 2^22 elements, ld_aux < 2^22 words), and M = 2^31 - 1 rows.
 
 The kernels address a tile's rows with 32-bit offsets from a per-tile or per-slab base and
 clamp each buffer extent below 2^31 bytes; a 256-row tile at ld = 2^22 - 8 spans 256 * ld * 2
-= 2,147,479,552 bytes, just inside that extent.  Each case keeps every operand at the maximum
-row stride (a few GiB per buffer), fills every byte outside the logical matrices with NaN or
-a sentinel, and checks the results against the oracle and the padding for stray writes.
-(Epilogs as in "Fusing Matmul Epilogs with nvmath-python"; dSwiGLU as in the
+= 2,147,479,552 bytes, just inside that extent.  Each such case keeps every operand at the
+maximum row stride (a few GiB per buffer), fills every byte outside the logical matrices
+with NaN or a sentinel, and checks the results against the oracle and the padding for stray
+writes.  At M = 2^31 - 1 (N = K = 8: 32 GiB per operand) tile and row indices reach the top
+of the 32-bit range; the rows repeat a 7-row pattern, so that every one of the 2^31 - 1 output
+rows is checked bit for bit against the pattern's rows on the device, those against the
+oracle, and the bias gradient against the oracle's pattern rows weighted by how often each
+occurs.  (Epilogs as in "Fusing Matmul Epilogs with nvmath-python"; dSwiGLU as in the
 gemm_swiglu_mlp_fusion.py docstring.)"""
 import numpy as np
 import pytest
@@ -158,4 +162,78 @@ def test_dswiglu_at_max_ld():
     assert untouched16(dgbuf, N) and untouched16(dubuf, N), "a write outside d_gate / d_up"
     p.free()
     del dout, wd, gate, up, dg, dgbuf, du, dubuf
+    free()
+
+
+MMAX = (1 << 31) - 1      # the largest M the C ABI accepts
+P = 7                     # period of the rows at MMAX (divides neither 32 nor 256)
+
+
+def periodic(pattern, rows, dev):
+    """rows x c tensor on the device whose row r is pattern[r % P]"""
+    reps = -(-rows // P)
+    return pattern.to(dev).repeat(reps, 1)[:rows]
+
+
+def rows_repeat(t):
+    """every row of t (M x c, c * elem_size a multiple of 8 bytes) equals row r % P, bit for bit"""
+    v = t.view(torch.int64) if t.element_size() * t.shape[1] % 8 == 0 else t.view(torch.int32)
+    full = (v.shape[0] // P) * P
+    ok = bool((v[:full].view(-1, P, v.shape[1]) == v[:P].unsqueeze(0)).all().item())
+    return ok and bool((v[full:] == v[:v.shape[0] - full]).all().item())
+
+
+def counts():
+    """how many of the MMAX rows repeat each pattern row"""
+    c = np.full(P, MMAX // P, dtype=np.float64)
+    c[:MMAX % P] += 1
+    return c
+
+
+@pytest.mark.parametrize("path", ["fused", "unfused"])
+def test_relu_aux_bias_at_max_m(path):
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev, dt = torch.device("cuda"), torch.float16
+    n = k = 8
+    say(f"case max-m RELU_AUX_BIAS f16 KN path={path} m={MMAX} n={n} k={k}")
+    pat_h, w_h, bias_h = randn((P, k), 21, 1.0, dt), randn((k, n), 22, k ** -0.5, dt), randn((n,), 23, 0.1, dt)
+    x = periodic(pat_h, MMAX, dev)
+    w, bias = w_h.to(dev), bias_h.to(dev)
+    p = ep.Plan(x, w, "RELU_AUX_BIAS", {"bias": bias}, b_layout="KN", path=path)
+    y, aux = p.execute()
+    torch.cuda.synchronize()
+    del x
+    yref, _, pre = oracle.relu_aux_bias(f64(pat_h), f64(w_h), f64(bias_h), "KN")
+    assert_half(f64(y[:P].contiguous()), yref, f"max-m RELU_AUX_BIAS {path} pattern rows")
+    ok, info = oracle.check_mask(words(aux["relu_aux"][:P].contiguous()), pre)
+    assert ok, f"max-m RELU_AUX_BIAS {path} mask: {info}"
+    assert rows_repeat(y), "an output row differs from its pattern row"
+    assert rows_repeat(aux["relu_aux"]), "a mask row differs from its pattern row"
+    p.free()
+    del y, aux, p
+    free()
+
+
+def test_drelu_bgrad_at_max_m():
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev, dt = torch.device("cuda"), torch.bfloat16
+    n = k = 8
+    say(f"case max-m DRELU_BGRAD bf16 NK m={MMAX} n={n} k={k}")
+    dy_pat, w_h = randn((P, k), 24, 1.0, dt), randn((n, k), 25, k ** -0.5, dt)
+    mask_pat = torch.from_numpy(oracle.pack_relu_mask(randn((P, n), 26, 1.0, torch.float32).numpy() > 0)
+                                .view(np.int32).copy())
+    dy = periodic(dy_pat, MMAX, dev)
+    mask = periodic(mask_pat, MMAX, dev)
+    p = ep.Plan(dy, w_h.to(dev), "DRELU_BGRAD", {"relu_aux": mask}, b_layout="NK")
+    dx, auxo = p.execute()
+    torch.cuda.synchronize()
+    del dy, mask
+    dref, _ = oracle.drelu_bgrad(f64(dy_pat), f64(w_h), "NK", words(mask_pat))
+    assert_half(f64(dx[:P].contiguous()), dref, "max-m DRELU_BGRAD pattern rows")
+    assert rows_repeat(dx), "a dX row differs from its pattern row"
+    assert_bgrad(auxo["drelu_bgrad"].cpu().numpy().astype(np.float64), counts() @ dref, "max-m DRELU_BGRAD bgrad")
+    p.free()
+    del dx, auxo, p
     free()

@@ -119,3 +119,18 @@ def test_refusals():
         ep.describe_plan(16384, 17408, 5120, "DSWIGLU", BF16, b_layout="KN", split_k=2, split_tail=True)
     with pytest.raises(ep.EPError, match="EP_ERR_INVALID_ARG"):
         ep.describe_plan(0, 256, 256)
+
+
+def test_largest_grids():
+    """M = 2^31 - 1 rows plan on 256-row tiles (2^23 workgroups: 2^31 threads); 128-row tiles
+    would need 2^32 threads in one launch, more than a launch can count, and are refused, as is
+    a grid of 2^31 - 1 by 2^22 - 8 outputs (the widest D a leading dimension below 2^22 allows)."""
+    mmax = (1 << 31) - 1
+    f = fields(ep.describe_plan(mmax, 8, 8, "RELU_AUX_BIAS", F16, b_layout="KN"))
+    assert f["grid"] == "8388608x1" and f["tile"].startswith("256x"), f
+    f = fields(ep.describe_plan(mmax, 8, 8, "DRELU_BGRAD", BF16, b_layout="NK"))
+    assert int(f["workspace_bytes"]) == 8388608 * 8 * 4, f
+    with pytest.raises(ep.EPError, match="EP_ERR_UNSUPPORTED.*exceeds one launch"):
+        ep.describe_plan(mmax, 8, 8, "DEFAULT", F16, b_layout="KN", tile_cfg=1)
+    with pytest.raises(ep.EPError, match="EP_ERR_UNSUPPORTED.*exceeds one launch"):
+        ep.describe_plan(mmax, (1 << 22) - 8, 8, "DEFAULT", F16, b_layout="NK")
