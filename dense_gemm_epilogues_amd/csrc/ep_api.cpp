@@ -318,8 +318,10 @@ ep_status validate(const ep_shape* s, ep_dtype dtype, ep_epilog epi, const ep_ep
   if (s->a_layout == EP_A_KM && epi != EP_EPILOG_DEFAULT)
     return fail(EP_ERR_UNSUPPORTED, "a K x M A operand is supported with the DEFAULT epilog only");
   if (s->m < 1 || s->n < 1 || s->k < 1) return fail(EP_ERR_INVALID_ARG, "m, n, k must be >= 1");
-  if (s->m >= kMaxDim || s->n >= kMaxDim || s->k >= kMaxDim)
-    return fail(EP_ERR_UNSUPPORTED, "m, n, k must be < 2^31");
+  if (s->m >= kMaxDim || s->n >= kMaxDim) return fail(EP_ERR_UNSUPPORTED, "m and n must be < 2^31");
+  // the kernels form k-offsets as (k-step index) x (k-step depth <= 64) in 32 bits, including
+  // the index one past the last k-step
+  if (s->k > kMaxDim - 64) return fail(EP_ERR_UNSUPPORTED, "k must be <= 2^31 - 64");
   if (s->n % 8 || s->k % 8) return fail(EP_ERR_UNSUPPORTED, "n and k must be multiples of 8");
   if (s->a_layout == EP_A_KM && s->m % 8) return fail(EP_ERR_UNSUPPORTED, "a K x M A needs m % 8 == 0");
   if (opt) {

@@ -199,9 +199,10 @@ typedef struct {
 /*
  * ep_plan: validate the request, pick a tile configuration, allocate the workspace and
  * bind all pointers.  Checks, in order, before any HIP call: non-null handle out-pointer
- * and shape; 1 <= m, n, k < 2^31; n % 8 == 0 and k % 8 == 0; the pointers the epilog needs
- * are non-null and the ones it does not use are null; a, b, b2, d, d2, bias, gate, up are
- * 16-byte aligned and relu_aux/relu_aux_in/bgrad 4-byte aligned; every leading dimension is
+ * and shape; 1 <= m, n < 2^31 and 1 <= k <= 2^31 - 64; n % 8 == 0 and k % 8 == 0; the
+ * pointers the epilog needs are non-null and the ones it does not use are null; a, b, b2, d,
+ * d2, bias, gate, up are 16-byte aligned and relu_aux/relu_aux_in/bgrad 4-byte aligned; every
+ * leading dimension is
  * a multiple of 8 elements, at least the row length and below 2^22; ld_aux >= ceil(n/32).
  * A plan whose GEMM grid would need 2^32 or more threads in one launch (for instance m near
  * 2^31 with a 128-row tile configuration) is EP_ERR_UNSUPPORTED.

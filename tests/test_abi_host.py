@@ -83,6 +83,7 @@ CASES = [
     ("n not multiple of 8", lambda L: plan(L, shape(n=60, ldd=64, ldb=64))[0], UNSUPPORTED),
     ("k not multiple of 8", lambda L: plan(L, shape(k=60, lda=64))[0], UNSUPPORTED),
     ("m >= 2^31", lambda L: plan(L, shape(m=1 << 31))[0], UNSUPPORTED),
+    ("k > 2^31 - 64", lambda L: plan(L, shape(k=(1 << 31) - 56))[0], UNSUPPORTED),
     ("unknown dtype", lambda L: plan(L, shape(), dtype=7)[0], UNSUPPORTED),
     ("unknown epilog", lambda L: plan(L, shape(), epi=11)[0], UNSUPPORTED),
     ("SWIGLU_AUX without d2", lambda L: plan(L, shape(lay=NK), E["SWIGLU_AUX"], ep_epilog_io(b2=X_PTR))[0], INVALID),

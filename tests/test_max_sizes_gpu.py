@@ -10,7 +10,8 @@ writes.  At M = 2^31 - 1 (N = K = 8: 32 GiB per operand) tile and row indices re
 of the 32-bit range; the rows repeat a 7-row pattern, so that every one of the 2^31 - 1 output
 rows is checked bit for bit against the pattern's rows on the device, those against the
 oracle, and the bias gradient against the oracle's pattern rows weighted by how often each
-occurs.  (Epilogs as in "Fusing Matmul Epilogs with nvmath-python"; dSwiGLU as in the
+occurs.  At K = 2^31 - 64 (A given K x M, B K x N) the k-offsets reach the top of the 32-bit
+range; that case is built so that float32 accumulation is exact (see its test).  (Epilogs as in "Fusing Matmul Epilogs with nvmath-python"; dSwiGLU as in the
 gemm_swiglu_mlp_fusion.py docstring.)"""
 import numpy as np
 import pytest
@@ -170,8 +171,8 @@ P = 7                     # period of the rows at MMAX (divides neither 32 nor 2
 
 
 def periodic(pattern, rows, dev):
-    """rows x c tensor on the device whose row r is pattern[r % P]"""
-    reps = -(-rows // P)
+    """rows x c tensor on the device whose row r is pattern[r % len(pattern)]"""
+    reps = -(-rows // pattern.shape[0])
     return pattern.to(dev).repeat(reps, 1)[:rows]
 
 
@@ -236,4 +237,37 @@ def test_drelu_bgrad_at_max_m():
     assert_bgrad(auxo["drelu_bgrad"].cpu().numpy().astype(np.float64), counts() @ dref, "max-m DRELU_BGRAD bgrad")
     p.free()
     del dx, auxo, p
+    free()
+
+
+KMAX = (1 << 31) - 64     # the largest K the C ABI accepts
+
+
+def test_transposed_a_at_max_k():
+    """K = 2^31 - 64 with A given K x M and B K x N (M = N = 8, 32 GiB per operand; the plan
+    splits the one tile's K range 8 ways).  The rows of A and B repeat a 6-row pattern of
+    -1 / 0 / 1 entries whose second half negates A's first half and repeats B's, so every run
+    of whole periods sums to exactly zero, every partial sum is a small integer (exact in
+    float32 whatever the order and the split), and the product is the sum over the pattern's
+    first K mod 6 rows: the result must equal the oracle's bit for bit."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev, dt = torch.device("cuda"), torch.float16
+    m = n = 8
+    say(f"case max-k DEFAULT A^T f16 KN m={m} n={n} k={KMAX}")
+    g = torch.Generator().manual_seed(31)
+    a3 = torch.randint(-1, 2, (3, m), generator=g).to(dt)
+    b3 = torch.randint(-1, 2, (3, n), generator=g).to(dt)
+    a_pat, b_pat = torch.cat([a3, -a3]), torch.cat([b3, b3])
+    at, b = periodic(a_pat, KMAX, dev), periodic(b_pat, KMAX, dev)
+    p = ep.Plan(at, b, "DEFAULT", b_layout="KN", a_layout="KM")
+    assert "splits=8" in p.info(), p.info()
+    y, _ = p.execute()
+    torch.cuda.synchronize()
+    r = KMAX % 6
+    ref = oracle.matmul(f64(a_pat[:r]).T, f64(b_pat[:r]), "KN")
+    assert np.abs(ref).max() > 0, "the expected product is not all zeros"
+    assert np.array_equal(f64(y.contiguous()), ref), (f64(y.contiguous()), ref)
+    p.free()
+    del at, b, y, p
     free()

@@ -134,3 +134,13 @@ def test_largest_grids():
         ep.describe_plan(mmax, 8, 8, "DEFAULT", F16, b_layout="KN", tile_cfg=1)
     with pytest.raises(ep.EPError, match="EP_ERR_UNSUPPORTED.*exceeds one launch"):
         ep.describe_plan(mmax, (1 << 22) - 8, 8, "DEFAULT", F16, b_layout="NK")
+
+
+def test_longest_k():
+    """K up to 2^31 - 64 (A given K x M and B K x N, the one layout pair whose leading
+    dimensions do not bound K): one 8 x 8 tile, split into the most ranges."""
+    kmax = (1 << 31) - 64
+    f = fields(ep.describe_plan(8, 8, kmax, "DEFAULT", F16, b_layout="KN", a_layout="KM"))
+    assert (f["grid"], f["splits"]) == ("1x1", "8"), f
+    with pytest.raises(ep.EPError, match="EP_ERR_UNSUPPORTED.*k must be"):
+        ep.describe_plan(8, 8, kmax + 8, "DEFAULT", F16, b_layout="KN", a_layout="KM")
