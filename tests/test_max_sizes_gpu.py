@@ -271,3 +271,49 @@ def test_transposed_a_at_max_k():
     p.free()
     del at, b, y, p
     free()
+
+
+NMAX = (1 << 22) - 8      # the widest N: ldd >= N and every leading dimension is below 2^22
+
+
+def test_relu_aux_bias_at_max_n():
+    """N = 2^22 - 8 output columns (16384 column tiles, 131072 mask words per row) against the
+    oracle in full."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev, dt = torch.device("cuda"), torch.float16
+    m, k = 8, 24
+    say(f"case max-n RELU_AUX_BIAS f16 KN m={m} n={NMAX} k={k}")
+    x_h, w_h, bias_h = randn((m, k), 41, 1.0, dt), randn((k, NMAX), 42, k ** -0.5, dt), randn((NMAX,), 43, 0.1, dt)
+    p = ep.Plan(x_h.to(dev), w_h.to(dev), "RELU_AUX_BIAS", {"bias": bias_h.to(dev)}, b_layout="KN")
+    y, aux = p.execute()
+    torch.cuda.synchronize()
+    yref, _, pre = oracle.relu_aux_bias(f64(x_h), f64(w_h), f64(bias_h), "KN")
+    assert_half(f64(y), yref, "max-n RELU_AUX_BIAS Y")
+    ok, info = oracle.check_mask(words(aux["relu_aux"]), pre)
+    assert ok, f"max-n RELU_AUX_BIAS mask: {info}"
+    p.free()
+    del y, aux, p
+    free()
+
+
+def test_drelu_bgrad_at_max_n():
+    """DRELU_BGRAD over N = 2^22 - 8 columns (B given N x K): dX and every bias-gradient column
+    against the oracle."""
+    require_gpu()
+    import dense_gemm_epilogues_amd as ep
+    dev, dt = torch.device("cuda"), torch.bfloat16
+    m, k = 16, 16
+    say(f"case max-n DRELU_BGRAD bf16 NK m={m} n={NMAX} k={k}")
+    dy_h, w_h = randn((m, k), 44, 1.0, dt), randn((NMAX, k), 45, k ** -0.5, dt)
+    mask_h = torch.from_numpy(oracle.pack_relu_mask(randn((m, NMAX), 46, 1.0, torch.float32).numpy() > 0)
+                              .view(np.int32).copy())
+    p = ep.Plan(dy_h.to(dev), w_h.to(dev), "DRELU_BGRAD", {"relu_aux": mask_h.to(dev)}, b_layout="NK")
+    dx, auxo = p.execute()
+    torch.cuda.synchronize()
+    dref, bref = oracle.drelu_bgrad(f64(dy_h), f64(w_h), "NK", words(mask_h))
+    assert_half(f64(dx), dref, "max-n DRELU_BGRAD dX")
+    assert_bgrad(auxo["drelu_bgrad"].cpu().numpy().astype(np.float64), bref, "max-n DRELU_BGRAD bgrad")
+    p.free()
+    del dx, auxo, p
+    free()
