@@ -204,10 +204,14 @@ __global__ void colsum_partial_kernel(const char* x, int64_t ldx, float* part, i
 // a 2^31-row matrix, 524288 per row group, drift by about 1e-3 relative.
 constexpr int kBgColsPerBlock = 64;
 constexpr int kBgGroups = kEwThreads / (kBgColsPerBlock / 4);
+// (Once a running sum is infinite or NaN, its compensation is reset to zero: (inf - inf) would
+// otherwise turn an infinite sum into NaN, where plain summation keeps the infinity.)
 __device__ __forceinline__ void kahan_add(f32x4& s, f32x4& c, f32x4 v) {
   const f32x4 y = v - c;
   const f32x4 t = s + y;
-  c = (t - s) - y;
+  const f32x4 e = (t - s) - y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = __builtin_isfinite(t[i]) ? e[i] : 0.0f;
   s = t;
 }
 __global__ __launch_bounds__(kEwThreads) void bgrad_reduce_kernel(const float* part, int nparts, float* bgrad, int N) {
