@@ -54,6 +54,14 @@ def free():
     torch.cuda.empty_cache()
 
 
+def require_free(gib):
+    """skip unless the device has `gib` GiB free (the 2^31-row and 2^31-deep cases hold two or
+    three 32 GiB operands; an MI355X has 288 GB)"""
+    free()
+    if torch.cuda.mem_get_info()[0] < gib << 30:
+        pytest.skip(f"needs {gib} GiB of free device memory")
+
+
 @pytest.mark.parametrize("path", ["fused", "unfused"])
 def test_relu_aux_bias_at_max_ld(path):
     require_gpu()
@@ -194,6 +202,7 @@ def counts():
 @pytest.mark.parametrize("path", ["fused", "unfused"])
 def test_relu_aux_bias_at_max_m(path):
     require_gpu()
+    require_free(90)
     import dense_gemm_epilogues_amd as ep
     dev, dt = torch.device("cuda"), torch.float16
     n = k = 8
@@ -218,6 +227,7 @@ def test_relu_aux_bias_at_max_m(path):
 
 def test_drelu_bgrad_at_max_m():
     require_gpu()
+    require_free(90)
     import dense_gemm_epilogues_amd as ep
     dev, dt = torch.device("cuda"), torch.bfloat16
     n = k = 8
@@ -251,6 +261,7 @@ def test_transposed_a_at_max_k():
     float32 whatever the order and the split), and the product is the sum over the pattern's
     first K mod 6 rows: the result must equal the oracle's bit for bit."""
     require_gpu()
+    require_free(70)
     import dense_gemm_epilogues_amd as ep
     dev, dt = torch.device("cuda"), torch.float16
     m = n = 8
