@@ -231,7 +231,9 @@ int choose_cfg(int64_t m, int64_t n, bool dual, ep_b_layout lay, int cus) {
 // 5120 at M 2048 and 16384, the split dx GEMM at K 34816) and the square layer, 0.5-1 %
 // slower on the 65536 x 8192 x 16384 forward (K 16384, 32 rounds).  With A given K x M as
 // well (the weight gradients, K 2048) it measured 2-2.5 % faster at 5120 x 17408 and
-// 34816 x 5120 and on par at 17408 x 5120; with A K x M and B N x K, 0.2-0.6 % slower.
+// 34816 x 5120 and on par at 17408 x 5120; with A K x M and B N x K, 0.2-0.6 % slower.  With
+// B given N x K (A M x K) the two measured equal within 0.1 % at 65536 x 16384 x 8192, 4096^3
+// and 16384^2 x 4096 (A/B runs alternating their order), so those keep configuration 11.
 constexpr int kVstCfg = 8;
 constexpr int kM16SpreadCfg = 9;
 constexpr int kM16RowsCfg = 10;
