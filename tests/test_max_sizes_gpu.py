@@ -244,7 +244,11 @@ def test_drelu_bgrad_at_max_m():
     dref, _ = oracle.drelu_bgrad(f64(dy_pat), f64(w_h), "NK", words(mask_pat))
     assert_half(f64(dx[:P].contiguous()), dref, "max-m DRELU_BGRAD pattern rows")
     assert rows_repeat(dx), "a dX row differs from its pattern row"
-    assert_bgrad(auxo["drelu_bgrad"].cpu().numpy().astype(np.float64), counts() @ dref, "max-m DRELU_BGRAD bgrad")
+    # over 8.4 million partials a plain float32 second pass drifts by about 1.3e-3 relative on
+    # this input (a CPU emulation of its order); the compensated one must stay within 1e-4
+    ok, info = oracle.check_bgrad(auxo["drelu_bgrad"].cpu().numpy().astype(np.float64), counts() @ dref, rel_tol=1e-4)
+    say(f"max-m DRELU_BGRAD bgrad {info}")
+    assert ok, f"max-m DRELU_BGRAD bgrad: {info}"
     p.free()
     del dx, auxo, p
     free()
